@@ -1,0 +1,185 @@
+"""Python binding of the C ABI (include/dspark.h): argument marshalling only.
+
+Every step of the forward runs in libdspark.so. torch supplies device memory
+and the current HIP stream; nothing here computes the method. Outputs and the
+workspace are allocated with torch when the caller does not pass them.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
+    "version", "kernel_names", "trace_begin", "trace_end", "DsparkError",
+]
+
+DsparkError = L.DsparkError
+
+_TORCH_DTYPE = {L.F32: torch.float32, L.BF16: torch.bfloat16}
+LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down")
+
+
+@dataclasses.dataclass
+class DsparkDims:
+    m: int
+    H: int
+    d: int
+    n_heads: int
+    gamma: int
+    n_layers: int
+    ff: int
+    eps: float = 1e-6
+    dtype: str = "bf16"      # "bf16" or "f32": storage of the long tensors
+
+    @property
+    def code(self) -> int:
+        return {"f32": L.F32, "bf16": L.BF16}[self.dtype]
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPE[self.code]
+
+    def c(self) -> L.Dims:
+        return L.Dims(self.m, self.H, self.d, self.n_heads, self.gamma, self.n_layers, self.ff,
+                      float(self.eps), self.code)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _cu_host(cu) -> ctypes.Array:
+    vals = [int(v) for v in (cu.tolist() if hasattr(cu, "tolist") else cu)]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def version() -> str:
+    return L.lib().dspark_version().decode()
+
+
+def kernel_names() -> List[str]:
+    lib = L.lib()
+    return [lib.dspark_kernel_name(i).decode() for i in range(lib.dspark_kernel_kinds())]
+
+
+def workspace_size(op: int, dims: DsparkDims, cu) -> int:
+    cu_h = _cu_host(cu)
+    A = len(cu_h) - 1
+    dm = dims.c()
+    n = L.lib().dspark_workspace_size(op, ctypes.byref(dm), A, cu_h)
+    if n == 0:
+        raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+    return int(n)
+
+
+def _workspace(op, dims, cu, ws, device):
+    need = workspace_size(op, dims, cu)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _tap_ptrs(taps) -> ctypes.Array:
+    if isinstance(taps, torch.Tensor):
+        taps = list(taps.unbind(0))
+    return (ctypes.c_void_p * len(taps))(*[t.data_ptr() for t in taps])
+
+
+def _tap_ld(taps) -> int:
+    t0 = taps[0] if not isinstance(taps, torch.Tensor) else taps[0]
+    return int(t0.stride(0))
+
+
+def _cu_dev(cu, cu_dev, device):
+    if cu_dev is not None:
+        return cu_dev
+    return torch.as_tensor([int(v) for v in (cu.tolist() if hasattr(cu, "tolist") else cu)],
+                           dtype=torch.int32, device=device)
+
+
+def _layer_struct(lw: Dict[str, torch.Tensor]) -> L.LayerWeights:
+    return L.LayerWeights(*[_ptr(lw[k]) for k in LAYER_KEYS])
+
+
+def ctx_fuse(dims: DsparkDims, cu, taps, w_c, ctx_norm, *, cu_dev=None, h_ctx=None, ws=None,
+             stream=None) -> torch.Tensor:
+    """Eq 2: H_ctx [T, d] from the m tapped hidden states (list of [T, H] or [m, T, H])."""
+    device = w_c.device
+    cu_h = _cu_host(cu)
+    T = cu_h[len(cu_h) - 1]
+    if h_ctx is None:
+        h_ctx = torch.empty((T, dims.d), dtype=dims.torch_dtype, device=device)
+    cu_dev = _cu_dev(cu, cu_dev, device)
+    ws, nbytes = _workspace(L.OP_CTX_FUSE, dims, cu, ws, device)
+    dm = dims.c()
+    L.check(L.lib().dspark_ctx_fuse(ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev),
+                                    _tap_ptrs(taps), _tap_ld(taps), _ptr(w_c), _ptr(ctx_norm),
+                                    _ptr(h_ctx), _ptr(ws), nbytes, _stream(stream)))
+    return h_ctx
+
+
+def block_layer(dims: DsparkDims, cu, h_ctx, d_in, lw: Dict[str, torch.Tensor], *, cu_dev=None,
+                d_out=None, ws=None, stream=None) -> torch.Tensor:
+    """Eq 3 + FFN for one draft layer: block rows [A, gamma, d] float32 in and out."""
+    device = d_in.device
+    cu_h = _cu_host(cu)
+    if d_out is None:
+        d_out = torch.empty_like(d_in)
+    cu_dev = _cu_dev(cu, cu_dev, device)
+    ws, nbytes = _workspace(L.OP_BLOCK_LAYER, dims, cu, ws, device)
+    dm = dims.c()
+    lws = _layer_struct(lw)
+    L.check(L.lib().dspark_block_layer(ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev),
+                                       _ptr(h_ctx), _ptr(d_in), _ptr(d_out), ctypes.byref(lws),
+                                       _ptr(ws), nbytes, _stream(stream)))
+    return d_out
+
+
+def block_forward(dims: DsparkDims, cu, taps, w_c, ctx_norm, block_in, block_pos,
+                  layers: Sequence[Dict[str, torch.Tensor]], out_norm=None, *, cu_dev=None,
+                  h_ctx_out=None, block_out=None, ws=None, stream=None) -> torch.Tensor:
+    """The whole draft block (Eq 2, block init, every layer, output norm)."""
+    device = block_in.device
+    cu_h = _cu_host(cu)
+    if block_out is None:
+        block_out = torch.empty_like(block_in)
+    cu_dev = _cu_dev(cu, cu_dev, device)
+    ws, nbytes = _workspace(L.OP_BLOCK_FORWARD, dims, cu, ws, device)
+    dm = dims.c()
+    arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+    L.check(L.lib().dspark_block_forward(
+        ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev), _tap_ptrs(taps), _tap_ld(taps),
+        _ptr(w_c), _ptr(ctx_norm), _ptr(block_in), _ptr(block_pos), arr, _ptr(out_norm),
+        _ptr(h_ctx_out), _ptr(block_out), _ptr(ws), nbytes, _stream(stream)))
+    return block_out
+
+
+def trace_begin(kinds: Sequence[str], capacity: int = 4096) -> None:
+    """Record HIP events around every later launch of the named kernel kinds."""
+    names = kernel_names()
+    mask = 0
+    for k in kinds:
+        mask |= 1 << names.index(k)
+    L.check(L.lib().dspark_trace_begin(mask, capacity))
+
+
+def trace_end() -> Dict[str, tuple]:
+    """Stop tracing; {kind: (total_ms, launches)} for kinds that launched."""
+    names = kernel_names()
+    n = len(names)
+    tot = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    L.check(L.lib().dspark_trace_end(tot, cnt, n))
+    return {names[i]: (tot[i], cnt[i]) for i in range(n) if cnt[i] > 0}

@@ -1,0 +1,377 @@
+// Eq 3 block attention over [context ++ block], split over context chunks.
+//
+// The gamma block queries of sequence b attend to its L_b context keys and
+// its gamma block keys with no causal mask (module-dflash.ts, #layer). The
+// context part is long and read once per layer, so it is split into chunks
+// of `chunk` keys: one workgroup per (chunk, head) streams the chunk's K and
+// V once and leaves an unnormalised partial (m, l, o) per query, as the
+// split-chunk attention + combine kernels of dspark-runtime.js do. The
+// combine pass then adds the gamma block keys as one more partial and merges
+// all partials per (sequence, head) with the log-sum-exp identity:
+//   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  o = sum_c o_c 2^(m_c - M) / l.
+// Scores are kept in base 2: Q arrives pre-multiplied by hd^-1/2 * log2(e).
+//
+// Work split inside a chunk: each wave takes 64-key blocks. For Q.K^T lane t
+// owns key t and reads its whole key row (hd/E 16-byte vectors, one 1 KiB
+// wave-wide run each, see kv_layout.h). For P.V lane (kg, cp) owns two value
+// columns and R keys per load, so each V load is again one 1 KiB run; the
+// block's probabilities are broadcast through LDS. All arithmetic is float32
+// on the vector ALUs: with gamma <= 16 queries the arithmetic intensity is a
+// few flop per byte, far below the matrix-core ridge.
+#include "common.h"
+#include "kernels.h"
+#include "kv_layout.h"
+
+namespace dspark {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// keys per chunk: aim for ~2048 (chunk, head) workgroups, chunk in [256, 8192]
+int attention_chunk(int64_t T, int n_heads, int A) {
+  (void)A;
+  int64_t c = (T * n_heads + 2047) / 2048;
+  c = ((c + 63) / 64) * 64;
+  if (c < 256) c = 256;
+  if (c > 8192) c = 8192;
+  return (int)c;
+}
+
+// chunk_prefix[b] = sum_{b' < b} ceil(L_b' / chunk), b = 0..A (one workgroup).
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int A, int chunk,
+                                                   int32_t* __restrict__ prefix) {
+  __shared__ int32_t sums[256];
+  const int tid = threadIdx.x;
+  const int per = (A + 255) / 256;
+  const int b0 = tid * per, b1 = min(A, b0 + per);
+  int32_t local = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t L = cu[b + 1] - cu[b];
+    local += L > 0 ? (L + chunk - 1) / chunk : 0;
+  }
+  sums[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {   // inclusive scan
+    const int32_t v = tid >= off ? sums[tid - off] : 0;
+    __syncthreads();
+    sums[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid > 0 ? sums[tid - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    prefix[b] = run;
+    const int32_t L = cu[b + 1] - cu[b];
+    run += L > 0 ? (L + chunk - 1) / chunk : 0;
+  }
+  if (tid == 255) prefix[A] = sums[255];
+}
+
+hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
+                       hipStream_t s) {
+  trace_pre(K_PLAN, s);
+  plan_kernel<<<1, 256, 0, s>>>(cu_dev, A, chunk, chunk_prefix);
+  trace_post(K_PLAN, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// partial kernel: grid (total_chunks, n_heads), 256 threads (4 waves)
+// part_o  [total_chunks][n_heads][G][HD]   unnormalised output
+// part_ml [total_chunks][n_heads][G][2]    (max, sum) in base-2 units
+// ---------------------------------------------------------------------------
+template <typename S, int HD, int G>
+__global__ __launch_bounds__(256) void attn_partial_kernel(
+    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads,
+    int layer, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A,
+    int chunk, int total_chunks, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using L = KVLayout<S>;
+  constexpr int E = L::E, R = L::R;
+  constexpr int NKV = HD / E;            // K vectors per key row
+  constexpr int KG = 128 / HD;           // key groups in the P.V lane split
+  constexpr int NLD = 64 / (KG * R);     // V loads per 64-key block
+  constexpr int d_model_unused = 0;
+  (void)d_model_unused;
+
+  __shared__ __attribute__((aligned(16))) float qs[G][HD];
+  __shared__ __attribute__((aligned(16))) float ps[4][G][64];
+  __shared__ float red_m[4][G];
+  __shared__ float red_l[4][G];
+  __shared__ __attribute__((aligned(16))) float red_o[4][G][HD];
+
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dev_total = prefix[A];
+  if (tile >= total_chunks || tile >= dev_total) return;
+
+  // sequence owning this chunk: largest b with prefix[b] <= tile
+  int lo = 0, hi = A - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int c = tile - prefix[b];
+  const int64_t k0 = (int64_t)cu[b] + (int64_t)c * chunk;
+  const int64_t k1 = min((int64_t)cu[b + 1], k0 + chunk);
+
+  const int d = HD * n_heads;
+  for (int i = tid; i < G * HD; i += 256) {
+    const int j = i / HD, cc = i % HD;
+    qs[j][cc] = Q[(int64_t)(b * G + j) * d + h * HD + cc];
+  }
+  __syncthreads();
+
+  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, h, n_heads, Tpad, HD);
+  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, h, n_heads, Tpad, HD);
+
+  float m_run[G], l_run[G];
+  float o[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+    o[j][0] = o[j][1] = 0.f;
+  }
+  const int kg = lane / (HD / 2), cp = lane % (HD / 2);
+
+  const int64_t blk0 = k0 >> 6, blk1 = (k1 - 1) >> 6;
+  for (int64_t blk = blk0 + wave; blk <= blk1; blk += 4) {
+    // ---- scores: lane owns key blk*64 + lane
+    const int64_t key = blk * 64 + lane;
+    const bool valid = key >= k0 && key < k1;
+    const S* kp = Kh + blk * 64 * HD + lane * E;
+    float s[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s[j] = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < NKV; ++i) {
+      float kf[E];
+      Vec16<S>::unpack(ld16(kp + i * 64 * E), kf);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qs[j][i * E + e]);
+          s[j] = fmaf(q4[0], kf[e], s[j]);
+          s[j] = fmaf(q4[1], kf[e + 1], s[j]);
+          s[j] = fmaf(q4[2], kf[e + 2], s[j]);
+          s[j] = fmaf(q4[3], kf[e + 3], s[j]);
+        }
+      }
+    }
+    // ---- online softmax over this block (wave-uniform max)
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float sv = valid ? s[j] : kNegInf;
+      const float bm = wave_max(sv);
+      const float mn = fmaxf(m_run[j], bm);
+      const float alpha = exp2f(m_run[j] - mn);   // 0 when m_run = -inf
+      const float p = exp2f(sv - mn);             // 0 for masked keys
+      l_run[j] = l_run[j] * alpha + p;
+      o[j][0] *= alpha;
+      o[j][1] *= alpha;
+      m_run[j] = mn;
+      ps[wave][j][lane] = p;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per load
+    const S* vp = Vh + blk * 64 * HD + lane * E;
+#pragma unroll 4
+    for (int ld = 0; ld < NLD; ++ld) {
+      float vf[E];
+      Vec16<S>::unpack(ld16(vp + ld * 64 * E), vf);
+      const int kb = ld * KG * R + kg * R;   // first key of this vector
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float pr[R];
+        if constexpr (R == 4) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(&ps[wave][j][kb]);
+          pr[0] = p4[0]; pr[1] = p4[1]; pr[2] = p4[2]; pr[3] = p4[3];
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) pr[r] = ps[wave][j][kb + r];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          o[j][0] = fmaf(pr[r], vf[2 * r], o[j][0]);
+          o[j][1] = fmaf(pr[r], vf[2 * r + 1], o[j][1]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- per-wave totals: l over lanes, o over key groups
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float lw = wave_sum(l_run[j]);
+    float o0 = o[j][0], o1 = o[j][1];
+#pragma unroll
+    for (int off = HD / 2; off < 64; off <<= 1) {
+      o0 += __shfl_xor(o0, off, kWave);
+      o1 += __shfl_xor(o1, off, kWave);
+    }
+    if (lane == 0) {
+      red_m[wave][j] = m_run[j];
+      red_l[wave][j] = lw;
+    }
+    if (kg == 0) {
+      red_o[wave][j][2 * cp] = o0;
+      red_o[wave][j][2 * cp + 1] = o1;
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the four waves and write this chunk's partial
+  const int64_t pbase = ((int64_t)tile * n_heads + h) * G;
+  for (int i = tid; i < G * HD; i += 256) {
+    const int j = i / HD, cc = i % HD;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][j]);
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (red_m[w][j] != kNegInf) acc += red_o[w][j][cc] * exp2f(red_m[w][j] - M);
+    part_o[(pbase + j) * HD + cc] = acc;
+  }
+  if (tid < G) {
+    const int j = tid;
+    float M = kNegInf;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][j]);
+    float l = 0.f;
+    for (int w = 0; w < 4; ++w)
+      if (red_m[w][j] != kNegInf) l += red_l[w][j] * exp2f(red_m[w][j] - M);
+    part_ml[(pbase + j) * 2 + 0] = M;
+    part_ml[(pbase + j) * 2 + 1] = l;
+  }
+}
+
+template <typename S, int HD, int G>
+static void launch_attn_t(dim3 grid, hipStream_t s, const float* Q, const KVDesc& kv, int layer,
+                          const int32_t* cu, const int32_t* prefix, int A, int chunk, int total,
+                          float* po, float* pml) {
+  attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(Q, static_cast<const S*>(kv.base), kv.Tpad,
+                                                      kv.n_heads, layer, cu, prefix, A, chunk,
+                                                      total, po, pml);
+}
+
+template <typename S, int HD>
+static bool dispatch_gamma(int gamma, dim3 grid, hipStream_t s, const float* Q, const KVDesc& kv,
+                           int layer, const int32_t* cu, const int32_t* prefix, int A, int chunk,
+                           int total, float* po, float* pml) {
+  switch (gamma) {
+#define DSPARK_G(g) \
+  case g: launch_attn_t<S, HD, g>(grid, s, Q, kv, layer, cu, prefix, A, chunk, total, po, pml); return true;
+    DSPARK_G(1) DSPARK_G(2) DSPARK_G(3) DSPARK_G(4) DSPARK_G(5) DSPARK_G(6) DSPARK_G(7)
+    DSPARK_G(8) DSPARK_G(9) DSPARK_G(10) DSPARK_G(11) DSPARK_G(12) DSPARK_G(13) DSPARK_G(14)
+    DSPARK_G(15) DSPARK_G(16)
+#undef DSPARK_G
+    default: return false;
+  }
+}
+
+hipError_t launch_attention(int dtype, const float* Q, const KVDesc& kv, int layer,
+                            const int32_t* cu_dev, const int32_t* chunk_prefix, int A, int gamma,
+                            int chunk, int total_chunks, float* part_o, float* part_ml,
+                            hipStream_t s) {
+  if (total_chunks == 0) return hipSuccess;
+  dim3 grid(total_chunks, kv.n_heads);
+  bool ok = false;
+  trace_pre(K_ATTN, s);
+  if (dtype == 1) {
+    if (kv.hd == 128) ok = dispatch_gamma<bf16, 128>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+    else if (kv.hd == 64) ok = dispatch_gamma<bf16, 64>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+    else if (kv.hd == 32) ok = dispatch_gamma<bf16, 32>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+  } else {
+    if (kv.hd == 128) ok = dispatch_gamma<float, 128>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+    else if (kv.hd == 64) ok = dispatch_gamma<float, 64>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+    else if (kv.hd == 32) ok = dispatch_gamma<float, 32>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+  }
+  trace_post(K_ATTN, s);
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// combine: grid (A, n_heads), 256 threads. Adds the gamma block keys (K_d,
+// V_d in float32) as one more partial, merges every chunk partial of the
+// sequence, normalises, writes attn[b*gamma + j][h*hd + c].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
+    int A, int gamma, int d, int n_heads, const int32_t* __restrict__ prefix, int total_chunks,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    float* __restrict__ attn) {
+  __shared__ float sb[kMaxGamma][kMaxGamma];   // block-key probabilities (unnormalised)
+  __shared__ float mb[kMaxGamma];              // block-key max per query
+  __shared__ float Mq[kMaxGamma];              // overall max per query
+  __shared__ float inv_l[kMaxGamma];
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int hd = d / n_heads;
+  const int tid = threadIdx.x;
+  const int c0 = min(prefix[b], total_chunks), c1 = min(prefix[b + 1], total_chunks);
+
+  // block-key scores: thread (j, jj) for j, jj < gamma (gamma^2 <= 256)
+  if (tid < gamma * gamma) {
+    const int j = tid / gamma, jj = tid % gamma;
+    const float* q = Q + (int64_t)(b * gamma + j) * d + h * hd;
+    const float* k = Kd + (int64_t)(b * gamma + jj) * d + h * hd;
+    float sc = 0.f;
+    for (int cc = 0; cc < hd; ++cc) sc = fmaf(q[cc], k[cc], sc);
+    sb[j][jj] = sc;
+  }
+  __syncthreads();
+  if (tid < gamma) {
+    const int j = tid;
+    float m = kNegInf;
+    for (int jj = 0; jj < gamma; ++jj) m = fmaxf(m, sb[j][jj]);
+    mb[j] = m;
+    float M = m;
+    for (int c = c0; c < c1; ++c) M = fmaxf(M, part_ml[(((int64_t)c * n_heads + h) * gamma + j) * 2]);
+    Mq[j] = M;
+    float l = 0.f;
+    for (int jj = 0; jj < gamma; ++jj) l += exp2f(sb[j][jj] - M);
+    for (int c = c0; c < c1; ++c) {
+      const float* ml = part_ml + (((int64_t)c * n_heads + h) * gamma + j) * 2;
+      l += ml[1] * exp2f(ml[0] - M);
+    }
+    inv_l[j] = 1.f / l;
+  }
+  __syncthreads();
+  if (tid < gamma * gamma) {
+    const int j = tid / gamma, jj = tid % gamma;
+    sb[j][jj] = exp2f(sb[j][jj] - Mq[j]);
+  }
+  __syncthreads();
+  for (int i = tid; i < gamma * hd; i += 256) {
+    const int j = i / hd, cc = i % hd;
+    const float M = Mq[j];
+    float acc = 0.f;
+    for (int jj = 0; jj < gamma; ++jj)
+      acc = fmaf(sb[j][jj], Vd[(int64_t)(b * gamma + jj) * d + h * hd + cc], acc);
+    for (int c = c0; c < c1; ++c) {
+      const int64_t pj = ((int64_t)c * n_heads + h) * gamma + j;
+      acc += part_o[pj * hd + cc] * exp2f(part_ml[pj * 2] - M);
+    }
+    attn[(int64_t)(b * gamma + j) * d + h * hd + cc] = acc * inv_l[j];
+  }
+}
+
+hipError_t launch_combine(const float* Q, const float* Kd, const float* Vd, int A, int gamma, int d,
+                          int n_heads, const int32_t* chunk_prefix, int total_chunks,
+                          const float* part_o, const float* part_ml, float* attn,
+                          hipStream_t s) {
+  dim3 grid(A, n_heads);
+  trace_pre(K_COMBINE, s);
+  combine_kernel<<<grid, 256, 0, s>>>(Q, Kd, Vd, A, gamma, d, n_heads, chunk_prefix, total_chunks,
+                                      part_o, part_ml, attn);
+  trace_post(K_COMBINE, s);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -1,0 +1,527 @@
+// C ABI of the draft-block library: argument checks, workspace planning and
+// the launch sequence of each entry point (include/dspark.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dspark.h"
+#include "kernels.h"
+
+namespace dspark {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_err;
+
+static dspark_status fail(dspark_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define DSPARK_HIP(expr)                                                             \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(DSPARK_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));       \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// tracing (per-kernel HIP events)
+// ---------------------------------------------------------------------------
+static const char* kNames[K_COUNT] = {
+    "prep_transpose", "gemm_ctx_fuse", "ctx_norm",   "rowstats",      "gemm_ctx_kv",
+    "attn_plan",      "attn_partial",  "attn_combine", "block_gemm",  "finish_qkv",
+    "finish_residual_norm", "finish_swiglu", "block_init"};
+
+const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
+
+struct Trace {
+  bool on = false;
+  uint64_t mask = 0;
+  int cap = 0;
+  int used = 0;
+  bool open = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;
+};
+static Trace g_trace;
+
+void trace_pre(int kind, hipStream_t s) {
+  Trace& t = g_trace;
+  if (!t.on || !((t.mask >> kind) & 1ull) || t.used >= t.cap) return;
+  (void)hipEventRecord(t.ev[2 * t.used], s);
+  t.open = true;
+}
+
+void trace_post(int kind, hipStream_t s) {
+  Trace& t = g_trace;
+  if (!t.on || !t.open) return;
+  (void)hipEventRecord(t.ev[2 * t.used + 1], s);
+  t.kind[t.used] = kind;
+  t.used += 1;
+  t.open = false;
+}
+
+// ---------------------------------------------------------------------------
+// planning
+// ---------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int64_t T = 0, Tpad = 0;
+  int hd = 0, M = 0, chunk = 0, total_chunks = 0, ctx_splits = 1, kv_layers = 0;
+  SkinnyPlan sk_qkv{}, sk_o{}, sk_gu{}, sk_down{};
+  size_t esz = 4;
+  // workspace offsets (bytes)
+  size_t wct = 0, wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
+  size_t D = 0, D2 = 0, U = 0, Q = 0, Kd = 0, Vd = 0, attn = 0, E = 0, Z = 0, hid = 0, skpart = 0;
+  size_t total = 0;
+};
+
+static int ctx_splits_for(int dtype, int64_t M, int N, int K) {
+  if (M <= 0) return 1;
+  const int bm = dtype == 1 ? (M >= 4096 ? 128 : 64) : 64;
+  const int bn = dtype == 1 ? 128 : 64;
+  const int bk = dtype == 1 ? 64 : 16;
+  const int64_t tiles = ((M + bm - 1) / bm) * (N / bn);
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t max_s = K / (4 * bk);
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+static dspark_status check_dims(const dspark_dims* dm, int op) {
+  if (!dm) return fail(DSPARK_EINVAL, "dims is NULL");
+  if (dm->dtype != DSPARK_F32 && dm->dtype != DSPARK_BF16)
+    return fail(DSPARK_EUNSUPPORTED, "dtype %d not supported (0 = f32, 1 = bf16)", dm->dtype);
+  if (dm->d <= 0 || dm->n_heads <= 0 || dm->gamma < 1 || dm->m < 1 || dm->H <= 0 || dm->ff <= 0)
+    return fail(DSPARK_EINVAL, "sizes must be positive (m=%d H=%d d=%d n_heads=%d gamma=%d ff=%d)",
+                dm->m, dm->H, dm->d, dm->n_heads, dm->gamma, dm->ff);
+  if (dm->d % dm->n_heads != 0)
+    return fail(DSPARK_EINVAL, "dDraft %d not divisible by nHeads %d", dm->d, dm->n_heads);
+  const int hd = dm->d / dm->n_heads;
+  if (hd != 32 && hd != 64 && hd != 128)
+    return fail(DSPARK_EUNSUPPORTED, "head_dim %d not in {32, 64, 128}", hd);
+  if (dm->gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "gamma %d > %d", dm->gamma, kMaxGamma);
+  if (dm->m > kMaxSegs) return fail(DSPARK_EUNSUPPORTED, "m %d > %d taps", dm->m, kMaxSegs);
+  if (dm->d % 128 != 0 || dm->d > 2048)
+    return fail(DSPARK_EUNSUPPORTED, "d %d must be a multiple of 128 and <= 2048", dm->d);
+  if (dm->H % 64 != 0) return fail(DSPARK_EUNSUPPORTED, "H %d must be a multiple of 64", dm->H);
+  if (dm->ff % 128 != 0) return fail(DSPARK_EUNSUPPORTED, "ff %d must be a multiple of 128", dm->ff);
+  if (!(dm->eps >= 0.f) || !std::isfinite(dm->eps)) return fail(DSPARK_EINVAL, "eps must be finite and >= 0");
+  if (op == DSPARK_OP_BLOCK_FORWARD && (dm->n_layers < 1 || dm->n_layers > 16))
+    return fail(dm->n_layers < 1 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "n_layers %d not in [1, 16]",
+                dm->n_layers);
+  return DSPARK_OK;
+}
+
+static dspark_status check_cu(int32_t A, const int32_t* cu_host, int gamma, int64_t* T) {
+  if (A < 1) return fail(DSPARK_EINVAL, "A = %d < 1", A);
+  if ((int64_t)A * gamma > 1024) return fail(DSPARK_EUNSUPPORTED, "A * gamma = %lld > 1024", (long long)A * gamma);
+  if (!cu_host) return fail(DSPARK_EINVAL, "cu_host is NULL");
+  if (cu_host[0] != 0) return fail(DSPARK_EINVAL, "cu[0] = %d, expected 0", cu_host[0]);
+  for (int b = 0; b < A; ++b)
+    if (cu_host[b + 1] < cu_host[b]) return fail(DSPARK_EINVAL, "cu is decreasing at %d", b);
+  *T = cu_host[A];
+  if (*T > (1ll << 30)) return fail(DSPARK_EUNSUPPORTED, "T = %lld too large", (long long)*T);
+  return DSPARK_OK;
+}
+
+static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const int32_t* cu_host, Plan* p) {
+  dspark_status st = check_dims(dm, op);
+  if (st != DSPARK_OK) return st;
+  int64_t T = 0;
+  st = check_cu(A, cu_host, dm->gamma, &T);
+  if (st != DSPARK_OK) return st;
+  const bool bf = dm->dtype == DSPARK_BF16;
+  p->esz = bf ? 2 : 4;
+  p->T = T;
+  p->Tpad = ((T + 63) / 64) * 64;
+  p->hd = dm->d / dm->n_heads;
+  p->M = A * dm->gamma;
+  const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
+  p->ctx_splits = ctx_splits_for(dm->dtype, T, d, mH);
+  p->chunk = attention_chunk(T, dm->n_heads, A);
+  int64_t chunks = 0;
+  for (int b = 0; b < A; ++b) {
+    const int64_t L = cu_host[b + 1] - cu_host[b];
+    chunks += (L + p->chunk - 1) / p->chunk;
+  }
+  p->total_chunks = (int)chunks;
+  p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;
+  p->sk_qkv = skinny_plan(M, 3 * d, d);
+  p->sk_o = skinny_plan(M, d, d);
+  p->sk_gu = skinny_plan(M, 2 * ff, d);
+  p->sk_down = skinny_plan(M, d, ff);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const bool need_ctx = op != DSPARK_OP_BLOCK_LAYER;
+  const bool need_block = op != DSPARK_OP_CTX_FUSE;
+  if (need_ctx) {
+    if (bf) p->wct = take((size_t)d * mH * 2);
+    p->ppart = take((size_t)p->ctx_splits * T * d * 4);
+  }
+  if (need_block) {
+    if (bf) p->wkvt = take((size_t)2 * p->kv_layers * d * d * 2);
+    if (op == DSPARK_OP_BLOCK_FORWARD) p->hctx = take((size_t)T * d * p->esz);
+    p->rinv = take((size_t)T * 4);
+    p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * d * p->esz);
+    p->prefix = take((size_t)(A + 1) * 4);
+    p->po = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * p->hd * 4);
+    p->pml = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * 2 * 4);
+    const size_t row = (size_t)M * d * 4;
+    p->D = take(row);
+    p->D2 = take(row);
+    p->U = take(row);
+    p->Q = take(row);
+    p->Kd = take(row);
+    p->Vd = take(row);
+    p->attn = take(row);
+    p->E = take(row);
+    p->Z = take(row);
+    p->hid = take((size_t)M * ff * 4);
+    size_t sk = (size_t)p->sk_qkv.splits * 3 * d;
+    sk = std::max(sk, (size_t)p->sk_o.splits * d);
+    sk = std::max(sk, (size_t)p->sk_gu.splits * 2 * ff);
+    sk = std::max(sk, (size_t)p->sk_down.splits * d);
+    p->skpart = take(sk * M * 4);
+  }
+  p->total = off == 0 ? 256 : off;
+  return DSPARK_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define NEED_PTR(p)                                                                  \
+  do {                                                                               \
+    if (!(p)) return fail(DSPARK_EINVAL, "%s is NULL", #p);                          \
+    if (!aligned16(p)) return fail(DSPARK_EINVAL, "%s is not 16-byte aligned", #p);  \
+  } while (0)
+#define OPT_PTR(p)                                                                   \
+  do {                                                                               \
+    if ((p) && !aligned16(p)) return fail(DSPARK_EINVAL, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+static dspark_status check_layer(const dspark_layer_weights* lw, int i) {
+  if (!lw) return fail(DSPARK_EINVAL, "layer weights %d is NULL", i);
+  const void* ptrs[9] = {lw->attn_norm, lw->wq, lw->wk, lw->wv, lw->wo,
+                         lw->ff_norm,   lw->w_gate, lw->w_up, lw->w_down};
+  static const char* names[9] = {"attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down"};
+  for (int k = 0; k < 9; ++k) {
+    if (!ptrs[k]) return fail(DSPARK_EINVAL, "layer %d: %s is NULL", i, names[k]);
+    if (!aligned16(ptrs[k])) return fail(DSPARK_EINVAL, "layer %d: %s is not 16-byte aligned", i, names[k]);
+  }
+  return DSPARK_OK;
+}
+
+static dspark_status check_taps(const dspark_dims* dm, const void* const* taps, int64_t ld_tap, int64_t T) {
+  if (!taps) return fail(DSPARK_EINVAL, "taps is NULL");
+  if (ld_tap < dm->H) return fail(DSPARK_EINVAL, "ld_tap %lld < H %d", (long long)ld_tap, dm->H);
+  const int esz = dm->dtype == DSPARK_BF16 ? 2 : 4;
+  if ((ld_tap * esz) % 16 != 0) return fail(DSPARK_EINVAL, "ld_tap * element size must be a multiple of 16 bytes");
+  for (int j = 0; j < dm->m; ++j) {
+    if (T > 0 && !taps[j]) return fail(DSPARK_EINVAL, "taps[%d] is NULL", j);
+    if (!aligned16(taps[j])) return fail(DSPARK_EINVAL, "taps[%d] is not 16-byte aligned", j);
+  }
+  return DSPARK_OK;
+}
+
+template <typename T>
+static T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// ---------------------------------------------------------------------------
+// launch sequences
+// ---------------------------------------------------------------------------
+static dspark_status run_ctx_fuse(const dspark_dims* dm, const Plan& p, const void* const* taps,
+                                  int64_t ld_tap, const void* w_c, const float* ctx_norm, void* h_ctx,
+                                  float* rinv, void* ws, hipStream_t s) {
+  if (p.T == 0) return DSPARK_OK;
+  const int d = dm->d, mH = dm->m * dm->H;
+  ASegs a{};
+  for (int j = 0; j < dm->m; ++j) a.seg[j] = taps[j];
+  a.ld = ld_tap;
+  a.seg_k = dm->H;
+  a.nseg = dm->m;
+  BMats b{};
+  b.mat[0] = w_c;
+  b.gain[0] = nullptr;
+  b.n_per = d;
+  b.nmat = 1;
+  void* wct = nullptr;
+  if (dm->dtype == DSPARK_BF16) {
+    wct = at<char>(ws, p.wct);
+    DSPARK_HIP(launch_prep_transpose_bf16(b, mH, wct, s));
+  }
+  float* part = at<float>(ws, p.ppart);
+  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, wct, part, (int)p.T, d, mH, p.ctx_splits, s));
+  DSPARK_HIP(launch_ctx_norm(dm->dtype, part, p.ctx_splits, (int)p.T, d, ctx_norm, dm->eps, h_ctx, rinv, s));
+  return DSPARK_OK;
+}
+
+// Context K/V of `nl` layers from H_ctx (rinv already computed).
+static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void* h_ctx, const float* rinv,
+                                const dspark_layer_weights* layers, int nl, void* ws, hipStream_t s) {
+  const int d = dm->d;
+  BMats b{};
+  for (int i = 0; i < nl; ++i) {
+    b.mat[2 * i] = layers[i].wk;
+    b.mat[2 * i + 1] = layers[i].wv;
+    b.gain[2 * i] = layers[i].attn_norm;
+    b.gain[2 * i + 1] = layers[i].attn_norm;
+  }
+  b.n_per = d;
+  b.nmat = 2 * nl;
+  void* wkvt = nullptr;
+  if (dm->dtype == DSPARK_BF16) {
+    wkvt = at<char>(ws, p.wkvt);
+    DSPARK_HIP(launch_prep_transpose_bf16(b, d, wkvt, s));
+  }
+  if (p.T == 0) return DSPARK_OK;
+  KVDesc kv{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
+  DSPARK_HIP(launch_gemm_kv(dm->dtype, h_ctx, b, wkvt, rinv, kv, d, nl, s));
+  return DSPARK_OK;
+}
+
+// One draft layer on the block rows. U holds RMSNorm(D; attn_norm) on entry.
+// Writes D_next = new rows and, when g_next is given, U_next = RMSNorm(D_next; g_next).
+static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, const int32_t* cu_dev,
+                               const dspark_layer_weights& lw, int kv_layer, const float* D,
+                               const float* U, float* D_next, const float* g_next, float* U_next,
+                               void* ws, hipStream_t s) {
+  const int d = dm->d, ff = dm->ff, M = p.M, G = dm->gamma;
+  const int dt = dm->dtype;
+  float* Q = at<float>(ws, p.Q);
+  float* Kd = at<float>(ws, p.Kd);
+  float* Vd = at<float>(ws, p.Vd);
+  float* attn = at<float>(ws, p.attn);
+  float* E = at<float>(ws, p.E);
+  float* Z = at<float>(ws, p.Z);
+  float* hid = at<float>(ws, p.hid);
+  float* skp = at<float>(ws, p.skpart);
+  int32_t* prefix = at<int32_t>(ws, p.prefix);
+
+  BMats b{};
+  // Q, K_d, V_d
+  b.mat[0] = lw.wq; b.mat[1] = lw.wk; b.mat[2] = lw.wv;
+  b.n_per = d; b.nmat = 3;
+  DSPARK_HIP(launch_skinny(dt, U, M, d, b, 3 * d, p.sk_qkv.splits, skp, s));
+  const float qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
+  DSPARK_HIP(launch_finish_qkv(skp, p.sk_qkv.splits, M, d, qscale, Q, Kd, Vd, s));
+  // attention over [context ++ block]
+  KVDesc kv{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
+  float* po = at<float>(ws, p.po);
+  float* pml = at<float>(ws, p.pml);
+  if (p.total_chunks > 0)
+    DSPARK_HIP(launch_attention(dt, Q, kv, kv_layer, cu_dev, prefix, A, G, p.chunk, p.total_chunks, po, pml, s));
+  DSPARK_HIP(launch_combine(Q, Kd, Vd, A, G, d, dm->n_heads, prefix, p.total_chunks, po, pml, attn, s));
+  // E = D + Attn Wo ; Z = RMSNorm(E; ff_norm)
+  b = BMats{};
+  b.mat[0] = lw.wo; b.n_per = d; b.nmat = 1;
+  DSPARK_HIP(launch_skinny(dt, attn, M, d, b, d, p.sk_o.splits, skp, s));
+  DSPARK_HIP(launch_finish_res(skp, p.sk_o.splits, M, d, D, lw.ff_norm, dm->eps, E, Z, s));
+  // SiLU(Z Wgate) * (Z Wup)
+  b = BMats{};
+  b.mat[0] = lw.w_gate; b.mat[1] = lw.w_up; b.n_per = ff; b.nmat = 2;
+  DSPARK_HIP(launch_skinny(dt, Z, M, d, b, 2 * ff, p.sk_gu.splits, skp, s));
+  DSPARK_HIP(launch_finish_swiglu(skp, p.sk_gu.splits, M, ff, hid, s));
+  // D' = E + hid Wdown (+ next norm)
+  b = BMats{};
+  b.mat[0] = lw.w_down; b.n_per = d; b.nmat = 1;
+  DSPARK_HIP(launch_skinny(dt, hid, M, ff, b, d, p.sk_down.splits, skp, s));
+  DSPARK_HIP(launch_finish_res(skp, p.sk_down.splits, M, d, E, g_next, dm->eps, D_next,
+                               g_next ? U_next : nullptr, s));
+  return DSPARK_OK;
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+size_t dspark_workspace_size(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host) {
+  if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_FORWARD) {
+    fail(DSPARK_EINVAL, "unknown op %d", op);
+    return 0;
+  }
+  Plan p;
+  if (make_plan(op, dims, A, cu_host, &p) != DSPARK_OK) return 0;
+  return p.total;
+}
+
+dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                              const int32_t* cu_dev, const void* const* taps, int64_t ld_tap,
+                              const void* w_c, const float* ctx_norm, void* h_ctx, void* ws,
+                              size_t ws_bytes, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_CTX_FUSE, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(cu_dev);
+  st = check_taps(dims, taps, ld_tap, p.T);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(w_c);
+  NEED_PTR(ctx_norm);
+  if (p.T > 0) NEED_PTR(h_ctx);
+  NEED_PTR(ws);
+  if (ws_bytes < p.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
+  return run_ctx_fuse(dims, p, taps, ld_tap, w_c, ctx_norm, h_ctx, nullptr, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                                 const int32_t* cu_dev, const void* h_ctx, const float* d_in,
+                                 float* d_out, const dspark_layer_weights* lw, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_LAYER, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(cu_dev);
+  if (p.T > 0) NEED_PTR(h_ctx);
+  NEED_PTR(d_in);
+  NEED_PTR(d_out);
+  st = check_layer(lw, 0);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(ws);
+  if (ws_bytes < p.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* rinv = at<float>(ws, p.rinv);
+  if (p.T > 0) DSPARK_HIP(launch_rowstats(dims->dtype, h_ctx, (int)p.T, dims->d, dims->eps, rinv, s));
+  st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, ws, s);
+  if (st != DSPARK_OK) return st;
+  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
+  float* U = at<float>(ws, p.U);
+  DSPARK_HIP(launch_block_init(d_in, nullptr, A, dims->gamma, dims->d, lw->attn_norm, dims->eps,
+                               nullptr, U, s));
+  return run_layer(dims, p, A, cu_dev, *lw, 0, d_in, U, d_out, nullptr, nullptr, ws, s);
+}
+
+dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                                   const int32_t* cu_dev, const void* const* taps, int64_t ld_tap,
+                                   const void* w_c, const float* ctx_norm, const float* block_in,
+                                   const float* block_pos, const dspark_layer_weights* layers,
+                                   const float* out_norm, void* h_ctx_out, float* block_out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_FORWARD, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(cu_dev);
+  st = check_taps(dims, taps, ld_tap, p.T);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(w_c);
+  NEED_PTR(ctx_norm);
+  NEED_PTR(block_in);
+  NEED_PTR(block_pos);
+  if (!layers) return fail(DSPARK_EINVAL, "layers is NULL");
+  for (int i = 0; i < dims->n_layers; ++i) {
+    st = check_layer(&layers[i], i);
+    if (st != DSPARK_OK) return st;
+  }
+  OPT_PTR(out_norm);
+  OPT_PTR(h_ctx_out);
+  NEED_PTR(block_out);
+  NEED_PTR(ws);
+  if (ws_bytes < p.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* h_ctx = h_ctx_out ? h_ctx_out : at<char>(ws, p.hctx);
+  float* rinv = at<float>(ws, p.rinv);
+  st = run_ctx_fuse(dims, p, taps, ld_tap, w_c, ctx_norm, h_ctx, rinv, ws, s);
+  if (st != DSPARK_OK) return st;
+  st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, ws, s);
+  if (st != DSPARK_OK) return st;
+  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
+  float* Da = at<float>(ws, p.D);
+  float* Db = at<float>(ws, p.D2);
+  float* U = at<float>(ws, p.U);
+  DSPARK_HIP(launch_block_init(block_in, block_pos, A, dims->gamma, dims->d, layers[0].attn_norm,
+                               dims->eps, Da, U, s));
+  const int N = dims->n_layers;
+  for (int i = 0; i < N; ++i) {
+    const bool last = i == N - 1;
+    float* Dn;
+    const float* gn;
+    float* Un;
+    if (!last) {
+      Dn = Db;
+      gn = layers[i + 1].attn_norm;
+      Un = U;
+    } else if (out_norm) {
+      Dn = Db;
+      gn = out_norm;
+      Un = block_out;
+    } else {
+      Dn = block_out;
+      gn = nullptr;
+      Un = nullptr;
+    }
+    st = run_layer(dims, p, A, cu_dev, layers[i], i, Da, U, Dn, gn, Un, ws, s);
+    if (st != DSPARK_OK) return st;
+    std::swap(Da, Db);
+  }
+  return DSPARK_OK;
+}
+
+const char* dspark_last_error(void) { return g_err.c_str(); }
+
+const char* dspark_version(void) { return "dspark-mi355x 0.1.0 (gfx950)"; }
+
+int32_t dspark_kernel_kinds(void) { return K_COUNT; }
+
+const char* dspark_kernel_name(int32_t kind) { return kernel_name(kind); }
+
+dspark_status dspark_trace_begin(uint64_t mask, int32_t capacity) {
+  Trace& t = g_trace;
+  if (capacity < 1) return fail(DSPARK_EINVAL, "capacity must be >= 1");
+  if ((int)t.ev.size() < 2 * capacity) {
+    const size_t old = t.ev.size();
+    t.ev.resize(2 * capacity);
+    for (size_t i = old; i < t.ev.size(); ++i) DSPARK_HIP(hipEventCreate(&t.ev[i]));
+  }
+  t.kind.assign(capacity, -1);
+  t.mask = mask;
+  t.cap = capacity;
+  t.used = 0;
+  t.open = false;
+  t.on = true;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_trace_end(double* total_ms, int64_t* launches, int32_t n_kinds) {
+  Trace& t = g_trace;
+  t.on = false;
+  if (!total_ms || !launches) return fail(DSPARK_EINVAL, "output arrays are NULL");
+  for (int k = 0; k < n_kinds; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  for (int i = 0; i < t.used; ++i) {
+    DSPARK_HIP(hipEventSynchronize(t.ev[2 * i + 1]));
+    float ms = 0.f;
+    DSPARK_HIP(hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]));
+    const int k = t.kind[i];
+    if (k >= 0 && k < n_kinds) {
+      total_ms[k] += ms;
+      launches[k] += 1;
+    }
+  }
+  t.used = 0;
+  return DSPARK_OK;
+}
+
+}  // extern "C"

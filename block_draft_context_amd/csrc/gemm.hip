@@ -1,0 +1,408 @@
+// Context-side dense contractions for gfx950:
+//   Eq 2   P = [H^{l1}; ...; H^{lm}] . W_c              (split-K fp32 partials)
+//          H_ctx = RMSNorm(P; ctx_norm)                  (row pass)
+//   Eq 3   K_c, V_c = RMSNorm(H_ctx; attn_norm_i) . W_{K,V}^i   for every layer i
+//
+// bf16 storage runs on the matrix cores (v_mfma_f32_32x32x16_bf16) with both
+// operands staged K-contiguous in LDS: the weights, stored [in, out], are
+// first transposed (and, for K/V, multiplied by the layer's attention-norm
+// gain, which commutes into the weight rows) into the workspace. The RMSNorm
+// row factor of the context rows is applied in the K/V epilogue:
+//   RMSNorm(h; g) W = diag(rinv) . h . (diag(g) W).
+// float32 storage uses a plain LDS-tiled FMA GEMM.
+#include "common.h"
+#include "kernels.h"
+#include "kv_layout.h"
+
+namespace dspark {
+
+// ---------------------------------------------------------------------------
+// weight transpose (+ gain) : Bt[n][k] = bf16(g(k) * W(k, n))
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prep_transpose_kernel(BMats b, int K, bf16* __restrict__ Bt) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64;
+  const int n0 = blockIdx.y * 64;
+  const int mi = n0 / b.n_per;
+  const int c0 = n0 % b.n_per;
+  const bf16* __restrict__ W = static_cast<const bf16*>(b.mat[mi]);
+  const float* __restrict__ g = b.gain[mi];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = ty + 4 * i;
+    float v = to_f32(W[(int64_t)(k0 + r) * b.n_per + c0 + tx]);
+    if (g) v *= g[k0 + r];
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = ty + 4 * i;   // n within the tile
+    Bt[(int64_t)(n0 + r) * K + k0 + tx] = from_f32<bf16>(tile[tx][r]);
+  }
+}
+
+hipError_t launch_prep_transpose_bf16(const BMats& b, int K, void* Bt, hipStream_t s) {
+  const int N = b.n_per * b.nmat;
+  dim3 grid(K / 64, N / 64);
+  trace_pre(K_PREP_T, s);
+  prep_transpose_kernel<<<grid, 256, 0, s>>>(b, K, static_cast<bf16*>(Bt));
+  trace_post(K_PREP_T, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM  C[M,N] = A[M,K] . Bt[N,K]^T  (bf16 in, fp32 accumulate)
+// 256 threads = 4 waves arranged WM x WN; each wave owns a (BM/WM) x (BN/WN)
+// sub-tile made of 32x32 MFMA blocks. BK = 64. LDS rows are 128 bytes with the
+// 16-byte chunk index XOR-swizzled by (row & 7), so both the cooperative
+// stores and the per-lane MFMA operand reads are free of bank conflicts.
+// Global tiles for step k+1 are fetched into registers while step k computes.
+// ---------------------------------------------------------------------------
+constexpr int BK = 64;
+
+struct EpiPartial {            // out[z][r][n] = acc, rows < M
+  float* out;
+  int64_t split_stride;
+  DSPARK_DEV void store(int z, int r, int n, float v, int M, int N) const {
+    if (r < M) out[z * split_stride + (int64_t)r * N + n] = v;
+  }
+};
+
+template <typename S>
+struct EpiKV {                 // K/V of every layer, row scale, tiled layout
+  S* base;
+  const float* rinv;
+  int64_t Tpad;
+  int T, d, hd, n_heads;
+  DSPARK_DEV void store(int /*z*/, int r, int n, float v, int /*M*/, int /*N*/) const {
+    if (r >= Tpad) return;
+    const int layer = n / (2 * d);
+    const int kv = (n / d) & 1;
+    const int w = n % d;
+    const int head = w / hd, c = w % hd;
+    const float val = (r < T) ? v * rinv[r] : 0.f;
+    const int64_t hb = KVLayout<S>::head_base(layer, kv, head, n_heads, Tpad, hd);
+    const int64_t off = kv == 0 ? KVLayout<S>::k_off(r, c, hd) : KVLayout<S>::v_off(r, c, hd);
+    base[hb + off] = from_f32<S>(val);
+  }
+};
+
+DSPARK_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// M = valid A rows (rows >= M read as zero); MR = rows covered by the grid.
+template <int BM, int BN, int WM, int WN, class Epi>
+__global__ __launch_bounds__(256) void gemm_bf16_nt(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                    int MR, int N, int K, int k_per_split,
+                                                    Epi epi) {
+  constexpr int FM = BM / WM / 32;
+  constexpr int FN = BN / WN / 32;
+  constexpr int A_CH = BM * BK / 8 / 256;   // 16-byte chunks per thread
+  constexpr int B_CH = BN * BK / 8 / 256;
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) char smem[(BM + BN) * BK * 2];
+  char* As = smem;
+  char* Bs = smem + BM * BK * 2;
+
+  const int tiles_m = (MR + BM - 1) / BM;
+  const int tiles_n = N / BN;
+  const int ntiles = tiles_m * tiles_n;
+  // XCD-aware order: consecutive workgroup ids land on different XCDs; give
+  // each XCD a contiguous run of tiles so its L2 sees shared panels.
+  int bid = blockIdx.x;
+  {
+    const int per = ntiles / 8;
+    if (per > 0 && bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.z;
+  const int kbeg = z * k_per_split;
+  const int kend = min(K, kbeg + k_per_split);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  u32x4 ra[A_CH], rb[B_CH];
+  auto load_tiles = [&](int k0) {
+    const int sgi = k0 / a.seg_k;
+    const int kin = k0 - sgi * a.seg_k;
+    const bf16* __restrict__ Ap = static_cast<const bf16*>(a.seg[sgi]);
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int q = tid + 256 * i;
+      const int row = q >> 3, ch = q & 7;
+      const int gr = m0 + row;
+      if (gr < M)
+        ra[i] = ld16(Ap + (int64_t)gr * a.ld + kin + ch * 8);
+      else
+        ra[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int q = tid + 256 * i;
+      const int row = q >> 3, ch = q & 7;
+      rb[i] = ld16(Bt + (int64_t)(n0 + row) * K + k0 + ch * 8);
+    }
+  };
+  auto store_tiles = [&]() {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int q = tid + 256 * i;
+      st16(As + swz(q >> 3, q & 7), ra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int q = tid + 256 * i;
+      st16(Bs + swz(q >> 3, q & 7), rb[i]);
+    }
+  };
+
+  if (kbeg < kend) load_tiles(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    __syncthreads();
+    store_tiles();
+    __syncthreads();
+    if (k0 + BK < kend) load_tiles(k0 + BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = ks * 2 + (lane >> 5);
+      bf16x8 av[FM], bv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * (BM / WM) + i * 32 + (lane & 31);
+        av[i] = *reinterpret_cast<const bf16x8*>(As + swz(row, ch));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * (BN / WN) + j * 32 + (lane & 31);
+        bv[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(row, ch));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // 32x32 accumulator layout: lane holds column (lane & 31) and rows
+  // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * (BM / WM) + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+        epi.store(z, row, col, acc[i][j][r], M, N);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// float32 FMA GEMM: C[M,N] = A(segments)[M,K] . B(mats)[K,N], 64x64 tiles,
+// BK = 16, 4x4 outputs per thread, gain applied to B rows while staging.
+// ---------------------------------------------------------------------------
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_f32(ASegs a, BMats b, int M, int MR, int N, int K,
+                                                int k_per_split, Epi epi) {
+  (void)MR;
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tiles_n = N / 64;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * 64, n0 = tn * 64;
+  const int z = blockIdx.z;
+  const int kbeg = z * k_per_split, kend = min(K, kbeg + k_per_split);
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int mi = n0 / b.n_per, c0 = n0 % b.n_per;
+  const float* __restrict__ W = static_cast<const float*>(b.mat[mi]);
+  const float* __restrict__ g = b.gain[mi];
+  float acc[4][4] = {};
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
+    const int sgi = k0 / a.seg_k, kin = k0 - sgi * a.seg_k;
+    const float* __restrict__ Ap = static_cast<const float*>(a.seg[sgi]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;          // 64 rows x 16 k
+      const int r = e >> 4, kk = e & 15;
+      As[kk][r] = (m0 + r < M) ? Ap[(int64_t)(m0 + r) * a.ld + kin + kk] : 0.f;
+      const int br = e >> 6, bc = e & 63;   // 16 k x 64 n
+      float v = W[(int64_t)(k0 + br) * b.n_per + c0 + bc];
+      if (g) v *= g[k0 + br];
+      Bs[br][bc] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) epi.store(z, m0 + ty * 4 + i, n0 + tx * 4 + j, acc[i][j], M, N);
+}
+
+static int pick_gemm_bm(int M) { return M >= 4096 ? 128 : 64; }
+
+hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, float* out,
+                           int M, int N, int K, int splits, hipStream_t s) {
+  const int kps = ((K / splits + BK - 1) / BK) * BK;
+  EpiPartial epi{out, (int64_t)M * N};
+  trace_pre(K_GEMM_CTX, s);
+  if (dtype == 1) {
+    const bf16* B = static_cast<const bf16*>(Bt);
+    if (pick_gemm_bm(M) == 128) {
+      dim3 grid(((M + 127) / 128) * (N / 128), 1, splits);
+      gemm_bf16_nt<128, 128, 2, 2, EpiPartial><<<grid, 256, 0, s>>>(a, B, M, M, N, K, kps, epi);
+    } else {
+      dim3 grid(((M + 63) / 64) * (N / 128), 1, splits);
+      gemm_bf16_nt<64, 128, 2, 2, EpiPartial><<<grid, 256, 0, s>>>(a, B, M, M, N, K, kps, epi);
+    }
+  } else {
+    const int kps16 = ((K / splits + 15) / 16) * 16;
+    dim3 grid(((M + 63) / 64) * (N / 64), 1, splits);
+    gemm_f32<EpiPartial><<<grid, 256, 0, s>>>(a, b, M, M, N, K, kps16, epi);
+  }
+  trace_post(K_GEMM_CTX, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const void* Bt,
+                          const float* rinv, const KVDesc& kv, int d, int n_layers,
+                          hipStream_t s) {
+  ASegs a{};
+  a.seg[0] = h_ctx;
+  a.ld = d;
+  a.seg_k = d;
+  a.nseg = 1;
+  const int N = 2 * n_layers * d;
+  const int M = kv.T;
+  const int Mrows = (int)kv.Tpad;  // rows T..Tpad-1 are written as zeros
+  trace_pre(K_GEMM_KV, s);
+  if (dtype == 1) {
+    EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
+    const bf16* B = static_cast<const bf16*>(Bt);
+    if (pick_gemm_bm(M) == 128) {
+      dim3 grid(((Mrows + 127) / 128) * (N / 128), 1, 1);
+      gemm_bf16_nt<128, 128, 2, 2, EpiKV<bf16>><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    } else {
+      dim3 grid(((Mrows + 63) / 64) * (N / 128), 1, 1);
+      gemm_bf16_nt<64, 128, 2, 2, EpiKV<bf16>><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    }
+  } else {
+    EpiKV<float> epi{static_cast<float*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
+    dim3 grid(((Mrows + 63) / 64) * (N / 64), 1, 1);
+    gemm_f32<EpiKV<float>><<<grid, 256, 0, s>>>(a, b, M, Mrows, N, d, d, epi);
+  }
+  trace_post(K_GEMM_KV, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row passes (one wave per row, d a multiple of 64)
+// ---------------------------------------------------------------------------
+template <typename S>
+__global__ __launch_bounds__(256) void ctx_norm_kernel(const float* __restrict__ part, int splits,
+                                                       int T, int d, const float* __restrict__ g,
+                                                       float eps, S* __restrict__ h,
+                                                       float* __restrict__ rinv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int per = d / 64;   // <= 32
+  float v[32];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < per) {
+      const int c = lane + 64 * i;
+      float x = 0.f;
+      for (int zz = 0; zz < splits; ++zz) x += part[((int64_t)zz * T + t) * d + c];
+      v[i] = x;
+      ss += x * x;
+    }
+  }
+  ss = wave_sum(ss);
+  const float sc = rsqrtf(ss / (float)d + eps);
+  float ss2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < per) {
+      const int c = lane + 64 * i;
+      const S o = from_f32<S>(v[i] * sc * g[c]);
+      h[t * d + c] = o;
+      const float of = to_f32(o);
+      ss2 += of * of;
+    }
+  }
+  if (rinv) {
+    ss2 = wave_sum(ss2);
+    if (lane == 0) rinv[t] = rsqrtf(ss2 / (float)d + eps);
+  }
+}
+
+hipError_t launch_ctx_norm(int dtype, const float* part, int splits, int T, int d, const float* g,
+                           float eps, void* h, float* rinv, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4);
+  trace_pre(K_CTX_NORM, s);
+  if (dtype == 1)
+    ctx_norm_kernel<bf16><<<grid, 256, 0, s>>>(part, splits, T, d, g, eps, static_cast<bf16*>(h), rinv);
+  else
+    ctx_norm_kernel<float><<<grid, 256, 0, s>>>(part, splits, T, d, g, eps, static_cast<float*>(h), rinv);
+  trace_post(K_CTX_NORM, s);
+  return hipGetLastError();
+}
+
+template <typename S>
+__global__ __launch_bounds__(256) void rowstats_kernel(const S* __restrict__ h, int T, int d,
+                                                       float eps, float* __restrict__ rinv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float ss = 0.f;
+  for (int c = lane; c < d; c += 64) {
+    const float x = to_f32(h[t * d + c]);
+    ss += x * x;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) rinv[t] = rsqrtf(ss / (float)d + eps);
+}
+
+hipError_t launch_rowstats(int dtype, const void* h, int T, int d, float eps, float* rinv,
+                           hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4);
+  trace_pre(K_ROWSTATS, s);
+  if (dtype == 1)
+    rowstats_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16*>(h), T, d, eps, rinv);
+  else
+    rowstats_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(h), T, d, eps, rinv);
+  trace_post(K_ROWSTATS, s);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

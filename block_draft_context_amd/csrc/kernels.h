@@ -1,0 +1,121 @@
+// Internal launcher interface between the C ABI (dspark.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kMaxSegs = 16;     // tapped layers (A-operand segments)
+constexpr int kMaxMats = 32;     // weight matrices in one batched launch (2 per layer)
+constexpr int kMaxGamma = 16;
+
+enum KernelKind : int {
+  K_PREP_T = 0,       // weight transpose (+ gain fold) into the workspace
+  K_GEMM_CTX,         // Eq 2 projection X . W_c (split-K partials)
+  K_CTX_NORM,         // Eq 2 RMSNorm epilogue pass (+ row inverse RMS)
+  K_ROWSTATS,         // row inverse RMS of a given H_ctx
+  K_GEMM_KV,          // Eq 3 context K/V re-projection (all layers at once)
+  K_PLAN,             // chunk prefix of the split-K attention
+  K_ATTN,             // split-K attention partials over context chunks
+  K_COMBINE,          // (m, l) combine + block keys
+  K_SKINNY,           // block-row projections (weight streaming)
+  K_FINISH_QKV,       // reduce Q/K_d/V_d partials
+  K_FINISH_RES,       // reduce + residual + RMSNorm of block rows
+  K_FINISH_SWIGLU,    // reduce gate/up + SiLU(gate) * up
+  K_BLOCK_INIT,       // D0 = block_in + block_pos, and its norm
+  K_COUNT
+};
+
+const char* kernel_name(int kind);
+void trace_pre(int kind, hipStream_t s);
+void trace_post(int kind, hipStream_t s);
+
+// A operand split along K into segments of equal width (the m taps):
+// A(r, k) = seg[k / seg_k][r * ld + k % seg_k].
+struct ASegs {
+  const void* seg[kMaxSegs];
+  int64_t ld;
+  int32_t seg_k;
+  int32_t nseg;
+};
+
+// B operand made of several [K, n_per] matrices side by side (column n lives in
+// mat[n / n_per]); an optional per-k gain g[n / n_per][k] scales row k.
+struct BMats {
+  const void* mat[kMaxMats];
+  const float* gain[kMaxMats];
+  int32_t n_per;
+  int32_t nmat;
+};
+
+// Attention-side layout of the context K and V (per layer, per head):
+// see kv_layout.h. Tpad is T rounded up to 64.
+struct KVDesc {
+  void* base;        // [n_layers][2][n_heads][Tpad][hd] in tiled order
+  int64_t Tpad;
+  int32_t T;
+  int32_t hd;
+  int32_t n_heads;
+};
+
+// ---- context side -------------------------------------------------------
+// bf16: Bt = [sum(n) rows][K] transposed (and gain-folded) copy of B.
+hipError_t launch_prep_transpose_bf16(const BMats& b, int K, void* Bt, hipStream_t s);
+
+// out[z][r][n] = sum_{k in split z} A(r,k) B(k,n); float32 partials.
+hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt,
+                           float* out, int M, int N, int K, int splits, hipStream_t s);
+
+// h[r] = RMSNorm(sum_z part[z][r]; g) in storage type; rinv[r] = inverse RMS of
+// the stored row (nullable).
+hipError_t launch_ctx_norm(int dtype, const float* part, int splits, int T, int d,
+                           const float* g, float eps, void* h, float* rinv, hipStream_t s);
+
+hipError_t launch_rowstats(int dtype, const void* h, int T, int d, float eps, float* rinv,
+                           hipStream_t s);
+
+// K/V for all layers of `b` (2 matrices per layer: K then V) from H_ctx with
+// the row scale rinv, written in the attention layout of `kv`.
+hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const void* Bt,
+                          const float* rinv, const KVDesc& kv, int d, int n_layers,
+                          hipStream_t s);
+
+// ---- attention ------------------------------------------------------------
+int attention_chunk(int64_t T, int n_heads, int A);   // keys per chunk (multiple of 64)
+hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
+                       hipStream_t s);
+// Q is pre-scaled by hd^-1/2 * log2(e).
+hipError_t launch_attention(int dtype, const float* Q, const KVDesc& kv, int layer,
+                            const int32_t* cu_dev, const int32_t* chunk_prefix, int A,
+                            int gamma, int chunk, int total_chunks, float* part_o,
+                            float* part_ml, hipStream_t s);
+hipError_t launch_combine(const float* Q, const float* Kd, const float* Vd, int A, int gamma,
+                          int d, int n_heads, const int32_t* chunk_prefix, int total_chunks,
+                          const float* part_o, const float* part_ml, float* attn,
+                          hipStream_t s);
+
+// ---- block side -----------------------------------------------------------
+struct SkinnyPlan {
+  int rpt;      // K rows per thread
+  int splits;   // K slabs (partials)
+};
+SkinnyPlan skinny_plan(int M, int N, int K);
+// part[z][r][n] = sum_{k in slab z} X[r][k] W(k, n), W = the matrices of b.
+hipError_t launch_skinny(int dtype, const float* X, int M, int K, const BMats& b, int N,
+                         int splits, float* part, hipStream_t s);
+hipError_t launch_finish_qkv(const float* part, int splits, int M, int d, float qscale,
+                             float* Q, float* Kd, float* Vd, hipStream_t s);
+// full[r] = res[r] + sum_z part[z][r]; normed[r] = RMSNorm(full[r]; g) (nullable).
+hipError_t launch_finish_res(const float* part, int splits, int M, int d, const float* res,
+                             const float* g, float eps, float* full, float* normed,
+                             hipStream_t s);
+hipError_t launch_finish_swiglu(const float* part, int splits, int M, int ff, float* hid,
+                                hipStream_t s);
+// D0 = block_in + block_pos (per sequence); U0 = RMSNorm(D0; g).
+hipError_t launch_block_init(const float* block_in, const float* block_pos, int A, int gamma,
+                             int d, const float* g, float eps, float* D0, float* U0,
+                             hipStream_t s);
+
+}  // namespace dspark

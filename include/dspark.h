@@ -1,0 +1,173 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) draft-block forward library.
+ *
+ * The library computes the DSpark / DFlash draft block with KV-injected
+ * context, as stated on the page "mlx-bun 0.0.7 -> 0.0.9,
+ * package/src/spec/dspark/module-dflash.ts" (header comment, Eq 2 and Eq 3;
+ * methods #buildContext, #layer and #backbone of DflashDrafter):
+ *
+ *   Eq 2   H_ctx = RMSNorm(W_c . [H^{l1}; ...; H^{lm}]; ctx_norm)
+ *   Eq 3   per draft layer i, with U = RMSNorm(D; attn_norm_i) on the block rows
+ *          and Uc = RMSNorm(H_ctx; attn_norm_i) on the context rows:
+ *            Q = U Wq,  K = [Uc Wk ; U Wk],  V = [Uc Wv ; U Wv]
+ *            Attn = softmax(Q K^T / sqrt(hd)) V   per head, no causal mask
+ *            E  = D + Attn Wo
+ *            D' = E + (SiLU(Z Wgate) * (Z Wup)) Wdown,   Z = RMSNorm(E; ff_norm_i)
+ *   output out = RMSNorm(D^N; out_norm)
+ *
+ * The gated FFN uses SiLU on the gate half as the page "src/dspark-runtime.js"
+ * does (its propose() runs upGate -> silu -> down for every draft layer).
+ * RMSNorm(x; g) = x * (mean_k x_k^2 + eps)^(-1/2) * g.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All matrices are row-major [in, out] and applied as x @ W (initFromDims
+ *   of module-dflash.ts). Norm gains are float32 [d].
+ * - dims->dtype is the storage type of the long tensors: the taps, W_c, every
+ *   layer matrix and H_ctx. DSPARK_BF16 means bfloat16 storage with float32
+ *   accumulation; DSPARK_F32 means float32 everywhere.
+ * - Block rows (block_in, d_in, d_out, block_out) and block_pos are always
+ *   float32, laid out [A, gamma, d].
+ * - Packing: A sequences share one context axis of T = cu[A] rows. cu holds
+ *   A+1 int32 prefix offsets, cu[0] = 0, non-decreasing; sequence b owns
+ *   rows cu[b] .. cu[b+1]-1 and attends only to them (the exact exclusion
+ *   that the key-padding bias of #maskBias gives). L_b = 0 is allowed: the
+ *   block then attends to its own gamma rows only. cu_host (host memory) and
+ *   cu_dev (device memory) must hold the same values; cu_host is read during
+ *   the call for validation and launch planning, cu_dev by the kernels.
+ * - Every device pointer must be 16-byte aligned; host arrays (cu_host,
+ *   taps, layers) are read only during the call.
+ * - The caller owns all memory. Scratch lives in the caller's workspace
+ *   (ws, ws_bytes); its size comes from dspark_workspace_size for the same
+ *   operation, dims, A and cu. Calls that may run concurrently need distinct
+ *   workspaces. The library allocates no device memory on these paths.
+ * - stream is a hipStream_t (NULL = the default stream). Calls enqueue work
+ *   and return without synchronising the device.
+ * - Errors: on any non-OK status nothing has been enqueued and no output has
+ *   been written; dspark_last_error() returns a message for the calling
+ *   thread. A failed kernel launch returns DSPARK_EHIP (work enqueued before
+ *   it in the same call may already run).
+ * - Supported: head_dim = d / n_heads in {32, 64, 128}; 1 <= gamma <= 16;
+ *   1 <= m <= 16; 1 <= n_layers <= 16; H, d and ff multiples of 64;
+ *   A * gamma <= 1024.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = 1,        /* bad argument: NULL, misaligned, inconsistent sizes */
+  DSPARK_EUNSUPPORTED = 2,  /* valid but not built: head_dim, gamma, dtype ... */
+  DSPARK_EWORKSPACE = 3,    /* ws_bytes below dspark_workspace_size */
+  DSPARK_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+typedef enum {
+  DSPARK_OP_CTX_FUSE = 0,
+  DSPARK_OP_BLOCK_LAYER = 1,
+  DSPARK_OP_BLOCK_FORWARD = 2
+} dspark_op;
+
+/* Problem sizes (DflashConfig and TargetDims of module-dflash.ts). */
+typedef struct {
+  int32_t m;         /* number of tapped target layers */
+  int32_t H;         /* target hidden width */
+  int32_t d;         /* draft width dDraft */
+  int32_t n_heads;   /* attention heads; head_dim = d / n_heads */
+  int32_t gamma;     /* block size */
+  int32_t n_layers;  /* draft layers (used by dspark_block_forward) */
+  int32_t ff;        /* FFN width, ffMult * d */
+  float eps;         /* RMSNorm epsilon (the target's rmsNormEps) */
+  int32_t dtype;     /* dspark_dtype: storage type of the long tensors */
+} dspark_dims;
+
+/* One draft layer's parameters (bb.{i}.* of module-dflash.ts), device
+ * pointers. Matrices in dims->dtype, gains float32. */
+typedef struct {
+  const float* attn_norm;   /* [d]    shared by block and context rows */
+  const void* wq;           /* [d, d] */
+  const void* wk;           /* [d, d] */
+  const void* wv;           /* [d, d] */
+  const void* wo;           /* [d, d] */
+  const float* ff_norm;     /* [d] */
+  const void* w_gate;       /* [d, ff] */
+  const void* w_up;         /* [d, ff] */
+  const void* w_down;       /* [ff, d] */
+} dspark_layer_weights;
+
+/* Bytes of workspace that `op` needs for these sizes (0 with a message in
+ * dspark_last_error() when the arguments are invalid). Pure host arithmetic. */
+size_t dspark_workspace_size(int32_t op, const dspark_dims* dims, int32_t A,
+                             const int32_t* cu_host);
+
+/* Eq 2 (#buildContext): h_ctx[t, :] = RMSNorm(sum_j taps[j][t, :] @ W_c[j*H:(j+1)*H, :]; ctx_norm).
+ *   taps     host array of m device pointers; row t of tap j starts at
+ *            taps[j] + t * ld_tap elements (ld_tap >= H), T = cu_host[A] rows
+ *   w_c      [m*H, d] dtype;  ctx_norm [d] float32
+ *   h_ctx    out [T, d] dtype */
+dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A,
+                              const int32_t* cu_host, const int32_t* cu_dev,
+                              const void* const* taps, int64_t ld_tap,
+                              const void* w_c, const float* ctx_norm,
+                              void* h_ctx, void* ws, size_t ws_bytes, void* stream);
+
+/* Eq 3 plus the block FFN for one draft layer (#layer).
+ *   h_ctx    [T, d] dtype, read-only context memory (bitwise unchanged)
+ *   d_in     [A, gamma, d] float32 block rows; d_out the same shape, may alias d_in
+ *   lw       host pointer to the layer's device parameters */
+dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A,
+                                 const int32_t* cu_host, const int32_t* cu_dev,
+                                 const void* h_ctx, const float* d_in, float* d_out,
+                                 const dspark_layer_weights* lw,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* The whole draft block (#backbone): Eq 2, D0 = block_in + block_pos,
+ * dims->n_layers x (Eq 3 + FFN), then the output norm.
+ *   block_in   [A, gamma, d] float32 token rows (anchor row, mask rows)
+ *   block_pos  [gamma, d] float32 (added to every sequence's block)
+ *   layers     host array of n_layers parameter sets
+ *   out_norm   [d] float32, or NULL to return D^N without the output norm
+ *   h_ctx_out  optional [T, d] dtype copy of H_ctx, or NULL
+ *   block_out  out [A, gamma, d] float32 */
+dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A,
+                                   const int32_t* cu_host, const int32_t* cu_dev,
+                                   const void* const* taps, int64_t ld_tap,
+                                   const void* w_c, const float* ctx_norm,
+                                   const float* block_in, const float* block_pos,
+                                   const dspark_layer_weights* layers,
+                                   const float* out_norm, void* h_ctx_out,
+                                   float* block_out, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* Library version string. */
+const char* dspark_version(void);
+
+/* ---- measurement support: per-kernel HIP-event timing -------------------
+ * Kernel kinds are numbered 0 .. dspark_kernel_kinds()-1 and named by
+ * dspark_kernel_name(). dspark_trace_begin(mask) makes every later launch of
+ * a kind whose bit is set in `mask` record a HIP event pair on its stream
+ * (at most `capacity` launches). dspark_trace_end() waits for those events,
+ * writes per-kind totals (milliseconds) and launch counts into the caller's
+ * arrays of length n_kinds, and stops tracing. Not for concurrent use. */
+int32_t dspark_kernel_kinds(void);
+const char* dspark_kernel_name(int32_t kind);
+dspark_status dspark_trace_begin(uint64_t mask, int32_t capacity);
+dspark_status dspark_trace_end(double* total_ms, int64_t* launches, int32_t n_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,150 @@
+"""C ABI contract on the host: the library loads, exports every function that
+include/dspark.h declares, sizes workspaces, and rejects bad arguments with
+the documented status before touching the GPU (these calls never reach a
+HIP API)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_draft_context_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_draft_context_amd.build import build
+        build()
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dspark_ctx_fuse", "dspark_block_layer", "dspark_block_forward",
+              "dspark_workspace_size", "dspark_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = L.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dspark_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTS) == declared_functions()
+
+
+def test_version_and_kernel_names(L):
+    import block_draft_context_amd as B
+    assert "gfx950" in B.version()
+    names = B.kernel_names()
+    assert "attn_partial" in names and "gemm_ctx_kv" in names and len(set(names)) == len(names)
+
+
+def _dims(L, **kw):
+    base = dict(m=4, H=2560, d=1024, n_heads=8, gamma=5, n_layers=5, ff=2048, eps=1e-6, dtype=1)
+    base.update(kw)
+    return L.Dims(**base)
+
+
+def _cu(vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def test_workspace_size_grows_with_context(L):
+    lib = L.lib()
+    dm = _dims(L)
+    sizes = [lib.dspark_workspace_size(L.OP_BLOCK_FORWARD, ctypes.byref(dm), 1, _cu([0, T]))
+             for T in (0, 64, 2048, 131072)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    # K/V of 5 layers for 131072 rows in bf16 alone is 2.5 GiB
+    assert sizes[-1] >= 5 * 2 * 131072 * 1024 * 2
+    one = lib.dspark_workspace_size(L.OP_BLOCK_LAYER, ctypes.byref(dm), 1, _cu([0, 131072]))
+    assert one < sizes[-1]
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=1000), 2, "head_dim"),
+    (dict(n_heads=3), 1, "not divisible"),
+    (dict(gamma=0), 1, "positive"),
+    (dict(gamma=17), 2, "gamma"),
+    (dict(dtype=7), 2, "dtype"),
+    (dict(H=100), 2, "multiple of 64"),
+    (dict(ff=100), 2, "multiple of 128"),
+    (dict(n_layers=0), 1, "n_layers"),
+    (dict(eps=-1.0), 1, "eps"),
+])
+def test_bad_dims_are_rejected(L, kw, status, msg):
+    lib = L.lib()
+    dm = _dims(L, **kw)
+    assert lib.dspark_workspace_size(L.OP_BLOCK_FORWARD, ctypes.byref(dm), 1, _cu([0, 8])) == 0
+    assert msg in lib.dspark_last_error().decode()
+    taps = (ctypes.c_void_p * 4)(*[0x1000] * 4)
+    st = lib.dspark_block_forward(ctypes.byref(dm), 1, _cu([0, 8]), 0x2000, taps, 2560, 0x3000, 0x4000,
+                                  0x5000, 0x6000, None, None, None, 0x7000, 0x8000, 1 << 40, None)
+    assert st == status
+
+
+@pytest.mark.parametrize("cu,msg", [([1, 8], "cu[0]"), ([0, 8, 4], "decreasing")])
+def test_bad_offsets_are_rejected(L, cu, msg):
+    lib = L.lib()
+    dm = _dims(L)
+    A = len(cu) - 1
+    assert lib.dspark_workspace_size(L.OP_CTX_FUSE, ctypes.byref(dm), A, _cu(cu)) == 0
+    assert msg in lib.dspark_last_error().decode()
+
+
+def test_entry_points_check_pointers_and_workspace(L):
+    lib = L.lib()
+    dm = _dims(L)
+    cu = _cu([0, 128])
+    taps = (ctypes.c_void_p * 4)(*[0x1000] * 4)
+    need = lib.dspark_workspace_size(L.OP_CTX_FUSE, ctypes.byref(dm), 1, cu)
+    # workspace too small
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps, 2560, 0x3000, 0x4000, 0x5000,
+                             0x6000, need - 1, None)
+    assert st == L.EWORKSPACE and "workspace" in lib.dspark_last_error().decode()
+    # misaligned output
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps, 2560, 0x3000, 0x4000, 0x5004,
+                             0x6000, need, None)
+    assert st == L.EINVAL and "aligned" in lib.dspark_last_error().decode()
+    # ld_tap below H
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps, 2048, 0x3000, 0x4000, 0x5000,
+                             0x6000, need, None)
+    assert st == L.EINVAL and "ld_tap" in lib.dspark_last_error().decode()
+    # NULL tap
+    taps0 = (ctypes.c_void_p * 4)(0x1000, None, 0x1000, 0x1000)
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps0, 2560, 0x3000, 0x4000, 0x5000,
+                             0x6000, need, None)
+    assert st == L.EINVAL and "taps[1]" in lib.dspark_last_error().decode()
+    # NULL layer weight
+    lw = L.LayerWeights(0x1000, 0x1000, None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    need_l = lib.dspark_workspace_size(L.OP_BLOCK_LAYER, ctypes.byref(dm), 1, cu)
+    st = lib.dspark_block_layer(ctypes.byref(dm), 1, cu, 0x2000, 0x3000, 0x4000, 0x4000,
+                                ctypes.byref(lw), 0x6000, need_l, None)
+    assert st == L.EINVAL and "wk" in lib.dspark_last_error().decode()
+    # too many block rows
+    st = lib.dspark_block_layer(ctypes.byref(dm), 300, _cu([0] * 301), 0x2000, 0x3000, 0x4000,
+                                0x4000, ctypes.byref(lw), 0x6000, need_l, None)
+    assert st == L.EUNSUPPORTED
+
+
+def test_python_binding_raises_with_message(L):
+    import block_draft_context_amd as B
+    with pytest.raises(B.DsparkError) as e:
+        B.workspace_size(B.OP_BLOCK_FORWARD, B.DsparkDims(m=2, H=64, d=128, n_heads=3, gamma=2,
+                                                          n_layers=1, ff=128), [0, 4])
+    assert "not divisible" in str(e.value)

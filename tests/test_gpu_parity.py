@@ -1,0 +1,230 @@
+"""HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Tolerances: normwise max relative error 1e-4 for float32 storage and 2e-2 for
+bfloat16 storage with float32 accumulation. Sizes span several GEMM tiles,
+several attention chunks and ragged tails; the oracle finishes each in
+seconds.
+"""
+import hashlib
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_helpers import TOL, Uploaded, dims_of, oracle_forward, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+B = pytest.importorskip("block_draft_context_amd")
+
+
+def _forward(w, x, u=None, h_ctx_out=False):
+    u = u or Uploaded(w, x)
+    dims = dims_of(B, w)
+    h = torch.empty((x["T"], w.d), dtype=u.dt, device="cuda:0") if h_ctx_out else None
+    out = B.block_forward(dims, u.cu, u.taps, u.w_c, u.ctx_norm, u.block_in, u.block_pos,
+                          u.layers, u.out_norm, cu_dev=u.cu_dev, h_ctx_out=h)
+    torch.cuda.synchronize()
+    return out, h, u
+
+
+CASES = {
+    # name: workload kwargs
+    "tiny-f32": dict(W.get_workload("tiny-f32-L64").__dict__),
+    "f32-ragged-hd32": dict(name="f32r", seed_id=11, A=3, m=2, H=128, d=128, n_heads=4, gamma=5,
+                            n_layers=2, ff=256, dtype="f32", lengths=[70, 0, 333]),
+    "bf16-ragged-hd128": dict(name="b1", seed_id=12, A=3, m=2, H=192, d=256, n_heads=2, gamma=5,
+                              n_layers=2, ff=512, dtype="bf16", lengths=[300, 0, 1000]),
+    "bf16-hd64-gamma8": dict(name="b2", seed_id=13, A=2, m=3, H=128, d=256, n_heads=4, gamma=8,
+                             n_layers=2, ff=256, dtype="bf16", lengths=[517, 64]),
+    "bf16-hd32-gamma1": dict(name="b3", seed_id=14, A=4, m=1, H=64, d=128, n_heads=4, gamma=1,
+                             n_layers=1, ff=384, dtype="bf16", lengths=[1, 65, 129, 0]),
+    "bf16-gamma16": dict(name="b4", seed_id=15, A=2, m=2, H=128, d=256, n_heads=2, gamma=16,
+                         n_layers=1, ff=256, dtype="bf16", lengths=[2000, 31]),
+    "bf16-all-empty": dict(name="b5", seed_id=16, A=2, m=2, H=64, d=128, n_heads=1, gamma=4,
+                           n_layers=2, ff=256, dtype="bf16", lengths=[0, 0]),
+    "bf16-long-one": dict(name="b6", seed_id=17, A=1, m=4, H=256, d=512, n_heads=4, gamma=5,
+                          n_layers=1, ff=1024, dtype="bf16", lengths=[9000]),
+}
+
+
+def _make(case, gains="unit"):
+    kw = dict(CASES[case])
+    lengths = kw.pop("lengths", None)
+    for k in ("L_range", "outlier_scale"):
+        kw.pop(k, None)
+    if lengths is None:
+        w = W.Workload(**kw)
+    else:
+        kw.pop("L", None)
+        w = W.Workload(**{**kw, "L": 0})
+    x = W.make_inputs(w, gains=gains, lengths=lengths)
+    return w, x
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_block_forward_matches_oracle(case):
+    w, x = _make(case)
+    out, h, _ = _forward(w, x, h_ctx_out=True)
+    tr = {}
+    ref = oracle_forward(O, w, x, trace=tr)
+    got = out.cpu().numpy()
+    print(f"{case}: lengths={x['lengths'].tolist()}")
+    assert np.all(np.isfinite(got))
+    e = rel_err(got, ref)
+    print(f"  block_out rel err {e:.3e}")
+    assert e < TOL[w.dtype]
+    if x["T"] > 0:
+        eh = rel_err(h.float().cpu().numpy(), tr["C"])
+        print(f"  H_ctx rel err {eh:.3e}")
+        assert eh < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-hd64-gamma8"])
+def test_random_gains(case):
+    """Norm gains ~ U(0.5, 1.5): unit gains would hide a kernel that skips them."""
+    w, x = _make(case, gains="random")
+    out, h, _ = _forward(w, x, h_ctx_out=True)
+    tr = {}
+    ref = oracle_forward(O, w, x, trace=tr)
+    assert rel_err(out.cpu().numpy(), ref) < TOL[w.dtype]
+    assert rel_err(h.float().cpu().numpy(), tr["C"]) < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-hd32-gamma1"])
+def test_ctx_fuse_matches_oracle(case):
+    w, x = _make(case, gains="random")
+    u = Uploaded(w, x)
+    h = B.ctx_fuse(dims_of(B, w), u.cu, u.taps, u.w_c, u.ctx_norm, cu_dev=u.cu_dev)
+    torch.cuda.synchronize()
+    ref = O.ctx_fuse(x["taps"], x["w_c"], x["ctx_norm"], w.eps)
+    e = rel_err(h.float().cpu().numpy(), ref)
+    print(f"{case}: H_ctx rel err {e:.3e}")
+    assert e < TOL[w.dtype]
+
+
+def _storage(w, a):
+    return W.bf16_round(np.asarray(a, dtype=np.float32)) if w.dtype == "bf16" else np.asarray(a, np.float32)
+
+
+@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-gamma16"])
+def test_block_layer_matches_oracle_and_keeps_context(case):
+    """One layer on a given context; H_ctx is bitwise unchanged by the call."""
+    w, x = _make(case, gains="random")
+    u = Uploaded(w, x)
+    C = _storage(w, O.ctx_fuse(x["taps"], x["w_c"], x["ctx_norm"], w.eps))
+    D = O.block_init(x["block_in"], x["block_pos"]).astype(np.float32)
+    h = torch.from_numpy(C).to(device="cuda:0", dtype=u.dt)
+    d_in = torch.from_numpy(D).to("cuda:0")
+    before = hashlib.sha256(h.view(torch.uint8).cpu().numpy().tobytes()).hexdigest()
+    out = B.block_layer(dims_of(B, w), u.cu, h, d_in, u.layers[0], cu_dev=u.cu_dev)
+    torch.cuda.synchronize()
+    after = hashlib.sha256(h.view(torch.uint8).cpu().numpy().tobytes()).hexdigest()
+    assert before == after, "H_ctx changed"
+    ref = O.block_layer(C, x["cu"], D, x["layers"][0], w.n_heads, w.eps)
+    e = rel_err(out.cpu().numpy(), ref)
+    print(f"{case}: layer rel err {e:.3e}")
+    assert e < TOL[w.dtype]
+
+
+def test_block_layer_in_place():
+    """d_out may alias d_in."""
+    w, x = _make("bf16-ragged-hd128")
+    u = Uploaded(w, x)
+    C = _storage(w, O.ctx_fuse(x["taps"], x["w_c"], x["ctx_norm"], w.eps))
+    D = O.block_init(x["block_in"], x["block_pos"]).astype(np.float32)
+    h = torch.from_numpy(C).to(device="cuda:0", dtype=u.dt)
+    d1 = torch.from_numpy(D).to("cuda:0")
+    d2 = d1.clone()
+    ref = B.block_layer(dims_of(B, w), u.cu, h, d1, u.layers[0], cu_dev=u.cu_dev)
+    B.block_layer(dims_of(B, w), u.cu, h, d2, u.layers[0], cu_dev=u.cu_dev, d_out=d2)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, d2)
+
+
+def test_layer_chain_equals_forward():
+    """ctx_fuse + block_layer per layer + output norm reproduces block_forward."""
+    w, x = _make("bf16-hd64-gamma8", gains="random")
+    out, h, u = _forward(w, x, h_ctx_out=True)
+    dims = dims_of(B, w)
+    h2 = B.ctx_fuse(dims, u.cu, u.taps, u.w_c, u.ctx_norm, cu_dev=u.cu_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h2)
+    D = (u.block_in + u.block_pos[None]).contiguous()
+    for lw in u.layers:
+        D = B.block_layer(dims, u.cu, h2, D, lw, cu_dev=u.cu_dev)
+    torch.cuda.synchronize()
+    ref = O.rmsnorm(D.cpu().numpy().astype(np.float64), x["out_norm"], w.eps)
+    assert rel_err(out.cpu().numpy(), ref) < 1e-5
+
+
+def test_deterministic():
+    w, x = _make("bf16-ragged-hd128")
+    a, _, u = _forward(w, x)
+    b, _, _ = _forward(w, x, u)
+    assert torch.equal(a, b)
+
+
+def test_varlen_equals_separate_runs():
+    """The packed batch equals single-sequence runs of the same inputs."""
+    w, x = _make("bf16-ragged-hd128")
+    out, _, _ = _forward(w, x)
+    cu = x["cu"]
+    for b in range(w.A):
+        xb = dict(x)
+        xb["taps"] = [t[cu[b]:cu[b + 1]] for t in x["taps"]]
+        xb["cu"] = np.array([0, cu[b + 1] - cu[b]])
+        xb["T"] = int(cu[b + 1] - cu[b])
+        xb["block_in"] = x["block_in"][b:b + 1]
+        wb = W.Workload(**{**w.__dict__, "A": 1})
+        ob, _, _ = _forward(wb, xb)
+        assert rel_err(ob[0].cpu().numpy(), out[b].cpu().numpy()) < 1e-5, b
+
+
+def test_block_permutation_equivariance():
+    """Bidirectional block: permuting block rows and block_pos permutes outputs."""
+    w, x = _make("bf16-hd64-gamma8")
+    out, _, _ = _forward(w, x)
+    perm = np.array([3, 0, 7, 1, 6, 2, 5, 4])
+    xp = dict(x)
+    xp["block_in"] = x["block_in"][:, perm]
+    xp["block_pos"] = x["block_pos"][perm]
+    outp, _, _ = _forward(w, xp)
+    assert rel_err(outp.cpu().numpy(), out[:, perm].cpu().numpy()) < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads against stored oracle outputs (tests/golden)
+# ---------------------------------------------------------------------------
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("mk", os.path.join(GOLD, "make_fullsize_expected.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    return mk
+
+
+@pytest.mark.parametrize("name", [n for n, w in W.WORKLOADS.items() if w.dtype == "bf16"])
+def test_full_size_against_stored_oracle(name):
+    mk = _golden(name)
+    path = mk.expected_path(name)
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle output {os.path.basename(path)}")
+    g = np.load(path, allow_pickle=False)
+    w = W.get_workload(name)
+    x = W.make_inputs(w)
+    assert str(g["fingerprint"]) == mk.fingerprint(x), "inputs differ from the stored run"
+    print(f"{name}: T={x['T']}", flush=True)
+    out, h, u = _forward(w, x, h_ctx_out=True)
+    e = rel_err(out.cpu().numpy(), g["out"])
+    idx = torch.as_tensor(g["C_idx"], device="cuda:0")
+    eh = rel_err(h.index_select(0, idx).float().cpu().numpy(), g["C_rows"])
+    print(f"  block_out rel err {e:.3e}, sampled H_ctx rel err {eh:.3e}")
+    assert e < TOL["bf16"] and eh < TOL["bf16"]
