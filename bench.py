@@ -1,0 +1,220 @@
+"""Throughput of the draft-block forward (Eq 2 + Eq 3) on one MI355X.
+
+One step = one dspark_block_forward over one batch of synthetic context:
+the Eq 2 fuse, the context K/V re-projection of every draft layer, and the
+block side of every layer (projections, split-K attention + combine, SwiGLU
+FFN, norms). Inputs are resident in HBM before the timed region.
+
+Prints one JSON line: context tokens/s (value) and draft blocks/s, the
+roofline of the dominant kernel (its average duration from HIP events taken
+inside the timed region), and the CPU oracle timed on a bounded sample of the
+same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+import workloads as W  # noqa: E402
+
+DEFAULT_WORKLOAD = "bf16-L2048-d1024"
+METRIC = "context tokens/s through Eq2+Eq3 and draft blocks/s; % MFMA / HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_work(name, w, T, A):
+    """Algorithmic work of ONE launch of a kernel kind: (amount, unit, bound).
+
+    gemm_ctx_fuse  2*T*(m*H)*d flop          (Eq 2 projection)
+    gemm_ctx_kv    2*T*d*(2*N*d) flop        (K and V of all N layers at once)
+    attn_partial   K_c + V_c of one layer (2*T*d*elt bytes) plus the queries
+                   read and partials written (4 * A*gamma*d * 4 bytes)
+    """
+    esz = 2 if w.dtype == "bf16" else 4
+    if name == "gemm_ctx_fuse":
+        return 2.0 * T * w.m * w.H * w.d, "flop", "mfma"
+    if name == "gemm_ctx_kv":
+        return 2.0 * T * w.d * 2 * w.n_layers * w.d, "flop", "mfma"
+    if name == "attn_partial":
+        return 2.0 * T * w.d * esz + 4.0 * A * w.gamma * w.d * 4, "byte", "hbm"
+    return None
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gemm_ctx_fuse": ["block_draft_context_amd/csrc/gemm.hip", "block_draft_context_amd/csrc/common.h"],
+    "gemm_ctx_kv": ["block_draft_context_amd/csrc/gemm.hip", "block_draft_context_amd/csrc/common.h",
+                    "block_draft_context_amd/csrc/kv_layout.h"],
+    "attn_partial": ["block_draft_context_amd/csrc/attention.hip", "block_draft_context_amd/csrc/common.h",
+                     "block_draft_context_amd/csrc/kv_layout.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current source of that kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, seconds):
+    """The oracle (float32 mode) on full forwards of the same workload, repeated
+    until `seconds` of host time have passed."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.block_forward(x["taps"], x["w_c"], x["ctx_norm"], x["cu"], x["block_in"],
+                        x["block_pos"], x["layers"], x["out_norm"], w.n_heads, w.eps,
+                        dtype=np.float32)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": reps * x["T"] / el, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} full forwards of {w.name} (T={x['T']}) in float32 numpy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernels", action="store_true", help="also print per-kernel times")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run a plain elementwise copy of BYTES bytes (3 launches), the "
+                         "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs on a single MI355X "
+              "(no sharding or collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_draft_context_amd as B
+    from gpu_helpers import Uploaded, dims_of
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    w = W.get_workload(args.workload)
+    x = W.make_inputs(w)
+    T, A = x["T"], w.A
+    u = Uploaded(w, x)
+    dims = dims_of(B, w)
+    fwd = B.PreparedForward(dims, u.cu, u.taps, u.w_c, u.ctx_norm, u.block_in, u.block_pos,
+                            u.layers, u.out_norm, cu_dev=u.cu_dev)
+    names = B.kernel_names()
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+
+    # untimed pass with every kind traced: per-kernel breakdown, dominant kernel
+    B.trace_begin(names, capacity=4096)
+    fwd()
+    torch.cuda.synchronize()
+    per_kind = B.trace_end()
+    candidates = {k: v for k, v in per_kind.items() if kernel_work(k, w, T, A)}
+    dominant = max(candidates, key=lambda k: candidates[k][0])
+
+    # timed region: K steps, events only around the dominant kernel's launches
+    B.trace_begin([dominant], capacity=args.steps * 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    dom = B.trace_end()[dominant]
+    ms_per_step = el * 1e3 / args.steps
+
+    amount, unit, bound = kernel_work(dominant, w, T, A)
+    avg_s = dom[0] / dom[1] / 1e3
+    if unit == "flop":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = amount / avg_s / 1e12
+        runit = "TFLOP/s"
+    else:
+        peak = PEAK_HBM_GBS
+        achieved = amount / avg_s / 1e9
+        runit = "GB/s"
+    roofline = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
+                "unit": runit, "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dominant, w.name),
+                "avg_launch_us": round(avg_s * 1e6, 2),
+                "work_per_launch": amount, "work_unit": unit}
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) taps, N(0,0.02) weights)",
+        "config": {"workload": w.name, "A": A, "T": T, "m": w.m, "H": w.H, "d": w.d,
+                   "n_heads": w.n_heads, "gamma": w.gamma, "n_layers": w.n_layers, "ff": w.ff},
+        "draft_blocks_per_s": round(A / (ms_per_step / 1e3), 2),
+        "roofline": roofline,
+    }
+    if args.kernels:
+        res["kernels_us_per_step"] = {k: round(v[0] * 1e3, 2) for k, v in
+                                      sorted(per_kind.items(), key=lambda kv: -kv[1][0])}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,7 @@ from . import _lib as L
 
 __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
-    "version", "kernel_names", "trace_begin", "trace_end", "DsparkError",
+    "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
 ]
 
 DsparkError = L.DsparkError
@@ -164,6 +164,36 @@ def block_forward(dims: DsparkDims, cu, taps, w_c, ctx_norm, block_in, block_pos
         _ptr(w_c), _ptr(ctx_norm), _ptr(block_in), _ptr(block_pos), arr, _ptr(out_norm),
         _ptr(h_ctx_out), _ptr(block_out), _ptr(ws), nbytes, _stream(stream)))
     return block_out
+
+
+class PreparedForward:
+    """block_forward with every argument marshalled once; calling it only
+    enqueues the forward (used to time the library without Python overhead).
+    The tensors passed in must stay alive while this object is used."""
+
+    def __init__(self, dims: DsparkDims, cu, taps, w_c, ctx_norm, block_in, block_pos,
+                 layers, out_norm=None, *, cu_dev=None, h_ctx_out=None, block_out=None,
+                 ws=None, stream=None):
+        device = block_in.device
+        self.cu_h = _cu_host(cu)
+        self.block_out = torch.empty_like(block_in) if block_out is None else block_out
+        self.cu_dev = _cu_dev(cu, cu_dev, device)
+        self.ws, nbytes = _workspace(L.OP_BLOCK_FORWARD, dims, cu, ws, device)
+        self.dm = dims.c()
+        self.layers = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+        self.taps = _tap_ptrs(taps)
+        self._keep = (taps, w_c, ctx_norm, block_in, block_pos, layers, out_norm, h_ctx_out)
+        self.args = (ctypes.byref(self.dm), len(self.cu_h) - 1, self.cu_h, _ptr(self.cu_dev),
+                     self.taps, _tap_ld(taps), _ptr(w_c), _ptr(ctx_norm), _ptr(block_in),
+                     _ptr(block_pos), self.layers, _ptr(out_norm), _ptr(h_ctx_out),
+                     _ptr(self.block_out), _ptr(self.ws), nbytes, _stream(stream))
+        self.fn = L.lib().dspark_block_forward
+
+    def __call__(self) -> torch.Tensor:
+        st = self.fn(*self.args)
+        if st != L.OK:
+            L.check(st)
+        return self.block_out
 
 
 def trace_begin(kinds: Sequence[str], capacity: int = 4096) -> None:

@@ -5,9 +5,10 @@
 // context part is long and read once per layer, so it is split into chunks
 // of `chunk` keys: one workgroup per (chunk, head) streams the chunk's K and
 // V once and leaves an unnormalised partial (m, l, o) per query, as the
-// split-chunk attention + combine kernels of dspark-runtime.js do. The
-// combine pass then adds the gamma block keys as one more partial and merges
-// all partials per (sequence, head) with the log-sum-exp identity:
+// split-chunk attention + combine kernels of dspark-runtime.js do. The last
+// workgroup of a (sequence, head) to finish (an atomic ticket; nobody waits)
+// then merges all its partials together with the gamma block keys by the
+// log-sum-exp identity
 //   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  o = sum_c o_c 2^(m_c - M) / l.
 // Scores are kept in base 2: Q arrives pre-multiplied by hd^-1/2 * log2(e).
 //
@@ -26,27 +27,40 @@ namespace dspark {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// keys per chunk: aim for ~2048 (chunk, head) workgroups, chunk in [256, 8192]
+// keys per chunk: aim for ~1024 (chunk, head) workgroups, chunk in [256, 8192]
 int attention_chunk(int64_t T, int n_heads, int A) {
   (void)A;
-  int64_t c = (T * n_heads + 2047) / 2048;
+  int64_t c = (T * n_heads + 1023) / 1024;
   c = ((c + 63) / 64) * 64;
   if (c < 256) c = 256;
   if (c > 8192) c = 8192;
   return (int)c;
 }
 
-// chunk_prefix[b] = sum_{b' < b} ceil(L_b' / chunk), b = 0..A (one workgroup).
+int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
+  int64_t n = 0;
+  for (int b = 0; b < A; ++b) {
+    const int64_t L = cu_host[b + 1] - cu_host[b];
+    n += L > 0 ? (L + chunk - 1) / chunk : 1;
+  }
+  return n;
+}
+
+// chunk_prefix[b] = sum_{b' < b} max(1, ceil(L_b' / chunk)), b = 0..A (one
+// workgroup; an empty sequence still gets one tile, which finds no keys and
+// runs the combine). Also zeroes `ncounters` counters.
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int A, int chunk,
-                                                   int32_t* __restrict__ prefix) {
+                                                   int32_t* __restrict__ prefix,
+                                                   unsigned* __restrict__ counters, int ncounters) {
   __shared__ int32_t sums[256];
   const int tid = threadIdx.x;
+  for (int i = tid; i < ncounters; i += 256) counters[i] = 0u;
   const int per = (A + 255) / 256;
   const int b0 = tid * per, b1 = min(A, b0 + per);
   int32_t local = 0;
   for (int b = b0; b < b1; ++b) {
     const int32_t L = cu[b + 1] - cu[b];
-    local += L > 0 ? (L + chunk - 1) / chunk : 0;
+    local += L > 0 ? (L + chunk - 1) / chunk : 1;
   }
   sums[tid] = local;
   __syncthreads();
@@ -60,50 +74,56 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
   for (int b = b0; b < b1; ++b) {
     prefix[b] = run;
     const int32_t L = cu[b + 1] - cu[b];
-    run += L > 0 ? (L + chunk - 1) / chunk : 0;
+    run += L > 0 ? (L + chunk - 1) / chunk : 1;
   }
   if (tid == 255) prefix[A] = sums[255];
 }
 
 hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
-                       hipStream_t s) {
+                       unsigned* counters, int ncounters, hipStream_t s) {
   trace_pre(K_PLAN, s);
-  plan_kernel<<<1, 256, 0, s>>>(cu_dev, A, chunk, chunk_prefix);
+  plan_kernel<<<1, 256, 0, s>>>(cu_dev, A, chunk, chunk_prefix, counters, ncounters);
   trace_post(K_PLAN, s);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// partial kernel: grid (total_chunks, n_heads), 256 threads (4 waves)
-// part_o  [total_chunks][n_heads][G][HD]   unnormalised output
-// part_ml [total_chunks][n_heads][G][2]    (max, sum) in base-2 units
+// grid (total_tiles, n_heads), 256 threads (4 waves)
+// part_o  [total_tiles][n_heads][G][HD]   unnormalised output
+// part_ml [total_tiles][n_heads][G][2]    (max, sum) in base-2 units
+// attn    [A*G][n_heads*HD]              normalised output (combine)
 // ---------------------------------------------------------------------------
 template <typename S, int HD, int G>
-__global__ __launch_bounds__(256) void attn_partial_kernel(
-    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads,
-    int layer, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A,
-    int chunk, int total_chunks, float* __restrict__ part_o, float* __restrict__ part_ml) {
+__global__ __launch_bounds__(256) void attn_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
+    const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int chunk,
+    int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml,
+    unsigned* __restrict__ counters, float* __restrict__ attn) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
   constexpr int NKV = HD / E;            // K vectors per key row
   constexpr int KG = 128 / HD;           // key groups in the P.V lane split
   constexpr int NLD = 64 / (KG * R);     // V loads per 64-key block
-  constexpr int d_model_unused = 0;
-  (void)d_model_unused;
+  constexpr int NG = 512 / HD;           // chunk groups in the combine (NG * HD/2 = 256)
 
   __shared__ __attribute__((aligned(16))) float qs[G][HD];
   __shared__ __attribute__((aligned(16))) float ps[4][G][64];
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
-  __shared__ __attribute__((aligned(16))) float red_o[4][G][HD];
+  __shared__ __attribute__((aligned(16))) float red_o[NG][G][HD];   // NG >= 4 waves
+  __shared__ float sb[G][G];
+  __shared__ float Mq[G];
+  __shared__ float Lq[G];
+  __shared__ unsigned s_ticket;
 
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int dev_total = prefix[A];
-  if (tile >= total_chunks || tile >= dev_total) return;
+  if (tile >= total_tiles || tile >= dev_total) return;
 
-  // sequence owning this chunk: largest b with prefix[b] <= tile
+  // sequence owning this tile: largest b with prefix[b] <= tile
   int lo = 0, hi = A - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -111,8 +131,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   const int b = lo;
   const int c = tile - prefix[b];
-  const int64_t k0 = (int64_t)cu[b] + (int64_t)c * chunk;
-  const int64_t k1 = min((int64_t)cu[b + 1], k0 + chunk);
+  const int64_t kseq0 = cu[b], kseq1 = cu[b + 1];
+  const int64_t k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
+  const int64_t k1 = min(kseq1, k0 + chunk);
 
   const int d = HD * n_heads;
   for (int i = tid; i < G * HD; i += 256) {
@@ -134,75 +155,78 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   const int kg = lane / (HD / 2), cp = lane % (HD / 2);
 
-  const int64_t blk0 = k0 >> 6, blk1 = (k1 - 1) >> 6;
-  for (int64_t blk = blk0 + wave; blk <= blk1; blk += 4) {
-    // ---- scores: lane owns key blk*64 + lane
-    const int64_t key = blk * 64 + lane;
-    const bool valid = key >= k0 && key < k1;
-    const S* kp = Kh + blk * 64 * HD + lane * E;
-    float s[G];
+  if (k1 > k0) {
+    const int64_t blk0 = k0 >> 6, blk1 = (k1 - 1) >> 6;
+    for (int64_t blk = blk0 + wave; blk <= blk1; blk += 4) {
+      // ---- scores: lane owns key blk*64 + lane
+      const int64_t key = blk * 64 + lane;
+      const bool valid = key >= k0 && key < k1;
+      const S* kp = Kh + blk * 64 * HD + lane * E;
+      float s[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) s[j] = 0.f;
+      for (int j = 0; j < G; ++j) s[j] = 0.f;
 #pragma unroll 4
-    for (int i = 0; i < NKV; ++i) {
-      float kf[E];
-      Vec16<S>::unpack(ld16(kp + i * 64 * E), kf);
+      for (int i = 0; i < NKV; ++i) {
+        float kf[E];
+        Vec16<S>::unpack(ld16(kp + i * 64 * E), kf);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
+        for (int j = 0; j < G; ++j) {
 #pragma unroll
-        for (int e = 0; e < E; e += 4) {
-          const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qs[j][i * E + e]);
-          s[j] = fmaf(q4[0], kf[e], s[j]);
-          s[j] = fmaf(q4[1], kf[e + 1], s[j]);
-          s[j] = fmaf(q4[2], kf[e + 2], s[j]);
-          s[j] = fmaf(q4[3], kf[e + 3], s[j]);
+          for (int e = 0; e < E; e += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qs[j][i * E + e]);
+            s[j] = fmaf(q4[0], kf[e], s[j]);
+            s[j] = fmaf(q4[1], kf[e + 1], s[j]);
+            s[j] = fmaf(q4[2], kf[e + 2], s[j]);
+            s[j] = fmaf(q4[3], kf[e + 3], s[j]);
+          }
         }
       }
-    }
-    // ---- online softmax over this block (wave-uniform max)
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float sv = valid ? s[j] : kNegInf;
-      const float bm = wave_max(sv);
-      const float mn = fmaxf(m_run[j], bm);
-      const float alpha = exp2f(m_run[j] - mn);   // 0 when m_run = -inf
-      const float p = exp2f(sv - mn);             // 0 for masked keys
-      l_run[j] = l_run[j] * alpha + p;
-      o[j][0] *= alpha;
-      o[j][1] *= alpha;
-      m_run[j] = mn;
-      ps[wave][j][lane] = p;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per load
-    const S* vp = Vh + blk * 64 * HD + lane * E;
-#pragma unroll 4
-    for (int ld = 0; ld < NLD; ++ld) {
-      float vf[E];
-      Vec16<S>::unpack(ld16(vp + ld * 64 * E), vf);
-      const int kb = ld * KG * R + kg * R;   // first key of this vector
+      // ---- online softmax over this block (wave-uniform max; every block
+      // holds at least one valid key)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        float pr[R];
-        if constexpr (R == 4) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(&ps[wave][j][kb]);
-          pr[0] = p4[0]; pr[1] = p4[1]; pr[2] = p4[2]; pr[3] = p4[3];
-        } else {
+        const float sv = valid ? s[j] : kNegInf;
+        const float bm = wave_max(sv);
+        const float mn = fmaxf(m_run[j], bm);
+        const float alpha = exp2f(m_run[j] - mn);   // 0 when m_run = -inf
+        const float p = exp2f(sv - mn);             // 0 for masked keys
+        l_run[j] = l_run[j] * alpha + p;
+        o[j][0] *= alpha;
+        o[j][1] *= alpha;
+        m_run[j] = mn;
+        ps[wave][j][lane] = p;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per load
+      const S* vp = Vh + blk * 64 * HD + lane * E;
+#pragma unroll 4
+      for (int ld = 0; ld < NLD; ++ld) {
+        float vf[E];
+        Vec16<S>::unpack(ld16(vp + ld * 64 * E), vf);
+        const int kb = ld * KG * R + kg * R;   // first key of this vector
 #pragma unroll
-          for (int r = 0; r < R; ++r) pr[r] = ps[wave][j][kb + r];
-        }
+        for (int j = 0; j < G; ++j) {
+          float pr[R];
+          if constexpr (R == 4) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&ps[wave][j][kb]);
+            pr[0] = p4[0]; pr[1] = p4[1]; pr[2] = p4[2]; pr[3] = p4[3];
+          } else {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          o[j][0] = fmaf(pr[r], vf[2 * r], o[j][0]);
-          o[j][1] = fmaf(pr[r], vf[2 * r + 1], o[j][1]);
+            for (int r = 0; r < R; ++r) pr[r] = ps[wave][j][kb + r];
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            o[j][0] = fmaf(pr[r], vf[2 * r], o[j][0]);
+            o[j][1] = fmaf(pr[r], vf[2 * r + 1], o[j][1]);
+          }
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   // ---- per-wave totals: l over lanes, o over key groups
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   __syncthreads();
 
-  // ---- merge the four waves and write this chunk's partial
+  // ---- merge the four waves and write this tile's partial
   const int64_t pbase = ((int64_t)tile * n_heads + h) * G;
   for (int i = tid; i < G * HD; i += 256) {
     const int j = i / HD, cc = i % HD;
@@ -249,24 +273,124 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     part_ml[(pbase + j) * 2 + 0] = M;
     part_ml[(pbase + j) * 2 + 1] = l;
   }
+
+  // ---- the last tile of (b, h) to finish merges every partial of (b, h)
+  __threadfence();
+  __syncthreads();
+  const int t0 = prefix[b], t1 = min(prefix[b + 1], total_tiles);
+  if (tid == 0) s_ticket = atomicAdd(&counters[b * n_heads + h], 1u);
+  __syncthreads();
+  if (s_ticket != (unsigned)(t1 - t0 - 1)) return;
+  __threadfence();
+  if (tid == 0) counters[b * n_heads + h] = 0u;
+
+  // block-key scores (the gamma block keys K_d, V_d in float32)
+  if (tid < G * G) {
+    const int j = tid / G, jj = tid % G;
+    const float* kr = Kd + (int64_t)(b * G + jj) * d + h * HD;
+    float sc = 0.f;
+    for (int cc = 0; cc < HD; ++cc) sc = fmaf(qs[j][cc], kr[cc], sc);
+    sb[j][jj] = sc;
+  }
+  __syncthreads();
+  // overall max per query (block keys and every tile), then the sum l
+  {
+    float mloc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) mloc[j] = kNegInf;
+    for (int t = t0 + tid; t < t1; t += 256) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        mloc[j] = fmaxf(mloc[j], part_ml[(((int64_t)t * n_heads + h) * G + j) * 2]);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float v = wave_max(mloc[j]);
+      if (lane == 0) red_m[wave][j] = v;
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int j = tid;
+      float M = fmaxf(fmaxf(red_m[0][j], red_m[1][j]), fmaxf(red_m[2][j], red_m[3][j]));
+      for (int jj = 0; jj < G; ++jj) M = fmaxf(M, sb[j][jj]);
+      Mq[j] = M;
+    }
+    __syncthreads();
+    float lloc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) lloc[j] = 0.f;
+    for (int t = t0 + tid; t < t1; t += 256) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float* ml = part_ml + (((int64_t)t * n_heads + h) * G + j) * 2;
+        const float mv = ml[0];
+        if (mv != kNegInf) lloc[j] += ml[1] * exp2f(mv - Mq[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float v = wave_sum(lloc[j]);
+      if (lane == 0) red_l[wave][j] = v;
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int j = tid;
+      float l = (red_l[0][j] + red_l[1][j]) + (red_l[2][j] + red_l[3][j]);
+      for (int jj = 0; jj < G; ++jj) l += exp2f(sb[j][jj] - Mq[j]);
+      Lq[j] = l;
+    }
+    __syncthreads();
+  }
+  // weighted sum of the tile outputs: thread (group grp, column pair cp2)
+  {
+    const int cp2 = tid % (HD / 2), grp = tid / (HD / 2);
+    float acc[G][2];
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = 0.f;
+    for (int t = t0 + grp; t < t1; t += NG) {
+      const int64_t pj = ((int64_t)t * n_heads + h) * G;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float mv = part_ml[(pj + j) * 2];
+        if (mv != kNegInf) {
+          const float wgt = exp2f(mv - Mq[j]);
+          const float* po = part_o + (pj + j) * HD + 2 * cp2;
+          acc[j][0] = fmaf(po[0], wgt, acc[j][0]);
+          acc[j][1] = fmaf(po[1], wgt, acc[j][1]);
+        }
+      }
+    }
+    float* red = &red_o[0][0][0];   // [NG][G][HD]
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      red[(grp * G + j) * HD + 2 * cp2] = acc[j][0];
+      red[(grp * G + j) * HD + 2 * cp2 + 1] = acc[j][1];
+    }
+    __syncthreads();
+    for (int i = tid; i < G * HD; i += 256) {
+      const int j = i / HD, cc = i % HD;
+      float v = 0.f;
+      for (int g2 = 0; g2 < NG; ++g2) v += red[(g2 * G + j) * HD + cc];
+      for (int jj = 0; jj < G; ++jj)
+        v = fmaf(exp2f(sb[j][jj] - Mq[j]), Vd[(int64_t)(b * G + jj) * d + h * HD + cc], v);
+      attn[(int64_t)(b * G + j) * d + h * HD + cc] = v / Lq[j];
+    }
+  }
 }
 
 template <typename S, int HD, int G>
-static void launch_attn_t(dim3 grid, hipStream_t s, const float* Q, const KVDesc& kv, int layer,
-                          const int32_t* cu, const int32_t* prefix, int A, int chunk, int total,
-                          float* po, float* pml) {
-  attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(Q, static_cast<const S*>(kv.base), kv.Tpad,
-                                                      kv.n_heads, layer, cu, prefix, A, chunk,
-                                                      total, po, pml);
+static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
+  attn_kernel<S, HD, G><<<grid, 256, 0, s>>>(a.Q, a.Kd, a.Vd, static_cast<const S*>(a.kv.base),
+                                             a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
+                                             a.chunk, a.total_tiles, a.part_o, a.part_ml,
+                                             a.counters, a.attn);
 }
 
 template <typename S, int HD>
-static bool dispatch_gamma(int gamma, dim3 grid, hipStream_t s, const float* Q, const KVDesc& kv,
-                           int layer, const int32_t* cu, const int32_t* prefix, int A, int chunk,
-                           int total, float* po, float* pml) {
+static bool dispatch_gamma(int gamma, dim3 grid, hipStream_t s, const AttnArgs& a) {
   switch (gamma) {
 #define DSPARK_G(g) \
-  case g: launch_attn_t<S, HD, g>(grid, s, Q, kv, layer, cu, prefix, A, chunk, total, po, pml); return true;
+  case g: launch_attn_t<S, HD, g>(grid, s, a); return true;
     DSPARK_G(1) DSPARK_G(2) DSPARK_G(3) DSPARK_G(4) DSPARK_G(5) DSPARK_G(6) DSPARK_G(7)
     DSPARK_G(8) DSPARK_G(9) DSPARK_G(10) DSPARK_G(11) DSPARK_G(12) DSPARK_G(13) DSPARK_G(14)
     DSPARK_G(15) DSPARK_G(16)
@@ -275,102 +399,22 @@ static bool dispatch_gamma(int gamma, dim3 grid, hipStream_t s, const float* Q, 
   }
 }
 
-hipError_t launch_attention(int dtype, const float* Q, const KVDesc& kv, int layer,
-                            const int32_t* cu_dev, const int32_t* chunk_prefix, int A, int gamma,
-                            int chunk, int total_chunks, float* part_o, float* part_ml,
-                            hipStream_t s) {
-  if (total_chunks == 0) return hipSuccess;
-  dim3 grid(total_chunks, kv.n_heads);
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  dim3 grid(a.total_tiles, a.kv.n_heads);
   bool ok = false;
   trace_pre(K_ATTN, s);
   if (dtype == 1) {
-    if (kv.hd == 128) ok = dispatch_gamma<bf16, 128>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
-    else if (kv.hd == 64) ok = dispatch_gamma<bf16, 64>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
-    else if (kv.hd == 32) ok = dispatch_gamma<bf16, 32>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+    if (a.kv.hd == 128) ok = dispatch_gamma<bf16, 128>(a.gamma, grid, s, a);
+    else if (a.kv.hd == 64) ok = dispatch_gamma<bf16, 64>(a.gamma, grid, s, a);
+    else if (a.kv.hd == 32) ok = dispatch_gamma<bf16, 32>(a.gamma, grid, s, a);
   } else {
-    if (kv.hd == 128) ok = dispatch_gamma<float, 128>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
-    else if (kv.hd == 64) ok = dispatch_gamma<float, 64>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
-    else if (kv.hd == 32) ok = dispatch_gamma<float, 32>(gamma, grid, s, Q, kv, layer, cu_dev, chunk_prefix, A, chunk, total_chunks, part_o, part_ml);
+    if (a.kv.hd == 128) ok = dispatch_gamma<float, 128>(a.gamma, grid, s, a);
+    else if (a.kv.hd == 64) ok = dispatch_gamma<float, 64>(a.gamma, grid, s, a);
+    else if (a.kv.hd == 32) ok = dispatch_gamma<float, 32>(a.gamma, grid, s, a);
   }
   trace_post(K_ATTN, s);
   if (!ok) return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// combine: grid (A, n_heads), 256 threads. Adds the gamma block keys (K_d,
-// V_d in float32) as one more partial, merges every chunk partial of the
-// sequence, normalises, writes attn[b*gamma + j][h*hd + c].
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
-    int A, int gamma, int d, int n_heads, const int32_t* __restrict__ prefix, int total_chunks,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    float* __restrict__ attn) {
-  __shared__ float sb[kMaxGamma][kMaxGamma];   // block-key probabilities (unnormalised)
-  __shared__ float mb[kMaxGamma];              // block-key max per query
-  __shared__ float Mq[kMaxGamma];              // overall max per query
-  __shared__ float inv_l[kMaxGamma];
-  const int b = blockIdx.x, h = blockIdx.y;
-  const int hd = d / n_heads;
-  const int tid = threadIdx.x;
-  const int c0 = min(prefix[b], total_chunks), c1 = min(prefix[b + 1], total_chunks);
-
-  // block-key scores: thread (j, jj) for j, jj < gamma (gamma^2 <= 256)
-  if (tid < gamma * gamma) {
-    const int j = tid / gamma, jj = tid % gamma;
-    const float* q = Q + (int64_t)(b * gamma + j) * d + h * hd;
-    const float* k = Kd + (int64_t)(b * gamma + jj) * d + h * hd;
-    float sc = 0.f;
-    for (int cc = 0; cc < hd; ++cc) sc = fmaf(q[cc], k[cc], sc);
-    sb[j][jj] = sc;
-  }
-  __syncthreads();
-  if (tid < gamma) {
-    const int j = tid;
-    float m = kNegInf;
-    for (int jj = 0; jj < gamma; ++jj) m = fmaxf(m, sb[j][jj]);
-    mb[j] = m;
-    float M = m;
-    for (int c = c0; c < c1; ++c) M = fmaxf(M, part_ml[(((int64_t)c * n_heads + h) * gamma + j) * 2]);
-    Mq[j] = M;
-    float l = 0.f;
-    for (int jj = 0; jj < gamma; ++jj) l += exp2f(sb[j][jj] - M);
-    for (int c = c0; c < c1; ++c) {
-      const float* ml = part_ml + (((int64_t)c * n_heads + h) * gamma + j) * 2;
-      l += ml[1] * exp2f(ml[0] - M);
-    }
-    inv_l[j] = 1.f / l;
-  }
-  __syncthreads();
-  if (tid < gamma * gamma) {
-    const int j = tid / gamma, jj = tid % gamma;
-    sb[j][jj] = exp2f(sb[j][jj] - Mq[j]);
-  }
-  __syncthreads();
-  for (int i = tid; i < gamma * hd; i += 256) {
-    const int j = i / hd, cc = i % hd;
-    const float M = Mq[j];
-    float acc = 0.f;
-    for (int jj = 0; jj < gamma; ++jj)
-      acc = fmaf(sb[j][jj], Vd[(int64_t)(b * gamma + jj) * d + h * hd + cc], acc);
-    for (int c = c0; c < c1; ++c) {
-      const int64_t pj = ((int64_t)c * n_heads + h) * gamma + j;
-      acc += part_o[pj * hd + cc] * exp2f(part_ml[pj * 2] - M);
-    }
-    attn[(int64_t)(b * gamma + j) * d + h * hd + cc] = acc * inv_l[j];
-  }
-}
-
-hipError_t launch_combine(const float* Q, const float* Kd, const float* Vd, int A, int gamma, int d,
-                          int n_heads, const int32_t* chunk_prefix, int total_chunks,
-                          const float* part_o, const float* part_ml, float* attn,
-                          hipStream_t s) {
-  dim3 grid(A, n_heads);
-  trace_pre(K_COMBINE, s);
-  combine_kernel<<<grid, 256, 0, s>>>(Q, Kd, Vd, A, gamma, d, n_heads, chunk_prefix, total_chunks,
-                                      part_o, part_ml, attn);
-  trace_post(K_COMBINE, s);
   return hipGetLastError();
 }
 

@@ -6,9 +6,12 @@
 // With at most a few dozen rows these products are weight-streaming bound, so
 // each one is a split-K "skinny" GEMM: every workgroup streams a 128-column x
 // KS-row slab of the [in, out] weight once (16-byte loads along the output
-// columns), multiplies it with the matching slab of the rows held in LDS, and
-// writes a float32 partial; small row kernels then reduce the partials and
-// apply the residual, the norms and the SiLU gate.
+// columns), multiplies it with the matching slab of the rows held in LDS and
+// writes a float32 partial. The last workgroup to finish a column slab (an
+// atomic ticket; nobody waits) sums the slab's partials in a fixed order and
+// applies the epilogue: the Q/K_d/V_d split, the residual, or SiLU(gate)*up;
+// the last slab to finish then applies the row RMSNorm that the next
+// projection needs.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,13 +24,16 @@ constexpr int SK_TK = 16;            // thread rows along K
 constexpr int SK_COLS = 8 * SK_TN;   // 128 columns per workgroup
 constexpr int SK_MT = 8;             // block rows per pass
 
-// K rows per thread (RPT) and K slabs (splits) so that (N/128) * splits
-// covers the GPU a few times over; the last slab may be partial.
+// K rows per thread (RPT) and K slabs (splits): about 256 workgroups over
+// the (N/128) column slabs, at least 2 rows per thread, and few enough slabs
+// that the last-arriving workgroup's reduction (M rows x 128 columns x splits
+// partials) stays short. The last slab may be partial.
 SkinnyPlan skinny_plan(int M, int N, int K) {
-  (void)M;
   const int nb = N / SK_COLS;
-  const int want = (1024 + nb - 1) / nb;
-  int rpt = 1;
+  int want = (256 + nb - 1) / nb;
+  const int cap = std::max(2, 512 / std::max(M, 1));
+  if (want > cap) want = cap;
+  int rpt = 2;
   while (rpt < 16 && (int64_t)SK_TK * rpt * want < K) rpt *= 2;
   SkinnyPlan p;
   p.rpt = rpt;
@@ -37,20 +43,31 @@ SkinnyPlan skinny_plan(int M, int N, int K) {
 
 template <typename S, int RPT>
 __global__ __launch_bounds__(256) void skinny_kernel(const float* __restrict__ X, int M, int K,
-                                                     BMats b, int N, float* __restrict__ part) {
+                                                     BMats b, int N, float* __restrict__ part,
+                                                     SkinnyEpi epi) {
   constexpr int KS = SK_TK * RPT;
   __shared__ __attribute__((aligned(16))) float xs[KS][SK_MT];
   __shared__ float red[SK_TK][SK_MT][SK_COLS + 4];
+  __shared__ unsigned s_ticket;
   const int tid = threadIdx.x;
   const int tn = tid % SK_TN, tk = tid / SK_TN;
-  const int n0 = blockIdx.x * SK_COLS;
+  const int nb = blockIdx.x;
   const int z = blockIdx.y;
+  const int nsplit = gridDim.y;
   const int kbase = z * KS;
-  const int mi = n0 / b.n_per;
-  const int c0 = n0 % b.n_per + tn * 8;
+  // this thread's 8 output columns: matrix `mi`, columns c0 .. c0+7 of it
+  int mi, c0;
+  if (epi.mode == SK_SWIGLU) {          // gate columns, then the matching up columns
+    mi = tn >> 3;
+    c0 = nb * 64 + (tn & 7) * 8;
+  } else {
+    const int gc = nb * SK_COLS + tn * 8;
+    mi = gc / b.n_per;
+    c0 = gc % b.n_per;
+  }
   const S* __restrict__ W = static_cast<const S*>(b.mat[mi]);
 
-  // this thread's weights: rows kbase + tk + SK_TK * r (< K), 8 columns
+  // weights of rows kbase + tk + SK_TK * r (< K), all loads issued up front
   float w[RPT][8];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
@@ -98,13 +115,91 @@ __global__ __launch_bounds__(256) void skinny_kernel(const float* __restrict__ X
       float v = 0.f;
 #pragma unroll
       for (int q = 0; q < SK_TK; ++q) v += red[q][mm][cc];
-      if (m0 + mm < M) part[((int64_t)z * M + m0 + mm) * N + n0 + cc] = v;
+      if (m0 + mm < M) part[((int64_t)z * M + m0 + mm) * N + nb * SK_COLS + cc] = v;
     }
+  }
+
+  // ---- the last workgroup of this column slab reduces the K slabs in a fixed
+  // order and applies the epilogue (no waiting: the others simply exit).
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_ticket = atomicAdd(&epi.counters[nb], 1u);
+  __syncthreads();
+  if (s_ticket != (unsigned)(nsplit - 1)) return;
+  __threadfence();
+  if (tid == 0) epi.counters[nb] = 0u;
+
+  float(*fin)[32][SK_COLS] = reinterpret_cast<float(*)[32][SK_COLS]>(&red[0][0][0]);
+  const int lc = tid & (SK_COLS - 1), half = tid >> 7;
+  const int zs = half == 0 ? 0 : nsplit / 2, ze = half == 0 ? nsplit / 2 : nsplit;
+  const int64_t zstride = (int64_t)M * N;
+  for (int m0 = 0; m0 < M; m0 += 32) {
+    const int mn = min(32, M - m0);
+    for (int mm = 0; mm < mn; ++mm) {
+      const float* pp = part + ((int64_t)m0 + mm) * N + nb * SK_COLS + lc;
+      float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+      int zz = zs;
+      for (; zz + 4 <= ze; zz += 4) {
+        v0 += pp[(zz + 0) * zstride];
+        v1 += pp[(zz + 1) * zstride];
+        v2 += pp[(zz + 2) * zstride];
+        v3 += pp[(zz + 3) * zstride];
+      }
+      for (; zz < ze; ++zz) v0 += pp[zz * zstride];
+      fin[half][mm][lc] = (v0 + v1) + (v2 + v3);
+    }
+    __syncthreads();
+    if (epi.mode == SK_SWIGLU) {
+      for (int i = tid; i < mn * 64; i += 256) {
+        const int mm = i / 64, c = i % 64;
+        const float g = fin[0][mm][c] + fin[1][mm][c];
+        const float u = fin[0][mm][c + 64] + fin[1][mm][c + 64];
+        epi.hid[(int64_t)(m0 + mm) * epi.ff + nb * 64 + c] = g / (1.f + __expf(-g)) * u;
+      }
+    } else {
+      for (int i = tid; i < mn * SK_COLS; i += 256) {
+        const int mm = i / SK_COLS, c = i % SK_COLS;
+        const int m = m0 + mm;
+        const float v = fin[0][mm][c] + fin[1][mm][c];
+        const int gc = nb * SK_COLS + c;
+        if (epi.mode == SK_QKV) {
+          const int seg = gc / epi.d, col = gc % epi.d;
+          const int64_t o = (int64_t)m * epi.d + col;
+          if (seg == 0) epi.q[o] = v * epi.qscale;
+          else if (seg == 1) epi.kd[o] = v;
+          else epi.vd[o] = v;
+        } else {
+          const int64_t o = (int64_t)m * N + gc;
+          epi.out[o] = epi.res[o] + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (epi.mode != SK_RESID || epi.g == nullptr) return;
+
+  // ---- the last slab to finish normalises every row: normed = RMSNorm(out; g)
+  const int nslabs = gridDim.x;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_ticket = atomicAdd(&epi.counters[nslabs], 1u);
+  __syncthreads();
+  if (s_ticket != (unsigned)(nslabs - 1)) return;
+  __threadfence();
+  if (tid == 0) epi.counters[nslabs] = 0u;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int m = wave; m < M; m += 4) {
+    const float* row = epi.out + (int64_t)m * N;
+    float ss = 0.f;
+    for (int c = lane; c < N; c += 64) ss += row[c] * row[c];
+    ss = wave_sum(ss);
+    const float sc = rsqrtf(ss / (float)N + epi.eps);
+    for (int c = lane; c < N; c += 64) epi.normed[(int64_t)m * N + c] = row[c] * sc * epi.g[c];
   }
 }
 
 hipError_t launch_skinny(int dtype, const float* X, int M, int K, const BMats& b, int N, int splits,
-                         float* part, hipStream_t s) {
+                         float* part, const SkinnyEpi& epi, hipStream_t s) {
   const SkinnyPlan plan = skinny_plan(M, N, K);
   if (plan.splits != splits) return hipErrorInvalidValue;
   const int rpt = plan.rpt;
@@ -114,105 +209,17 @@ hipError_t launch_skinny(int dtype, const float* X, int M, int K, const BMats& b
 #define DSPARK_SK(R)                                                                     \
   case R:                                                                                \
     if (dtype == 1)                                                                      \
-      skinny_kernel<bf16, R><<<grid, 256, 0, s>>>(X, M, K, b, N, part);                  \
+      skinny_kernel<bf16, R><<<grid, 256, 0, s>>>(X, M, K, b, N, part, epi);             \
     else                                                                                 \
-      skinny_kernel<float, R><<<grid, 256, 0, s>>>(X, M, K, b, N, part);                 \
+      skinny_kernel<float, R><<<grid, 256, 0, s>>>(X, M, K, b, N, part, epi);            \
     break;
   switch (rpt) {
-    DSPARK_SK(1) DSPARK_SK(2) DSPARK_SK(4) DSPARK_SK(8) DSPARK_SK(16)
+    DSPARK_SK(2) DSPARK_SK(4) DSPARK_SK(8) DSPARK_SK(16)
     default: ok = false;
   }
 #undef DSPARK_SK
   trace_post(K_SKINNY, s);
   if (!ok) return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// reductions of the split-K partials
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void finish_qkv_kernel(const float* __restrict__ part, int splits,
-                                                         int M, int d, float qscale,
-                                                         float* __restrict__ Q, float* __restrict__ Kd,
-                                                         float* __restrict__ Vd) {
-  const int64_t n3 = 3 * (int64_t)d;
-  const int64_t total = (int64_t)M * n3;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    float v = 0.f;
-    for (int z = 0; z < splits; ++z) v += part[(int64_t)z * total + i];
-    const int64_t r = i / n3, c = i % n3;
-    if (c < d) Q[r * d + c] = v * qscale;
-    else if (c < 2 * d) Kd[r * d + c - d] = v;
-    else Vd[r * d + c - 2 * d] = v;
-  }
-}
-
-hipError_t launch_finish_qkv(const float* part, int splits, int M, int d, float qscale, float* Q,
-                             float* Kd, float* Vd, hipStream_t s) {
-  const int64_t total = (int64_t)M * 3 * d;
-  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 1024);
-  trace_pre(K_FINISH_QKV, s);
-  finish_qkv_kernel<<<blocks, 256, 0, s>>>(part, splits, M, d, qscale, Q, Kd, Vd);
-  trace_post(K_FINISH_QKV, s);
-  return hipGetLastError();
-}
-
-// one workgroup per row: full = res + sum_z part; normed = RMSNorm(full; g)
-__global__ __launch_bounds__(256) void finish_res_kernel(const float* __restrict__ part, int splits,
-                                                         int M, int d, const float* __restrict__ res,
-                                                         const float* __restrict__ g, float eps,
-                                                         float* __restrict__ full,
-                                                         float* __restrict__ normed) {
-  __shared__ float wsum[4];
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  float ss = 0.f;
-  for (int c = tid; c < d; c += 256) {
-    float v = res[(int64_t)r * d + c];
-    for (int z = 0; z < splits; ++z) v += part[((int64_t)z * M + r) * d + c];
-    full[(int64_t)r * d + c] = v;
-    ss += v * v;
-  }
-  if (!normed) return;
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  const float sc = rsqrtf(tot / (float)d + eps);
-  for (int c = tid; c < d; c += 256) normed[(int64_t)r * d + c] = full[(int64_t)r * d + c] * sc * g[c];
-}
-
-hipError_t launch_finish_res(const float* part, int splits, int M, int d, const float* res,
-                             const float* g, float eps, float* full, float* normed, hipStream_t s) {
-  trace_pre(K_FINISH_RES, s);
-  finish_res_kernel<<<M, 256, 0, s>>>(part, splits, M, d, res, g, eps, full, normed);
-  trace_post(K_FINISH_RES, s);
-  return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void finish_swiglu_kernel(const float* __restrict__ part, int splits,
-                                                            int M, int ff, float* __restrict__ hid) {
-  const int64_t n2 = 2 * (int64_t)ff;
-  const int64_t total = (int64_t)M * ff;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / ff, c = i % ff;
-    float gt = 0.f, up = 0.f;
-    for (int z = 0; z < splits; ++z) {
-      const float* p = part + ((int64_t)z * M + r) * n2;
-      gt += p[c];
-      up += p[ff + c];
-    }
-    hid[i] = gt / (1.f + __expf(-gt)) * up;
-  }
-}
-
-hipError_t launch_finish_swiglu(const float* part, int splits, int M, int ff, float* hid,
-                                hipStream_t s) {
-  const int64_t total = (int64_t)M * ff;
-  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 1024);
-  trace_pre(K_FINISH_SWIGLU, s);
-  finish_swiglu_kernel<<<blocks, 256, 0, s>>>(part, splits, M, ff, hid);
-  trace_post(K_FINISH_SWIGLU, s);
   return hipGetLastError();
 }
 

@@ -41,9 +41,8 @@ static dspark_status fail(dspark_status st, const char* fmt, ...) {
 // tracing (per-kernel HIP events)
 // ---------------------------------------------------------------------------
 static const char* kNames[K_COUNT] = {
-    "prep_transpose", "gemm_ctx_fuse", "ctx_norm",   "rowstats",      "gemm_ctx_kv",
-    "attn_plan",      "attn_partial",  "attn_combine", "block_gemm",  "finish_qkv",
-    "finish_residual_norm", "finish_swiglu", "block_init"};
+    "prep_transpose", "gemm_ctx_fuse", "ctx_norm",   "rowstats", "gemm_ctx_kv",
+    "attn_plan",      "attn_split_k",  "block_gemm", "block_init"};
 
 const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
 
@@ -86,6 +85,8 @@ struct Plan {
   size_t esz = 4;
   // workspace offsets (bytes)
   size_t wct = 0, wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
+  size_t counters = 0;
+  int n_attn_counters = 0, n_counters = 0;
   size_t D = 0, D2 = 0, U = 0, Q = 0, Kd = 0, Vd = 0, attn = 0, E = 0, Z = 0, hid = 0, skpart = 0;
   size_t total = 0;
 };
@@ -155,12 +156,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
   p->ctx_splits = ctx_splits_for(dm->dtype, T, d, mH);
   p->chunk = attention_chunk(T, dm->n_heads, A);
-  int64_t chunks = 0;
-  for (int b = 0; b < A; ++b) {
-    const int64_t L = cu_host[b + 1] - cu_host[b];
-    chunks += (L + p->chunk - 1) / p->chunk;
-  }
-  p->total_chunks = (int)chunks;
+  p->total_chunks = (int)attention_tiles(cu_host, A, p->chunk);
   p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;
   p->sk_qkv = skinny_plan(M, 3 * d, d);
   p->sk_o = skinny_plan(M, d, d);
@@ -181,6 +177,10 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
     p->rinv = take((size_t)T * 4);
     p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * d * p->esz);
     p->prefix = take((size_t)(A + 1) * 4);
+    p->n_attn_counters = A * dm->n_heads;
+    const int slabs = std::max(3 * d, 2 * ff) / 128 + 1;
+    p->n_counters = p->n_attn_counters + slabs;
+    p->counters = take((size_t)p->n_counters * 4);
     p->po = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * p->hd * 4);
     p->pml = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * 2 * 4);
     const size_t row = (size_t)M * d * 4;
@@ -312,38 +312,57 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   float* Z = at<float>(ws, p.Z);
   float* hid = at<float>(ws, p.hid);
   float* skp = at<float>(ws, p.skpart);
-  int32_t* prefix = at<int32_t>(ws, p.prefix);
+  unsigned* cnt = at<unsigned>(ws, p.counters);
+  unsigned* sk_cnt = cnt + p.n_attn_counters;
 
+  // Q (pre-scaled for base-2 softmax), K_d, V_d
   BMats b{};
-  // Q, K_d, V_d
   b.mat[0] = lw.wq; b.mat[1] = lw.wk; b.mat[2] = lw.wv;
   b.n_per = d; b.nmat = 3;
-  DSPARK_HIP(launch_skinny(dt, U, M, d, b, 3 * d, p.sk_qkv.splits, skp, s));
-  const float qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
-  DSPARK_HIP(launch_finish_qkv(skp, p.sk_qkv.splits, M, d, qscale, Q, Kd, Vd, s));
-  // attention over [context ++ block]
-  KVDesc kv{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
-  float* po = at<float>(ws, p.po);
-  float* pml = at<float>(ws, p.pml);
-  if (p.total_chunks > 0)
-    DSPARK_HIP(launch_attention(dt, Q, kv, kv_layer, cu_dev, prefix, A, G, p.chunk, p.total_chunks, po, pml, s));
-  DSPARK_HIP(launch_combine(Q, Kd, Vd, A, G, d, dm->n_heads, prefix, p.total_chunks, po, pml, attn, s));
+  SkinnyEpi e{};
+  e.mode = SK_QKV;
+  e.d = d;
+  e.qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
+  e.q = Q; e.kd = Kd; e.vd = Vd;
+  e.counters = sk_cnt;
+  DSPARK_HIP(launch_skinny(dt, U, M, d, b, 3 * d, p.sk_qkv.splits, skp, e, s));
+  // attention over [context ++ block] (split-K partials + combine)
+  AttnArgs aa{};
+  aa.Q = Q; aa.Kd = Kd; aa.Vd = Vd;
+  aa.kv = KVDesc{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
+  aa.layer = kv_layer;
+  aa.cu = cu_dev;
+  aa.prefix = at<int32_t>(ws, p.prefix);
+  aa.A = A; aa.gamma = G; aa.chunk = p.chunk; aa.total_tiles = p.total_chunks;
+  aa.part_o = at<float>(ws, p.po);
+  aa.part_ml = at<float>(ws, p.pml);
+  aa.counters = cnt;
+  aa.attn = attn;
+  DSPARK_HIP(launch_attention(dt, aa, s));
   // E = D + Attn Wo ; Z = RMSNorm(E; ff_norm)
   b = BMats{};
   b.mat[0] = lw.wo; b.n_per = d; b.nmat = 1;
-  DSPARK_HIP(launch_skinny(dt, attn, M, d, b, d, p.sk_o.splits, skp, s));
-  DSPARK_HIP(launch_finish_res(skp, p.sk_o.splits, M, d, D, lw.ff_norm, dm->eps, E, Z, s));
-  // SiLU(Z Wgate) * (Z Wup)
+  e = SkinnyEpi{};
+  e.mode = SK_RESID;
+  e.res = D; e.out = E; e.g = lw.ff_norm; e.normed = Z; e.eps = dm->eps;
+  e.counters = sk_cnt;
+  DSPARK_HIP(launch_skinny(dt, attn, M, d, b, d, p.sk_o.splits, skp, e, s));
+  // hid = SiLU(Z Wgate) * (Z Wup)
   b = BMats{};
   b.mat[0] = lw.w_gate; b.mat[1] = lw.w_up; b.n_per = ff; b.nmat = 2;
-  DSPARK_HIP(launch_skinny(dt, Z, M, d, b, 2 * ff, p.sk_gu.splits, skp, s));
-  DSPARK_HIP(launch_finish_swiglu(skp, p.sk_gu.splits, M, ff, hid, s));
-  // D' = E + hid Wdown (+ next norm)
+  e = SkinnyEpi{};
+  e.mode = SK_SWIGLU;
+  e.hid = hid; e.ff = ff;
+  e.counters = sk_cnt;
+  DSPARK_HIP(launch_skinny(dt, Z, M, d, b, 2 * ff, p.sk_gu.splits, skp, e, s));
+  // D' = E + hid Wdown (+ the next norm)
   b = BMats{};
   b.mat[0] = lw.w_down; b.n_per = d; b.nmat = 1;
-  DSPARK_HIP(launch_skinny(dt, hid, M, ff, b, d, p.sk_down.splits, skp, s));
-  DSPARK_HIP(launch_finish_res(skp, p.sk_down.splits, M, d, E, g_next, dm->eps, D_next,
-                               g_next ? U_next : nullptr, s));
+  e = SkinnyEpi{};
+  e.mode = SK_RESID;
+  e.res = E; e.out = D_next; e.g = g_next; e.normed = g_next ? U_next : nullptr; e.eps = dm->eps;
+  e.counters = sk_cnt;
+  DSPARK_HIP(launch_skinny(dt, hid, M, ff, b, d, p.sk_down.splits, skp, e, s));
   return DSPARK_OK;
 }
 
@@ -404,7 +423,8 @@ dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32
   if (p.T > 0) DSPARK_HIP(launch_rowstats(dims->dtype, h_ctx, (int)p.T, dims->d, dims->eps, rinv, s));
   st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, ws, s);
   if (st != DSPARK_OK) return st;
-  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
+  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), at<unsigned>(ws, p.counters),
+                         p.n_counters, s));
   float* U = at<float>(ws, p.U);
   DSPARK_HIP(launch_block_init(d_in, nullptr, A, dims->gamma, dims->d, lw->attn_norm, dims->eps,
                                nullptr, U, s));
@@ -445,7 +465,8 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   if (st != DSPARK_OK) return st;
   st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, ws, s);
   if (st != DSPARK_OK) return st;
-  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
+  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), at<unsigned>(ws, p.counters),
+                         p.n_counters, s));
   float* Da = at<float>(ws, p.D);
   float* Db = at<float>(ws, p.D2);
   float* U = at<float>(ws, p.U);

@@ -18,12 +18,8 @@ enum KernelKind : int {
   K_ROWSTATS,         // row inverse RMS of a given H_ctx
   K_GEMM_KV,          // Eq 3 context K/V re-projection (all layers at once)
   K_PLAN,             // chunk prefix of the split-K attention
-  K_ATTN,             // split-K attention partials over context chunks
-  K_COMBINE,          // (m, l) combine + block keys
-  K_SKINNY,           // block-row projections (weight streaming)
-  K_FINISH_QKV,       // reduce Q/K_d/V_d partials
-  K_FINISH_RES,       // reduce + residual + RMSNorm of block rows
-  K_FINISH_SWIGLU,    // reduce gate/up + SiLU(gate) * up
+  K_ATTN,             // split-K attention over context chunks + (m, l) combine
+  K_SKINNY,           // block-row projections (weight streaming + fused epilogue)
   K_BLOCK_INIT,       // D0 = block_in + block_pos, and its norm
   K_COUNT
 };
@@ -84,17 +80,27 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
 
 // ---- attention ------------------------------------------------------------
 int attention_chunk(int64_t T, int n_heads, int A);   // keys per chunk (multiple of 64)
+// tiles = sum_b max(1, ceil(L_b / chunk))
+int64_t attention_tiles(const int32_t* cu_host, int A, int chunk);
+// device tile prefix (same formula) and zeroing of `ncounters` counters
 hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
-                       hipStream_t s);
-// Q is pre-scaled by hd^-1/2 * log2(e).
-hipError_t launch_attention(int dtype, const float* Q, const KVDesc& kv, int layer,
-                            const int32_t* cu_dev, const int32_t* chunk_prefix, int A,
-                            int gamma, int chunk, int total_chunks, float* part_o,
-                            float* part_ml, hipStream_t s);
-hipError_t launch_combine(const float* Q, const float* Kd, const float* Vd, int A, int gamma,
-                          int d, int n_heads, const int32_t* chunk_prefix, int total_chunks,
-                          const float* part_o, const float* part_ml, float* attn,
-                          hipStream_t s);
+                       unsigned* counters, int ncounters, hipStream_t s);
+
+struct AttnArgs {
+  const float* Q;       // [A*gamma][d], pre-scaled by hd^-1/2 * log2(e)
+  const float* Kd;      // [A*gamma][d] block keys
+  const float* Vd;      // [A*gamma][d] block values
+  KVDesc kv;            // context K/V (attention layout)
+  int layer;
+  const int32_t* cu;    // device prefix offsets [A+1]
+  const int32_t* prefix;  // device tile prefix [A+1]
+  int A, gamma, chunk, total_tiles;
+  float* part_o;        // [tiles][n_heads][gamma][hd]
+  float* part_ml;       // [tiles][n_heads][gamma][2]
+  unsigned* counters;   // [A*n_heads], zero on entry, left zero
+  float* attn;          // out [A*gamma][d]
+};
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 // ---- block side -----------------------------------------------------------
 struct SkinnyPlan {
@@ -102,17 +108,30 @@ struct SkinnyPlan {
   int splits;   // K slabs (partials)
 };
 SkinnyPlan skinny_plan(int M, int N, int K);
-// part[z][r][n] = sum_{k in slab z} X[r][k] W(k, n), W = the matrices of b.
+
+// Epilogue of a block-row projection, applied by the last workgroup of each
+// 128-column slab once every K slab has written its partial.
+enum SkinnyMode { SK_QKV = 0, SK_RESID = 1, SK_SWIGLU = 2 };
+struct SkinnyEpi {
+  int mode;
+  int d = 0;                  // SK_QKV: columns of each of Q, K_d, V_d
+  float qscale = 1.f;
+  float* q = nullptr;         // SK_QKV outputs [M][d]
+  float* kd = nullptr;
+  float* vd = nullptr;
+  const float* res = nullptr; // SK_RESID: out = res + X.W   [M][N]
+  float* out = nullptr;
+  const float* g = nullptr;   // SK_RESID: then normed = RMSNorm(out; g) when g != null
+  float* normed = nullptr;
+  float eps = 0.f;
+  float* hid = nullptr;       // SK_SWIGLU: hid[M][ff] = SiLU(X.Wgate) * (X.Wup)
+  int ff = 0;
+  unsigned* counters = nullptr;  // [N/128 + 1] zero on entry, left zero on exit
+};
+// part[z][r][n] = sum_{k in slab z} X[r][k] W(k, n), then the epilogue.
+// SK_SWIGLU takes b = {Wgate, Wup} with n_per = ff and N = 2 ff.
 hipError_t launch_skinny(int dtype, const float* X, int M, int K, const BMats& b, int N,
-                         int splits, float* part, hipStream_t s);
-hipError_t launch_finish_qkv(const float* part, int splits, int M, int d, float qscale,
-                             float* Q, float* Kd, float* Vd, hipStream_t s);
-// full[r] = res[r] + sum_z part[z][r]; normed[r] = RMSNorm(full[r]; g) (nullable).
-hipError_t launch_finish_res(const float* part, int splits, int M, int d, const float* res,
-                             const float* g, float eps, float* full, float* normed,
-                             hipStream_t s);
-hipError_t launch_finish_swiglu(const float* part, int splits, int M, int ff, float* hid,
-                                hipStream_t s);
+                         int splits, float* part, const SkinnyEpi& epi, hipStream_t s);
 // D0 = block_in + block_pos (per sequence); U0 = RMSNorm(D0; g).
 hipError_t launch_block_init(const float* block_in, const float* block_pos, int A, int gamma,
                              int d, const float* g, float eps, float* D0, float* U0,

@@ -50,7 +50,7 @@ def test_version_and_kernel_names(L):
     import block_draft_context_amd as B
     assert "gfx950" in B.version()
     names = B.kernel_names()
-    assert "attn_partial" in names and "gemm_ctx_kv" in names and len(set(names)) == len(names)
+    assert "attn_split_k" in names and "gemm_ctx_kv" in names and len(set(names)) == len(names)
 
 
 def _dims(L, **kw):
