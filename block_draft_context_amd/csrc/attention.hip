@@ -5,10 +5,9 @@
 // context part is long and read once per layer, so it is split into chunks
 // of `chunk` keys: one workgroup per (chunk, head) streams the chunk's K and
 // V once and leaves an unnormalised partial (m, l, o) per query, as the
-// split-chunk attention + combine kernels of dspark-runtime.js do. The last
-// workgroup of a (sequence, head) to finish (an atomic ticket; nobody waits)
-// then merges all its partials together with the gamma block keys by the
-// log-sum-exp identity
+// split-chunk attention + combine kernels of dspark-runtime.js do. A second
+// kernel, one workgroup per (sequence, head, query), merges those partials
+// together with the gamma block keys by the log-sum-exp identity
 //   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  o = sum_c o_c 2^(m_c - M) / l.
 // Scores are kept in base 2: Q arrives pre-multiplied by hd^-1/2 * log2(e).
 //
@@ -18,7 +17,7 @@
 // columns and R keys per load, so each V load is again one 1 KiB run; the
 // block's probabilities are broadcast through LDS. All arithmetic is float32
 // on the vector ALUs: with gamma <= 16 queries the arithmetic intensity is a
-// few flop per byte, far below the matrix-core ridge.
+// few flop per byte, far below the matrix cores'.
 #include "common.h"
 #include "kernels.h"
 #include "kv_layout.h"
@@ -27,13 +26,13 @@ namespace dspark {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// keys per chunk: aim for ~1024 (chunk, head) workgroups, chunk in [256, 8192]
+// keys per chunk: aim for ~512 (chunk, head) workgroups, chunk in [256, 16384]
 int attention_chunk(int64_t T, int n_heads, int A) {
   (void)A;
-  int64_t c = (T * n_heads + 1023) / 1024;
+  int64_t c = (T * n_heads + 511) / 512;
   c = ((c + 63) / 64) * 64;
   if (c < 256) c = 256;
-  if (c > 8192) c = 8192;
+  if (c > 16384) c = 16384;
   return (int)c;
 }
 
@@ -48,13 +47,11 @@ int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
 
 // chunk_prefix[b] = sum_{b' < b} max(1, ceil(L_b' / chunk)), b = 0..A (one
 // workgroup; an empty sequence still gets one tile, which finds no keys and
-// runs the combine). Also zeroes `ncounters` counters.
+// leaves an empty partial).
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int A, int chunk,
-                                                   int32_t* __restrict__ prefix,
-                                                   unsigned* __restrict__ counters, int ncounters) {
+                                                   int32_t* __restrict__ prefix) {
   __shared__ int32_t sums[256];
   const int tid = threadIdx.x;
-  for (int i = tid; i < ncounters; i += 256) counters[i] = 0u;
   const int per = (A + 255) / 256;
   const int b0 = tid * per, b1 = min(A, b0 + per);
   int32_t local = 0;
@@ -80,42 +77,34 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 }
 
 hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
-                       unsigned* counters, int ncounters, hipStream_t s) {
+                       hipStream_t s) {
   trace_pre(K_PLAN, s);
-  plan_kernel<<<1, 256, 0, s>>>(cu_dev, A, chunk, chunk_prefix, counters, ncounters);
+  plan_kernel<<<1, 256, 0, s>>>(cu_dev, A, chunk, chunk_prefix);
   trace_post(K_PLAN, s);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// grid (total_tiles, n_heads), 256 threads (4 waves)
+// partials: grid (total_tiles, n_heads), 256 threads (4 waves)
 // part_o  [total_tiles][n_heads][G][HD]   unnormalised output
 // part_ml [total_tiles][n_heads][G][2]    (max, sum) in base-2 units
-// attn    [A*G][n_heads*HD]              normalised output (combine)
 // ---------------------------------------------------------------------------
 template <typename S, int HD, int G>
-__global__ __launch_bounds__(256) void attn_kernel(
-    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
-    const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
+__global__ __launch_bounds__(256) void attn_partial_kernel(
+    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int chunk,
-    int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml,
-    unsigned* __restrict__ counters, float* __restrict__ attn) {
+    int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
   constexpr int NKV = HD / E;            // K vectors per key row
   constexpr int KG = 128 / HD;           // key groups in the P.V lane split
   constexpr int NLD = 64 / (KG * R);     // V loads per 64-key block
-  constexpr int NG = 512 / HD;           // chunk groups in the combine (NG * HD/2 = 256)
 
   __shared__ __attribute__((aligned(16))) float qs[G][HD];
   __shared__ __attribute__((aligned(16))) float ps[4][G][64];
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
-  __shared__ __attribute__((aligned(16))) float red_o[NG][G][HD];   // NG >= 4 waves
-  __shared__ float sb[G][G];
-  __shared__ float Mq[G];
-  __shared__ float Lq[G];
-  __shared__ unsigned s_ticket;
+  __shared__ __attribute__((aligned(16))) float red_o[4][G][HD];
 
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
@@ -199,7 +188,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per load
+      // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per vector
       const S* vp = Vh + blk * 64 * HD + lane * E;
 #pragma unroll 4
       for (int ld = 0; ld < NLD; ++ld) {
@@ -273,117 +262,100 @@ __global__ __launch_bounds__(256) void attn_kernel(
     part_ml[(pbase + j) * 2 + 0] = M;
     part_ml[(pbase + j) * 2 + 1] = l;
   }
+}
 
-  // ---- the last tile of (b, h) to finish merges every partial of (b, h)
-  __threadfence();
-  __syncthreads();
-  const int t0 = prefix[b], t1 = min(prefix[b + 1], total_tiles);
-  if (tid == 0) s_ticket = atomicAdd(&counters[b * n_heads + h], 1u);
-  __syncthreads();
-  if (s_ticket != (unsigned)(t1 - t0 - 1)) return;
-  __threadfence();
-  if (tid == 0) counters[b * n_heads + h] = 0u;
+// ---------------------------------------------------------------------------
+// combine: grid (A * n_heads, gamma), 256 threads. Query j of (sequence b,
+// head h): every tile partial of b plus the gamma block keys (K_d, V_d in
+// float32). Thread (tg, cc) sums tiles tg, tg + NG, ... for column cc.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd, int A,
+    int gamma, int d, int n_heads, const int32_t* __restrict__ prefix, int total_tiles,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, float* __restrict__ attn) {
+  __shared__ float sb[kMaxGamma];
+  __shared__ float redw[4];
+  __shared__ float red_acc[256];
+  __shared__ float Msh, Lsh;
+  const int b = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
+  const int j = blockIdx.y;
+  const int hd = d / n_heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = min(prefix[b], total_tiles), t1 = min(prefix[b + 1], total_tiles);
+  const float* q = Q + (int64_t)(b * gamma + j) * d + h * hd;
 
-  // block-key scores (the gamma block keys K_d, V_d in float32)
-  if (tid < G * G) {
-    const int j = tid / G, jj = tid % G;
-    const float* kr = Kd + (int64_t)(b * G + jj) * d + h * HD;
+  // block-key scores (one wave per key)
+  for (int jj = wave; jj < gamma; jj += 4) {
+    const float* kr = Kd + (int64_t)(b * gamma + jj) * d + h * hd;
     float sc = 0.f;
-    for (int cc = 0; cc < HD; ++cc) sc = fmaf(qs[j][cc], kr[cc], sc);
-    sb[j][jj] = sc;
+    for (int cc = lane; cc < hd; cc += 64) sc = fmaf(q[cc], kr[cc], sc);
+    sc = wave_sum(sc);
+    if (lane == 0) sb[jj] = sc;
+  }
+  // max over tiles
+  float mloc = kNegInf;
+  for (int t = t0 + tid; t < t1; t += 256)
+    mloc = fmaxf(mloc, part_ml[(((int64_t)t * n_heads + h) * gamma + j) * 2]);
+  mloc = wave_max(mloc);
+  if (lane == 0) redw[wave] = mloc;
+  __syncthreads();
+  if (tid == 0) {
+    float M = fmaxf(fmaxf(redw[0], redw[1]), fmaxf(redw[2], redw[3]));
+    for (int jj = 0; jj < gamma; ++jj) M = fmaxf(M, sb[jj]);
+    Msh = M;
   }
   __syncthreads();
-  // overall max per query (block keys and every tile), then the sum l
-  {
-    float mloc[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) mloc[j] = kNegInf;
-    for (int t = t0 + tid; t < t1; t += 256) {
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-        mloc[j] = fmaxf(mloc[j], part_ml[(((int64_t)t * n_heads + h) * G + j) * 2]);
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float v = wave_max(mloc[j]);
-      if (lane == 0) red_m[wave][j] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-      const int j = tid;
-      float M = fmaxf(fmaxf(red_m[0][j], red_m[1][j]), fmaxf(red_m[2][j], red_m[3][j]));
-      for (int jj = 0; jj < G; ++jj) M = fmaxf(M, sb[j][jj]);
-      Mq[j] = M;
-    }
-    __syncthreads();
-    float lloc[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) lloc[j] = 0.f;
-    for (int t = t0 + tid; t < t1; t += 256) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float* ml = part_ml + (((int64_t)t * n_heads + h) * G + j) * 2;
-        const float mv = ml[0];
-        if (mv != kNegInf) lloc[j] += ml[1] * exp2f(mv - Mq[j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float v = wave_sum(lloc[j]);
-      if (lane == 0) red_l[wave][j] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-      const int j = tid;
-      float l = (red_l[0][j] + red_l[1][j]) + (red_l[2][j] + red_l[3][j]);
-      for (int jj = 0; jj < G; ++jj) l += exp2f(sb[j][jj] - Mq[j]);
-      Lq[j] = l;
-    }
-    __syncthreads();
+  const float M = Msh;
+  // l over tiles
+  float lloc = 0.f;
+  for (int t = t0 + tid; t < t1; t += 256) {
+    const float* ml = part_ml + (((int64_t)t * n_heads + h) * gamma + j) * 2;
+    if (ml[0] != kNegInf) lloc += ml[1] * exp2f(ml[0] - M);
   }
-  // weighted sum of the tile outputs: thread (group grp, column pair cp2)
-  {
-    const int cp2 = tid % (HD / 2), grp = tid / (HD / 2);
-    float acc[G][2];
+  lloc = wave_sum(lloc);
+  __syncthreads();
+  if (lane == 0) redw[wave] = lloc;
+  __syncthreads();
+  if (tid == 0) {
+    float l = (redw[0] + redw[1]) + (redw[2] + redw[3]);
+    for (int jj = 0; jj < gamma; ++jj) l += exp2f(sb[jj] - M);
+    Lsh = l;
+  }
+  // weighted tile outputs: 8 tiles per batch, loads issued together
+  const int ng = 256 / hd;
+  const int cc = tid % hd, tg = tid / hd;
+  float acc = 0.f;
+  for (int tb = t0 + tg; tb < t1; tb += 8 * ng) {
+    float mv[8], ov[8];
 #pragma unroll
-    for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = 0.f;
-    for (int t = t0 + grp; t < t1; t += NG) {
-      const int64_t pj = ((int64_t)t * n_heads + h) * G;
+    for (int i = 0; i < 8; ++i) {
+      const int t = min(tb + i * ng, t1 - 1);
+      const int64_t pj = ((int64_t)t * n_heads + h) * gamma + j;
+      mv[i] = part_ml[pj * 2];
+      ov[i] = part_o[pj * hd + cc];
+    }
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float mv = part_ml[(pj + j) * 2];
-        if (mv != kNegInf) {
-          const float wgt = exp2f(mv - Mq[j]);
-          const float* po = part_o + (pj + j) * HD + 2 * cp2;
-          acc[j][0] = fmaf(po[0], wgt, acc[j][0]);
-          acc[j][1] = fmaf(po[1], wgt, acc[j][1]);
-        }
-      }
+    for (int i = 0; i < 8; ++i) {
+      const bool in = tb + i * ng < t1 && mv[i] != kNegInf;
+      acc = fmaf(in ? ov[i] : 0.f, in ? exp2f(mv[i] - M) : 0.f, acc);
     }
-    float* red = &red_o[0][0][0];   // [NG][G][HD]
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      red[(grp * G + j) * HD + 2 * cp2] = acc[j][0];
-      red[(grp * G + j) * HD + 2 * cp2 + 1] = acc[j][1];
-    }
-    __syncthreads();
-    for (int i = tid; i < G * HD; i += 256) {
-      const int j = i / HD, cc = i % HD;
-      float v = 0.f;
-      for (int g2 = 0; g2 < NG; ++g2) v += red[(g2 * G + j) * HD + cc];
-      for (int jj = 0; jj < G; ++jj)
-        v = fmaf(exp2f(sb[j][jj] - Mq[j]), Vd[(int64_t)(b * G + jj) * d + h * HD + cc], v);
-      attn[(int64_t)(b * G + j) * d + h * HD + cc] = v / Lq[j];
-    }
+  }
+  red_acc[tid] = acc;
+  __syncthreads();
+  if (tid < hd) {
+    float v = 0.f;
+    for (int g2 = 0; g2 < ng; ++g2) v += red_acc[g2 * hd + tid];
+    for (int jj = 0; jj < gamma; ++jj)
+      v = fmaf(exp2f(sb[jj] - M), Vd[(int64_t)(b * gamma + jj) * d + h * hd + tid], v);
+    attn[(int64_t)(b * gamma + j) * d + h * hd + tid] = v / Lsh;
   }
 }
 
 template <typename S, int HD, int G>
 static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
-  attn_kernel<S, HD, G><<<grid, 256, 0, s>>>(a.Q, a.Kd, a.Vd, static_cast<const S*>(a.kv.base),
-                                             a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-                                             a.chunk, a.total_tiles, a.part_o, a.part_ml,
-                                             a.counters, a.attn);
+  attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(
+      a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
+      a.chunk, a.total_tiles, a.part_o, a.part_ml);
 }
 
 template <typename S, int HD>
@@ -415,6 +387,14 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
   }
   trace_post(K_ATTN, s);
   if (!ok) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 cgrid(a.A * a.kv.n_heads, a.gamma);
+  trace_pre(K_COMBINE, s);
+  combine_kernel<<<cgrid, 256, 0, s>>>(a.Q, a.Kd, a.Vd, a.A, a.gamma, a.kv.hd * a.kv.n_heads,
+                                       a.kv.n_heads, a.prefix, a.total_tiles, a.part_o, a.part_ml,
+                                       a.attn);
+  trace_post(K_COMBINE, s);
   return hipGetLastError();
 }
 

@@ -41,8 +41,8 @@ static dspark_status fail(dspark_status st, const char* fmt, ...) {
 // tracing (per-kernel HIP events)
 // ---------------------------------------------------------------------------
 static const char* kNames[K_COUNT] = {
-    "prep_transpose", "gemm_ctx_fuse", "ctx_norm",   "rowstats", "gemm_ctx_kv",
-    "attn_plan",      "attn_split_k",  "block_gemm", "block_init"};
+    "prep_transpose", "gemm_ctx_fuse", "ctx_norm",    "rowstats",   "gemm_ctx_kv",
+    "attn_plan",      "attn_split_k",  "attn_combine", "block_gemm", "block_rows"};
 
 const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
 
@@ -81,13 +81,10 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   int64_t T = 0, Tpad = 0;
   int hd = 0, M = 0, chunk = 0, total_chunks = 0, ctx_splits = 1, kv_layers = 0;
-  SkinnyPlan sk_qkv{}, sk_o{}, sk_gu{}, sk_down{};
   size_t esz = 4;
   // workspace offsets (bytes)
   size_t wct = 0, wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
-  size_t counters = 0;
-  int n_attn_counters = 0, n_counters = 0;
-  size_t D = 0, D2 = 0, U = 0, Q = 0, Kd = 0, Vd = 0, attn = 0, E = 0, Z = 0, hid = 0, skpart = 0;
+  size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, attn = 0, E = 0, GU = 0;
   size_t total = 0;
 };
 
@@ -158,10 +155,6 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   p->chunk = attention_chunk(T, dm->n_heads, A);
   p->total_chunks = (int)attention_tiles(cu_host, A, p->chunk);
   p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;
-  p->sk_qkv = skinny_plan(M, 3 * d, d);
-  p->sk_o = skinny_plan(M, d, d);
-  p->sk_gu = skinny_plan(M, 2 * ff, d);
-  p->sk_down = skinny_plan(M, d, ff);
 
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
@@ -177,28 +170,17 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
     p->rinv = take((size_t)T * 4);
     p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * d * p->esz);
     p->prefix = take((size_t)(A + 1) * 4);
-    p->n_attn_counters = A * dm->n_heads;
-    const int slabs = std::max(3 * d, 2 * ff) / 128 + 1;
-    p->n_counters = p->n_attn_counters + slabs;
-    p->counters = take((size_t)p->n_counters * 4);
     p->po = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * p->hd * 4);
     p->pml = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * 2 * 4);
     const size_t row = (size_t)M * d * 4;
     p->D = take(row);
     p->D2 = take(row);
-    p->U = take(row);
     p->Q = take(row);
     p->Kd = take(row);
     p->Vd = take(row);
     p->attn = take(row);
     p->E = take(row);
-    p->Z = take(row);
-    p->hid = take((size_t)M * ff * 4);
-    size_t sk = (size_t)p->sk_qkv.splits * 3 * d;
-    sk = std::max(sk, (size_t)p->sk_o.splits * d);
-    sk = std::max(sk, (size_t)p->sk_gu.splits * 2 * ff);
-    sk = std::max(sk, (size_t)p->sk_down.splits * d);
-    p->skpart = take(sk * M * 4);
+    p->GU = take((size_t)M * 2 * ff * 4);
   }
   p->total = off == 0 ? 256 : off;
   return DSPARK_OK;
@@ -296,12 +278,10 @@ static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void
   return DSPARK_OK;
 }
 
-// One draft layer on the block rows. U holds RMSNorm(D; attn_norm) on entry.
-// Writes D_next = new rows and, when g_next is given, U_next = RMSNorm(D_next; g_next).
+// One draft layer on the block rows D (float32 [M][d]); writes D_next.
 static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, const int32_t* cu_dev,
                                const dspark_layer_weights& lw, int kv_layer, const float* D,
-                               const float* U, float* D_next, const float* g_next, float* U_next,
-                               void* ws, hipStream_t s) {
+                               float* D_next, void* ws, hipStream_t s) {
   const int d = dm->d, ff = dm->ff, M = p.M, G = dm->gamma;
   const int dt = dm->dtype;
   float* Q = at<float>(ws, p.Q);
@@ -309,24 +289,18 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   float* Vd = at<float>(ws, p.Vd);
   float* attn = at<float>(ws, p.attn);
   float* E = at<float>(ws, p.E);
-  float* Z = at<float>(ws, p.Z);
-  float* hid = at<float>(ws, p.hid);
-  float* skp = at<float>(ws, p.skpart);
-  unsigned* cnt = at<unsigned>(ws, p.counters);
-  unsigned* sk_cnt = cnt + p.n_attn_counters;
+  float* GU = at<float>(ws, p.GU);
 
-  // Q (pre-scaled for base-2 softmax), K_d, V_d
-  BMats b{};
-  b.mat[0] = lw.wq; b.mat[1] = lw.wk; b.mat[2] = lw.wv;
-  b.n_per = d; b.nmat = 3;
-  SkinnyEpi e{};
-  e.mode = SK_QKV;
-  e.d = d;
-  e.qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
-  e.q = Q; e.kd = Kd; e.vd = Vd;
-  e.counters = sk_cnt;
-  DSPARK_HIP(launch_skinny(dt, U, M, d, b, 3 * d, p.sk_qkv.splits, skp, e, s));
-  // attention over [context ++ block] (split-K partials + combine)
+  // Q (pre-scaled for the base-2 softmax), K_d, V_d from RMSNorm(D; attn_norm)
+  RowGemmArgs r{};
+  r.X = D; r.ldx = d; r.M = M; r.K = d; r.N = 3 * d;
+  r.g = lw.attn_norm; r.eps = dm->eps;
+  r.b.mat[0] = lw.wq; r.b.mat[1] = lw.wk; r.b.mat[2] = lw.wv;
+  r.b.n_per = d; r.b.nmat = 3;
+  r.q = Q; r.kd = Kd; r.vd = Vd; r.d = d;
+  r.qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
+  DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_QKV, r, s));
+  // attention over [context ++ block]: split-K partials, then the combine
   AttnArgs aa{};
   aa.Q = Q; aa.Kd = Kd; aa.Vd = Vd;
   aa.kv = KVDesc{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
@@ -336,33 +310,27 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   aa.A = A; aa.gamma = G; aa.chunk = p.chunk; aa.total_tiles = p.total_chunks;
   aa.part_o = at<float>(ws, p.po);
   aa.part_ml = at<float>(ws, p.pml);
-  aa.counters = cnt;
   aa.attn = attn;
   DSPARK_HIP(launch_attention(dt, aa, s));
-  // E = D + Attn Wo ; Z = RMSNorm(E; ff_norm)
-  b = BMats{};
-  b.mat[0] = lw.wo; b.n_per = d; b.nmat = 1;
-  e = SkinnyEpi{};
-  e.mode = SK_RESID;
-  e.res = D; e.out = E; e.g = lw.ff_norm; e.normed = Z; e.eps = dm->eps;
-  e.counters = sk_cnt;
-  DSPARK_HIP(launch_skinny(dt, attn, M, d, b, d, p.sk_o.splits, skp, e, s));
-  // hid = SiLU(Z Wgate) * (Z Wup)
-  b = BMats{};
-  b.mat[0] = lw.w_gate; b.mat[1] = lw.w_up; b.n_per = ff; b.nmat = 2;
-  e = SkinnyEpi{};
-  e.mode = SK_SWIGLU;
-  e.hid = hid; e.ff = ff;
-  e.counters = sk_cnt;
-  DSPARK_HIP(launch_skinny(dt, Z, M, d, b, 2 * ff, p.sk_gu.splits, skp, e, s));
-  // D' = E + hid Wdown (+ the next norm)
-  b = BMats{};
-  b.mat[0] = lw.w_down; b.n_per = d; b.nmat = 1;
-  e = SkinnyEpi{};
-  e.mode = SK_RESID;
-  e.res = E; e.out = D_next; e.g = g_next; e.normed = g_next ? U_next : nullptr; e.eps = dm->eps;
-  e.counters = sk_cnt;
-  DSPARK_HIP(launch_skinny(dt, hid, M, ff, b, d, p.sk_down.splits, skp, e, s));
+  // E = D + Attn Wo
+  r = RowGemmArgs{};
+  r.X = attn; r.ldx = d; r.M = M; r.K = d; r.N = d;
+  r.b.mat[0] = lw.wo; r.b.n_per = d; r.b.nmat = 1;
+  r.res = D; r.out = E; r.ldo = d;
+  DSPARK_HIP(launch_rowgemm(dt, RP_NONE, RE_RESID, r, s));
+  // [G | U] = RMSNorm(E; ff_norm) [Wgate | Wup]
+  r = RowGemmArgs{};
+  r.X = E; r.ldx = d; r.M = M; r.K = d; r.N = 2 * ff;
+  r.g = lw.ff_norm; r.eps = dm->eps;
+  r.b.mat[0] = lw.w_gate; r.b.mat[1] = lw.w_up; r.b.n_per = ff; r.b.nmat = 2;
+  r.out = GU; r.ldo = 2 * ff;
+  DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_STORE, r, s));
+  // D' = E + (SiLU(G) * U) Wdown
+  r = RowGemmArgs{};
+  r.X = GU; r.ldx = 2 * ff; r.M = M; r.K = ff; r.N = d;
+  r.b.mat[0] = lw.w_down; r.b.n_per = d; r.b.nmat = 1;
+  r.res = E; r.out = D_next; r.ldo = d;
+  DSPARK_HIP(launch_rowgemm(dt, RP_SWIGLU, RE_RESID, r, s));
   return DSPARK_OK;
 }
 
@@ -423,12 +391,8 @@ dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32
   if (p.T > 0) DSPARK_HIP(launch_rowstats(dims->dtype, h_ctx, (int)p.T, dims->d, dims->eps, rinv, s));
   st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, ws, s);
   if (st != DSPARK_OK) return st;
-  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), at<unsigned>(ws, p.counters),
-                         p.n_counters, s));
-  float* U = at<float>(ws, p.U);
-  DSPARK_HIP(launch_block_init(d_in, nullptr, A, dims->gamma, dims->d, lw->attn_norm, dims->eps,
-                               nullptr, U, s));
-  return run_layer(dims, p, A, cu_dev, *lw, 0, d_in, U, d_out, nullptr, nullptr, ws, s);
+  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
+  return run_layer(dims, p, A, cu_dev, *lw, 0, d_in, d_out, ws, s);
 }
 
 dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
@@ -465,36 +429,21 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   if (st != DSPARK_OK) return st;
   st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, ws, s);
   if (st != DSPARK_OK) return st;
-  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), at<unsigned>(ws, p.counters),
-                         p.n_counters, s));
+  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
   float* Da = at<float>(ws, p.D);
   float* Db = at<float>(ws, p.D2);
-  float* U = at<float>(ws, p.U);
-  DSPARK_HIP(launch_block_init(block_in, block_pos, A, dims->gamma, dims->d, layers[0].attn_norm,
-                               dims->eps, Da, U, s));
+  DSPARK_HIP(launch_block_rows(block_in, block_pos, A, dims->gamma, dims->d, nullptr, dims->eps, Da,
+                               nullptr, s));
   const int N = dims->n_layers;
   for (int i = 0; i < N; ++i) {
-    const bool last = i == N - 1;
-    float* Dn;
-    const float* gn;
-    float* Un;
-    if (!last) {
-      Dn = Db;
-      gn = layers[i + 1].attn_norm;
-      Un = U;
-    } else if (out_norm) {
-      Dn = Db;
-      gn = out_norm;
-      Un = block_out;
-    } else {
-      Dn = block_out;
-      gn = nullptr;
-      Un = nullptr;
-    }
-    st = run_layer(dims, p, A, cu_dev, layers[i], i, Da, U, Dn, gn, Un, ws, s);
+    float* Dn = (i == N - 1 && !out_norm) ? block_out : Db;
+    st = run_layer(dims, p, A, cu_dev, layers[i], i, Da, Dn, ws, s);
     if (st != DSPARK_OK) return st;
     std::swap(Da, Db);
   }
+  if (out_norm)   // out = RMSNorm(D^N; out_norm)
+    DSPARK_HIP(launch_block_rows(Da, nullptr, A, dims->gamma, dims->d, out_norm, dims->eps, nullptr,
+                                 block_out, s));
   return DSPARK_OK;
 }
 

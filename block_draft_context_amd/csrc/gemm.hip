@@ -143,10 +143,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(ASegs a, const bf16* __restr
       const int q = tid + 256 * i;
       const int row = q >> 3, ch = q & 7;
       const int gr = m0 + row;
-      if (gr < M)
-        ra[i] = ld16(Ap + (int64_t)gr * a.ld + kin + ch * 8);
-      else
-        ra[i] = u32x4{0u, 0u, 0u, 0u};
+      // rows past M: load a valid row, then zero it (no branch around the load)
+      const u32x4 v = ld16(Ap + (int64_t)min(gr, M - 1) * a.ld + kin + ch * 8);
+      ra[i] = gr < M ? v : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
@@ -324,6 +323,9 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
 // ---------------------------------------------------------------------------
 // Row passes (one wave per row, d a multiple of 64)
 // ---------------------------------------------------------------------------
+// one wave per row; each lane owns d/128 float2 column pairs (d <= 2048), and
+// all of a split's loads are issued together
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <typename S>
 __global__ __launch_bounds__(256) void ctx_norm_kernel(const float* __restrict__ part, int splits,
                                                        int T, int d, const float* __restrict__ g,
@@ -332,30 +334,43 @@ __global__ __launch_bounds__(256) void ctx_norm_kernel(const float* __restrict__
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int per = d / 64;   // <= 32
-  float v[32];
+  const int nv = d / 128;   // float2 per lane, <= 16
+  f32x2 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = f32x2{0.f, 0.f};
+  for (int zz = 0; zz < splits; ++zz) {
+    const f32x2* row = reinterpret_cast<const f32x2*>(part + ((int64_t)zz * T + t) * d);
+    f32x2 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = row[min(i, nv - 1) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] += x[i];
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < per) {
-      const int c = lane + 64 * i;
-      float x = 0.f;
-      for (int zz = 0; zz < splits; ++zz) x += part[((int64_t)zz * T + t) * d + c];
-      v[i] = x;
-      ss += x * x;
-    }
-  }
+  for (int i = 0; i < 16; ++i)
+    if (i < nv) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1];
   ss = wave_sum(ss);
   const float sc = rsqrtf(ss / (float)d + eps);
+  const f32x2* g2 = reinterpret_cast<const f32x2*>(g);
+  f32x2 gv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gv[i] = g2[min(i, nv - 1) * 64 + lane];
   float ss2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < per) {
-      const int c = lane + 64 * i;
-      const S o = from_f32<S>(v[i] * sc * g[c]);
-      h[t * d + c] = o;
-      const float of = to_f32(o);
-      ss2 += of * of;
+  for (int i = 0; i < 16; ++i) {
+    if (i < nv) {
+      const int c = (i * 64 + lane) * 2;
+      const S o0 = from_f32<S>(v[i][0] * sc * gv[i][0]);
+      const S o1 = from_f32<S>(v[i][1] * sc * gv[i][1]);
+      const float f0 = to_f32(o0), f1 = to_f32(o1);
+      ss2 += f0 * f0 + f1 * f1;
+      if constexpr (sizeof(S) == 2) {
+        *reinterpret_cast<uint32_t*>(h + t * d + c) =
+            (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+      } else {
+        *reinterpret_cast<f32x2*>(h + t * d + c) = f32x2{f0, f1};
+      }
     }
   }
   if (rinv) {
@@ -383,11 +398,14 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const S* __restrict__ h, 
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  const int nv = d / 64;   // <= 32 values per lane, loaded together
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = to_f32(h[t * d + min(i, nv - 1) * 64 + lane]);
   float ss = 0.f;
-  for (int c = lane; c < d; c += 64) {
-    const float x = to_f32(h[t * d + c]);
-    ss += x * x;
-  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < nv) ss += x[i] * x[i];
   ss = wave_sum(ss);
   if (lane == 0) rinv[t] = rsqrtf(ss / (float)d + eps);
 }

@@ -17,10 +17,11 @@ enum KernelKind : int {
   K_CTX_NORM,         // Eq 2 RMSNorm epilogue pass (+ row inverse RMS)
   K_ROWSTATS,         // row inverse RMS of a given H_ctx
   K_GEMM_KV,          // Eq 3 context K/V re-projection (all layers at once)
-  K_PLAN,             // chunk prefix of the split-K attention
-  K_ATTN,             // split-K attention over context chunks + (m, l) combine
-  K_SKINNY,           // block-row projections (weight streaming + fused epilogue)
-  K_BLOCK_INIT,       // D0 = block_in + block_pos, and its norm
+  K_PLAN,             // tile prefix of the split-K attention
+  K_ATTN,             // split-K attention partials over context chunks
+  K_COMBINE,          // (m, l) combine of the partials + block keys
+  K_ROWGEMM,          // block-row projections (weight streaming, fused norm/epilogue)
+  K_BLOCK_ROWS,       // D0 = block_in + block_pos and row norms
   K_COUNT
 };
 
@@ -82,9 +83,9 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
 int attention_chunk(int64_t T, int n_heads, int A);   // keys per chunk (multiple of 64)
 // tiles = sum_b max(1, ceil(L_b / chunk))
 int64_t attention_tiles(const int32_t* cu_host, int A, int chunk);
-// device tile prefix (same formula) and zeroing of `ncounters` counters
+// device tile prefix (same formula)
 hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
-                       unsigned* counters, int ncounters, hipStream_t s);
+                       hipStream_t s);
 
 struct AttnArgs {
   const float* Q;       // [A*gamma][d], pre-scaled by hd^-1/2 * log2(e)
@@ -97,43 +98,36 @@ struct AttnArgs {
   int A, gamma, chunk, total_tiles;
   float* part_o;        // [tiles][n_heads][gamma][hd]
   float* part_ml;       // [tiles][n_heads][gamma][2]
-  unsigned* counters;   // [A*n_heads], zero on entry, left zero
   float* attn;          // out [A*gamma][d]
 };
+// partial kernel, then the combine kernel
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 // ---- block side -----------------------------------------------------------
-struct SkinnyPlan {
-  int rpt;      // K rows per thread
-  int splits;   // K slabs (partials)
-};
-SkinnyPlan skinny_plan(int M, int N, int K);
-
-// Epilogue of a block-row projection, applied by the last workgroup of each
-// 128-column slab once every K slab has written its partial.
-enum SkinnyMode { SK_QKV = 0, SK_RESID = 1, SK_SWIGLU = 2 };
-struct SkinnyEpi {
-  int mode;
-  int d = 0;                  // SK_QKV: columns of each of Q, K_d, V_d
-  float qscale = 1.f;
-  float* q = nullptr;         // SK_QKV outputs [M][d]
+// Y = prologue(X) . W with a fused epilogue, full K per workgroup (32 columns).
+enum RowPro { RP_NONE = 0, RP_RMSNORM = 1, RP_SWIGLU = 2 };
+enum RowEpi { RE_STORE = 0, RE_QKV = 1, RE_RESID = 2 };
+struct RowGemmArgs {
+  const float* X = nullptr;   // [M][ldx]; RP_SWIGLU: [M][2K] = [gate | up]
+  int ldx = 0;
+  int M = 0, K = 0, N = 0;
+  const float* g = nullptr;   // RP_RMSNORM gain [K]
+  float eps = 0.f;
+  BMats b{};                  // weights: K rows, N columns over b.nmat matrices
+  float* out = nullptr;       // RE_STORE / RE_RESID: out[m][n] (row stride ldo)
+  int ldo = 0;
+  const float* res = nullptr; // RE_RESID: out = res + X.W
+  float* q = nullptr;         // RE_QKV: columns [0,d) -> q (scaled), [d,2d) -> kd, [2d,3d) -> vd
   float* kd = nullptr;
   float* vd = nullptr;
-  const float* res = nullptr; // SK_RESID: out = res + X.W   [M][N]
-  float* out = nullptr;
-  const float* g = nullptr;   // SK_RESID: then normed = RMSNorm(out; g) when g != null
-  float* normed = nullptr;
-  float eps = 0.f;
-  float* hid = nullptr;       // SK_SWIGLU: hid[M][ff] = SiLU(X.Wgate) * (X.Wup)
-  int ff = 0;
-  unsigned* counters = nullptr;  // [N/128 + 1] zero on entry, left zero on exit
+  int d = 0;
+  float qscale = 1.f;
 };
-// part[z][r][n] = sum_{k in slab z} X[r][k] W(k, n), then the epilogue.
-// SK_SWIGLU takes b = {Wgate, Wup} with n_per = ff and N = 2 ff.
-hipError_t launch_skinny(int dtype, const float* X, int M, int K, const BMats& b, int N,
-                         int splits, float* part, const SkinnyEpi& epi, hipStream_t s);
-// D0 = block_in + block_pos (per sequence); U0 = RMSNorm(D0; g).
-hipError_t launch_block_init(const float* block_in, const float* block_pos, int A, int gamma,
+int rowgemm_rows_per_pass(int K);
+hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s);
+// D0 = block_in + block_pos (per sequence; block_pos, D0 nullable);
+// U0 = RMSNorm(D0; g) (nullable).
+hipError_t launch_block_rows(const float* block_in, const float* block_pos, int A, int gamma,
                              int d, const float* g, float eps, float* D0, float* U0,
                              hipStream_t s);
 
