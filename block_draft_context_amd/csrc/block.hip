@@ -39,55 +39,78 @@ __global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
 
   // weight batches (rows k = lane + 64 r): all loads of a batch are
   // unconditional (rows past K repeat the last row and are weighted by zero)
-  // so they issue back to back; the first batch is requested before the
-  // input rows are staged, so the two latencies overlap
-  u32x4 wv[RG_BATCH][sizeof(S) / 2];
-  auto load_batch = [&](int r0) {
+  // so they issue back to back; the first batch is requested before the input
+  // rows are staged, so the two latencies overlap
+  u32x4 wv[1][RG_BATCH][sizeof(S) / 2];
+  auto load_batch = [&](int buf, int r0) {
 #pragma unroll
     for (int r = 0; r < RG_BATCH; ++r) {
       const int k = lane + 64 * min(r0 + r, rpl - 1);
       const S* p = W + (int64_t)k * a.b.n_per + c0;
-      wv[r][0] = ld16(p);
-      if constexpr (sizeof(S) == 4) wv[r][1] = ld16(p + 4);
+      wv[buf][r][0] = ld16(p);
+      if constexpr (sizeof(S) == 4) wv[buf][r][1] = ld16(p + 4);
     }
   };
-  load_batch(0);
+  load_batch(0, 0);
 
   for (int m0 = 0; m0 < M; m0 += MC) {
-    // ---- stage MC input rows (prologue applied) into LDS as xs[mm][k]; each
-    // lane moves 16 values per batch with all its loads issued together
+    // ---- stage MC input rows (prologue applied) into LDS as xs[mm][k]: all
+    // 256 threads move float4s, thread t owning column group t, t+256, ... of
+    // every row, so a thread's loads are all issued together
+    __shared__ float part_ss[RG_WAVES][MC];
     __syncthreads();
-    for (int mm = wave; mm < MC; mm += RG_WAVES) {
-      const int m = m0 + mm;
-      float* xr = xs + mm * K;
-      const bool live = m < M;
-      const float* x = a.X + (int64_t)(live ? m : 0) * a.ldx;
-      float ss = 0.f;
-      for (int k0 = 0; k0 < K; k0 += 64 * 16) {
-        float v[16], u[16];
+    {
+      const int K4 = K / 4;
+      constexpr int NQ = 8;                 // float4 per thread per round
+      float ssr[MC];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = min(k0 + 64 * i + lane, K - 1);
-          v[i] = x[k];
-          if constexpr (PRO == RP_SWIGLU) u[i] = x[K + k];
-          if constexpr (PRO == RP_RMSNORM) u[i] = a.g[k];
+      for (int mm = 0; mm < MC; ++mm) ssr[mm] = 0.f;
+      const f32x4* gain4 = reinterpret_cast<const f32x4*>(a.g);
+      for (int q0 = 0; q0 < MC * K4; q0 += 256 * NQ) {
+        f32x4 v[NQ], u[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const int q = min(q0 + tid + 256 * i, MC * K4 - 1);
+          const int mm = q / K4, c4 = q % K4;
+          const int m = min(m0 + mm, M - 1);
+          const f32x4* x = reinterpret_cast<const f32x4*>(a.X + (int64_t)m * a.ldx);
+          v[i] = x[c4];
+          if constexpr (PRO == RP_SWIGLU) u[i] = x[K4 + c4];
+          if constexpr (PRO == RP_RMSNORM) u[i] = gain4[c4];
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = k0 + 64 * i + lane;
-          float val = live ? v[i] : 0.f;
-          if constexpr (PRO == RP_SWIGLU) val = val / (1.f + __expf(-val)) * (live ? u[i] : 0.f);
-          if (k < K) {
-            ss += val * val;
-            if constexpr (PRO == RP_RMSNORM) val *= u[i];   // gain now, row scale below
-            xr[k] = val;
+        for (int i = 0; i < NQ; ++i) {
+          const int q = q0 + tid + 256 * i;
+          if (q < MC * K4) {
+            const int mm = q / K4, c4 = q % K4;
+            f32x4 val = (m0 + mm < M) ? v[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (PRO == RP_SWIGLU) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) val[e] = val[e] / (1.f + __expf(-val[e])) * u[i][e];
+            }
+            if constexpr (PRO == RP_RMSNORM) {
+              const float sq = val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
+#pragma unroll
+              for (int mq = 0; mq < MC; ++mq) ssr[mq] += (mq == mm) ? sq : 0.f;
+              val *= u[i];   // gain now, row scale below
+            }
+            *reinterpret_cast<f32x4*>(xs + mm * K + 4 * c4) = val;
           }
         }
       }
       if constexpr (PRO == RP_RMSNORM) {
-        ss = wave_sum(ss);
-        const float sc = rsqrtf(ss / (float)K + a.eps);
-        for (int k = lane; k < K; k += 64) xr[k] *= sc;
+#pragma unroll
+        for (int mm = 0; mm < MC; ++mm) {
+          const float t = wave_sum(ssr[mm]);
+          if (lane == 0) part_ss[wave][mm] = t;
+        }
+        __syncthreads();
+        for (int q = tid; q < MC * K4; q += 256) {
+          const int mm = q / K4, c4 = q % K4;
+          const float tot = (part_ss[0][mm] + part_ss[1][mm]) + (part_ss[2][mm] + part_ss[3][mm]);
+          const float sc = rsqrtf(tot / (float)K + a.eps);
+          *reinterpret_cast<f32x4*>(xs + mm * K + 4 * c4) *= sc;
+        }
       }
     }
     __syncthreads();
@@ -98,13 +121,13 @@ __global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
     for (int mm = 0; mm < MC; ++mm)
 #pragma unroll
       for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = 0.f;
-    for (int r0 = 0; r0 < rpl; r0 += RG_BATCH) {
-      if (r0 > 0 || m0 > 0) load_batch(r0);
+    const int nbatch = (rpl + RG_BATCH - 1) / RG_BATCH;
+    auto mac = [&](const u32x4 (&w)[RG_BATCH][sizeof(S) / 2], int r0) {
 #pragma unroll
       for (int r = 0; r < RG_BATCH; ++r) {
         float wf[RG_COLS];
-        Vec16<S>::unpack(wv[r][0], wf);
-        if constexpr (sizeof(S) == 4) Vec16<S>::unpack(wv[r][1], wf + 4);
+        Vec16<S>::unpack(w[r][0], wf);
+        if constexpr (sizeof(S) == 4) Vec16<S>::unpack(w[r][1], wf + 4);
         const bool in = r0 + r < rpl;
         const int k = lane + 64 * min(r0 + r, rpl - 1);
 #pragma unroll
@@ -114,6 +137,10 @@ __global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
           for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = fmaf(xv, wf[c], acc[mm][c]);
         }
       }
+    };
+    for (int bi = 0; bi < nbatch; ++bi) {
+      if (bi > 0 || m0 > 0) load_batch(0, bi * RG_BATCH);
+      mac(wv[0], bi * RG_BATCH);
     }
 
     // ---- reduce over the 64 lanes through LDS (xs is free now), 32 sums at a time

@@ -88,19 +88,6 @@ struct Plan {
   size_t total = 0;
 };
 
-static int ctx_splits_for(int dtype, int64_t M, int N, int K) {
-  if (M <= 0) return 1;
-  const int bm = dtype == 1 ? (M >= 4096 ? 128 : 64) : 64;
-  const int bn = dtype == 1 ? 128 : 64;
-  const int bk = dtype == 1 ? 64 : 16;
-  const int64_t tiles = ((M + bm - 1) / bm) * (N / bn);
-  int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t max_s = K / (4 * bk);
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return (int)s;
-}
-
 static dspark_status check_dims(const dspark_dims* dm, int op) {
   if (!dm) return fail(DSPARK_EINVAL, "dims is NULL");
   if (dm->dtype != DSPARK_F32 && dm->dtype != DSPARK_BF16)
@@ -151,7 +138,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   p->hd = dm->d / dm->n_heads;
   p->M = A * dm->gamma;
   const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
-  p->ctx_splits = ctx_splits_for(dm->dtype, T, d, mH);
+  p->ctx_splits = ctx_gemm_splits(dm->dtype, T, d, mH);
   p->chunk = attention_chunk(T, dm->n_heads, A);
   p->total_chunks = (int)attention_tiles(cu_host, A, p->chunk);
   p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;

@@ -14,6 +14,8 @@
 #include "kernels.h"
 #include "kv_layout.h"
 
+#include <type_traits>
+
 namespace dspark {
 
 // ---------------------------------------------------------------------------
@@ -264,14 +266,283 @@ __global__ __launch_bounds__(256) void gemm_f32(ASegs a, BMats b, int M, int MR,
     for (int j = 0; j < 4; ++j) epi.store(z, m0 + ty * 4 + i, n0 + tx * 4 + j, acc[i][j], M, N);
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile MFMA GEMM for the long context (M = T rows): 256x256 tiles, 4
+// waves in 2x2, each wave a 128x128 sub-tile of 4x4 32x32 MFMA blocks (its 256
+// accumulators live in the AGPR file), so each k-substep of 16 issues 16 MFMAs
+// against 8 LDS operand reads and LDS bandwidth stays below the matrix-core
+// rate. Operands move global -> LDS with the gfx950 direct 16-byte loads (no
+// register staging) through a ring of 4 stages of 32-deep k tiles, so a
+// stage's loads have three k-steps to land. Within a k-step the operands of
+// substep 1 are read while substep 0's MFMAs run. Lane l of a load
+// instruction lands at LDS base + 16 l, so each lane fetches the global chunk
+// that its (swizzled) LDS slot stands for.
+// ---------------------------------------------------------------------------
+constexpr int BG_M = 256, BG_N = 256, BG_K = 32, BG_NST = 4;
+constexpr int BG_STAGE = (BG_M + BG_N) * BG_K * 2;   // 32 KiB per stage
+constexpr int BG_SROW = 264;                          // bf16 per row of the epilogue stage
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 64-byte LDS rows (32 bf16 = 4 chunks of 16 B); chunk c of row r sits in slot
+// c ^ ((r >> 1) & 3): eight consecutive rows read at one chunk hit eight
+// distinct 16-byte bank groups.
+DSPARK_DEV int swz64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+struct EpiPartialBig {         // out[z][r][n] = acc for r < M
+  float* out;
+  int64_t split_stride;
+  static constexpr bool kStaged = false;
+};
+
+template <typename S>
+struct EpiKVBig {              // all layers' K/V, row scale, attention layout
+  S* base;
+  const float* rinv;
+  int64_t Tpad;
+  int T, d, hd, n_heads;
+  static constexpr bool kStaged = true;
+};
+
+// Workgroup barrier without the release fence that __syncthreads() implies:
+// that fence waits for every outstanding global load, including the direct
+// LDS loads of later pipeline stages. The stage being consumed is waited for
+// explicitly (wait_vmcnt); the memory clobber keeps LDS reads below it.
+DSPARK_DEV void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+DSPARK_DEV void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
+
+// Two scheduling regions per k-step: each runs 16 MFMAs of one k-substep
+// with the 8 operand reads of the next substep interleaved (2 MFMA : 1 read).
+#define DSPARK_MFMA_READ_INTERLEAVE()                                                      \
+  do {                                                                                     \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+    }                                                                                      \
+  } while (0)
+
+template <class Epi, int HD>
+__global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                       int MR, int N, int K, int k_per_split, Epi epi) {
+  __shared__ __attribute__((aligned(16))) char smem[BG_NST * BG_STAGE];
+  const int tiles_m = (MR + BG_M - 1) / BG_M;
+  const int tiles_n = N / BG_N;
+  const int ntiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  {
+    const int per = ntiles / 8;
+    if (per > 0 && bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  const int m0 = tm * BG_M, n0 = tn * BG_N;
+  const int z = blockIdx.z;
+  const int kbeg = z * k_per_split;
+  const int kend = min(K, kbeg + k_per_split);
+  const int nsteps = kend > kbeg ? (kend - kbeg) / BG_K : 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, hi = lane >> 5;
+
+  // ---- direct global -> LDS loads of one stage (4 A + 4 B per thread)
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const int k0 = kbeg + step * BG_K;
+    const int sgi = k0 / a.seg_k;
+    const int kin = k0 - sgi * a.seg_k;
+    const bf16* __restrict__ Ap = static_cast<const bf16*>(a.seg[sgi]);
+    char* base = smem + (step % BG_NST) * BG_STAGE;
+    const int rl = lane >> 2, slot = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 64 + wave * 16 + rl;
+      const int ch = slot ^ ((row >> 1) & 3);
+      const bf16* g = Ap + (int64_t)min(m0 + row, M - 1) * a.ld + kin + ch * 8;
+      __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(base + (i * 64 + wave * 16) * 64), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 64 + wave * 16 + rl;
+      const int ch = slot ^ ((row >> 1) & 3);
+      const bf16* g = Bt + (int64_t)(n0 + row) * K + k0 + ch * 8;
+      __builtin_amdgcn_global_load_lds(
+          g, (lds_ptr_t)(base + BG_M * BG_K * 2 + (i * 64 + wave * 16) * 64), 16, 0, 0);
+    }
+  };
+  auto read_ops = [&](int step, int ks, bf16x8 (&av)[4], bf16x8 (&bv)[4]) __attribute__((always_inline)) {
+    const char* As = smem + (step % BG_NST) * BG_STAGE;
+    const char* Bs = As + BG_M * BG_K * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = *reinterpret_cast<const bf16x8*>(As + swz64(wm * 128 + i * 32 + r32, 2 * ks + hi));
+      bv[i] = *reinterpret_cast<const bf16x8*>(Bs + swz64(wn * 128 + i * 32 + r32, 2 * ks + hi));
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mfma16 = [&](const bf16x8 (&av)[4], const bf16x8 (&bv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+
+  for (int st = 0; st < BG_NST - 1 && st < nsteps; ++st) issue(st);
+  for (int step = 0; step < nsteps; ++step) {
+    const int later = min(BG_NST - 2, nsteps - 1 - step);
+    if (later >= 2) wait_vmcnt<16>();
+    else if (later == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (step + BG_NST - 1 < nsteps) issue(step + BG_NST - 1);
+    bf16x8 av0[4], bv0[4], av1[4], bv1[4];
+    read_ops(step, 0, av0, bv0);
+    read_ops(step, 1, av1, bv1);
+    mfma16(av0, bv0);
+    mfma16(av1, bv1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    DSPARK_MFMA_READ_INTERLEAVE();
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  }
+
+  // accumulator (i, j, r) of this lane: tile row wm*128 + i*32 + 8*(r/4) +
+  // 4*(lane/32) + r%4, tile column wn*128 + j*32 + lane%32
+  if constexpr (!Epi::kStaged) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+          if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
+        }
+  } else {
+    // Each wave moves its 128x128 sub-tile one 32x32 block at a time through
+    // a private fp32 LDS scratch (row stride 36 floats: 16-byte aligned rows,
+    // conflict-free column writes) and stores 16-byte vectors in the
+    // attention layout: K as one row x 8 columns, V as 4 rows x 2 columns.
+    using S = std::remove_pointer_t<decltype(epi.base)>;
+    using L = KVLayout<S>;
+    static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
+    constexpr int SS = 36;
+    __syncthreads();
+    float* scr = reinterpret_cast<float*>(smem) + wave * (32 * SS + 128);
+    float* rsc = scr + 32 * SS;
+    const int64_t rw0 = (int64_t)m0 + wm * 128;   // first row of this wave's sub-tile
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t row = rw0 + lane + 64 * q;
+      rsc[lane + 64 * q] = row < epi.T ? epi.rinv[row] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lrow = (r >> 2) * 8 + hi * 4 + (r & 3);
+          scr[lrow * SS + r32] = acc[i][j][r] * rsc[i * 32 + lrow];
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int n = n0 + wn * 128 + j * 32;          // 32 columns inside one head
+        const int layer = n / (2 * epi.d);
+        const int kv = (n / epi.d) & 1;
+        const int w = n % epi.d;
+        const int head = w / HD, c0 = w % HD;
+        const int64_t tb = rw0 + i * 32;
+        if (kv == 0) {
+          S* kb = epi.base + L::head_base(layer, 0, head, epi.n_heads, epi.Tpad, HD);
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int row = r32, cg = hi + 2 * it;
+            const int64_t t = tb + row;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(scr + row * SS + cg * 8);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(scr + row * SS + cg * 8 + 4);
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = from_f32<bf16>(x0[e]);
+              v[4 + e] = from_f32<bf16>(x1[e]);
+            }
+            if (t < epi.Tpad) *reinterpret_cast<bf16x8*>(kb + L::k_off(t, c0 + cg * 8, HD)) = v;
+          }
+        } else {
+          S* vb = epi.base + L::head_base(layer, 1, head, epi.n_heads, epi.Tpad, HD);
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int v = lane + 64 * it;
+            const int cp = v & 15, rq = v >> 4;         // 16 column pairs x 8 row quads
+            const int64_t t = tb + rq * 4;
+            bf16x8 out;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const float* src = scr + (rq * 4 + rr) * SS + cp * 2;
+              out[2 * rr] = from_f32<bf16>(src[0]);
+              out[2 * rr + 1] = from_f32<bf16>(src[1]);
+            }
+            if (t < epi.Tpad) *reinterpret_cast<bf16x8*>(vb + L::v_off(t, c0 + cp * 2, HD)) = out;
+          }
+        }
+      }
+    }
+  }
+}
+
 static int pick_gemm_bm(int M) { return M >= 4096 ? 128 : 64; }
+static bool use_big_tiles(int dtype, int64_t M, int N) { return dtype == 1 && N % BG_N == 0 && M >= 512; }
+
+int ctx_gemm_splits(int dtype, int64_t M, int N, int K) {
+  if (M <= 0) return 1;
+  int64_t tiles, target;
+  int bk;
+  if (use_big_tiles(dtype, M, N)) {
+    tiles = ((M + BG_M - 1) / BG_M) * (N / BG_N);
+    target = 256;   // one 128 KiB-LDS workgroup per CU
+    bk = BG_K;
+  } else {
+    const int bm = dtype == 1 ? pick_gemm_bm((int)M) : 64;
+    const int bn = dtype == 1 ? 128 : 64;
+    tiles = ((M + bm - 1) / bm) * (N / bn);
+    target = 512;
+    bk = dtype == 1 ? BK : 16;
+  }
+  int64_t sp = (target + tiles - 1) / tiles;
+  const int64_t max_s = K / (4 * bk);
+  if (sp > max_s) sp = max_s;
+  if (sp < 1) sp = 1;
+  return (int)sp;
+}
 
 hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, float* out,
                            int M, int N, int K, int splits, hipStream_t s) {
   const int kps = ((K / splits + BK - 1) / BK) * BK;
-  EpiPartial epi{out, (int64_t)M * N};
   trace_pre(K_GEMM_CTX, s);
-  if (dtype == 1) {
+  if (use_big_tiles(dtype, M, N)) {
+    EpiPartialBig epi{out, (int64_t)M * N};
+    const int kps = ((K / splits + BG_K - 1) / BG_K) * BG_K;
+    dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), 1, splits);
+    gemm_big_kernel<EpiPartialBig, 128><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt), M, M,
+                                                             N, K, kps, epi);
+  } else if (dtype == 1) {
+    EpiPartial epi{out, (int64_t)M * N};
     const bf16* B = static_cast<const bf16*>(Bt);
     if (pick_gemm_bm(M) == 128) {
       dim3 grid(((M + 127) / 128) * (N / 128), 1, splits);
@@ -281,6 +552,7 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
       gemm_bf16_nt<64, 128, 2, 2, EpiPartial><<<grid, 256, 0, s>>>(a, B, M, M, N, K, kps, epi);
     }
   } else {
+    EpiPartial epi{out, (int64_t)M * N};
     const int kps16 = ((K / splits + 15) / 16) * 16;
     dim3 grid(((M + 63) / 64) * (N / 64), 1, splits);
     gemm_f32<EpiPartial><<<grid, 256, 0, s>>>(a, b, M, M, N, K, kps16, epi);
@@ -301,7 +573,17 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
   const int M = kv.T;
   const int Mrows = (int)kv.Tpad;  // rows T..Tpad-1 are written as zeros
   trace_pre(K_GEMM_KV, s);
-  if (dtype == 1) {
+  if (use_big_tiles(dtype, M, N)) {
+    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
+    dim3 grid(((Mrows + BG_M - 1) / BG_M) * (N / BG_N), 1, 1);
+    const bf16* B = static_cast<const bf16*>(Bt);
+    if (kv.hd == 128)
+      gemm_big_kernel<EpiKVBig<bf16>, 128><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    else if (kv.hd == 64)
+      gemm_big_kernel<EpiKVBig<bf16>, 64><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    else
+      gemm_big_kernel<EpiKVBig<bf16>, 32><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+  } else if (dtype == 1) {
     EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
     const bf16* B = static_cast<const bf16*>(Bt);
     if (pick_gemm_bm(M) == 128) {

@@ -61,6 +61,8 @@ struct KVDesc {
 // bf16: Bt = [sum(n) rows][K] transposed (and gain-folded) copy of B.
 hipError_t launch_prep_transpose_bf16(const BMats& b, int K, void* Bt, hipStream_t s);
 
+// K splits of the Eq 2 projection for these sizes (sizes the partial buffer)
+int ctx_gemm_splits(int dtype, int64_t M, int N, int K);
 // out[z][r][n] = sum_{k in split z} A(r,k) B(k,n); float32 partials.
 hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt,
                            float* out, int M, int N, int K, int splits, hipStream_t s);

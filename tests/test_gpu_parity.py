@@ -182,7 +182,12 @@ def test_varlen_equals_separate_runs():
         xb["block_in"] = x["block_in"][b:b + 1]
         wb = W.Workload(**{**w.__dict__, "A": 1})
         ob, _, _ = _forward(wb, xb)
-        assert rel_err(ob[0].cpu().numpy(), out[b].cpu().numpy()) < 1e-5, b
+        # a single-sequence run may take a different GEMM tiling than the
+        # packed one (its K/V round to bf16 differently); a packing error
+        # would be O(1)
+        e = rel_err(ob[0].cpu().numpy(), out[b].cpu().numpy())
+        print(f"  sequence {b}: packed vs alone rel err {e:.2e}")
+        assert e < 1e-3, b
 
 
 def test_block_permutation_equivariance():
