@@ -285,9 +285,12 @@ constexpr int BG_SROW = 264;                          // bf16 per row of the epi
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 64-byte LDS rows (32 bf16 = 4 chunks of 16 B); chunk c of row r sits in slot
-// c ^ ((r >> 1) & 3): eight consecutive rows read at one chunk hit eight
-// distinct 16-byte bank groups.
-DSPARK_DEV int swz64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// c ^ f(r), f(r) = (r >> 2) & 3. The MFMA operand reads (lane -> row lane % 32,
+// chunk 2 * ks + lane / 32) then take no bank-conflict cycles on gfx950, as
+// the SQ_LDS_BANK_CONFLICT counter shows; swizzles whose pattern repeats every
+// 8 rows of r >> 1 cost about 4 conflict cycles per ds_read_b128.
+DSPARK_DEV int swz64_f(int row) { return (row >> 2) & 3; }
+DSPARK_DEV int swz64(int row, int chunk) { return row * 64 + ((chunk ^ swz64_f(row)) << 4); }
 
 struct EpiPartialBig {         // out[z][r][n] = acc for r < M
   float* out;
@@ -334,14 +337,21 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   const int tiles_m = (MR + BG_M - 1) / BG_M;
   const int tiles_n = N / BG_N;
   const int ntiles = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  {
-    const int per = ntiles / 8;
-    if (per > 0 && bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
-  }
-  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  // Work items (split z, tile) are dealt to the 8 XCDs (workgroup i runs on
+  // XCD i % 8) in contiguous runs, z-major, so an XCD owns whole K slices;
+  // inside a slice, tiles go in groups of up to 8 m-tiles swept n by n, so
+  // the XCD's L2 holds a few A panels while it walks the B panels.
+  const int total = ntiles * (int)gridDim.y;
+  int logical = blockIdx.x + (int)gridDim.x * (int)blockIdx.y;
+  if (total % 8 == 0) logical = (logical % 8) * (total / 8) + logical / 8;
+  const int z = logical / ntiles;
+  const int t = logical % ntiles;
+  const int G = min(tiles_m, 8);
+  const int gsize = G * tiles_n;
+  const int grp = t / gsize, first_m = grp * G;
+  const int gm = min(tiles_m - first_m, G);
+  const int tm = first_m + (t % gsize) % gm, tn = (t % gsize) / gm;
   const int m0 = tm * BG_M, n0 = tn * BG_N;
-  const int z = blockIdx.z;
   const int kbeg = z * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
   const int nsteps = kend > kbeg ? (kend - kbeg) / BG_K : 0;
@@ -360,14 +370,14 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = i * 64 + wave * 16 + rl;
-      const int ch = slot ^ ((row >> 1) & 3);
+      const int ch = slot ^ swz64_f(row);
       const bf16* g = Ap + (int64_t)min(m0 + row, M - 1) * a.ld + kin + ch * 8;
       __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(base + (i * 64 + wave * 16) * 64), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = i * 64 + wave * 16 + rl;
-      const int ch = slot ^ ((row >> 1) & 3);
+      const int ch = slot ^ swz64_f(row);
       const bf16* g = Bt + (int64_t)(n0 + row) * K + k0 + ch * 8;
       __builtin_amdgcn_global_load_lds(
           g, (lds_ptr_t)(base + BG_M * BG_K * 2 + (i * 64 + wave * 16) * 64), 16, 0, 0);
@@ -538,7 +548,7 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
   if (use_big_tiles(dtype, M, N)) {
     EpiPartialBig epi{out, (int64_t)M * N};
     const int kps = ((K / splits + BG_K - 1) / BG_K) * BG_K;
-    dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), 1, splits);
+    dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);
     gemm_big_kernel<EpiPartialBig, 128><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt), M, M,
                                                              N, K, kps, epi);
   } else if (dtype == 1) {
