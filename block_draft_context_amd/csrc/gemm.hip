@@ -296,6 +296,7 @@ struct EpiPartialBig {         // out[z][r][n] = acc for r < M
   float* out;
   int64_t split_stride;
   static constexpr bool kStaged = false;
+  static constexpr bool kSwap = false;
 };
 
 template <typename S>
@@ -305,6 +306,7 @@ struct EpiKVBig {              // all layers' K/V, row scale, attention layout
   int64_t Tpad;
   int T, d, hd, n_heads;
   static constexpr bool kStaged = true;
+  static constexpr bool kSwap = true;     // accumulate C^T: a lane holds one row
 };
 
 // Workgroup barrier without the release fence that __syncthreads() implies:
@@ -313,22 +315,65 @@ struct EpiKVBig {              // all layers' K/V, row scale, attention layout
 // explicitly (wait_vmcnt); the memory clobber keeps LDS reads below it.
 DSPARK_DEV void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8). The builtin, unlike inline asm, lets the compiler's
+// own wait insertion see that the counters were drained.
 template <int N>
 DSPARK_DEV void wait_vmcnt() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+DSPARK_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-// Two scheduling regions per k-step: each runs 16 MFMAs of one k-substep
-// with the 8 operand reads of the next substep interleaved (2 MFMA : 1 read).
-#define DSPARK_MFMA_READ_INTERLEAVE()                                                      \
+// Each k-step is two scheduling regions of 16 MFMAs. The first runs the
+// MFMAs of k-substep 0 with the operand reads of substep 1 interleaved; the
+// second, after the stage barrier, runs those of substep 1 with the reads of
+// the next step's substep 0 and the direct loads of a later stage interleaved.
+#define DSPARK_BIG_SCHED_A()                                                               \
   do {                                                                                     \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                   \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                     \
   } while (0)
+#define DSPARK_BIG_SCHED_B()                                                               \
+  do {                                                                                     \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+    }                                                                                      \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+    }                                                                                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                     \
+  } while (0)
+
+// Two floats rounded to bf16 and packed low, high into one dword.
+DSPARK_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(lo)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(hi)) << 16);
+}
+
+// 4x4 dword transpose among the 4 lanes of a DPP quad: afterwards a[m] of
+// lane k is the a[k] that lane m held. Two exchange stages, lane ^ 2 then
+// lane ^ 1, each moving two dwords per lane.
+DSPARK_DEV void transpose4_quad(uint32_t (&a)[4], int k) {
+  const bool lo2 = k < 2, even = (k & 1) == 0;
+  const uint32_t s0 = lo2 ? a[2] : a[0], s1 = lo2 ? a[3] : a[1];
+  const uint32_t r0 = __builtin_amdgcn_mov_dpp((int)s0, 0x4E, 0xf, 0xf, true);   // quad_perm 2,3,0,1
+  const uint32_t r1 = __builtin_amdgcn_mov_dpp((int)s1, 0x4E, 0xf, 0xf, true);
+  const uint32_t t0 = lo2 ? a[0] : r0, t1 = lo2 ? a[1] : r1;
+  const uint32_t t2 = lo2 ? r0 : a[2], t3 = lo2 ? r1 : a[3];
+  const uint32_t u0 = even ? t1 : t0, u1 = even ? t3 : t2;
+  const uint32_t w0 = __builtin_amdgcn_mov_dpp((int)u0, 0xB1, 0xf, 0xf, true);   // quad_perm 1,0,3,2
+  const uint32_t w1 = __builtin_amdgcn_mov_dpp((int)u1, 0xB1, 0xf, 0xf, true);
+  a[0] = even ? t0 : w0;
+  a[1] = even ? w0 : t1;
+  a[2] = even ? t2 : w1;
+  a[3] = even ? w1 : t3;
+}
 
 template <class Epi, int HD>
 __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
@@ -359,12 +404,23 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, hi = lane >> 5;
 
+  // lane i holds the address of A segment i; the loop reads it with a lane
+  // select instead of a scalar memory load, whose wait would also drain the
+  // LDS reads in flight
+  uint64_t my_seg = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSegs; ++i)
+    if (lane == i && i < a.nseg) my_seg = reinterpret_cast<uint64_t>(a.seg[i]);
+  const uint32_t seg_lo = (uint32_t)my_seg, seg_hi = (uint32_t)(my_seg >> 32);
+
   // ---- direct global -> LDS loads of one stage (4 A + 4 B per thread)
   auto issue = [&](int step) __attribute__((always_inline)) {
     const int k0 = kbeg + step * BG_K;
     const int sgi = k0 / a.seg_k;
     const int kin = k0 - sgi * a.seg_k;
-    const bf16* __restrict__ Ap = static_cast<const bf16*>(a.seg[sgi]);
+    const uint64_t ap = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)seg_hi, sgi) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)seg_lo, sgi);
+    const bf16* __restrict__ Ap = reinterpret_cast<const bf16*>(ap);
     char* base = smem + (step % BG_NST) * BG_STAGE;
     const int rl = lane >> 2, slot = lane & 3;
 #pragma unroll
@@ -405,30 +461,55 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = Epi::kSwap
+                        ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
-  for (int st = 0; st < BG_NST - 1 && st < nsteps; ++st) issue(st);
-  for (int step = 0; step < nsteps; ++step) {
-    const int later = min(BG_NST - 2, nsteps - 1 - step);
-    if (later >= 2) wait_vmcnt<16>();
-    else if (later == 1) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    if (step + BG_NST - 1 < nsteps) issue(step + BG_NST - 1);
-    bf16x8 av0[4], bv0[4], av1[4], bv1[4];
-    read_ops(step, 0, av0, bv0);
-    read_ops(step, 1, av1, bv1);
-    mfma16(av0, bv0);
-    mfma16(av1, bv1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    DSPARK_MFMA_READ_INTERLEAVE();
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  // Ring of BG_NST stages. All four are loaded up front; the barrier in the
+  // middle of step s (everyone has read stage s, stage s+1 has landed) frees
+  // stage s for the load of step s+4. Loads past the last step repeat the
+  // last one (in bounds, never read), which keeps every wait count fixed.
+  // row scales of the K/V epilogue (one row per lane per 32-row block),
+  // loaded ahead of the stage loads so the in-order wait counts still hold
+  float rsc[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (Epi::kSwap) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * 128 + i * 32 + r32;
+      rsc[i] = epi.rinv[min(row, epi.T - 1)];
+      if (row >= epi.T) rsc[i] = 0.f;
+    }
   }
 
-  // accumulator (i, j, r) of this lane: tile row wm*128 + i*32 + 8*(r/4) +
-  // 4*(lane/32) + r%4, tile column wn*128 + j*32 + lane%32
-  if constexpr (!Epi::kStaged) {
+  bf16x8 av0[4], bv0[4], av1[4], bv1[4];
+  if (nsteps > 0) {
+#pragma unroll
+    for (int st = 0; st < BG_NST; ++st) issue(min(st, nsteps - 1));
+    wait_vmcnt<24>();
+    stage_barrier();
+    read_ops(0, 0, av0, bv0);
+    for (int step = 0; step < nsteps - 1; ++step) {
+      read_ops(step, 1, av1, bv1);
+      mfma16(av0, bv0);
+      DSPARK_BIG_SCHED_A();
+      wait_vmcnt<16>();
+      wait_lgkm0();
+      stage_barrier();
+      read_ops(step + 1, 0, av0, bv0);
+      issue(min(step + BG_NST, nsteps - 1));
+      mfma16(av1, bv1);
+      DSPARK_BIG_SCHED_B();
+    }
+    read_ops(nsteps - 1, 1, av1, bv1);
+    mfma16(av0, bv0);
+    mfma16(av1, bv1);
+    wait_vmcnt<0>();
+  }
+
+  if constexpr (!Epi::kSwap) {
+    // accumulator (i, j, r) of this lane: tile row wm*128 + i*32 + 8*(r/4) +
+    // 4*(lane/32) + r%4, tile column wn*128 + j*32 + lane%32
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -440,75 +521,57 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
           if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
         }
   } else {
-    // Each wave moves its 128x128 sub-tile one 32x32 block at a time through
-    // a private fp32 LDS scratch (row stride 36 floats: 16-byte aligned rows,
-    // conflict-free column writes) and stores 16-byte vectors in the
-    // attention layout: K as one row x 8 columns, V as 4 rows x 2 columns.
+    // Transposed accumulators: (i, j, r) of this lane is tile row (token)
+    // wm*128 + i*32 + lane%32 and tile column wn*128 + j*32 + 8*(r/4) +
+    // 4*(lane/32) + r%4. After the row scale and rounding, each 32x32 block
+    // becomes 16-byte vectors of the attention layout with lane exchanges
+    // only: K (one token x 8 columns) pairs lane l with l^32, V (4 tokens x 2
+    // columns) transposes dwords among the 4 lanes of consecutive tokens.
     using S = std::remove_pointer_t<decltype(epi.base)>;
     using L = KVLayout<S>;
     static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
-    constexpr int SS = 36;
-    __syncthreads();
-    float* scr = reinterpret_cast<float*>(smem) + wave * (32 * SS + 128);
-    float* rsc = scr + 32 * SS;
-    const int64_t rw0 = (int64_t)m0 + wm * 128;   // first row of this wave's sub-tile
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t row = rw0 + lane + 64 * q;
-      rsc[lane + 64 * q] = row < epi.T ? epi.rinv[row] : 0.f;
-    }
+    const int nw = n0 + wn * 128;     // the wave's 128 columns lie in one K or V block
+    const int layer = nw / (2 * epi.d);
+    const int kv = (nw / epi.d) & 1;
+    const int k4 = lane & 3;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int64_t tb = (int64_t)m0 + wm * 128 + i * 32;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lrow = (r >> 2) * 8 + hi * 4 + (r & 3);
-          scr[lrow * SS + r32] = acc[i][j][r] * rsc[i * 32 + lrow];
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int n = n0 + wn * 128 + j * 32;          // 32 columns inside one head
-        const int layer = n / (2 * epi.d);
-        const int kv = (n / epi.d) & 1;
-        const int w = n % epi.d;
+        const int w = (nw + j * 32) % epi.d;
         const int head = w / HD, c0 = w % HD;
-        const int64_t tb = rw0 + i * 32;
+        S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
+        // P[q][x]: columns 8q + 4*(lane/32) + 2x, +1 of token tb + lane%32
+        uint32_t P[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rsc[i], acc[i][j][4 * q + 2 * x + 1] * rsc[i]);
         if (kv == 0) {
-          S* kb = epi.base + L::head_base(layer, 0, head, epi.n_heads, epi.Tpad, HD);
+          const int64_t t = tb + r32;
 #pragma unroll
-          for (int it = 0; it < 2; ++it) {
-            const int row = r32, cg = hi + 2 * it;
-            const int64_t t = tb + row;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(scr + row * SS + cg * 8);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(scr + row * SS + cg * 8 + 4);
-            bf16x8 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[e] = from_f32<bf16>(x0[e]);
-              v[4 + e] = from_f32<bf16>(x1[e]);
-            }
-            if (t < epi.Tpad) *reinterpret_cast<bf16x8*>(kb + L::k_off(t, c0 + cg * 8, HD)) = v;
+          for (int qq = 0; qq < 2; ++qq) {
+            // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
+            const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
+            const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+            const int g = qq + 2 * hi;
+            if (t < epi.Tpad) *reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)) = v;
           }
         } else {
-          S* vb = epi.base + L::head_base(layer, 1, head, epi.n_heads, epi.Tpad, HD);
+          const int64_t t0 = tb + (r32 & ~3);
 #pragma unroll
-          for (int it = 0; it < 2; ++it) {
-            const int v = lane + 64 * it;
-            const int cp = v & 15, rq = v >> 4;         // 16 column pairs x 8 row quads
-            const int64_t t = tb + rq * 4;
-            bf16x8 out;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const float* src = scr + (rq * 4 + rr) * SS + cp * 2;
-              out[2 * rr] = from_f32<bf16>(src[0]);
-              out[2 * rr + 1] = from_f32<bf16>(src[1]);
-            }
-            if (t < epi.Tpad) *reinterpret_cast<bf16x8*>(vb + L::v_off(t, c0 + cp * 2, HD)) = out;
+          for (int set = 0; set < 2; ++set) {
+            // a[c] = column pair 4*(2*set + c/2) + 2*(lane/32) + c%2 of this
+            // lane's token; after the transpose lane k of the quad holds pair
+            // c = k for tokens t0 .. t0+3
+            uint32_t a[4] = {P[2 * set][0], P[2 * set][1], P[2 * set + 1][0], P[2 * set + 1][1]};
+            transpose4_quad(a, k4);
+            const int p = 4 * (2 * set + (k4 >> 1)) + 2 * hi + (k4 & 1);
+            const u32x4 v = {a[0], a[1], a[2], a[3]};
+            if (t0 < epi.Tpad) *reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)) = v;
           }
         }
       }
