@@ -6,12 +6,15 @@
 //   D' = E + (SiLU(G) * U) . Wdown
 // With at most a few dozen rows these products stream their weights once and
 // are bound by memory latency, so each is one "row GEMM" launch with no
-// cross-workgroup communication: a workgroup owns 32 output columns (a wave
-// owns 8, one 16-byte bf16 vector per weight row) and the full K; its lanes
-// split K, so each lane keeps 16 independent 16-byte weight loads in flight,
-// and the wave reduces its lanes through LDS. The row norm / SwiGLU that feeds
-// a product is applied while its input rows are staged in LDS (prologue), the
-// residual and the Q/K_d/V_d split on the way out (epilogue).
+// cross-workgroup communication and as many workgroups as the weights allow:
+// a workgroup owns 8 output columns (one 16-byte bf16 vector per weight row)
+// and the full K, and its 256 threads split K, each with its few weight
+// vectors requested before anything else. The row norm / SwiGLU that feeds a
+// product is applied while its input rows are staged in LDS (prologue); the
+// residual and the Q/K_d/V_d split are applied on the way out (epilogue).
+// Workgroup i runs on XCD i % 8, so column groups are dealt to the XCDs in
+// contiguous runs: the workgroups that share a 128-byte weight line then
+// share one L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,71 +22,85 @@
 
 namespace dspark {
 
-constexpr int RG_COLS = 8;          // columns per wave
-constexpr int RG_WAVES = 4;
-constexpr int RG_WG_COLS = RG_COLS * RG_WAVES;
+constexpr int RG_COLS = 8;          // columns per workgroup
+constexpr int RG_THREADS = 256;
+constexpr int RG_WAVES = RG_THREADS / 64;
+constexpr int RG_MC = 8;            // block rows per pass
 constexpr int RG_XS = 16384;        // floats of staged rows (64 KiB)
-constexpr int RG_BATCH = 16;        // weight rows per lane per batch
+constexpr int RG_RB = 8;            // weight rows per thread held at once
+constexpr int RG_RED = 64 * 65;     // floats of one wave's reduction block
+constexpr int RG_LDS = RG_XS > RG_WAVES * RG_RED ? RG_XS : RG_WAVES * RG_RED;
 
-int rowgemm_rows_per_pass(int K) { return std::max(1, std::min(8, RG_XS / K)); }
+int rowgemm_rows_per_pass(int K) { return std::max(1, std::min(RG_MC, RG_XS / K)); }
 
-template <typename S, int PRO, int EPI, int MC>
-__global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) float xs[RG_XS];
+template <typename S, int PRO, int EPI>
+__global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) float xs[RG_LDS];   // staged rows, then reductions
+  __shared__ float part_ss[RG_WAVES][RG_MC];
+  __shared__ float wred[RG_WAVES][RG_MC * RG_COLS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, M = a.M;
-  const int n0 = blockIdx.x * RG_WG_COLS + wave * RG_COLS;   // this wave's first column
+  const int G = gridDim.x;
+  const int cg = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int n0 = cg * RG_COLS;
   const int mi = n0 / a.b.n_per, c0 = n0 % a.b.n_per;
   const S* __restrict__ W = static_cast<const S*>(a.b.mat[mi]);
-  const int rpl = K / 64;                                     // weight rows per lane
+  const int rpt = (K + RG_THREADS - 1) / RG_THREADS;          // weight rows per thread
+  const int mc = max(1, min(RG_MC, RG_XS / K));
+  constexpr int NV = sizeof(S) / 2;                            // 16-byte vectors per row
 
-  // weight batches (rows k = lane + 64 r): all loads of a batch are
-  // unconditional (rows past K repeat the last row and are weighted by zero)
-  // so they issue back to back; the first batch is requested before the input
-  // rows are staged, so the two latencies overlap
-  u32x4 wv[1][RG_BATCH][sizeof(S) / 2];
-  auto load_batch = [&](int buf, int r0) {
+  // weight rows k = tid + 256 r, RG_RB at a time; loads are unconditional
+  // (rows past K repeat row K-1 and are weighted by zero) so they issue back
+  // to back, and the first batch is requested before the rows are staged
+  u32x4 wv[RG_RB][NV];
+  auto load_batch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < RG_BATCH; ++r) {
-      const int k = lane + 64 * min(r0 + r, rpl - 1);
+    for (int r = 0; r < RG_RB; ++r) {
+      const int k = min(tid + RG_THREADS * (r0 + r), K - 1);
       const S* p = W + (int64_t)k * a.b.n_per + c0;
-      wv[buf][r][0] = ld16(p);
-      if constexpr (sizeof(S) == 4) wv[buf][r][1] = ld16(p + 4);
+      wv[r][0] = ld16(p);
+      if constexpr (NV == 2) wv[r][1] = ld16(p + 4);
     }
   };
-  load_batch(0, 0);
+  load_batch(0);
 
-  for (int m0 = 0; m0 < M; m0 += MC) {
-    // ---- stage MC input rows (prologue applied) into LDS as xs[mm][k]: all
-    // 256 threads move float4s, thread t owning column group t, t+256, ... of
-    // every row, so a thread's loads are all issued together
-    __shared__ float part_ss[RG_WAVES][MC];
+  for (int m0 = 0; m0 < M; m0 += mc) {
+    const int mp = min(mc, M - m0);                             // live rows of this pass
+    // residual of this thread's output (wave 0, lane o = m * 8 + c), early
+    float resv = 0.f;
+    if constexpr (EPI == RE_RESID) {
+      if (wave == 0) {
+        const int m = m0 + min(lane / RG_COLS, mp - 1);
+        resv = a.res[(int64_t)m * a.ldo + n0 + lane % RG_COLS];
+      }
+    }
+    // ---- stage the pass's rows (prologue applied) as xs[mm][k]: thread t
+    // moves float4 t, t+256, ... of the [mp][K] block, all loads together
     __syncthreads();
     {
       const int K4 = K / 4;
-      constexpr int NQ = 8;                 // float4 per thread per round
-      float ssr[MC];
+      constexpr int NQ = 8;
+      float ssr[RG_MC];
 #pragma unroll
-      for (int mm = 0; mm < MC; ++mm) ssr[mm] = 0.f;
+      for (int mm = 0; mm < RG_MC; ++mm) ssr[mm] = 0.f;
       const f32x4* gain4 = reinterpret_cast<const f32x4*>(a.g);
-      for (int q0 = 0; q0 < MC * K4; q0 += 256 * NQ) {
+      for (int q0 = 0; q0 < mp * K4; q0 += RG_THREADS * NQ) {
         f32x4 v[NQ], u[NQ];
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-          const int q = min(q0 + tid + 256 * i, MC * K4 - 1);
+          const int q = min(q0 + tid + RG_THREADS * i, mp * K4 - 1);
           const int mm = q / K4, c4 = q % K4;
-          const int m = min(m0 + mm, M - 1);
-          const f32x4* x = reinterpret_cast<const f32x4*>(a.X + (int64_t)m * a.ldx);
+          const f32x4* x = reinterpret_cast<const f32x4*>(a.X + (int64_t)(m0 + mm) * a.ldx);
           v[i] = x[c4];
           if constexpr (PRO == RP_SWIGLU) u[i] = x[K4 + c4];
           if constexpr (PRO == RP_RMSNORM) u[i] = gain4[c4];
         }
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-          const int q = q0 + tid + 256 * i;
-          if (q < MC * K4) {
+          const int q = q0 + tid + RG_THREADS * i;
+          if (q < mp * K4) {
             const int mm = q / K4, c4 = q % K4;
-            f32x4 val = (m0 + mm < M) ? v[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 val = v[i];
             if constexpr (PRO == RP_SWIGLU) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) val[e] = val[e] / (1.f + __expf(-val[e])) * u[i][e];
@@ -91,7 +108,7 @@ __global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
             if constexpr (PRO == RP_RMSNORM) {
               const float sq = val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
 #pragma unroll
-              for (int mq = 0; mq < MC; ++mq) ssr[mq] += (mq == mm) ? sq : 0.f;
+              for (int mq = 0; mq < RG_MC; ++mq) ssr[mq] += (mq == mm) ? sq : 0.f;
               val *= u[i];   // gain now, row scale below
             }
             *reinterpret_cast<f32x4*>(xs + mm * K + 4 * c4) = val;
@@ -100,12 +117,14 @@ __global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
       }
       if constexpr (PRO == RP_RMSNORM) {
 #pragma unroll
-        for (int mm = 0; mm < MC; ++mm) {
-          const float t = wave_sum(ssr[mm]);
-          if (lane == 0) part_ss[wave][mm] = t;
+        for (int mm = 0; mm < RG_MC; ++mm) {
+          if (mm < mp) {
+            const float t = wave_sum(ssr[mm]);
+            if (lane == 0) part_ss[wave][mm] = t;
+          }
         }
         __syncthreads();
-        for (int q = tid; q < MC * K4; q += 256) {
+        for (int q = tid; q < mp * K4; q += RG_THREADS) {
           const int mm = q / K4, c4 = q % K4;
           const float tot = (part_ss[0][mm] + part_ss[1][mm]) + (part_ss[2][mm] + part_ss[3][mm]);
           const float sc = rsqrtf(tot / (float)K + a.eps);
@@ -115,117 +134,89 @@ __global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmArgs a) {
     }
     __syncthreads();
 
-    // ---- partial dot products over this lane's rows k = lane + 64 r
-    float acc[MC][RG_COLS];
+    // ---- partial dot products over this thread's rows
+    float acc[RG_MC][RG_COLS];
 #pragma unroll
-    for (int mm = 0; mm < MC; ++mm)
+    for (int mm = 0; mm < RG_MC; ++mm)
 #pragma unroll
       for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = 0.f;
-    const int nbatch = (rpl + RG_BATCH - 1) / RG_BATCH;
-    auto mac = [&](const u32x4 (&w)[RG_BATCH][sizeof(S) / 2], int r0) {
+    for (int r0 = 0; r0 < rpt; r0 += RG_RB) {
+      if (r0 > 0 || m0 > 0) load_batch(r0);
 #pragma unroll
-      for (int r = 0; r < RG_BATCH; ++r) {
-        float wf[RG_COLS];
-        Vec16<S>::unpack(w[r][0], wf);
-        if constexpr (sizeof(S) == 4) Vec16<S>::unpack(w[r][1], wf + 4);
-        const bool in = r0 + r < rpl;
-        const int k = lane + 64 * min(r0 + r, rpl - 1);
+      for (int r = 0; r < RG_RB; ++r) {
+        const int k = tid + RG_THREADS * (r0 + r);
+        if (r0 + r < rpt) {
+          float wf[RG_COLS];
+          Vec16<S>::unpack(wv[r][0], wf);
+          if constexpr (NV == 2) Vec16<S>::unpack(wv[r][1], wf + 4);
+          const bool in = k < K;
 #pragma unroll
-        for (int mm = 0; mm < MC; ++mm) {
-          const float xv = in ? xs[mm * K + k] : 0.f;
+          for (int mm = 0; mm < RG_MC; ++mm) {
+            if (mm < mp) {
+              const float xv = in ? xs[mm * K + k] : 0.f;
 #pragma unroll
-          for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = fmaf(xv, wf[c], acc[mm][c]);
+              for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = fmaf(xv, wf[c], acc[mm][c]);
+            }
+          }
         }
       }
-    };
-    for (int bi = 0; bi < nbatch; ++bi) {
-      if (bi > 0 || m0 > 0) load_batch(0, bi * RG_BATCH);
-      mac(wv[0], bi * RG_BATCH);
     }
 
-    // ---- reduce over the 64 lanes through LDS (xs is free now), 32 sums at a time
-    constexpr int NH = (MC * RG_COLS + 31) / 32;
-    float resv[NH];   // residual rows, requested before the reduction
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      resv[h] = 0.f;
-      if constexpr (EPI == RE_RESID) {
-        const int idx = h * 32 + (lane & 31);
-        const int m = min(m0 + idx / RG_COLS, M - 1);
-        resv[h] = a.res[(int64_t)m * a.ldo + n0 + idx % RG_COLS];
-      }
-    }
+    // ---- reduce: over the wave's 64 lanes through LDS (row stride 65 keeps
+    // both the writes and the column reads conflict-free), then over the 4 waves
     __syncthreads();
-    float* red = xs + wave * (32 * 65);
-    float outv[NH];
+    float* red = xs + wave * RG_RED;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
+    for (int mm = 0; mm < RG_MC; ++mm) {
+      if (mm < mp) {
 #pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        const int idx = h * 32 + v;
-        if (idx < MC * RG_COLS) red[v * 65 + lane] = acc[idx / RG_COLS][idx % RG_COLS];
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float sum = 0.f;
-      if (lane < 32) {
-#pragma unroll 8
-        for (int j = 0; j < 64; ++j) sum += red[lane * 65 + j];
-      }
-      outv[h] = sum;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-
-    // ---- epilogue: lane < 32 owns output idx = h*32 + lane
-    if (lane < 32) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const int idx = h * 32 + lane;
-        if (idx >= MC * RG_COLS) continue;
-        const int m = m0 + idx / RG_COLS;
-        if (m >= M) continue;
-        const int n = n0 + idx % RG_COLS;
-        const float v = outv[h];
-        if constexpr (EPI == RE_QKV) {
-          const int seg = n / a.d, col = n % a.d;
-          const int64_t o = (int64_t)m * a.d + col;
-          if (seg == 0) a.q[o] = v * a.qscale;
-          else if (seg == 1) a.kd[o] = v;
-          else a.vd[o] = v;
-        } else if constexpr (EPI == RE_RESID) {
-          a.out[(int64_t)m * a.ldo + n] = resv[h] + v;
-        } else {
-          a.out[(int64_t)m * a.ldo + n] = v;
-        }
+        for (int c = 0; c < RG_COLS; ++c) red[lane * 65 + mm * RG_COLS + c] = acc[mm][c];
       }
     }
-  }
-}
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int o = lane;                                   // output o = mm * 8 + c
+    const bool live = o / RG_COLS < mp;
+    float sum = 0.f;
+    if (live) {
+#pragma unroll 16
+      for (int j = 0; j < 64; ++j) sum += red[j * 65 + o];
+    }
+    wred[wave][o] = sum;
+    __syncthreads();
 
-template <typename S, int PRO, int EPI>
-static void rowgemm_mc(const RowGemmArgs& a, dim3 grid, hipStream_t s) {
-  switch (rowgemm_rows_per_pass(a.K)) {
-    case 8: rowgemm_kernel<S, PRO, EPI, 8><<<grid, 256, 0, s>>>(a); break;
-    case 4: rowgemm_kernel<S, PRO, EPI, 4><<<grid, 256, 0, s>>>(a); break;
-    case 2: rowgemm_kernel<S, PRO, EPI, 2><<<grid, 256, 0, s>>>(a); break;
-    default: rowgemm_kernel<S, PRO, EPI, 1><<<grid, 256, 0, s>>>(a); break;
+    // ---- epilogue: wave 0, lane o
+    if (wave == 0 && live) {
+      const float v = (wred[0][o] + wred[1][o]) + (wred[2][o] + wred[3][o]);
+      const int m = m0 + o / RG_COLS;
+      const int n = n0 + o % RG_COLS;
+      if constexpr (EPI == RE_QKV) {
+        const int seg = n / a.d, col = n % a.d;
+        const int64_t off = (int64_t)m * a.d + col;
+        if (seg == 0) a.q[off] = v * a.qscale;
+        else if (seg == 1) a.kd[off] = v;
+        else a.vd[off] = v;
+      } else if constexpr (EPI == RE_RESID) {
+        a.out[(int64_t)m * a.ldo + n] = resv + v;
+      } else {
+        a.out[(int64_t)m * a.ldo + n] = v;
+      }
+    }
   }
 }
 
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s) {
-  if (a.N % RG_WG_COLS != 0 || a.K % 64 != 0 || a.b.n_per % RG_COLS != 0 || a.K > RG_XS)
+  if (a.N % RG_COLS != 0 || a.K % 64 != 0 || a.b.n_per % RG_COLS != 0 || a.K > RG_XS)
     return hipErrorInvalidValue;
-  dim3 grid(a.N / RG_WG_COLS);
+  dim3 grid(a.N / RG_COLS);
   bool ok = false;
   trace_pre(K_ROWGEMM, s);
 #define DSPARK_RG(P, E)                                                        \
   if (pro == P && epi == E) {                                                  \
     ok = true;                                                                 \
-    if (dtype == 1) rowgemm_mc<bf16, P, E>(a, grid, s);                        \
-    else rowgemm_mc<float, P, E>(a, grid, s);                                  \
+    if (dtype == 1) rowgemm_kernel<bf16, P, E><<<grid, RG_THREADS, 0, s>>>(a); \
+    else rowgemm_kernel<float, P, E><<<grid, RG_THREADS, 0, s>>>(a);           \
   }
   DSPARK_RG(RP_RMSNORM, RE_QKV)
   DSPARK_RG(RP_NONE, RE_RESID)
