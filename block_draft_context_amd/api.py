@@ -3,6 +3,10 @@
 Every step of the forward runs in libdspark.so. torch supplies device memory
 and the current HIP stream; nothing here computes the method. Outputs and the
 workspace are allocated with torch when the caller does not pass them.
+
+Matrices are passed as the library takes them: row-major [out, in] (y = x W^T),
+W_c as [d, m*H] and the layer matrices as wq/wk/wv/wo [d, d], w_gate/w_up
+[ff, d], w_down [d, ff].
 """
 from __future__ import annotations
 

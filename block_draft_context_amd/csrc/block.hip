@@ -6,217 +6,238 @@
 //   D' = E + (SiLU(G) * U) . Wdown
 // With at most a few dozen rows these products stream their weights once and
 // are bound by memory latency, so each is one "row GEMM" launch with no
-// cross-workgroup communication and as many workgroups as the weights allow:
-// a workgroup owns 8 output columns (one 16-byte bf16 vector per weight row)
-// and the full K, and its 256 threads split K, each with its few weight
-// vectors requested before anything else. The row norm / SwiGLU that feeds a
-// product is applied while its input rows are staged in LDS (prologue); the
-// residual and the Q/K_d/V_d split are applied on the way out (epilogue).
-// Workgroup i runs on XCD i % 8, so column groups are dealt to the XCDs in
-// contiguous runs: the workgroups that share a 128-byte weight line then
-// share one L2.
+// cross-workgroup communication and as many workgroups as the weights allow.
+// Weights are [out, in] row-major, so an output column's weights are one
+// contiguous run over K: a workgroup owns COLS columns (COLS / 4 per wave),
+// and the 64 lanes of a wave read consecutive 16-byte chunks of a column's
+// run (1 KiB per load instruction), every load issued before anything else.
+// The input rows are staged in LDS once per workgroup with the SwiGLU or the
+// RMSNorm gain applied; the RMSNorm row scale, which factors out of the dot
+// products, the residual and the Q/K_d/V_d split are applied on the outputs.
 #include "common.h"
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dspark {
 
-constexpr int RG_COLS = 8;          // columns per workgroup
 constexpr int RG_THREADS = 256;
 constexpr int RG_WAVES = RG_THREADS / 64;
 constexpr int RG_MC = 8;            // block rows per pass
-constexpr int RG_XS = 16384;        // floats of staged rows (64 KiB)
-constexpr int RG_RB = 8;            // weight rows per thread held at once
-constexpr int RG_RED = 64 * 65;     // floats of one wave's reduction block
-constexpr int RG_LDS = RG_XS > RG_WAVES * RG_RED ? RG_XS : RG_WAVES * RG_RED;
+constexpr int RG_XS = 16256;        // floats of staged rows (with the static arrays <= 64 KiB)
+constexpr int RG_JB = 4;            // weight chunks per lane and column held at once
+constexpr int RG_XC = 2;            // float4 input columns per thread per staging round
 
 int rowgemm_rows_per_pass(int K) { return std::max(1, std::min(RG_MC, RG_XS / K)); }
+// rows staged per pass for M block rows (LDS is sized to them at launch)
+static int rowgemm_mc(int M, int K) { return std::max(1, std::min(std::min(RG_MC, M), RG_XS / K)); }
 
-template <typename S, int PRO, int EPI>
-__global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) float xs[RG_LDS];   // staged rows, then reductions
-  __shared__ float part_ss[RG_WAVES][RG_MC];
-  __shared__ float wred[RG_WAVES][RG_MC * RG_COLS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K, M = a.M;
-  const int G = gridDim.x;
-  const int cg = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int n0 = cg * RG_COLS;
-  const int mi = n0 / a.b.n_per, c0 = n0 % a.b.n_per;
-  const S* __restrict__ W = static_cast<const S*>(a.b.mat[mi]);
-  const int rpt = (K + RG_THREADS - 1) / RG_THREADS;          // weight rows per thread
-  const int mc = max(1, min(RG_MC, RG_XS / K));
-  constexpr int NV = sizeof(S) / 2;                            // 16-byte vectors per row
-
-  // weight rows k = tid + 256 r, RG_RB at a time; loads are unconditional
-  // (rows past K repeat row K-1 and are weighted by zero) so they issue back
-  // to back, and the first batch is requested before the rows are staged
-  u32x4 wv[RG_RB][NV];
-  auto load_batch = [&](int r0) __attribute__((always_inline)) {
+// Sum of v[] over the 64 lanes, scattered: V values are halved at each of the
+// butterfly distances 32, 16, ... (lanes whose distance bit is set keep the
+// upper half), then the last value is summed over the remaining distances.
+// Afterwards every lane holds the full sum of value index lane / (64 / V).
+template <int V>
+DSPARK_DEV float reduce_scatter64(float (&v)[V], int lane) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V power of two");
 #pragma unroll
-    for (int r = 0; r < RG_RB; ++r) {
-      const int k = min(tid + RG_THREADS * (r0 + r), K - 1);
-      const S* p = W + (int64_t)k * a.b.n_per + c0;
-      wv[r][0] = ld16(p);
-      if constexpr (NV == 2) wv[r][1] = ld16(p + 4);
+  for (int n = V, s = 32; n > 1; n >>= 1, s >>= 1) {
+    const bool up = (lane & s) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float keep = up ? v[i + n / 2] : v[i];
+      const float send = up ? v[i] : v[i + n / 2];
+      v[i] = keep + __shfl_xor(send, s);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int s = 32 / V; s >= 1; s >>= 1) r += __shfl_xor(r, s);
+  return r;
+}
+
+template <typename S, int PRO, int EPI, int COLS>
+__global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
+  // staged rows: element k of row mm at xs[mm*K + (k/4 % 2)*(K/2) + 4*(k/8) + k%4],
+  // so lane j's two 16-byte reads of chunk j (elements 8j .. 8j+7) are
+  // contiguous across lanes
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [mc][K], sized at launch
+  __shared__ float part_ss[RG_WAVES][RG_MC];
+  constexpr int CPW = COLS / RG_WAVES;                         // columns per wave
+  constexpr int V = CPW * RG_MC;                               // sums per lane
+  constexpr int NV = (int)sizeof(S) / 2;                       // 16-byte loads per chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, M = a.M, K4 = K / 4, nch = K / 8;
+  const int cpl = (nch + 63) / 64;                             // chunks per lane
+  const int mc = max(1, min(min(RG_MC, M), RG_XS / K));
+  const int nw = blockIdx.x * COLS + wave * CPW;               // the wave's first column
+  const S* wcol[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int n = nw + cc;
+    wcol[cc] = static_cast<const S*>(a.b.mat[n / a.b.n_per]) + (int64_t)(n % a.b.n_per) * K;
+  }
+
+  u32x4 wv[RG_JB][CPW][NV];
+  auto load_batch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < RG_JB; ++b) {
+      if (j0 + b < cpl) {
+        const int j = min(lane + 64 * (j0 + b), nch - 1);
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+          for (int v = 0; v < NV; ++v) wv[b][cc][v] = ld16(wcol[cc] + 8 * j + 4 * v);
+      }
     }
   };
-  load_batch(0);
-
   for (int m0 = 0; m0 < M; m0 += mc) {
     const int mp = min(mc, M - m0);                             // live rows of this pass
-    // residual of this thread's output (wave 0, lane o = m * 8 + c), early
+    // this lane's output after the reduction: value index lane / (64 / V)
+    const int vo = lane / (64 / V);
+    const int om_l = vo % RG_MC, on = nw + vo / RG_MC;
+    const bool live = om_l < mp && (lane % (64 / V)) == 0;
+    const int om = m0 + min(om_l, mp - 1);
     float resv = 0.f;
-    if constexpr (EPI == RE_RESID) {
-      if (wave == 0) {
-        const int m = m0 + min(lane / RG_COLS, mp - 1);
-        resv = a.res[(int64_t)m * a.ldo + n0 + lane % RG_COLS];
-      }
-    }
-    // ---- stage the pass's rows (prologue applied) as xs[mm][k]: thread t
-    // moves float4 t, t+256, ... of the [mp][K] block, all loads together
+    if constexpr (EPI == RE_RESID) resv = a.res[(int64_t)om * a.ldo + on];
+
+    // ---- stage the pass's rows: thread t moves float4 columns t, t+256, ...
     __syncthreads();
-    {
-      const int K4 = K / 4;
-      constexpr int NQ = 8;
-      float ssr[RG_MC];
+    float ssr[RG_MC];
 #pragma unroll
-      for (int mm = 0; mm < RG_MC; ++mm) ssr[mm] = 0.f;
-      const f32x4* gain4 = reinterpret_cast<const f32x4*>(a.g);
-      for (int q0 = 0; q0 < mp * K4; q0 += RG_THREADS * NQ) {
-        f32x4 v[NQ], u[NQ];
+    for (int mm = 0; mm < RG_MC; ++mm) ssr[mm] = 0.f;
+    for (int q0 = 0; q0 < K4; q0 += RG_THREADS * RG_XC) {
+      f32x4 v[RG_XC][RG_MC], u[RG_XC][RG_MC], gv[RG_XC];
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          const int q = min(q0 + tid + RG_THREADS * i, mp * K4 - 1);
-          const int mm = q / K4, c4 = q % K4;
-          const f32x4* x = reinterpret_cast<const f32x4*>(a.X + (int64_t)(m0 + mm) * a.ldx);
-          v[i] = x[c4];
-          if constexpr (PRO == RP_SWIGLU) u[i] = x[K4 + c4];
-          if constexpr (PRO == RP_RMSNORM) u[i] = gain4[c4];
-        }
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          const int q = q0 + tid + RG_THREADS * i;
-          if (q < mp * K4) {
-            const int mm = q / K4, c4 = q % K4;
-            f32x4 val = v[i];
-            if constexpr (PRO == RP_SWIGLU) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) val[e] = val[e] / (1.f + __expf(-val[e])) * u[i][e];
-            }
-            if constexpr (PRO == RP_RMSNORM) {
-              const float sq = val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
-#pragma unroll
-              for (int mq = 0; mq < RG_MC; ++mq) ssr[mq] += (mq == mm) ? sq : 0.f;
-              val *= u[i];   // gain now, row scale below
-            }
-            *reinterpret_cast<f32x4*>(xs + mm * K + 4 * c4) = val;
-          }
-        }
-      }
-      if constexpr (PRO == RP_RMSNORM) {
+      for (int i = 0; i < RG_XC; ++i) {
+        const int c4 = min(q0 + tid + RG_THREADS * i, K4 - 1);
+        if constexpr (PRO == RP_RMSNORM) gv[i] = reinterpret_cast<const f32x4*>(a.g)[c4];
 #pragma unroll
         for (int mm = 0; mm < RG_MC; ++mm) {
           if (mm < mp) {
-            const float t = wave_sum(ssr[mm]);
-            if (lane == 0) part_ss[wave][mm] = t;
+            const f32x4* x = reinterpret_cast<const f32x4*>(a.X + (int64_t)(m0 + mm) * a.ldx);
+            v[i][mm] = x[c4];
+            if constexpr (PRO == RP_SWIGLU) u[i][mm] = x[K4 + c4];
           }
         }
-        __syncthreads();
-        for (int q = tid; q < mp * K4; q += RG_THREADS) {
-          const int mm = q / K4, c4 = q % K4;
-          const float tot = (part_ss[0][mm] + part_ss[1][mm]) + (part_ss[2][mm] + part_ss[3][mm]);
-          const float sc = rsqrtf(tot / (float)K + a.eps);
-          *reinterpret_cast<f32x4*>(xs + mm * K + 4 * c4) *= sc;
+      }
+      // the first weights go out right behind the first input rows: loads
+      // complete in order, so the staging below waits only for its own
+      if (m0 == 0 && q0 == 0) load_batch(0);
+#pragma unroll
+      for (int i = 0; i < RG_XC; ++i) {
+        const int c4 = q0 + tid + RG_THREADS * i;
+        if (c4 < K4) {
+          float* dst = xs + (c4 & 1) * (K / 2) + 4 * (c4 >> 1);
+#pragma unroll
+          for (int mm = 0; mm < RG_MC; ++mm) {
+            if (mm < mp) {
+              f32x4 val = v[i][mm];
+              if constexpr (PRO == RP_SWIGLU) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = val[e] / (1.f + __expf(-val[e])) * u[i][mm][e];
+              }
+              if constexpr (PRO == RP_RMSNORM) {
+                ssr[mm] += val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
+                val *= gv[i];
+              }
+              *reinterpret_cast<f32x4*>(dst + mm * K) = val;
+            }
+          }
+        }
+      }
+    }
+    if constexpr (PRO == RP_RMSNORM) {
+#pragma unroll
+      for (int mm = 0; mm < RG_MC; ++mm) {
+        if (mm < mp) {
+          const float t = wave_sum(ssr[mm]);
+          if (lane == 0) part_ss[wave][mm] = t;
         }
       }
     }
     __syncthreads();
 
-    // ---- partial dot products over this thread's rows
-    float acc[RG_MC][RG_COLS];
+    // ---- dot products of this lane's chunks with every live row
+    float acc[V];
 #pragma unroll
-    for (int mm = 0; mm < RG_MC; ++mm)
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < cpl; j0 += RG_JB) {
+      if (j0 > 0 || m0 > 0) load_batch(j0);
 #pragma unroll
-      for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = 0.f;
-    for (int r0 = 0; r0 < rpt; r0 += RG_RB) {
-      if (r0 > 0 || m0 > 0) load_batch(r0);
+      for (int b = 0; b < RG_JB; ++b) {
+        if (j0 + b < cpl) {
+          const int j = lane + 64 * (j0 + b);
+          const bool in = j < nch;
+          const int jc = min(j, nch - 1);
+          float wf[CPW][8];
 #pragma unroll
-      for (int r = 0; r < RG_RB; ++r) {
-        const int k = tid + RG_THREADS * (r0 + r);
-        if (r0 + r < rpt) {
-          float wf[RG_COLS];
-          Vec16<S>::unpack(wv[r][0], wf);
-          if constexpr (NV == 2) Vec16<S>::unpack(wv[r][1], wf + 4);
-          const bool in = k < K;
+          for (int cc = 0; cc < CPW; ++cc) {
+            Vec16<S>::unpack(wv[b][cc][0], wf[cc]);
+            if constexpr (NV == 2) Vec16<S>::unpack(wv[b][cc][1], wf[cc] + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wf[cc][e] = in ? wf[cc][e] : 0.f;
+          }
 #pragma unroll
           for (int mm = 0; mm < RG_MC; ++mm) {
             if (mm < mp) {
-              const float xv = in ? xs[mm * K + k] : 0.f;
+              const f32x4 xl = *reinterpret_cast<const f32x4*>(xs + mm * K + 4 * jc);
+              const f32x4 xh = *reinterpret_cast<const f32x4*>(xs + mm * K + K / 2 + 4 * jc);
 #pragma unroll
-              for (int c = 0; c < RG_COLS; ++c) acc[mm][c] = fmaf(xv, wf[c], acc[mm][c]);
+              for (int cc = 0; cc < CPW; ++cc) {
+                float t = acc[cc * RG_MC + mm];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t = fmaf(xl[e], wf[cc][e], t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t = fmaf(xh[e], wf[cc][4 + e], t);
+                acc[cc * RG_MC + mm] = t;
+              }
             }
           }
         }
       }
     }
 
-    // ---- reduce: over the wave's 64 lanes through LDS (row stride 65 keeps
-    // both the writes and the column reads conflict-free), then over the 4 waves
-    __syncthreads();
-    float* red = xs + wave * RG_RED;
-#pragma unroll
-    for (int mm = 0; mm < RG_MC; ++mm) {
-      if (mm < mp) {
-#pragma unroll
-        for (int c = 0; c < RG_COLS; ++c) red[lane * 65 + mm * RG_COLS + c] = acc[mm][c];
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int o = lane;                                   // output o = mm * 8 + c
-    const bool live = o / RG_COLS < mp;
-    float sum = 0.f;
+    // ---- reduce over the wave's lanes; the wave owns whole columns, so no
+    // cross-wave step is needed
+    float v = reduce_scatter64<V>(acc, lane);
     if (live) {
-#pragma unroll 16
-      for (int j = 0; j < 64; ++j) sum += red[j * 65 + o];
-    }
-    wred[wave][o] = sum;
-    __syncthreads();
-
-    // ---- epilogue: wave 0, lane o
-    if (wave == 0 && live) {
-      const float v = (wred[0][o] + wred[1][o]) + (wred[2][o] + wred[3][o]);
-      const int m = m0 + o / RG_COLS;
-      const int n = n0 + o % RG_COLS;
+      if constexpr (PRO == RP_RMSNORM) {
+        const float tot = (part_ss[0][om_l] + part_ss[1][om_l]) + (part_ss[2][om_l] + part_ss[3][om_l]);
+        v *= rsqrtf(tot / (float)K + a.eps);
+      }
       if constexpr (EPI == RE_QKV) {
-        const int seg = n / a.d, col = n % a.d;
-        const int64_t off = (int64_t)m * a.d + col;
+        const int seg = on / a.d, col = on % a.d;
+        const int64_t off = (int64_t)om * a.d + col;
         if (seg == 0) a.q[off] = v * a.qscale;
         else if (seg == 1) a.kd[off] = v;
         else a.vd[off] = v;
       } else if constexpr (EPI == RE_RESID) {
-        a.out[(int64_t)m * a.ldo + n] = resv + v;
+        a.out[(int64_t)om * a.ldo + on] = resv + v;
       } else {
-        a.out[(int64_t)m * a.ldo + n] = v;
+        a.out[(int64_t)om * a.ldo + on] = v;
       }
     }
   }
 }
 
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s) {
-  if (a.N % RG_COLS != 0 || a.K % 64 != 0 || a.b.n_per % RG_COLS != 0 || a.K > RG_XS)
-    return hipErrorInvalidValue;
-  dim3 grid(a.N / RG_COLS);
+  if (a.N % 8 != 0 || a.K % 64 != 0 || a.b.n_per % 8 != 0 || a.K > RG_XS) return hipErrorInvalidValue;
+  const bool narrow = a.N / 8 < 256;
+  dim3 grid(a.N / (narrow ? 4 : 8));
+  const size_t lds = (size_t)rowgemm_mc(a.M, a.K) * a.K * sizeof(float);
   bool ok = false;
   trace_pre(K_ROWGEMM, s);
-#define DSPARK_RG(P, E)                                                        \
-  if (pro == P && epi == E) {                                                  \
-    ok = true;                                                                 \
-    if (dtype == 1) rowgemm_kernel<bf16, P, E><<<grid, RG_THREADS, 0, s>>>(a); \
-    else rowgemm_kernel<float, P, E><<<grid, RG_THREADS, 0, s>>>(a);           \
+#define DSPARK_RG(P, E)                                                                      \
+  if (pro == P && epi == E) {                                                                \
+    ok = true;                                                                               \
+    if (dtype == 1) {                                                                        \
+      if (narrow) rowgemm_kernel<bf16, P, E, 4><<<grid, RG_THREADS, lds, s>>>(a);              \
+      else rowgemm_kernel<bf16, P, E, 8><<<grid, RG_THREADS, lds, s>>>(a);                     \
+    } else {                                                                                 \
+      if (narrow) rowgemm_kernel<float, P, E, 4><<<grid, RG_THREADS, lds, s>>>(a);             \
+      else rowgemm_kernel<float, P, E, 8><<<grid, RG_THREADS, lds, s>>>(a);                    \
+    }                                                                                        \
   }
   DSPARK_RG(RP_RMSNORM, RE_QKV)
   DSPARK_RG(RP_NONE, RE_RESID)

@@ -41,7 +41,7 @@ static dspark_status fail(dspark_status st, const char* fmt, ...) {
 // tracing (per-kernel HIP events)
 // ---------------------------------------------------------------------------
 static const char* kNames[K_COUNT] = {
-    "prep_transpose", "gemm_ctx_fuse", "ctx_norm",    "rowstats",   "gemm_ctx_kv",
+    "prep_kv_weights", "gemm_ctx_fuse", "ctx_norm",    "rowstats",   "gemm_ctx_kv",
     "attn_plan",      "attn_split_k",  "attn_combine", "block_gemm", "block_rows"};
 
 const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
@@ -83,7 +83,7 @@ struct Plan {
   int hd = 0, M = 0, chunk = 0, total_chunks = 0, ctx_splits = 1, kv_layers = 0;
   size_t esz = 4;
   // workspace offsets (bytes)
-  size_t wct = 0, wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
+  size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
   size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, attn = 0, E = 0, GU = 0;
   size_t total = 0;
 };
@@ -106,6 +106,7 @@ static dspark_status check_dims(const dspark_dims* dm, int op) {
     return fail(DSPARK_EUNSUPPORTED, "d %d must be a multiple of 128 and <= 2048", dm->d);
   if (dm->H % 64 != 0) return fail(DSPARK_EUNSUPPORTED, "H %d must be a multiple of 64", dm->H);
   if (dm->ff % 128 != 0) return fail(DSPARK_EUNSUPPORTED, "ff %d must be a multiple of 128", dm->ff);
+  if (dm->ff > 16256) return fail(DSPARK_EUNSUPPORTED, "ff %d above the supported 16256", dm->ff);
   if (!(dm->eps >= 0.f) || !std::isfinite(dm->eps)) return fail(DSPARK_EINVAL, "eps must be finite and >= 0");
   if (op == DSPARK_OP_BLOCK_FORWARD && (dm->n_layers < 1 || dm->n_layers > 16))
     return fail(dm->n_layers < 1 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "n_layers %d not in [1, 16]",
@@ -148,7 +149,6 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   const bool need_ctx = op != DSPARK_OP_BLOCK_LAYER;
   const bool need_block = op != DSPARK_OP_CTX_FUSE;
   if (need_ctx) {
-    if (bf) p->wct = take((size_t)d * mH * 2);
     p->ppart = take((size_t)p->ctx_splits * T * d * 4);
   }
   if (need_block) {
@@ -230,13 +230,9 @@ static dspark_status run_ctx_fuse(const dspark_dims* dm, const Plan& p, const vo
   b.gain[0] = nullptr;
   b.n_per = d;
   b.nmat = 1;
-  void* wct = nullptr;
-  if (dm->dtype == DSPARK_BF16) {
-    wct = at<char>(ws, p.wct);
-    DSPARK_HIP(launch_prep_transpose_bf16(b, mH, wct, s));
-  }
+  // W_c [d, m*H] is already the K-contiguous B operand
   float* part = at<float>(ws, p.ppart);
-  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, wct, part, (int)p.T, d, mH, p.ctx_splits, s));
+  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, w_c, part, (int)p.T, d, mH, p.ctx_splits, s));
   DSPARK_HIP(launch_ctx_norm(dm->dtype, part, p.ctx_splits, (int)p.T, d, ctx_norm, dm->eps, h_ctx, rinv, s));
   return DSPARK_OK;
 }
@@ -257,7 +253,7 @@ static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void
   void* wkvt = nullptr;
   if (dm->dtype == DSPARK_BF16) {
     wkvt = at<char>(ws, p.wkvt);
-    DSPARK_HIP(launch_prep_transpose_bf16(b, d, wkvt, s));
+    DSPARK_HIP(launch_prep_kv_bf16(b, d, wkvt, s));
   }
   if (p.T == 0) return DSPARK_OK;
   KVDesc kv{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};

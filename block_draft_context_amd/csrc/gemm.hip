@@ -4,11 +4,12 @@
 //   Eq 3   K_c, V_c = RMSNorm(H_ctx; attn_norm_i) . W_{K,V}^i   for every layer i
 //
 // bf16 storage runs on the matrix cores (v_mfma_f32_32x32x16_bf16) with both
-// operands staged K-contiguous in LDS: the weights, stored [in, out], are
-// first transposed (and, for K/V, multiplied by the layer's attention-norm
-// gain, which commutes into the weight rows) into the workspace. The RMSNorm
-// row factor of the context rows is applied in the K/V epilogue:
-//   RMSNorm(h; g) W = diag(rinv) . h . (diag(g) W).
+// operands staged K-contiguous in LDS. Weights are stored [out, in], which is
+// already the K-contiguous B operand: W_c is used as given, and the K/V
+// weights of all layers are copied into one matrix with the layer's
+// attention-norm gain folded into their columns. The RMSNorm row factor of
+// the context rows is applied in the K/V epilogue:
+//   RMSNorm(h; g) W^T = diag(rinv) . h . (W diag(g))^T.
 // float32 storage uses a plain LDS-tiled FMA GEMM.
 #include "common.h"
 #include "kernels.h"
@@ -18,38 +19,38 @@
 
 namespace dspark {
 
-// ---------------------------------------------------------------------------
-// weight transpose (+ gain) : Bt[n][k] = bf16(g(k) * W(k, n))
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prep_transpose_kernel(BMats b, int K, bf16* __restrict__ Bt) {
-  __shared__ float tile[64][65];
-  const int k0 = blockIdx.x * 64;
-  const int n0 = blockIdx.y * 64;
-  const int mi = n0 / b.n_per;
-  const int c0 = n0 % b.n_per;
-  const bf16* __restrict__ W = static_cast<const bf16*>(b.mat[mi]);
+// The K/V projection's B operand: every layer's W_K and W_V ([d, d] rows of
+// [out, in] weights) stacked into one [2 * n_layers * d, d] bf16 matrix with
+// the layer's attn_norm gain folded into its columns: Bt[r][k] = W[r][k] * g[k].
+// One row per workgroup, 16-byte vectors.
+__global__ __launch_bounds__(128) void prep_kv_kernel(BMats b, int K, bf16* __restrict__ Bt) {
+  const int row = blockIdx.x;
+  const int mi = row / b.n_per, n = row % b.n_per;
+  const bf16* __restrict__ W = static_cast<const bf16*>(b.mat[mi]) + (int64_t)n * K;
   const float* __restrict__ g = b.gain[mi];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int r = ty + 4 * i;
-    float v = to_f32(W[(int64_t)(k0 + r) * b.n_per + c0 + tx]);
-    if (g) v *= g[k0 + r];
-    tile[r][tx] = v;
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int r = ty + 4 * i;   // n within the tile
-    Bt[(int64_t)(n0 + r) * K + k0 + tx] = from_f32<bf16>(tile[tx][r]);
+  bf16* __restrict__ out = Bt + (int64_t)row * K;
+  for (int c = threadIdx.x; c < K / 8; c += 128) {
+    float f[8];
+    Vec16<bf16>::unpack(ld16(W + 8 * c), f);
+    if (g) {
+      const f32x4 g0 = reinterpret_cast<const f32x4*>(g)[2 * c];
+      const f32x4 g1 = reinterpret_cast<const f32x4*>(g)[2 * c + 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] *= g0[e];
+        f[4 + e] *= g1[e];
+      }
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(f[e]);
+    *reinterpret_cast<bf16x8*>(out + 8 * c) = o;
   }
 }
 
-hipError_t launch_prep_transpose_bf16(const BMats& b, int K, void* Bt, hipStream_t s) {
-  const int N = b.n_per * b.nmat;
-  dim3 grid(K / 64, N / 64);
+hipError_t launch_prep_kv_bf16(const BMats& b, int K, void* Bt, hipStream_t s) {
   trace_pre(K_PREP_T, s);
-  prep_transpose_kernel<<<grid, 256, 0, s>>>(b, K, static_cast<bf16*>(Bt));
+  prep_kv_kernel<<<b.n_per * b.nmat, 128, 0, s>>>(b, K, static_cast<bf16*>(Bt));
   trace_post(K_PREP_T, s);
   return hipGetLastError();
 }
@@ -240,10 +241,10 @@ __global__ __launch_bounds__(256) void gemm_f32(ASegs a, BMats b, int M, int MR,
       const int e = tid + 256 * i;          // 64 rows x 16 k
       const int r = e >> 4, kk = e & 15;
       As[kk][r] = (m0 + r < M) ? Ap[(int64_t)(m0 + r) * a.ld + kin + kk] : 0.f;
-      const int br = e >> 6, bc = e & 63;   // 16 k x 64 n
-      float v = W[(int64_t)(k0 + br) * b.n_per + c0 + bc];
-      if (g) v *= g[k0 + br];
-      Bs[br][bc] = v;
+      const int bn = e >> 4, bk = e & 15;   // 64 n x 16 k of [out, in] weights
+      float v = W[(int64_t)(c0 + bn) * K + k0 + bk];
+      if (g) v *= g[k0 + bk];
+      Bs[bk][bn] = v;
     }
     __syncthreads();
 #pragma unroll

@@ -12,7 +12,7 @@ constexpr int kMaxMats = 32;     // weight matrices in one batched launch (2 per
 constexpr int kMaxGamma = 16;
 
 enum KernelKind : int {
-  K_PREP_T = 0,       // weight transpose (+ gain fold) into the workspace
+  K_PREP_T = 0,       // K/V weights stacked with the attn_norm gain folded in
   K_GEMM_CTX,         // Eq 2 projection X . W_c (split-K partials)
   K_CTX_NORM,         // Eq 2 RMSNorm epilogue pass (+ row inverse RMS)
   K_ROWSTATS,         // row inverse RMS of a given H_ctx
@@ -58,8 +58,8 @@ struct KVDesc {
 };
 
 // ---- context side -------------------------------------------------------
-// bf16: Bt = [sum(n) rows][K] transposed (and gain-folded) copy of B.
-hipError_t launch_prep_transpose_bf16(const BMats& b, int K, void* Bt, hipStream_t s);
+// bf16: Bt = [n_per * nmat rows][K] copy of the [out, in] matrices with gains folded.
+hipError_t launch_prep_kv_bf16(const BMats& b, int K, void* Bt, hipStream_t s);
 
 // K splits of the Eq 2 projection for these sizes (sizes the partial buffer)
 int ctx_gemm_splits(int dtype, int64_t M, int N, int K);
@@ -115,7 +115,7 @@ struct RowGemmArgs {
   int M = 0, K = 0, N = 0;
   const float* g = nullptr;   // RP_RMSNORM gain [K]
   float eps = 0.f;
-  BMats b{};                  // weights: K rows, N columns over b.nmat matrices
+  BMats b{};                  // weights [out, in]: N rows of K over b.nmat matrices
   float* out = nullptr;       // RE_STORE / RE_RESID: out[m][n] (row stride ldo)
   int ldo = 0;
   const float* res = nullptr; // RE_RESID: out = res + X.W

@@ -21,8 +21,12 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - All matrices are row-major [in, out] and applied as x @ W (initFromDims
- *   of module-dflash.ts). Norm gains are float32 [d].
+ * - Every matrix is row-major [out, in] and applied as y = x W^T: the layout
+ *   checkpoints store and the page "src/dspark-runtime.js" multiplies with a
+ *   transposed B operand. (module-dflash.ts, initFromDims, keeps the same
+ *   parameters as [in, out] and computes x @ W; its W is this W^T.) An
+ *   output feature's weights are then one contiguous run over the input,
+ *   which is what the kernels stream. Norm gains are float32 [d].
  * - dims->dtype is the storage type of the long tensors: the taps, W_c, every
  *   layer matrix and H_ctx. DSPARK_BF16 means bfloat16 storage with float32
  *   accumulation; DSPARK_F32 means float32 everywhere.
@@ -48,8 +52,8 @@
  *   thread. A failed kernel launch returns DSPARK_EHIP (work enqueued before
  *   it in the same call may already run).
  * - Supported: head_dim = d / n_heads in {32, 64, 128}; 1 <= gamma <= 16;
- *   1 <= m <= 16; 1 <= n_layers <= 16; H, d and ff multiples of 64;
- *   A * gamma <= 1024.
+ *   1 <= m <= 16; 1 <= n_layers <= 16; H a multiple of 64; d a multiple of
+ *   128 up to 2048; ff a multiple of 128 up to 16256; A * gamma <= 1024.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -94,14 +98,14 @@ typedef struct {
  * pointers. Matrices in dims->dtype, gains float32. */
 typedef struct {
   const float* attn_norm;   /* [d]    shared by block and context rows */
-  const void* wq;           /* [d, d] */
+  const void* wq;           /* [d, d]   [out, in] */
   const void* wk;           /* [d, d] */
   const void* wv;           /* [d, d] */
   const void* wo;           /* [d, d] */
   const float* ff_norm;     /* [d] */
-  const void* w_gate;       /* [d, ff] */
-  const void* w_up;         /* [d, ff] */
-  const void* w_down;       /* [ff, d] */
+  const void* w_gate;       /* [ff, d] */
+  const void* w_up;         /* [ff, d] */
+  const void* w_down;       /* [d, ff] */
 } dspark_layer_weights;
 
 /* Bytes of workspace that `op` needs for these sizes (0 with a message in
@@ -109,10 +113,10 @@ typedef struct {
 size_t dspark_workspace_size(int32_t op, const dspark_dims* dims, int32_t A,
                              const int32_t* cu_host);
 
-/* Eq 2 (#buildContext): h_ctx[t, :] = RMSNorm(sum_j taps[j][t, :] @ W_c[j*H:(j+1)*H, :]; ctx_norm).
+/* Eq 2 (#buildContext): h_ctx[t, :] = RMSNorm(sum_j W_c[:, j*H:(j+1)*H] taps[j][t, :]; ctx_norm).
  *   taps     host array of m device pointers; row t of tap j starts at
  *            taps[j] + t * ld_tap elements (ld_tap >= H), T = cu_host[A] rows
- *   w_c      [m*H, d] dtype;  ctx_norm [d] float32
+ *   w_c      [d, m*H] dtype ([out, in]);  ctx_norm [d] float32
  *   h_ctx    out [T, d] dtype */
 dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A,
                               const int32_t* cu_host, const int32_t* cu_dev,

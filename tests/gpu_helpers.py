@@ -38,9 +38,11 @@ class Uploaded:
             for j, t in enumerate(x["taps"]):
                 taps[j].copy_(up(t, dt))
             self.taps = taps
-        self.w_c = up(x["w_c"], dt)
+        # the library takes every matrix [out, in] (y = x W^T); the oracle
+        # keeps the [in, out] form of module-dflash.ts (y = x @ W)
+        self.w_c = up(x["w_c"].T, dt)
         self.ctx_norm = up(x["ctx_norm"], f32)
-        self.layers = [{k: up(v, f32 if k.endswith("norm") else dt) for k, v in lw.items()}
+        self.layers = [{k: up(v, f32) if k.endswith("norm") else up(v.T, dt) for k, v in lw.items()}
                        for lw in x["layers"]]
         self.block_in = up(x["block_in"], f32)
         self.block_pos = up(x["block_pos"], f32)

@@ -84,6 +84,7 @@ def test_workspace_size_grows_with_context(L):
     (dict(dtype=7), 2, "dtype"),
     (dict(H=100), 2, "multiple of 64"),
     (dict(ff=100), 2, "multiple of 128"),
+    (dict(ff=16384), 2, "16256"),
     (dict(n_layers=0), 1, "n_layers"),
     (dict(eps=-1.0), 1, "eps"),
 ])
