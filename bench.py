@@ -41,7 +41,7 @@ def kernel_work(name, w, T, A):
 
     gemm_ctx_fuse  2*T*(m*H)*d flop          (Eq 2 projection)
     gemm_ctx_kv    2*T*d*(2*N*d) flop        (K and V of all N layers at once)
-    attn_partial   K_c + V_c of one layer (2*T*d*elt bytes) plus the queries
+    attn_split_k   K_c + V_c of one layer (2*T*d*elt bytes) plus the queries
                    read and partials written (4 * A*gamma*d * 4 bytes)
     """
     esz = 2 if w.dtype == "bf16" else 4
@@ -49,7 +49,7 @@ def kernel_work(name, w, T, A):
         return 2.0 * T * w.m * w.H * w.d, "flop", "mfma"
     if name == "gemm_ctx_kv":
         return 2.0 * T * w.d * 2 * w.n_layers * w.d, "flop", "mfma"
-    if name == "attn_partial":
+    if name == "attn_split_k":
         return 2.0 * T * w.d * esz + 4.0 * A * w.gamma * w.d * 4, "byte", "hbm"
     return None
 
@@ -66,7 +66,7 @@ KERNEL_SOURCES = {
     "gemm_ctx_fuse": ["block_draft_context_amd/csrc/gemm.hip", "block_draft_context_amd/csrc/common.h"],
     "gemm_ctx_kv": ["block_draft_context_amd/csrc/gemm.hip", "block_draft_context_amd/csrc/common.h",
                     "block_draft_context_amd/csrc/kv_layout.h"],
-    "attn_partial": ["block_draft_context_amd/csrc/attention.hip", "block_draft_context_amd/csrc/common.h",
+    "attn_split_k": ["block_draft_context_amd/csrc/attention.hip", "block_draft_context_amd/csrc/common.h",
                      "block_draft_context_amd/csrc/kv_layout.h"],
 }
 
@@ -83,6 +83,58 @@ def measured_traffic(kernel, workload):
     if not e or e.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return e.get("bytes_per_launch")
+
+
+# rocprofv3 kernel names -> kernel kinds of the roofline (substring match)
+PMC_KINDS = (("EpiKV", "gemm_ctx_kv"), ("EpiPartial", "gemm_ctx_fuse"),
+             ("attn_partial_kernel", "attn_split_k"))
+CALIBRATION_KERNEL = "AUnaryFunctor"   # torch.mul(src, 1.0, out=dst) of --copy-calibration
+
+
+def write_traffic(fetch_csv, write_csv, workload, copy_bytes):
+    """HBM bytes per launch of the roofline kernels from two rocprofv3 --pmc
+    runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+    scaled so that the plain copy of --copy-calibration bytes reads and writes
+    exactly copy_bytes; merged into profiles/hbm_traffic.json."""
+    import csv
+    import statistics
+
+    def per_kind(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                kind = CALIBRATION_KERNEL if CALIBRATION_KERNEL in name else next(
+                    (k for sub, k in PMC_KINDS if sub in name), None)
+                if kind:
+                    vals.setdefault(kind, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch = per_kind(fetch_csv, "FETCH_SIZE")
+    write = per_kind(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / fetch[CALIBRATION_KERNEL]
+    w_scale = copy_bytes / write[CALIBRATION_KERNEL]
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    rec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+    entry = rec.setdefault(workload, {})
+    for kind in sorted(set(fetch) & set(write) - {CALIBRATION_KERNEL}):
+        entry[kind] = {
+            "fetch_bytes": round(fetch[kind] * f_scale),
+            "write_bytes": round(write[kind] * w_scale),
+            "bytes_per_launch": round(fetch[kind] * f_scale + write[kind] * w_scale),
+            "source_hash": source_hash(KERNEL_SOURCES[kind]),
+        }
+    rec["calibration"] = {"copy_bytes": copy_bytes, "fetch_scale": round(f_scale, 4),
+                          "write_scale": round(w_scale, 4)}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec[workload], indent=1))
 
 
 def cpu_baseline(w, x, seconds):
@@ -121,7 +173,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain elementwise copy of BYTES bytes (3 launches), the "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no run: turn the counter_collection.csv files of two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE) of this script into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.workload,
+                      args.copy_calibration or 268435456)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs on a single MI355X "
               "(no sharding or collectives); use --gpus 1", file=sys.stderr)
@@ -206,6 +265,12 @@ def main():
         "draft_blocks_per_s": round(A / (ms_per_step / 1e3), 2),
         "roofline": roofline,
     }
+    # the context / block split of the step, from the event-traced pass
+    ctx_kinds = ("gemm_ctx_fuse", "ctx_norm", "rowstats", "prep_kv_weights", "gemm_ctx_kv")
+    t_ctx = sum(v[0] for k, v in per_kind.items() if k in ctx_kinds) / 1e3
+    t_blk = sum(v[0] for k, v in per_kind.items() if k not in ctx_kinds) / 1e3
+    res["context_side_tokens_per_s"] = round(T / t_ctx, 1) if t_ctx > 0 else None
+    res["block_side_blocks_per_s"] = round(A / t_blk, 2) if t_blk > 0 else None
     if args.kernels:
         res["kernels_us_per_step"] = {k: round(v[0] * 1e3, 2) for k, v in
                                       sorted(per_kind.items(), key=lambda kv: -kv[1][0])}
