@@ -11,9 +11,10 @@
 //   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  o = sum_c o_c 2^(m_c - M) / l.
 // Scores are kept in base 2: Q arrives pre-multiplied by hd^-1/2 * log2(e).
 //
-// Work split inside a chunk: each wave takes 64-key blocks. For Q.K^T lane t
-// owns key t and reads its whole key row (hd/E 16-byte vectors, one 1 KiB
-// wave-wide run each, see kv_layout.h). For P.V lane (kg, cp) owns two value
+// Work split inside a chunk: each wave takes every fourth 64-key block, with
+// the next block's loads in flight while the current one is computed. For
+// Q.K^T lane t owns key t and reads its whole key row (hd/E 16-byte vectors,
+// one 1 KiB wave-wide run each, see kv_layout.h). For P.V lane (kg, cp) owns two value
 // columns and R keys per load, so each V load is again one 1 KiB run; the
 // block's probabilities are broadcast through LDS. All arithmetic is float32
 // on the vector ALUs: with gamma <= 16 queries the arithmetic intensity is a
@@ -144,20 +145,41 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   const int kg = lane / (HD / 2), cp = lane % (HD / 2);
 
-  if (k1 > k0) {
-    const int64_t blk0 = k0 >> 6, blk1 = (k1 - 1) >> 6;
-    for (int64_t blk = blk0 + wave; blk <= blk1; blk += 4) {
+  // The wave's 64-key blocks are blk0 + wave, +4, ... <= blk1. A block's K
+  // (NKV vectors) and V (NLD vectors) live in registers; the next block's K
+  // is requested as soon as the scores are done and its V as soon as P.V is
+  // done, so each load's latency hides behind the other half's arithmetic.
+  // On the wave's last block the "next" loads repeat that block (in bounds,
+  // unused), which keeps every wait count static.
+  const int64_t blk0 = k0 >> 6, blk1 = k1 > k0 ? (k1 - 1) >> 6 : blk0 - 1;
+  const int64_t first = blk0 + wave;
+  if (first <= blk1) {
+    const int64_t last = first + ((blk1 - first) / 4) * 4;
+    u32x4 kreg[NKV], vreg[NLD];
+    auto load_k = [&](int64_t blk) __attribute__((always_inline)) {
+      const S* kp = Kh + blk * 64 * HD + lane * E;
+#pragma unroll
+      for (int i = 0; i < NKV; ++i) kreg[i] = ld16(kp + i * 64 * E);
+    };
+    auto load_v = [&](int64_t blk) __attribute__((always_inline)) {
+      const S* vp = Vh + blk * 64 * HD + lane * E;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) vreg[i] = ld16(vp + i * 64 * E);
+    };
+    load_k(first);
+    load_v(first);
+    for (int64_t blk = first; blk <= last; blk += 4) {
+      const int64_t nxt = min(blk + 4, last);
       // ---- scores: lane owns key blk*64 + lane
       const int64_t key = blk * 64 + lane;
       const bool valid = key >= k0 && key < k1;
-      const S* kp = Kh + blk * 64 * HD + lane * E;
       float s[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) s[j] = 0.f;
-#pragma unroll 4
+#pragma unroll
       for (int i = 0; i < NKV; ++i) {
         float kf[E];
-        Vec16<S>::unpack(ld16(kp + i * 64 * E), kf);
+        Vec16<S>::unpack(kreg[i], kf);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
 #pragma unroll
@@ -170,6 +192,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
           }
         }
       }
+      load_k(nxt);
       // ---- online softmax over this block (wave-uniform max; every block
       // holds at least one valid key)
 #pragma unroll
@@ -189,11 +212,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per vector
-      const S* vp = Vh + blk * 64 * HD + lane * E;
-#pragma unroll 4
+#pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         float vf[E];
-        Vec16<S>::unpack(ld16(vp + ld * 64 * E), vf);
+        Vec16<S>::unpack(vreg[ld], vf);
         const int kb = ld * KG * R + kg * R;   // first key of this vector
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -212,6 +234,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
           }
         }
       }
+      load_v(nxt);
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
