@@ -401,7 +401,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   const int kbeg = z * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
   const int nsteps = kend > kbeg ? (kend - kbeg) / BG_K : 0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, hi = lane >> 5;
 
@@ -414,31 +415,36 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
     if (lane == i && i < a.nseg) my_seg = reinterpret_cast<uint64_t>(a.seg[i]);
   const uint32_t seg_lo = (uint32_t)my_seg, seg_hi = (uint32_t)(my_seg >> 32);
 
-  // ---- direct global -> LDS loads of one stage (4 A + 4 B per thread)
+  // ---- direct global -> LDS loads of one stage (4 A + 4 B per thread).
+  // Each lane's byte offsets from the stage's scalar base addresses are
+  // fixed for the whole tile, so a load is one instruction on a scalar base
+  // and a 32-bit lane offset (the host guarantees the offsets fit), and the
+  // LDS destinations are scalar values.
+  const int rl = lane >> 2, slot = lane & 3;
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = i * 64 + wave * 16 + rl;
+    const int ch = slot ^ swz64_f(row);
+    aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(a.ld * 2) + (uint32_t)(ch * 16);
+    boff[i] = (uint32_t)(n0 + row) * (uint32_t)(K * 2) + (uint32_t)(ch * 16);
+  }
   auto issue = [&](int step) __attribute__((always_inline)) {
     const int k0 = kbeg + step * BG_K;
     const int sgi = k0 / a.seg_k;
     const int kin = k0 - sgi * a.seg_k;
     const uint64_t ap = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)seg_hi, sgi) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane((int)seg_lo, sgi);
-    const bf16* __restrict__ Ap = reinterpret_cast<const bf16*>(ap);
-    char* base = smem + (step % BG_NST) * BG_STAGE;
-    const int rl = lane >> 2, slot = lane & 3;
+    const char* __restrict__ abase = reinterpret_cast<const char*>(ap) + (int64_t)kin * 2;
+    const char* __restrict__ bbase = reinterpret_cast<const char*>(Bt) + (int64_t)k0 * 2;
+    char* base = smem + (step % BG_NST) * BG_STAGE + wave * 16 * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = i * 64 + wave * 16 + rl;
-      const int ch = slot ^ swz64_f(row);
-      const bf16* g = Ap + (int64_t)min(m0 + row, M - 1) * a.ld + kin + ch * 8;
-      __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(base + (i * 64 + wave * 16) * 64), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(abase + aoff[i], (lds_ptr_t)(base + i * 64 * 64), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = i * 64 + wave * 16 + rl;
-      const int ch = slot ^ swz64_f(row);
-      const bf16* g = Bt + (int64_t)(n0 + row) * K + k0 + ch * 8;
-      __builtin_amdgcn_global_load_lds(
-          g, (lds_ptr_t)(base + BG_M * BG_K * 2 + (i * 64 + wave * 16) * 64), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(bbase + boff[i], (lds_ptr_t)(base + BG_M * BG_K * 2 + i * 64 * 64),
+                                       16, 0, 0);
   };
   auto read_ops = [&](int step, int ks, bf16x8 (&av)[4], bf16x8 (&bv)[4]) __attribute__((always_inline)) {
     const char* As = smem + (step % BG_NST) * BG_STAGE;
@@ -467,10 +473,6 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
-  // Ring of BG_NST stages. All four are loaded up front; the barrier in the
-  // middle of step s (everyone has read stage s, stage s+1 has landed) frees
-  // stage s for the load of step s+4. Loads past the last step repeat the
-  // last one (in bounds, never read), which keeps every wait count fixed.
   // row scales of the K/V epilogue (one row per lane per 32-row block),
   // loaded ahead of the stage loads so the in-order wait counts still hold
   float rsc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -483,18 +485,23 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
     }
   }
 
+  // Ring of BG_NST stages (8 direct loads per thread each). All stages are
+  // loaded up front; the barrier in the middle of step s (everyone has read
+  // stage s, stage s+1 has landed) frees stage s for the load of step
+  // s+BG_NST. Loads past the last step repeat the last one (in bounds, never
+  // read), which keeps every wait count fixed.
   bf16x8 av0[4], bv0[4], av1[4], bv1[4];
   if (nsteps > 0) {
 #pragma unroll
     for (int st = 0; st < BG_NST; ++st) issue(min(st, nsteps - 1));
-    wait_vmcnt<24>();
+    wait_vmcnt<8 * (BG_NST - 1)>();
     stage_barrier();
     read_ops(0, 0, av0, bv0);
     for (int step = 0; step < nsteps - 1; ++step) {
       read_ops(step, 1, av1, bv1);
       mfma16(av0, bv0);
       DSPARK_BIG_SCHED_A();
-      wait_vmcnt<16>();
+      wait_vmcnt<8 * (BG_NST - 2)>();
       wait_lgkm0();
       stage_barrier();
       read_ops(step + 1, 0, av0, bv0);
