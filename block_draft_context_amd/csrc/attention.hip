@@ -27,9 +27,13 @@ namespace dspark {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// keys per chunk: aim for ~512 (chunk, head) workgroups, chunk in [256, 16384]
+// Keys per chunk. Short contexts (at most ~1024 64-key blocks over all
+// heads) use one block per tile and the head-split kernel, whose four waves
+// share each block; longer ones use chunks of >= 256 keys streamed by the
+// four waves of a workgroup, aiming for ~512 (chunk, head) workgroups.
 int attention_chunk(int64_t T, int n_heads, int A) {
-  (void)A;
+  const int64_t blocks = (T + 63) / 64 + A;   // bound on sum_b ceil(L_b / 64)
+  if (blocks * n_heads <= 1024) return 64;
   int64_t c = (T * n_heads + 511) / 512;
   c = ((c + 63) / 64) * 64;
   if (c < 256) c = 256;
@@ -288,6 +292,186 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Head-split partials for short contexts: grid (total_tiles, n_heads), one
+// 64-key chunk per tile (at most two physical 64-key blocks, since a
+// sequence's keys need not start on a block boundary), 4 waves. For Q.K^T
+// wave w takes a quarter of the head dimension for all 64 keys (lane = key)
+// and the four partial scores are summed through LDS; every wave then runs
+// the same softmax, and for P.V wave w takes a quarter of the block's keys
+// for all columns. Each wave thus does a quarter of the arithmetic of a
+// block, which is what bounds these launches when there are few blocks.
+// ---------------------------------------------------------------------------
+template <typename S, int HD, int G>
+__global__ __launch_bounds__(256) void attn_hsplit_kernel(
+    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int chunk,
+    int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using L = KVLayout<S>;
+  constexpr int E = L::E, R = L::R;
+  constexpr int NKV = HD / E;            // K vectors per key row
+  constexpr int KG = 128 / HD;           // key groups in the P.V lane split
+  constexpr int NLD = 64 / (KG * R);     // V loads per 64-key block
+  constexpr int NKW = NKV / 4;           // K vectors per lane and wave (a quarter of the row)
+  constexpr int NLW = NLD / 4;           // V loads per wave (a quarter of the keys)
+  static_assert(NKV % 4 == 0 && NLD % 4 == 0, "head split");
+
+  __shared__ __attribute__((aligned(16))) float qs[G][HD];
+  __shared__ float sp[4][G][64];         // partial scores, one slice of the head per wave
+  __shared__ __attribute__((aligned(16))) float ps[4][G][64];   // each wave's copy of p
+  __shared__ __attribute__((aligned(16))) float red_o[4][G][HD];
+
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dev_total = prefix[A];
+  if (tile >= total_tiles || tile >= dev_total) return;
+  int lo = 0, hi = A - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int c = tile - prefix[b];
+  const int64_t kseq0 = cu[b], kseq1 = cu[b + 1];
+  const int64_t k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
+  const int64_t k1 = min(kseq1, k0 + chunk);
+  const int64_t blk0 = k0 >> 6;
+  const int nblk = k1 > k0 ? (int)(((k1 - 1) >> 6) - blk0 + 1) : 0;   // 0, 1 or 2
+
+  // both blocks' slices are requested first (the second repeats the first
+  // when there is only one), then the queries are staged
+  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, h, n_heads, Tpad, HD);
+  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, h, n_heads, Tpad, HD);
+  u32x4 kreg[2][NKW], vreg[2][NLW];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int64_t blk = blk0 + min(bb, max(nblk - 1, 0));
+    const S* kp = Kh + blk * 64 * HD + (wave * NKW) * 64 * E + lane * E;
+    const S* vp = Vh + blk * 64 * HD + (wave * NLW) * 64 * E + lane * E;
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) kreg[bb][i] = ld16(kp + i * 64 * E);
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) vreg[bb][i] = ld16(vp + i * 64 * E);
+  }
+  const int d = HD * n_heads;
+  for (int i = tid; i < G * HD; i += 256) {
+    const int j = i / HD, cc = i % HD;
+    qs[j][cc] = Q[(int64_t)(b * G + j) * d + h * HD + cc];
+  }
+  __syncthreads();
+
+  float m_run[G], l_run[G];
+  float o[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+    o[j][0] = o[j][1] = 0.f;
+  }
+  const int kg = lane / (HD / 2), cp = lane % (HD / 2);
+
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    if (bb < nblk) {
+      // ---- partial scores over this wave's quarter of the head
+      float s[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) s[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NKW; ++i) {
+        float kf[E];
+        Vec16<S>::unpack(kreg[bb][i], kf);
+        const int c0 = (wave * NKW + i) * E;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+#pragma unroll
+          for (int e = 0; e < E; e += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qs[j][c0 + e]);
+            s[j] = fmaf(q4[0], kf[e], s[j]);
+            s[j] = fmaf(q4[1], kf[e + 1], s[j]);
+            s[j] = fmaf(q4[2], kf[e + 2], s[j]);
+            s[j] = fmaf(q4[3], kf[e + 3], s[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) sp[wave][j][lane] = s[j];
+      __syncthreads();
+      // ---- full scores and the online softmax (the same in every wave)
+      const int64_t key = (blk0 + bb) * 64 + lane;
+      const bool valid = key >= k0 && key < k1;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float sc = (sp[0][j][lane] + sp[1][j][lane]) + (sp[2][j][lane] + sp[3][j][lane]);
+        const float sv = valid ? sc : kNegInf;
+        const float bm = wave_max(sv);
+        const float mn = fmaxf(m_run[j], bm);
+        const float alpha = exp2f(m_run[j] - mn);   // 0 when m_run = -inf
+        const float p = exp2f(sv - mn);             // 0 for masked keys
+        l_run[j] = l_run[j] * alpha + p;
+        o[j][0] *= alpha;
+        o[j][1] *= alpha;
+        m_run[j] = mn;
+        ps[wave][j][lane] = p;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // ---- P.V over this wave's quarter of the keys, all columns
+#pragma unroll
+      for (int i = 0; i < NLW; ++i) {
+        float vf[E];
+        Vec16<S>::unpack(vreg[bb][i], vf);
+        const int kb = (wave * NLW + i) * KG * R + kg * R;   // first key of this vector
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float pr = ps[wave][j][kb + r];
+            o[j][0] = fmaf(pr, vf[2 * r], o[j][0]);
+            o[j][1] = fmaf(pr, vf[2 * r + 1], o[j][1]);
+          }
+        }
+      }
+      __syncthreads();   // sp is rewritten by the next block
+    }
+  }
+
+  // ---- o over key groups and waves (m and l are the same in every wave)
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float o0 = o[j][0], o1 = o[j][1];
+#pragma unroll
+    for (int off = HD / 2; off < 64; off <<= 1) {
+      o0 += __shfl_xor(o0, off, kWave);
+      o1 += __shfl_xor(o1, off, kWave);
+    }
+    if (kg == 0) {
+      red_o[wave][j][2 * cp] = o0;
+      red_o[wave][j][2 * cp + 1] = o1;
+    }
+  }
+  float lsum[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) lsum[j] = wave_sum(l_run[j]);
+  __syncthreads();
+  const int64_t pbase = ((int64_t)tile * n_heads + h) * G;
+  for (int i = tid; i < G * HD; i += 256) {
+    const int j = i / HD, cc = i % HD;
+    part_o[(pbase + j) * HD + cc] = (red_o[0][j][cc] + red_o[1][j][cc]) + (red_o[2][j][cc] + red_o[3][j][cc]);
+  }
+  if (wave == 0 && lane < G) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (lane == j) {
+        part_ml[(pbase + j) * 2 + 0] = m_run[j];
+        part_ml[(pbase + j) * 2 + 1] = lsum[j];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine: grid (A * n_heads, gamma), 256 threads. Query j of (sequence b,
 // head h): every tile partial of b plus the gamma block keys (K_d, V_d in
 // float32). Thread (tg, cc) sums tiles tg, tg + NG, ... for column cc.
@@ -376,6 +560,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 template <typename S, int HD, int G>
 static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
+  if (a.chunk == 64) {
+    attn_hsplit_kernel<S, HD, G><<<grid, 256, 0, s>>>(
+        a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
+        a.chunk, a.total_tiles, a.part_o, a.part_ml);
+    return;
+  }
   attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(
       a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
       a.chunk, a.total_tiles, a.part_o, a.part_ml);

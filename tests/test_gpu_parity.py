@@ -49,6 +49,11 @@ CASES = {
                            n_layers=2, ff=256, dtype="bf16", lengths=[0, 0]),
     "bf16-long-one": dict(name="b6", seed_id=17, A=1, m=4, H=256, d=512, n_heads=4, gamma=5,
                           n_layers=1, ff=1024, dtype="bf16", lengths=[9000]),
+    # enough 64-key blocks over the heads (> 1024) for the streaming
+    # split-K attention rather than the head-split one
+    "bf16-streaming-ragged": dict(name="b7", seed_id=18, A=3, m=2, H=128, d=256, n_heads=2,
+                                  gamma=6, n_layers=1, ff=512, dtype="bf16",
+                                  lengths=[30011, 0, 11111]),
 }
 
 
