@@ -202,6 +202,10 @@ static dspark_status check_taps(const dspark_dims* dm, const void* const* taps, 
   if (ld_tap < dm->H) return fail(DSPARK_EINVAL, "ld_tap %lld < H %d", (long long)ld_tap, dm->H);
   const int esz = dm->dtype == DSPARK_BF16 ? 2 : 4;
   if ((ld_tap * esz) % 16 != 0) return fail(DSPARK_EINVAL, "ld_tap * element size must be a multiple of 16 bytes");
+  // the projection kernels address a tap with 32-bit byte offsets
+  if (T * ld_tap * esz >= (int64_t)1 << 32)
+    return fail(DSPARK_EUNSUPPORTED, "a tap spans %lld bytes (T * ld_tap); at most 4 GiB is supported",
+                (long long)(T * ld_tap * esz));
   for (int j = 0; j < dm->m; ++j) {
     if (T > 0 && !taps[j]) return fail(DSPARK_EINVAL, "taps[%d] is NULL", j);
     if (!aligned16(taps[j])) return fail(DSPARK_EINVAL, "taps[%d] is not 16-byte aligned", j);

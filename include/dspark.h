@@ -53,7 +53,8 @@
  *   it in the same call may already run).
  * - Supported: head_dim = d / n_heads in {32, 64, 128}; 1 <= gamma <= 16;
  *   1 <= m <= 16; 1 <= n_layers <= 16; H a multiple of 64; d a multiple of
- *   128 up to 2048; ff a multiple of 128 up to 16256; A * gamma <= 1024.
+ *   128 up to 2048; ff a multiple of 128 up to 16256; A * gamma <= 1024;
+ *   each tap spans less than 4 GiB (T * ld_tap elements).
  */
 #ifndef DSPARK_H
 #define DSPARK_H

@@ -143,6 +143,18 @@ def test_entry_points_check_pointers_and_workspace(L):
     assert st == L.EUNSUPPORTED
 
 
+def test_taps_over_4gib_are_rejected(L):
+    """The projection kernels address a tap with 32-bit byte offsets."""
+    lib = L.lib()
+    dm = _dims(L)
+    T = 900000                                   # 900000 * 2560 * 2 bytes > 4 GiB
+    cu = _cu([0, T])
+    taps = (ctypes.c_void_p * 4)(*[0x1000] * 4)
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps, 2560, 0x3000, 0x4000, 0x5000,
+                             0x6000, 1 << 50, None)
+    assert st == L.EUNSUPPORTED and "4 GiB" in lib.dspark_last_error().decode()
+
+
 def test_python_binding_raises_with_message(L):
     import block_draft_context_amd as B
     with pytest.raises(B.DsparkError) as e:
