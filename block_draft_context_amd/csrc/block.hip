@@ -34,26 +34,62 @@ int rowgemm_rows_per_pass(int K) { return std::max(1, std::min(RG_MC, RG_XS / K)
 static int rowgemm_mc(int M, int K) { return std::max(1, std::min(std::min(RG_MC, M), RG_XS / K)); }
 
 // Sum of v[] over the 64 lanes, scattered: V values are halved at each of the
-// butterfly distances 32, 16, ... (lanes whose distance bit is set keep the
-// upper half), then the last value is summed over the remaining distances.
+// butterfly levels 32, 16, 8, ... (lanes whose level bit is set keep the
+// upper half), then the last value is summed over the remaining levels.
 // Afterwards every lane holds the full sum of value index lane / (64 / V).
+// Levels 32 and 16 use the permlane swaps (a lane receives its own and its
+// partner's value of a pair at once), levels 8 .. 1 the DPP row mirrors and
+// quad permutations; nothing goes through LDS.
+template <int S>
+DSPARK_DEV float partner(float x) {
+  if constexpr (S == 8) return dpp_f<kDppMirror>(x);
+  else if constexpr (S == 4) return dpp_f<kDppHalfMirror>(x);
+  else if constexpr (S == 2) return dpp_f<kDppXor2>(x);
+  else return dpp_f<kDppXor1>(x);
+}
+
+template <int S, int N>
+DSPARK_DEV void rs_level(float (&v)[64], int lane) {
+  if constexpr (N > 1) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      if constexpr (S >= 16) {
+        // lanes below the partner keep value i, the others value i + N/2:
+        // a swap of (v[i], v[i + N/2]) hands each lane both terms of its sum
+        const auto r = S == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                                   __float_as_uint(v[i + N / 2]), false, false)
+                               : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                                   __float_as_uint(v[i + N / 2]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      } else {
+        const bool up = (lane & S) != 0;
+        const float keep = up ? v[i + N / 2] : v[i];
+        const float send = up ? v[i] : v[i + N / 2];
+        v[i] = keep + partner<S>(send);
+      }
+    }
+    rs_level<S / 2, N / 2>(v, lane);
+  } else if constexpr (S >= 1) {
+    // one value left: sum it over the remaining levels
+    if constexpr (S >= 16) {
+      float a, b;
+      if constexpr (S == 32) swap32(v[0], a, b); else swap16(v[0], a, b);
+      v[0] = a + b;
+    } else {
+      v[0] += partner<S>(v[0]);
+    }
+    rs_level<S / 2, 1>(v, lane);
+  }
+}
+
 template <int V>
 DSPARK_DEV float reduce_scatter64(float (&v)[V], int lane) {
   static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V power of two");
+  float w[64];
 #pragma unroll
-  for (int n = V, s = 32; n > 1; n >>= 1, s >>= 1) {
-    const bool up = (lane & s) != 0;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float keep = up ? v[i + n / 2] : v[i];
-      const float send = up ? v[i] : v[i + n / 2];
-      v[i] = keep + __shfl_xor(send, s);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int s = 32 / V; s >= 1; s >>= 1) r += __shfl_xor(r, s);
-  return r;
+  for (int i = 0; i < V; ++i) w[i] = v[i];
+  rs_level<32, V>(w, lane);
+  return w[0];
 }
 
 template <typename S, int PRO, int EPI, int COLS>

@@ -48,16 +48,67 @@ template <> struct Vec16<float> {
 DSPARK_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 DSPARK_DEV void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Wave-wide reductions (64 lanes) through cross-lane shuffles.
-DSPARK_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Cross-lane moves on the vector ALUs only (no LDS): DPP within rows of 16
+// lanes, and gfx950's permlane swaps across rows. The DPP patterns pair lane
+// l with l^1 and l^2 (quad permutations) and with 7-l and 15-l inside each
+// group of 8 and 16 (the half-row and row mirrors); every pattern pairs a lane
+// with a partner whose bit 0, 1, 2 or 3 respectively is the opposite, which
+// is all a butterfly needs.
+constexpr int kDppXor1 = 0xB1;        // quad_perm 1,0,3,2
+constexpr int kDppXor2 = 0x4E;        // quad_perm 2,3,0,1
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+DSPARK_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// Sum (or max) over each row of 16 lanes; every lane of the row gets it.
+DSPARK_DEV float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
   return v;
 }
-DSPARK_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+DSPARK_DEV float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
   return v;
+}
+// The two halves of a permlane swap of (x, x): across rows 2k <-> 2k+1
+// (16-lane swap) or lanes l <-> l+32 (32-lane swap), each lane gets its own
+// value and its partner's, in some order.
+DSPARK_DEV void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+DSPARK_DEV void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Wave-wide reductions (64 lanes); every lane receives the result. The
+// whole wave must be active.
+DSPARK_DEV float wave_max(float v) {
+  float a, b;
+  v = row16_max(v);
+  swap16(v, a, b);
+  v = fmaxf(a, b);
+  swap32(v, a, b);
+  return fmaxf(a, b);
+}
+DSPARK_DEV float wave_sum(float v) {
+  float a, b;
+  v = row16_sum(v);
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
 }
 
 DSPARK_DEV int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
