@@ -2,8 +2,8 @@
 // rows, kept in float32 between kernels:
 //   Q, K_d, V_d = RMSNorm(D; attn_norm) . {Wq, Wk, Wv}
 //   E  = D + Attn . Wo
-//   GU = RMSNorm(E; ff_norm) . [Wgate | Wup]
-//   D' = E + (SiLU(G) * U) . Wdown
+//   H  = SiLU(Z . Wgate) * (Z . Wup),  Z = RMSNorm(E; ff_norm)
+//   D' = E + H . Wdown
 // With at most a few dozen rows these products stream their weights once and
 // are bound by memory latency, so each is one "row GEMM" launch with no
 // cross-workgroup communication and as many workgroups as the weights allow.
@@ -11,9 +11,10 @@
 // contiguous run over K: a workgroup owns COLS columns (COLS / 4 per wave),
 // and the 64 lanes of a wave read consecutive 16-byte chunks of a column's
 // run (1 KiB per load instruction), every load issued before anything else.
-// The input rows are staged in LDS once per workgroup with the SwiGLU or the
-// RMSNorm gain applied; the RMSNorm row scale, which factors out of the dot
-// products, the residual and the Q/K_d/V_d split are applied on the outputs.
+// The input rows are staged in LDS once per workgroup with the RMSNorm gain
+// applied; the RMSNorm row scale, which factors out of the dot products, the
+// residual, the Q/K_d/V_d split and the SwiGLU (a wave owns one gate column
+// and the matching up column) are applied on the outputs.
 #include "common.h"
 #include "kernels.h"
 
@@ -106,12 +107,19 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
   const int K = a.K, M = a.M, K4 = K / 4, nch = K / 8;
   const int cpl = (nch + 63) / 64;                             // chunks per lane
   const int mc = max(1, min(min(RG_MC, M), RG_XS / K));
-  const int nw = blockIdx.x * COLS + wave * CPW;               // the wave's first column
+  // the wave's columns: nw .. nw+CPW-1, or for RE_SWIGLU gate column nw and
+  // up column nw (one pair per wave)
+  const int nw = EPI == RE_SWIGLU ? blockIdx.x * RG_WAVES + wave : blockIdx.x * COLS + wave * CPW;
+  static_assert(EPI != RE_SWIGLU || CPW == 2, "SwiGLU pairs");
   const S* wcol[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; ++cc) {
-    const int n = nw + cc;
-    wcol[cc] = static_cast<const S*>(a.b.mat[n / a.b.n_per]) + (int64_t)(n % a.b.n_per) * K;
+    if constexpr (EPI == RE_SWIGLU) {
+      wcol[cc] = static_cast<const S*>(a.b.mat[cc]) + (int64_t)nw * K;
+    } else {
+      const int n = nw + cc;
+      wcol[cc] = static_cast<const S*>(a.b.mat[n / a.b.n_per]) + (int64_t)(n % a.b.n_per) * K;
+    }
   }
 
   u32x4 wv[RG_JB][CPW][NV];
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
     const int mp = min(mc, M - m0);                             // live rows of this pass
     // this lane's output after the reduction: value index lane / (64 / V)
     const int vo = lane / (64 / V);
-    const int om_l = vo % RG_MC, on = nw + vo / RG_MC;
+    const int om_l = vo % RG_MC, on = EPI == RE_SWIGLU ? nw : nw + vo / RG_MC;
     const bool live = om_l < mp && (lane % (64 / V)) == 0;
     const int om = m0 + min(om_l, mp - 1);
     float resv = 0.f;
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
 #pragma unroll
     for (int mm = 0; mm < RG_MC; ++mm) ssr[mm] = 0.f;
     for (int q0 = 0; q0 < K4; q0 += RG_THREADS * RG_XC) {
-      f32x4 v[RG_XC][RG_MC], u[RG_XC][RG_MC], gv[RG_XC];
+      f32x4 v[RG_XC][RG_MC], gv[RG_XC];
 #pragma unroll
       for (int i = 0; i < RG_XC; ++i) {
         const int c4 = min(q0 + tid + RG_THREADS * i, K4 - 1);
@@ -153,7 +161,6 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
           if (mm < mp) {
             const f32x4* x = reinterpret_cast<const f32x4*>(a.X + (int64_t)(m0 + mm) * a.ldx);
             v[i][mm] = x[c4];
-            if constexpr (PRO == RP_SWIGLU) u[i][mm] = x[K4 + c4];
           }
         }
       }
@@ -169,10 +176,6 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
           for (int mm = 0; mm < RG_MC; ++mm) {
             if (mm < mp) {
               f32x4 val = v[i][mm];
-              if constexpr (PRO == RP_SWIGLU) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = val[e] / (1.f + __expf(-val[e])) * u[i][mm][e];
-              }
               if constexpr (PRO == RP_RMSNORM) {
                 ssr[mm] += val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
                 val *= gv[i];
@@ -237,11 +240,19 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
     // ---- reduce over the wave's lanes; the wave owns whole columns, so no
     // cross-wave step is needed
     float v = reduce_scatter64<V>(acc, lane);
-    if (live) {
-      if constexpr (PRO == RP_RMSNORM) {
-        const float tot = (part_ss[0][om_l] + part_ss[1][om_l]) + (part_ss[2][om_l] + part_ss[3][om_l]);
-        v *= rsqrtf(tot / (float)K + a.eps);
-      }
+    if constexpr (PRO == RP_RMSNORM) {
+      const float tot = (part_ss[0][om_l] + part_ss[1][om_l]) + (part_ss[2][om_l] + part_ss[3][om_l]);
+      v *= rsqrtf(tot / (float)K + a.eps);
+    }
+    if constexpr (EPI == RE_SWIGLU) {
+      // lane l < 32 holds the gate sum of row l/4, lane l + 32 the up sum
+      // of the same row: one swap gives every lane both
+      float g, u;
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      g = __uint_as_float(r[0]);
+      u = __uint_as_float(r[1]);
+      if (live && lane < 32) a.out[(int64_t)om * a.ldo + on] = g / (1.f + expf(-g)) * u;
+    } else if (live) {
       if constexpr (EPI == RE_QKV) {
         const int seg = on / a.d, col = on % a.d;
         const int64_t off = (int64_t)om * a.d + col;
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
 
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s) {
   if (a.N % 8 != 0 || a.K % 64 != 0 || a.b.n_per % 8 != 0 || a.K > RG_XS) return hipErrorInvalidValue;
-  const bool narrow = a.N / 8 < 256;
+  const bool narrow = epi != RE_SWIGLU && a.N / 8 < 256;   // SwiGLU pairs need 2 columns per wave
   dim3 grid(a.N / (narrow ? 4 : 8));
   const size_t lds = (size_t)rowgemm_mc(a.M, a.K) * a.K * sizeof(float);
   bool ok = false;
@@ -268,17 +279,16 @@ hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hip
   if (pro == P && epi == E) {                                                                \
     ok = true;                                                                               \
     if (dtype == 1) {                                                                        \
-      if (narrow) rowgemm_kernel<bf16, P, E, 4><<<grid, RG_THREADS, lds, s>>>(a);              \
+      if (narrow) rowgemm_kernel<bf16, P, E, E == RE_SWIGLU ? 8 : 4><<<grid, RG_THREADS, lds, s>>>(a); \
       else rowgemm_kernel<bf16, P, E, 8><<<grid, RG_THREADS, lds, s>>>(a);                     \
     } else {                                                                                 \
-      if (narrow) rowgemm_kernel<float, P, E, 4><<<grid, RG_THREADS, lds, s>>>(a);             \
+      if (narrow) rowgemm_kernel<float, P, E, E == RE_SWIGLU ? 8 : 4><<<grid, RG_THREADS, lds, s>>>(a); \
       else rowgemm_kernel<float, P, E, 8><<<grid, RG_THREADS, lds, s>>>(a);                    \
     }                                                                                        \
   }
   DSPARK_RG(RP_RMSNORM, RE_QKV)
   DSPARK_RG(RP_NONE, RE_RESID)
-  DSPARK_RG(RP_RMSNORM, RE_STORE)
-  DSPARK_RG(RP_SWIGLU, RE_RESID)
+  DSPARK_RG(RP_RMSNORM, RE_SWIGLU)
 #undef DSPARK_RG
   trace_post(K_ROWGEMM, s);
   if (!ok) return hipErrorInvalidValue;

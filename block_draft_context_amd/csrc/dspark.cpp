@@ -305,19 +305,19 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   r.b.mat[0] = lw.wo; r.b.n_per = d; r.b.nmat = 1;
   r.res = D; r.out = E; r.ldo = d;
   DSPARK_HIP(launch_rowgemm(dt, RP_NONE, RE_RESID, r, s));
-  // [G | U] = RMSNorm(E; ff_norm) [Wgate | Wup]
+  // H = SiLU(Z Wgate^T) * (Z Wup^T), Z = RMSNorm(E; ff_norm)
   r = RowGemmArgs{};
   r.X = E; r.ldx = d; r.M = M; r.K = d; r.N = 2 * ff;
   r.g = lw.ff_norm; r.eps = dm->eps;
   r.b.mat[0] = lw.w_gate; r.b.mat[1] = lw.w_up; r.b.n_per = ff; r.b.nmat = 2;
-  r.out = GU; r.ldo = 2 * ff;
-  DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_STORE, r, s));
-  // D' = E + (SiLU(G) * U) Wdown
+  r.out = GU; r.ldo = ff;
+  DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_SWIGLU, r, s));
+  // D' = E + H Wdown^T
   r = RowGemmArgs{};
-  r.X = GU; r.ldx = 2 * ff; r.M = M; r.K = ff; r.N = d;
+  r.X = GU; r.ldx = ff; r.M = M; r.K = ff; r.N = d;
   r.b.mat[0] = lw.w_down; r.b.n_per = d; r.b.nmat = 1;
   r.res = E; r.out = D_next; r.ldo = d;
-  DSPARK_HIP(launch_rowgemm(dt, RP_SWIGLU, RE_RESID, r, s));
+  DSPARK_HIP(launch_rowgemm(dt, RP_NONE, RE_RESID, r, s));
   return DSPARK_OK;
 }
 

@@ -107,16 +107,18 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 // ---- block side -----------------------------------------------------------
 // Y = prologue(X) . W with a fused epilogue, full K per workgroup (32 columns).
-enum RowPro { RP_NONE = 0, RP_RMSNORM = 1, RP_SWIGLU = 2 };
-enum RowEpi { RE_STORE = 0, RE_QKV = 1, RE_RESID = 2 };
+enum RowPro { RP_NONE = 0, RP_RMSNORM = 1 };
+// RE_SWIGLU: the columns are (gate, up) pairs: b.mat[0] = W_gate and
+// b.mat[1] = W_up, both [n_per][K]; out[m][c] = SiLU(gate_c) * up_c, c < n_per.
+enum RowEpi { RE_STORE = 0, RE_QKV = 1, RE_RESID = 2, RE_SWIGLU = 3 };
 struct RowGemmArgs {
-  const float* X = nullptr;   // [M][ldx]; RP_SWIGLU: [M][2K] = [gate | up]
+  const float* X = nullptr;   // [M][ldx]
   int ldx = 0;
   int M = 0, K = 0, N = 0;
   const float* g = nullptr;   // RP_RMSNORM gain [K]
   float eps = 0.f;
   BMats b{};                  // weights [out, in]: N rows of K over b.nmat matrices
-  float* out = nullptr;       // RE_STORE / RE_RESID: out[m][n] (row stride ldo)
+  float* out = nullptr;       // RE_STORE / RE_RESID / RE_SWIGLU: out[m][n] (row stride ldo)
   int ldo = 0;
   const float* res = nullptr; // RE_RESID: out = res + X.W
   float* q = nullptr;         // RE_QKV: columns [0,d) -> q (scaled), [d,2d) -> kd, [2d,3d) -> vd
