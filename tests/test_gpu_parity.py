@@ -54,6 +54,11 @@ CASES = {
     "bf16-streaming-ragged": dict(name="b7", seed_id=18, A=3, m=2, H=128, d=256, n_heads=2,
                                   gamma=6, n_layers=1, ff=512, dtype="bf16",
                                   lengths=[30011, 0, 11111]),
+    # three layers at the full draft width over two sequences (several
+    # rounds of K/V projection tiles, a partly filled last one)
+    "bf16-3layer-d1024": dict(name="b8", seed_id=19, A=2, m=2, H=128, d=1024, n_heads=8,
+                               gamma=4, n_layers=3, ff=2048, dtype="bf16",
+                               lengths=[3000, 1096]),
 }
 
 
