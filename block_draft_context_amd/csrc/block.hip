@@ -135,6 +135,10 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
       }
     }
   };
+  // the first weights (the larger transfer) are requested before anything
+  // else, so they stream in while the input rows' latency passes
+  load_batch(0);
+
   for (int m0 = 0; m0 < M; m0 += mc) {
     const int mp = min(mc, M - m0);                             // live rows of this pass
     // this lane's output after the reduction: value index lane / (64 / V)
@@ -164,9 +168,6 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
           }
         }
       }
-      // the first weights go out right behind the first input rows: loads
-      // complete in order, so the staging below waits only for its own
-      if (m0 == 0 && q0 == 0) load_batch(0);
 #pragma unroll
       for (int i = 0; i < RG_XC; ++i) {
         const int c4 = q0 + tid + RG_THREADS * i;
