@@ -266,7 +266,7 @@ def main():
         "roofline": roofline,
     }
     # the context / block split of the step, from the event-traced pass
-    ctx_kinds = ("gemm_ctx_fuse", "ctx_norm", "rowstats", "prep_kv_weights", "gemm_ctx_kv")
+    ctx_kinds = ("gemm_ctx_fuse", "setup", "gemm_ctx_kv")
     t_ctx = sum(v[0] for k, v in per_kind.items() if k in ctx_kinds) / 1e3
     t_blk = sum(v[0] for k, v in per_kind.items() if k not in ctx_kinds) / 1e3
     res["context_side_tokens_per_s"] = round(T / t_ctx, 1) if t_ctx > 0 else None

@@ -50,45 +50,6 @@ int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
   return n;
 }
 
-// chunk_prefix[b] = sum_{b' < b} max(1, ceil(L_b' / chunk)), b = 0..A (one
-// workgroup; an empty sequence still gets one tile, which finds no keys and
-// leaves an empty partial).
-__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int A, int chunk,
-                                                   int32_t* __restrict__ prefix) {
-  __shared__ int32_t sums[256];
-  const int tid = threadIdx.x;
-  const int per = (A + 255) / 256;
-  const int b0 = tid * per, b1 = min(A, b0 + per);
-  int32_t local = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int32_t L = cu[b + 1] - cu[b];
-    local += L > 0 ? (L + chunk - 1) / chunk : 1;
-  }
-  sums[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {   // inclusive scan
-    const int32_t v = tid >= off ? sums[tid - off] : 0;
-    __syncthreads();
-    sums[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = tid > 0 ? sums[tid - 1] : 0;
-  for (int b = b0; b < b1; ++b) {
-    prefix[b] = run;
-    const int32_t L = cu[b + 1] - cu[b];
-    run += L > 0 ? (L + chunk - 1) / chunk : 1;
-  }
-  if (tid == 255) prefix[A] = sums[255];
-}
-
-hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
-                       hipStream_t s) {
-  trace_pre(K_PLAN, s);
-  plan_kernel<<<1, 256, 0, s>>>(cu_dev, A, chunk, chunk_prefix);
-  trace_post(K_PLAN, s);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // partials: grid (total_tiles, n_heads), 256 threads (4 waves)
 // part_o  [total_tiles][n_heads][G][HD]   unnormalised output

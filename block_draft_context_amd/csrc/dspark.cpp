@@ -41,8 +41,8 @@ static dspark_status fail(dspark_status st, const char* fmt, ...) {
 // tracing (per-kernel HIP events)
 // ---------------------------------------------------------------------------
 static const char* kNames[K_COUNT] = {
-    "prep_kv_weights", "gemm_ctx_fuse", "ctx_norm",    "rowstats",   "gemm_ctx_kv",
-    "attn_plan",      "attn_split_k",  "attn_combine", "block_gemm", "block_rows"};
+    "gemm_ctx_fuse", "setup",      "gemm_ctx_kv", "attn_split_k",
+    "attn_combine",  "block_gemm", "block_rows"};
 
 const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
 
@@ -219,9 +219,10 @@ static T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<cha
 // ---------------------------------------------------------------------------
 // launch sequences
 // ---------------------------------------------------------------------------
-static dspark_status run_ctx_fuse(const dspark_dims* dm, const Plan& p, const void* const* taps,
-                                  int64_t ld_tap, const void* w_c, const float* ctx_norm, void* h_ctx,
-                                  float* rinv, void* ws, hipStream_t s) {
+// Eq 2 projection: split-K fp32 partials of X . W_c^T into the workspace (the
+// RMSNorm row pass runs in the set-up launch).
+static dspark_status run_ctx_gemm(const dspark_dims* dm, const Plan& p, const void* const* taps,
+                                  int64_t ld_tap, const void* w_c, void* ws, hipStream_t s) {
   if (p.T == 0) return DSPARK_OK;
   const int d = dm->d, mH = dm->m * dm->H;
   ASegs a{};
@@ -235,16 +236,13 @@ static dspark_status run_ctx_fuse(const dspark_dims* dm, const Plan& p, const vo
   b.n_per = d;
   b.nmat = 1;
   // W_c [d, m*H] is already the K-contiguous B operand
-  float* part = at<float>(ws, p.ppart);
-  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, w_c, part, (int)p.T, d, mH, p.ctx_splits, s));
-  DSPARK_HIP(launch_ctx_norm(dm->dtype, part, p.ctx_splits, (int)p.T, d, ctx_norm, dm->eps, h_ctx, rinv, s));
+  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, w_c, at<float>(ws, p.ppart), (int)p.T, d, mH,
+                             p.ctx_splits, s));
   return DSPARK_OK;
 }
 
-// Context K/V of `nl` layers from H_ctx (rinv already computed).
-static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void* h_ctx, const float* rinv,
-                                const dspark_layer_weights* layers, int nl, void* ws, hipStream_t s) {
-  const int d = dm->d;
+// The K/V GEMM's B operand: W_K, W_V of `nl` layers with the attn_norm gains.
+static BMats kv_mats(const dspark_layer_weights* layers, int nl, int d) {
   BMats b{};
   for (int i = 0; i < nl; ++i) {
     b.mat[2 * i] = layers[i].wk;
@@ -254,15 +252,34 @@ static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void
   }
   b.n_per = d;
   b.nmat = 2 * nl;
-  void* wkvt = nullptr;
-  if (dm->dtype == DSPARK_BF16) {
-    wkvt = at<char>(ws, p.wkvt);
-    DSPARK_HIP(launch_prep_kv_bf16(b, d, wkvt, s));
-  }
+  return b;
+}
+
+// Context K/V of `nl` layers from H_ctx (rinv, and for bf16 the stacked
+// weights, already written by the set-up pass).
+static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void* h_ctx, const float* rinv,
+                                const dspark_layer_weights* layers, int nl, void* ws, hipStream_t s) {
   if (p.T == 0) return DSPARK_OK;
+  const int d = dm->d;
+  const BMats b = kv_mats(layers, nl, d);
+  void* wkvt = dm->dtype == DSPARK_BF16 ? at<char>(ws, p.wkvt) : nullptr;
   KVDesc kv{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
   DSPARK_HIP(launch_gemm_kv(dm->dtype, h_ctx, b, wkvt, rinv, kv, d, nl, s));
   return DSPARK_OK;
+}
+
+// Set-up roles shared by the block ops: tile plan and, for bf16, the stacked
+// K/V weights.
+static void setup_block_roles(const dspark_dims* dm, const Plan& p, int A, const int32_t* cu_dev,
+                              const dspark_layer_weights* layers, int nl, void* ws, SetupArgs* sa) {
+  sa->cu = cu_dev;
+  sa->A = A;
+  sa->chunk = p.chunk;
+  sa->prefix = at<int32_t>(ws, p.prefix);
+  if (dm->dtype == DSPARK_BF16 && p.T > 0) {
+    sa->b = kv_mats(layers, nl, dm->d);
+    sa->Bt = at<char>(ws, p.wkvt);
+  }
 }
 
 // One draft layer on the block rows D (float32 [M][d]); writes D_next.
@@ -353,8 +370,20 @@ dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A, const int32_t*
   NEED_PTR(ws);
   if (ws_bytes < p.total)
     return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
-  return run_ctx_fuse(dims, p, taps, ld_tap, w_c, ctx_norm, h_ctx, nullptr, ws,
-                      static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.T == 0) return DSPARK_OK;
+  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ws, s);
+  if (st != DSPARK_OK) return st;
+  SetupArgs sa{};
+  sa.d = dims->d;
+  sa.eps = dims->eps;
+  sa.T = p.T;
+  sa.part = at<float>(ws, p.ppart);
+  sa.splits = p.ctx_splits;
+  sa.g = ctx_norm;
+  sa.h = h_ctx;
+  DSPARK_HIP(launch_setup(dims->dtype, sa, s));
+  return DSPARK_OK;
 }
 
 dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
@@ -375,10 +404,18 @@ dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32
     return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* rinv = at<float>(ws, p.rinv);
-  if (p.T > 0) DSPARK_HIP(launch_rowstats(dims->dtype, h_ctx, (int)p.T, dims->d, dims->eps, rinv, s));
+  SetupArgs sa{};
+  sa.d = dims->d;
+  sa.eps = dims->eps;
+  setup_block_roles(dims, p, A, cu_dev, lw, 1, ws, &sa);
+  if (p.T > 0) {
+    sa.T = p.T;
+    sa.h_in = h_ctx;
+    sa.rinv = rinv;
+  }
+  DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, ws, s);
   if (st != DSPARK_OK) return st;
-  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
   return run_layer(dims, p, A, cu_dev, *lw, 0, d_in, d_out, ws, s);
 }
 
@@ -412,15 +449,30 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* h_ctx = h_ctx_out ? h_ctx_out : at<char>(ws, p.hctx);
   float* rinv = at<float>(ws, p.rinv);
-  st = run_ctx_fuse(dims, p, taps, ld_tap, w_c, ctx_norm, h_ctx, rinv, ws, s);
-  if (st != DSPARK_OK) return st;
-  st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, ws, s);
-  if (st != DSPARK_OK) return st;
-  DSPARK_HIP(launch_plan(cu_dev, A, p.chunk, at<int32_t>(ws, p.prefix), s));
   float* Da = at<float>(ws, p.D);
   float* Db = at<float>(ws, p.D2);
-  DSPARK_HIP(launch_block_rows(block_in, block_pos, A, dims->gamma, dims->d, nullptr, dims->eps, Da,
-                               nullptr, s));
+  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ws, s);
+  if (st != DSPARK_OK) return st;
+  // Eq 2's row norm, K/V weight prep, tile plan and D0 = block_in + block_pos
+  SetupArgs sa{};
+  sa.d = dims->d;
+  sa.eps = dims->eps;
+  setup_block_roles(dims, p, A, cu_dev, layers, dims->n_layers, ws, &sa);
+  sa.block_in = block_in;
+  sa.block_pos = block_pos;
+  sa.gamma = dims->gamma;
+  sa.D0 = Da;
+  if (p.T > 0) {
+    sa.T = p.T;
+    sa.part = at<float>(ws, p.ppart);
+    sa.splits = p.ctx_splits;
+    sa.g = ctx_norm;
+    sa.h = h_ctx;
+    sa.rinv = rinv;
+  }
+  DSPARK_HIP(launch_setup(dims->dtype, sa, s));
+  st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, ws, s);
+  if (st != DSPARK_OK) return st;
   const int N = dims->n_layers;
   for (int i = 0; i < N; ++i) {
     float* Dn = (i == N - 1 && !out_norm) ? block_out : Db;

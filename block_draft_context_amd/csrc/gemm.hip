@@ -1,14 +1,14 @@
 // Context-side dense contractions for gfx950:
 //   Eq 2   P = [H^{l1}; ...; H^{lm}] . W_c              (split-K fp32 partials)
-//          H_ctx = RMSNorm(P; ctx_norm)                  (row pass)
+//          H_ctx = RMSNorm(P; ctx_norm)                  (row pass, setup.hip)
 //   Eq 3   K_c, V_c = RMSNorm(H_ctx; attn_norm_i) . W_{K,V}^i   for every layer i
 //
 // bf16 storage runs on the matrix cores (v_mfma_f32_32x32x16_bf16) with both
 // operands staged K-contiguous in LDS. Weights are stored [out, in], which is
 // already the K-contiguous B operand: W_c is used as given, and the K/V
 // weights of all layers are copied into one matrix with the layer's
-// attention-norm gain folded into their columns. The RMSNorm row factor of
-// the context rows is applied in the K/V epilogue:
+// attention-norm gain folded into their columns (set-up pass, setup.hip).
+// The RMSNorm row factor of the context rows is applied in the K/V epilogue:
 //   RMSNorm(h; g) W^T = diag(rinv) . h . (W diag(g))^T.
 // float32 storage uses a plain LDS-tiled FMA GEMM.
 #include "common.h"
@@ -18,42 +18,6 @@
 #include <type_traits>
 
 namespace dspark {
-
-// The K/V projection's B operand: every layer's W_K and W_V ([d, d] rows of
-// [out, in] weights) stacked into one [2 * n_layers * d, d] bf16 matrix with
-// the layer's attn_norm gain folded into its columns: Bt[r][k] = W[r][k] * g[k].
-// One row per workgroup, 16-byte vectors.
-__global__ __launch_bounds__(128) void prep_kv_kernel(BMats b, int K, bf16* __restrict__ Bt) {
-  const int row = blockIdx.x;
-  const int mi = row / b.n_per, n = row % b.n_per;
-  const bf16* __restrict__ W = static_cast<const bf16*>(b.mat[mi]) + (int64_t)n * K;
-  const float* __restrict__ g = b.gain[mi];
-  bf16* __restrict__ out = Bt + (int64_t)row * K;
-  for (int c = threadIdx.x; c < K / 8; c += 128) {
-    float f[8];
-    Vec16<bf16>::unpack(ld16(W + 8 * c), f);
-    if (g) {
-      const f32x4 g0 = reinterpret_cast<const f32x4*>(g)[2 * c];
-      const f32x4 g1 = reinterpret_cast<const f32x4*>(g)[2 * c + 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] *= g0[e];
-        f[4 + e] *= g1[e];
-      }
-    }
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(f[e]);
-    *reinterpret_cast<bf16x8*>(out + 8 * c) = o;
-  }
-}
-
-hipError_t launch_prep_kv_bf16(const BMats& b, int K, void* Bt, hipStream_t s) {
-  trace_pre(K_PREP_T, s);
-  prep_kv_kernel<<<b.n_per * b.nmat, 128, 0, s>>>(b, K, static_cast<bf16*>(Bt));
-  trace_post(K_PREP_T, s);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // MFMA GEMM  C[M,N] = A[M,K] . Bt[N,K]^T  (bf16 in, fp32 accumulate)
@@ -680,109 +644,6 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
     gemm_f32<EpiKV<float>><<<grid, 256, 0, s>>>(a, b, M, Mrows, N, d, d, epi);
   }
   trace_post(K_GEMM_KV, s);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Row passes (one wave per row, d a multiple of 64)
-// ---------------------------------------------------------------------------
-// one wave per row; each lane owns d/128 float2 column pairs (d <= 2048), and
-// all of a split's loads are issued together
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-template <typename S>
-__global__ __launch_bounds__(256) void ctx_norm_kernel(const float* __restrict__ part, int splits,
-                                                       int T, int d, const float* __restrict__ g,
-                                                       float eps, S* __restrict__ h,
-                                                       float* __restrict__ rinv) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int nv = d / 128;   // float2 per lane, <= 16
-  f32x2 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = f32x2{0.f, 0.f};
-  for (int zz = 0; zz < splits; ++zz) {
-    const f32x2* row = reinterpret_cast<const f32x2*>(part + ((int64_t)zz * T + t) * d);
-    f32x2 x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = row[min(i, nv - 1) * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] += x[i];
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (i < nv) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1];
-  ss = wave_sum(ss);
-  const float sc = rsqrtf(ss / (float)d + eps);
-  const f32x2* g2 = reinterpret_cast<const f32x2*>(g);
-  f32x2 gv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) gv[i] = g2[min(i, nv - 1) * 64 + lane];
-  float ss2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < nv) {
-      const int c = (i * 64 + lane) * 2;
-      const S o0 = from_f32<S>(v[i][0] * sc * gv[i][0]);
-      const S o1 = from_f32<S>(v[i][1] * sc * gv[i][1]);
-      const float f0 = to_f32(o0), f1 = to_f32(o1);
-      ss2 += f0 * f0 + f1 * f1;
-      if constexpr (sizeof(S) == 2) {
-        *reinterpret_cast<uint32_t*>(h + t * d + c) =
-            (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
-      } else {
-        *reinterpret_cast<f32x2*>(h + t * d + c) = f32x2{f0, f1};
-      }
-    }
-  }
-  if (rinv) {
-    ss2 = wave_sum(ss2);
-    if (lane == 0) rinv[t] = rsqrtf(ss2 / (float)d + eps);
-  }
-}
-
-hipError_t launch_ctx_norm(int dtype, const float* part, int splits, int T, int d, const float* g,
-                           float eps, void* h, float* rinv, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  dim3 grid((T + 3) / 4);
-  trace_pre(K_CTX_NORM, s);
-  if (dtype == 1)
-    ctx_norm_kernel<bf16><<<grid, 256, 0, s>>>(part, splits, T, d, g, eps, static_cast<bf16*>(h), rinv);
-  else
-    ctx_norm_kernel<float><<<grid, 256, 0, s>>>(part, splits, T, d, g, eps, static_cast<float*>(h), rinv);
-  trace_post(K_CTX_NORM, s);
-  return hipGetLastError();
-}
-
-template <typename S>
-__global__ __launch_bounds__(256) void rowstats_kernel(const S* __restrict__ h, int T, int d,
-                                                       float eps, float* __restrict__ rinv) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int nv = d / 64;   // <= 32 values per lane, loaded together
-  float x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = to_f32(h[t * d + min(i, nv - 1) * 64 + lane]);
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (i < nv) ss += x[i] * x[i];
-  ss = wave_sum(ss);
-  if (lane == 0) rinv[t] = rsqrtf(ss / (float)d + eps);
-}
-
-hipError_t launch_rowstats(int dtype, const void* h, int T, int d, float eps, float* rinv,
-                           hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  dim3 grid((T + 3) / 4);
-  trace_pre(K_ROWSTATS, s);
-  if (dtype == 1)
-    rowstats_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16*>(h), T, d, eps, rinv);
-  else
-    rowstats_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(h), T, d, eps, rinv);
-  trace_post(K_ROWSTATS, s);
   return hipGetLastError();
 }
 

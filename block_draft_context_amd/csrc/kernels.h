@@ -12,12 +12,10 @@ constexpr int kMaxMats = 32;     // weight matrices in one batched launch (2 per
 constexpr int kMaxGamma = 16;
 
 enum KernelKind : int {
-  K_PREP_T = 0,       // K/V weights stacked with the attn_norm gain folded in
-  K_GEMM_CTX,         // Eq 2 projection X . W_c (split-K partials)
-  K_CTX_NORM,         // Eq 2 RMSNorm epilogue pass (+ row inverse RMS)
-  K_ROWSTATS,         // row inverse RMS of a given H_ctx
+  K_GEMM_CTX = 0,     // Eq 2 projection X . W_c (split-K partials)
+  K_SETUP,            // Eq 2 RMSNorm row pass (or row statistics) + K/V weight prep,
+                      // attention tile plan and D0, in one launch
   K_GEMM_KV,          // Eq 3 context K/V re-projection (all layers at once)
-  K_PLAN,             // tile prefix of the split-K attention
   K_ATTN,             // split-K attention partials over context chunks
   K_COMBINE,          // (m, l) combine of the partials + block keys
   K_ROWGEMM,          // block-row projections (weight streaming, fused norm/epilogue)
@@ -57,23 +55,47 @@ struct KVDesc {
   int32_t n_heads;
 };
 
-// ---- context side -------------------------------------------------------
-// bf16: Bt = [n_per * nmat rows][K] copy of the [out, in] matrices with gains folded.
-hipError_t launch_prep_kv_bf16(const BMats& b, int K, void* Bt, hipStream_t s);
+// ---- set-up pass ----------------------------------------------------------
+// One launch of independent roles, each skipped when its output is null:
+//   prefix  attention tile prefix from cu (see launch_attention)
+//   D0      [A*gamma][d] = block_in + block_pos[row % gamma]
+//   Bt      bf16 only: [n_per * nmat rows][d] copy of b's [out, in] matrices
+//           with b.gain folded into the columns
+//   h       part != null: h[t] = RMSNorm(sum_z part[z][t]; g), rinv[t] = inverse
+//           RMS of the stored row (rinv nullable); part == null and h_in != null:
+//           only rinv[t] of the given rows
+struct SetupArgs {
+  int d = 0;
+  float eps = 0.f;
+  // plan
+  const int32_t* cu = nullptr;
+  int A = 0, chunk = 0;
+  int32_t* prefix = nullptr;
+  // D0
+  const float* block_in = nullptr;
+  const float* block_pos = nullptr;
+  int gamma = 0;
+  float* D0 = nullptr;
+  // K/V weight prep
+  BMats b{};
+  void* Bt = nullptr;
+  // row pass over the T context rows
+  int64_t T = 0;
+  const float* part = nullptr;
+  int splits = 0;
+  const float* g = nullptr;
+  void* h = nullptr;
+  const void* h_in = nullptr;
+  float* rinv = nullptr;
+};
+hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s);
 
+// ---- context side -------------------------------------------------------
 // K splits of the Eq 2 projection for these sizes (sizes the partial buffer)
 int ctx_gemm_splits(int dtype, int64_t M, int N, int K);
 // out[z][r][n] = sum_{k in split z} A(r,k) B(k,n); float32 partials.
 hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt,
                            float* out, int M, int N, int K, int splits, hipStream_t s);
-
-// h[r] = RMSNorm(sum_z part[z][r]; g) in storage type; rinv[r] = inverse RMS of
-// the stored row (nullable).
-hipError_t launch_ctx_norm(int dtype, const float* part, int splits, int T, int d,
-                           const float* g, float eps, void* h, float* rinv, hipStream_t s);
-
-hipError_t launch_rowstats(int dtype, const void* h, int T, int d, float eps, float* rinv,
-                           hipStream_t s);
 
 // K/V for all layers of `b` (2 matrices per layer: K then V) from H_ctx with
 // the row scale rinv, written in the attention layout of `kv`.
@@ -83,11 +105,9 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
 
 // ---- attention ------------------------------------------------------------
 int attention_chunk(int64_t T, int n_heads, int A);   // keys per chunk (multiple of 64)
-// tiles = sum_b max(1, ceil(L_b / chunk))
+// tiles = sum_b max(1, ceil(L_b / chunk)); the device prefix of the same sum
+// comes from the set-up pass
 int64_t attention_tiles(const int32_t* cu_host, int A, int chunk);
-// device tile prefix (same formula)
-hipError_t launch_plan(const int32_t* cu_dev, int A, int chunk, int32_t* chunk_prefix,
-                       hipStream_t s);
 
 struct AttnArgs {
   const float* Q;       // [A*gamma][d], pre-scaled by hd^-1/2 * log2(e)

@@ -1,0 +1,229 @@
+// The forward's row passes and independent set-up work, in one launch.
+//
+// After the Eq 2 projection, four pieces of work need nothing but the call's
+// inputs and that projection, and none needs another:
+//   plan   the split-K attention's tile prefix over the ragged context lengths
+//   D0     block_in + block_pos (the block rows entering the first layer)
+//   prep   every layer's W_K, W_V stacked into the K/V GEMM's B operand, with
+//          the layer's attn_norm gain folded into the columns
+//   norm   H_ctx = RMSNorm(sum of the projection's K splits; ctx_norm) and the
+//          inverse RMS of each stored row, or, when H_ctx is given, only the
+//          inverse RMS ("DFlash draft layer", `#buildContext` and `#layer`)
+// Each is a range of workgroups of one grid (256 threads, one wave per row),
+// so a forward pays one kernel boundary for all of them.
+#include "common.h"
+#include "kernels.h"
+
+namespace dspark {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// chunk_prefix[b] = sum_{b' < b} max(1, ceil(L_b' / chunk)) for b = 0..A. An
+// empty sequence still gets one tile, which finds no keys and leaves an empty
+// partial. One workgroup.
+__device__ __forceinline__ void plan_role(const int32_t* __restrict__ cu, int A, int chunk,
+                                          int32_t* __restrict__ prefix, int32_t* sums) {
+  const int tid = threadIdx.x;
+  const int per = (A + 255) / 256;
+  const int b0 = tid * per, b1 = min(A, b0 + per);
+  int32_t local = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t L = cu[b + 1] - cu[b];
+    local += L > 0 ? (L + chunk - 1) / chunk : 1;
+  }
+  sums[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {   // inclusive scan
+    const int32_t v = tid >= off ? sums[tid - off] : 0;
+    __syncthreads();
+    sums[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid > 0 ? sums[tid - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    prefix[b] = run;
+    const int32_t L = cu[b + 1] - cu[b];
+    run += L > 0 ? (L + chunk - 1) / chunk : 1;
+  }
+  if (tid == 255) prefix[A] = sums[255];
+}
+
+// D0[r] = block_in[r] + block_pos[r % gamma]; one wave per row, d / 256
+// float4 per lane.
+__device__ __forceinline__ void d0_row(const SetupArgs& a, int r, int lane) {
+  const int j = r % a.gamma;
+  const f32x4* __restrict__ bin = reinterpret_cast<const f32x4*>(a.block_in + (int64_t)r * a.d);
+  const f32x4* __restrict__ pos = reinterpret_cast<const f32x4*>(a.block_pos + (int64_t)j * a.d);
+  f32x4* __restrict__ out = reinterpret_cast<f32x4*>(a.D0 + (int64_t)r * a.d);
+  for (int c = lane; c < a.d / 4; c += 64) out[c] = bin[c] + pos[c];
+}
+
+// Bt[row][k] = W[n][k] * g[k] (row = matrix mi, output feature n); one wave
+// per row, all of the row's 16-byte loads issued before any store (K <= 2048
+// gives at most four per lane).
+__device__ __forceinline__ void prep_row(const SetupArgs& a, int row, int lane) {
+  const int K = a.d;
+  const int mi = row / a.b.n_per, n = row % a.b.n_per;
+  const bf16* __restrict__ W = static_cast<const bf16*>(a.b.mat[mi]) + (int64_t)n * K;
+  const float* __restrict__ g = a.b.gain[mi];
+  bf16* __restrict__ out = static_cast<bf16*>(a.Bt) + (int64_t)row * K;
+  const int nc = K / 8;   // 16-byte chunks in the row
+  u32x4 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (lane + 64 * i < nc) w[i] = ld16(W + 8 * (lane + 64 * i));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nc) break;
+    float f[8];
+    Vec16<bf16>::unpack(w[i], f);
+    if (g) {
+      const f32x4 g0 = reinterpret_cast<const f32x4*>(g)[2 * c];
+      const f32x4 g1 = reinterpret_cast<const f32x4*>(g)[2 * c + 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] *= g0[e];
+        f[4 + e] *= g1[e];
+      }
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(f[e]);
+    *reinterpret_cast<bf16x8*>(out + 8 * c) = o;
+  }
+}
+
+// H_ctx row t = RMSNorm(sum_z part[z][t]; g) in the storage type, and the
+// inverse RMS of the row as stored. Each lane owns d / 128 float2 column
+// pairs (d <= 2048); all of a split's loads are issued together.
+template <typename S>
+__device__ __forceinline__ void norm_row(const SetupArgs& a, int64_t t, int lane) {
+  const int d = a.d, T = a.T;
+  const int nv = d / 128;
+  f32x2 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = f32x2{0.f, 0.f};
+  for (int zz = 0; zz < a.splits; ++zz) {
+    const f32x2* row = reinterpret_cast<const f32x2*>(a.part + ((int64_t)zz * T + t) * d);
+    f32x2 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = row[min(i, nv - 1) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] += x[i];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < nv) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1];
+  ss = wave_sum(ss);
+  const float sc = rsqrtf(ss / (float)d + a.eps);
+  const f32x2* g2 = reinterpret_cast<const f32x2*>(a.g);
+  f32x2 gv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gv[i] = g2[min(i, nv - 1) * 64 + lane];
+  S* __restrict__ h = static_cast<S*>(a.h);
+  float ss2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nv) {
+      const int c = (i * 64 + lane) * 2;
+      const S o0 = from_f32<S>(v[i][0] * sc * gv[i][0]);
+      const S o1 = from_f32<S>(v[i][1] * sc * gv[i][1]);
+      const float f0 = to_f32(o0), f1 = to_f32(o1);
+      ss2 += f0 * f0 + f1 * f1;
+      if constexpr (sizeof(S) == 2) {
+        *reinterpret_cast<uint32_t*>(h + t * d + c) =
+            (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+      } else {
+        *reinterpret_cast<f32x2*>(h + t * d + c) = f32x2{f0, f1};
+      }
+    }
+  }
+  if (a.rinv) {
+    ss2 = wave_sum(ss2);
+    if (lane == 0) a.rinv[t] = rsqrtf(ss2 / (float)d + a.eps);
+  }
+}
+
+// rinv[t] = inverse RMS of a given H_ctx row; d / 64 <= 32 values per lane,
+// loaded together.
+template <typename S>
+__device__ __forceinline__ void stats_row(const SetupArgs& a, int64_t t, int lane) {
+  const int d = a.d;
+  const S* __restrict__ h = static_cast<const S*>(a.h_in);
+  const int nv = d / 64;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = to_f32(h[t * d + min(i, nv - 1) * 64 + lane]);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < nv) ss += x[i] * x[i];
+  ss = wave_sum(ss);
+  if (lane == 0) a.rinv[t] = rsqrtf(ss / (float)d + a.eps);
+}
+
+// Workgroup ranges, in dispatch order: [plan][D0][prep][norm]. The small
+// roles come first so that none of them lands in the grid's tail.
+struct SetupGrid {
+  int plan, d0, prep, norm;
+  int total() const { return plan + d0 + prep + norm; }
+};
+
+static SetupGrid setup_grid(const SetupArgs& a) {
+  SetupGrid g;
+  g.plan = a.prefix ? 1 : 0;
+  g.d0 = a.D0 ? (a.A * a.gamma + 3) / 4 : 0;
+  g.prep = a.Bt ? (a.b.n_per * a.b.nmat + 3) / 4 : 0;
+  g.norm = (a.part || a.h_in) ? (int)((a.T + 3) / 4) : 0;
+  return g;
+}
+
+template <typename S>
+__global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
+  __shared__ int32_t sums[256];
+  int blk = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  if (blk < sg.plan) {
+    plan_role(a.cu, a.A, a.chunk, a.prefix, sums);
+    return;
+  }
+  blk -= sg.plan;
+  if (blk < sg.d0) {
+    const int r = blk * 4 + w;
+    if (r < a.A * a.gamma) d0_row(a, r, lane);
+    return;
+  }
+  blk -= sg.d0;
+  if (blk < sg.prep) {
+    if constexpr (sizeof(S) == 2) {
+      const int row = blk * 4 + w;
+      if (row < a.b.n_per * a.b.nmat) prep_row(a, row, lane);
+    }
+    return;
+  }
+  blk -= sg.prep;
+  const int64_t t = (int64_t)blk * 4 + w;
+  if (t >= a.T) return;
+  if (a.part)
+    norm_row<S>(a, t, lane);
+  else
+    stats_row<S>(a, t, lane);
+}
+
+hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s) {
+  if (a.Bt && dtype != 1) return hipErrorInvalidValue;   // prep serves the bf16 MFMA path only
+  const SetupGrid sg = setup_grid(a);
+  if (sg.total() == 0) return hipSuccess;
+  trace_pre(K_SETUP, s);
+  if (dtype == 1)
+    setup_kernel<bf16><<<sg.total(), 256, 0, s>>>(a, sg);
+  else
+    setup_kernel<float><<<sg.total(), 256, 0, s>>>(a, sg);
+  trace_post(K_SETUP, s);
+  return hipGetLastError();
+}
+
+}  // namespace dspark
