@@ -343,7 +343,9 @@ DSPARK_DEV void transpose4_quad(uint32_t (&a)[4], int k) {
 template <class Epi, int HD>
 __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
                                                        int MR, int N, int K, int k_per_split, Epi epi) {
-  __shared__ __attribute__((aligned(16))) char smem[BG_NST * BG_STAGE];
+  // the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
+  // so the compiler's tracking of direct LDS loads sees a single target
+  __shared__ __attribute__((aligned(16))) char smem[BG_NST * BG_STAGE + (Epi::kSwap ? BG_M * 4 : 0)];
   const int tiles_m = (MR + BG_M - 1) / BG_M;
   const int tiles_n = N / BG_N;
   const int ntiles = tiles_m * tiles_n;
@@ -437,20 +439,19 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
-  // row scales of the K/V epilogue (one row per lane per 32-row block),
-  // loaded ahead of the stage loads so the in-order wait counts still hold
-  float rsc[4] = {0.f, 0.f, 0.f, 0.f};
+  // Row scales of the K/V epilogue: one direct LDS load per lane (the
+  // tile's 256 rows), issued ahead of the stage loads, so they hold no
+  // registers through the main loop and are waited for with the first stage.
+  float* rsc_lds = reinterpret_cast<float*>(smem + BG_NST * BG_STAGE);
   if constexpr (Epi::kSwap) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * 128 + i * 32 + r32;
-      rsc[i] = epi.rinv[min(row, epi.T - 1)];
-      if (row >= epi.T) rsc[i] = 0.f;
+    if (nsteps > 0) {
+      const int row = min(m0 + wave * 64 + lane, epi.T - 1);
+      __builtin_amdgcn_global_load_lds(epi.rinv + row, (lds_ptr_t)(rsc_lds + wave * 64), 4, 0, 0);
     }
   }
 
   // Ring of BG_NST stages (8 direct loads per thread each). All stages are
-  // loaded up front; the barrier in the middle of step s (everyone has read
+  // loaded up front (after the row-scale load, which the first wait covers); the barrier in the middle of step s (everyone has read
   // stage s, stage s+1 has landed) frees stage s for the load of step
   // s+BG_NST. Loads past the last step repeat the last one (in bounds, never
   // read), which keeps every wait count fixed.
@@ -509,6 +510,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t tb = (int64_t)m0 + wm * 128 + i * 32;
+      // padding rows (T <= row < Tpad) are written as zeros
+      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[wm * 128 + i * 32 + r32] : 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int w = (nw + j * 32) % epi.d;
@@ -520,7 +523,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int x = 0; x < 2; ++x)
-            P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rsc[i], acc[i][j][4 * q + 2 * x + 1] * rsc[i]);
+            P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rs, acc[i][j][4 * q + 2 * x + 1] * rs);
         if (kv == 0) {
           const int64_t t = tb + r32;
 #pragma unroll
