@@ -1,4 +1,5 @@
-// Eq 3 block attention over [context ++ block], split over context chunks.
+// Eq 3 block attention over [context ++ block], split over context chunks,
+// and the attention output projection.
 //
 // The gamma block queries of sequence b attend to its L_b context keys and
 // its gamma block keys with no causal mask (module-dflash.ts, #layer). The
@@ -6,9 +7,11 @@
 // of `chunk` keys: one workgroup per (chunk, head) streams the chunk's K and
 // V once and leaves an unnormalised partial (m, l, o) per query, as the
 // split-chunk attention + combine kernels of dspark-runtime.js do. A second
-// kernel, one workgroup per (sequence, head, query), merges those partials
-// together with the gamma block keys by the log-sum-exp identity
-//   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  o = sum_c o_c 2^(m_c - M) / l.
+// kernel merges those partials together with the gamma block keys by the
+// log-sum-exp identity
+//   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  o = sum_c o_c 2^(m_c - M) / l
+// and applies W_o head by head: E = D + sum_h o_h W_o[:, h]^T (#layer's
+// output projection and residual).
 // Scores are kept in base 2: Q arrives pre-multiplied by hd^-1/2 * log2(e).
 //
 // Work split inside a chunk: each wave takes every fourth 64-key block, with
@@ -433,89 +436,262 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// combine: grid (A * n_heads, gamma), 256 threads. Query j of (sequence b,
-// head h): every tile partial of b plus the gamma block keys (K_d, V_d in
-// float32). Thread (tg, cc) sums tiles tg, tg + NG, ... for column cc.
+// Combine + output projection: grid (d / NC column blocks, n_heads, A), 256
+// threads. Workgroup (nb, h, b) merges every context partial of sequence b
+// and head h with the gamma block keys (K_d, V_d in float32) into the head's
+// attention output o_h [gamma][hd], then adds o_h . W_o[cols, h*hd : (h+1)*hd]^T
+// for its NC output columns into E with float atomics, so the heads' shares
+// sum there: E = D + sum_h o_h W_o,h^T (the head-0 workgroups add D). E must
+// be zero on entry.
+//
+// Merge: thread (tg, c4) runs an online log-sum-exp over tiles tg, tg + TG,
+// ... for four output columns of every query, with the loads of TB tiles in
+// flight together; the TG groups are merged in LDS. Projection: a 16-byte
+// weight load covers CPL columns, LPC lanes per column (VPL dims each); the
+// per-lane dot products are summed over each column's LPC lanes with DPP /
+// permlane moves. The weights, residual and block rows are requested before
+// the tile range is known, so the only dependent round trips are the tile
+// prefix (skipped for a single sequence) and the partials.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd, int A,
-    int gamma, int d, int n_heads, const int32_t* __restrict__ prefix, int total_tiles,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, float* __restrict__ attn) {
-  __shared__ float sb[kMaxGamma];
-  __shared__ float redw[4];
-  __shared__ float red_acc[256];
-  __shared__ float Msh, Lsh;
-  const int b = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
-  const int j = blockIdx.y;
-  const int hd = d / n_heads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = min(prefix[b], total_tiles), t1 = min(prefix[b + 1], total_tiles);
-  const float* q = Q + (int64_t)(b * gamma + j) * d + h * hd;
+template <int LPC>
+DSPARK_DEV float seg_sum(float v) {   // sum over aligned groups of LPC lanes
+  static_assert(LPC == 4 || LPC == 8 || LPC == 16 || LPC == 32, "segment");
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  if constexpr (LPC >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (LPC >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (LPC >= 32) {
+    float x, y;
+    swap16(v, x, y);
+    v = x + y;
+  }
+  return v;
+}
 
-  // block-key scores (one wave per key)
-  for (int jj = wave; jj < gamma; jj += 4) {
-    const float* kr = Kd + (int64_t)(b * gamma + jj) * d + h * hd;
+template <typename WT, int HD>
+struct OProjShape {
+  static constexpr int C4 = HD / 4;               // float4 columns of a head
+  static constexpr int TG = 256 / C4;             // tile groups of the merge
+  static constexpr int VPL = 16 / (int)sizeof(WT);  // weights per 16-byte load
+  static constexpr int LPC = HD / VPL;            // lanes per weight column
+  static constexpr int CPL = 64 / LPC;            // columns per wave load
+  static constexpr int kLoads = 2;                // wave loads per wave
+  static constexpr int NC = 4 * CPL * kLoads;     // columns per workgroup (divides d)
+  // LDS floats: q, k, v rows, block scores, group (o, m, l)
+  static constexpr int lds_floats(int g) {
+    return 3 * g * HD + ((g * g + 3) & ~3) + TG * g * HD + 2 * TG * g;
+  }
+};
+
+template <typename WT, int HD, int G>
+__global__ __launch_bounds__(256) void combine_oproj_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
+    int n_heads, const int32_t* __restrict__ prefix, int total_tiles,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, const WT* __restrict__ Wo,
+    const float* __restrict__ resid, float* __restrict__ out) {
+  using Sh = OProjShape<WT, HD>;
+  constexpr int C4 = Sh::C4, TG = Sh::TG, VPL = Sh::VPL, LPC = Sh::LPC, CPL = Sh::CPL;
+  constexpr int NL = Sh::kLoads;
+  constexpr int RPL = (G + LPC - 1) / LPC;   // output rows per lane and column
+  constexpr int TB = G <= 5 ? 4 : (G <= 10 ? 2 : 1);   // tiles whose loads are issued together
+  constexpr int QE = (G * C4 + 255) / 256;   // q / k / v float4 per thread
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  float* qs = lds;                        // [G][HD], later the merged o_h
+  float* ks = qs + G * HD;                // [G][HD]
+  float* vs = ks + G * HD;                // [G][HD]
+  float* sb = vs + G * HD;                // [G][G] block-key scores
+  float* og = sb + ((G * G + 3) & ~3);    // [TG][G][HD]
+  float* mg = og + TG * G * HD;           // [TG][G]
+  float* lg = mg + TG * G;                // [TG][G]
+
+  const int d = n_heads * HD;
+  const int b = blockIdx.z, h = blockIdx.y, col0 = blockIdx.x * Sh::NC;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane / LPC, ch = lane % LPC;
+
+  // Everything that does not depend on the tile range is requested first:
+  // this workgroup's W_o slice, the residual (head 0), the block rows.
+  u32x4 wv[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int col = col0 + (wave * NL + i) * CPL + cl;
+    wv[i] = ld16(Wo + (int64_t)col * d + h * HD + ch * VPL);
+  }
+  float rv[NL][RPL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int k = 0; k < RPL; ++k) rv[i][k] = 0.f;
+  if (h == 0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int col = col0 + (wave * NL + i) * CPL + cl;
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) {
+        const int j = min(ch + k * LPC, G - 1);
+        rv[i][k] = resid[(int64_t)(b * G + j) * d + col];
+      }
+    }
+  }
+  f32x4 qv[QE], kv[QE], vv[QE];
+#pragma unroll
+  for (int u = 0; u < QE; ++u) {
+    const int e = min(tid + 256 * u, G * C4 - 1);
+    const int j = e / C4, c = e % C4;
+    const int64_t off = (int64_t)(b * G + j) * d + h * HD + 4 * c;
+    qv[u] = *reinterpret_cast<const f32x4*>(Q + off);
+    kv[u] = *reinterpret_cast<const f32x4*>(Kd + off);
+    vv[u] = *reinterpret_cast<const f32x4*>(Vd + off);
+  }
+
+  // context partials: online merge over this thread's tiles, TB at a time
+  const bool one_seq = gridDim.z == 1;
+  const int t0 = one_seq ? 0 : min(prefix[b], total_tiles);
+  const int t1 = one_seq ? total_tiles : min(prefix[b + 1], total_tiles);
+  const int tg = tid / C4, c4 = tid % C4;
+  float mrun[G], lrun[G];
+  f32x4 acc[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    mrun[j] = kNegInf;
+    lrun[j] = 0.f;
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int tb = t0 + tg; tb < t1; tb += TG * TB) {
+    f32x2 ml[TB][G];
+    f32x4 o[TB][G];
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      const int64_t pj = ((int64_t)min(tb + k * TG, t1 - 1) * n_heads + h) * G;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        ml[k][j] = *reinterpret_cast<const f32x2*>(part_ml + (pj + j) * 2);
+        o[k][j] = *reinterpret_cast<const f32x4*>(part_o + (pj + j) * HD + 4 * c4);
+      }
+    }
+    // all of the batch's loads are issued before any is used; the merge is
+    // branch-free, so no load is moved into a conditional block
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      const bool in = tb + k * TG < t1;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float mt = in ? ml[k][j][0] : kNegInf;   // an empty tile adds nothing
+        const float mn = fmaxf(mrun[j], mt);
+        const float so = mrun[j] == mn ? 1.f : exp2f(mrun[j] - mn);
+        const float sn = mt == kNegInf ? 0.f : exp2f(mt - mn);
+        acc[j] = acc[j] * so + o[k][j] * sn;
+        lrun[j] = lrun[j] * so + ml[k][j][1] * sn;
+        mrun[j] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QE; ++u) {
+    const int e = tid + 256 * u;
+    if (e < G * C4) {
+      const int j = e / C4, c = e % C4;
+      *reinterpret_cast<f32x4*>(qs + j * HD + 4 * c) = qv[u];
+      *reinterpret_cast<f32x4*>(ks + j * HD + 4 * c) = kv[u];
+      *reinterpret_cast<f32x4*>(vs + j * HD + 4 * c) = vv[u];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    *reinterpret_cast<f32x4*>(og + (tg * G + j) * HD + 4 * c4) = acc[j];
+    if (c4 == 0) {
+      mg[tg * G + j] = mrun[j];
+      lg[tg * G + j] = lrun[j];
+    }
+  }
+  __syncthreads();
+  // block-key scores (base 2: q carries hd^-1/2 log2 e), one wave per pair
+  for (int pq = wave; pq < G * G; pq += 4) {
+    const int j = pq / G, jj = pq % G;
     float sc = 0.f;
-    for (int cc = lane; cc < hd; cc += 64) sc = fmaf(q[cc], kr[cc], sc);
+#pragma unroll
+    for (int c = lane; c < HD; c += 64) sc = fmaf(qs[j * HD + c], ks[jj * HD + c], sc);
     sc = wave_sum(sc);
-    if (lane == 0) sb[jj] = sc;
-  }
-  // max over tiles
-  float mloc = kNegInf;
-  for (int t = t0 + tid; t < t1; t += 256)
-    mloc = fmaxf(mloc, part_ml[(((int64_t)t * n_heads + h) * gamma + j) * 2]);
-  mloc = wave_max(mloc);
-  if (lane == 0) redw[wave] = mloc;
-  __syncthreads();
-  if (tid == 0) {
-    float M = fmaxf(fmaxf(redw[0], redw[1]), fmaxf(redw[2], redw[3]));
-    for (int jj = 0; jj < gamma; ++jj) M = fmaxf(M, sb[jj]);
-    Msh = M;
+    if (lane == 0) sb[pq] = sc;
   }
   __syncthreads();
-  const float M = Msh;
-  // l over tiles
-  float lloc = 0.f;
-  for (int t = t0 + tid; t < t1; t += 256) {
-    const float* ml = part_ml + (((int64_t)t * n_heads + h) * gamma + j) * 2;
-    if (ml[0] != kNegInf) lloc += ml[1] * exp2f(ml[0] - M);
-  }
-  lloc = wave_sum(lloc);
-  __syncthreads();
-  if (lane == 0) redw[wave] = lloc;
-  __syncthreads();
-  if (tid == 0) {
-    float l = (redw[0] + redw[1]) + (redw[2] + redw[3]);
-    for (int jj = 0; jj < gamma; ++jj) l += exp2f(sb[jj] - M);
-    Lsh = l;
-  }
-  // weighted tile outputs: 8 tiles per batch, loads issued together
-  const int ng = 256 / hd;
-  const int cc = tid % hd, tg = tid / hd;
-  float acc = 0.f;
-  for (int tb = t0 + tg; tb < t1; tb += 8 * ng) {
-    float mv[8], ov[8];
+  // o_h[j] = (sum_g o_g 2^(m_g - M) + sum_jj 2^(s_jj - M) v_jj) / l
+  for (int e = tid; e < G * C4; e += 256) {
+    const int j = e / C4, c = e % C4;
+    float M = kNegInf;
+    for (int g2 = 0; g2 < TG; ++g2) M = fmaxf(M, mg[g2 * G + j]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = min(tb + i * ng, t1 - 1);
-      const int64_t pj = ((int64_t)t * n_heads + h) * gamma + j;
-      mv[i] = part_ml[pj * 2];
-      ov[i] = part_o[pj * hd + cc];
+    for (int jj = 0; jj < G; ++jj) M = fmaxf(M, sb[j * G + jj]);
+    float l = 0.f;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g2 = 0; g2 < TG; ++g2) {
+      const float m = mg[g2 * G + j];
+      if (m != kNegInf) {
+        const float w = exp2f(m - M);
+        l = fmaf(lg[g2 * G + j], w, l);
+        o += *reinterpret_cast<const f32x4*>(og + (g2 * G + j) * HD + 4 * c) * w;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool in = tb + i * ng < t1 && mv[i] != kNegInf;
-      acc = fmaf(in ? ov[i] : 0.f, in ? exp2f(mv[i] - M) : 0.f, acc);
+    for (int jj = 0; jj < G; ++jj) {
+      const float w = exp2f(sb[j * G + jj] - M);
+      l += w;
+      o += *reinterpret_cast<const f32x4*>(vs + jj * HD + 4 * c) * w;
+    }
+    *reinterpret_cast<f32x4*>(qs + j * HD + 4 * c) = o * (1.f / l);
+  }
+  __syncthreads();
+  // E[b*G + j][col] += o_h[j] . W_o[col, h*hd : (h+1)*hd]  (+ D on head 0)
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int col = col0 + (wave * NL + i) * CPL + cl;
+    float w[VPL];
+    Vec16<WT>::unpack(wv[i], w);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float* x = qs + j * HD + ch * VPL;
+      float sdot = 0.f;
+#pragma unroll
+      for (int e4 = 0; e4 < VPL / 4; ++e4) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(x + 4 * e4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdot = fmaf(xv[e], w[4 * e4 + e], sdot);
+      }
+      sdot = seg_sum<LPC>(sdot);
+      if (ch == j % LPC) unsafeAtomicAdd(out + (int64_t)(b * G + j) * d + col, sdot + rv[i][j / LPC]);
     }
   }
-  red_acc[tid] = acc;
-  __syncthreads();
-  if (tid < hd) {
-    float v = 0.f;
-    for (int g2 = 0; g2 < ng; ++g2) v += red_acc[g2 * hd + tid];
-    for (int jj = 0; jj < gamma; ++jj)
-      v = fmaf(exp2f(sb[jj] - M), Vd[(int64_t)(b * gamma + jj) * d + h * hd + tid], v);
-    attn[(int64_t)(b * gamma + j) * d + h * hd + tid] = v / Lsh;
+}
+
+template <typename WT, int HD, int G>
+static hipError_t launch_oproj_t(const AttnArgs& a, hipStream_t s) {
+  using Sh = OProjShape<WT, HD>;
+  const int d = HD * a.kv.n_heads;
+  if (d % Sh::NC != 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t)Sh::lds_floats(G) * 4;
+  auto kern = combine_oproj_kernel<WT, HD, G>;
+  if (lds > 65536) {
+    static hipError_t set = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (set != hipSuccess) return set;
+  }
+  dim3 grid(d / Sh::NC, a.kv.n_heads, a.A);
+  kern<<<grid, 256, lds, s>>>(a.Q, a.Kd, a.Vd, a.kv.n_heads, a.prefix, a.total_tiles, a.part_o,
+                              a.part_ml, static_cast<const WT*>(a.wo), a.resid, a.out);
+  return hipGetLastError();
+}
+
+template <typename WT, int HD>
+static hipError_t oproj_gamma(const AttnArgs& a, hipStream_t s) {
+  switch (a.gamma) {
+#define DSPARK_G(g) \
+  case g: return launch_oproj_t<WT, HD, g>(a, s);
+    DSPARK_G(1) DSPARK_G(2) DSPARK_G(3) DSPARK_G(4) DSPARK_G(5) DSPARK_G(6) DSPARK_G(7)
+    DSPARK_G(8) DSPARK_G(9) DSPARK_G(10) DSPARK_G(11) DSPARK_G(12) DSPARK_G(13) DSPARK_G(14)
+    DSPARK_G(15) DSPARK_G(16)
+#undef DSPARK_G
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -546,7 +722,7 @@ static bool dispatch_gamma(int gamma, dim3 grid, hipStream_t s, const AttnArgs& 
 }
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
-  if (a.total_tiles == 0) return hipSuccess;
+  if (a.total_tiles < a.A) return hipErrorInvalidValue;   // every sequence has a tile
   dim3 grid(a.total_tiles, a.kv.n_heads);
   bool ok = false;
   trace_pre(K_ATTN, s);
@@ -563,13 +739,18 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
   if (!ok) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(a.A * a.kv.n_heads, a.gamma);
   trace_pre(K_COMBINE, s);
-  combine_kernel<<<cgrid, 256, 0, s>>>(a.Q, a.Kd, a.Vd, a.A, a.gamma, a.kv.hd * a.kv.n_heads,
-                                       a.kv.n_heads, a.prefix, a.total_tiles, a.part_o, a.part_ml,
-                                       a.attn);
+  if (dtype == 1) {
+    if (a.kv.hd == 128) e = oproj_gamma<bf16, 128>(a, s);
+    else if (a.kv.hd == 64) e = oproj_gamma<bf16, 64>(a, s);
+    else e = oproj_gamma<bf16, 32>(a, s);
+  } else {
+    if (a.kv.hd == 128) e = oproj_gamma<float, 128>(a, s);
+    else if (a.kv.hd == 64) e = oproj_gamma<float, 64>(a, s);
+    else e = oproj_gamma<float, 32>(a, s);
+  }
   trace_post(K_COMBINE, s);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace dspark

@@ -41,8 +41,8 @@ static dspark_status fail(dspark_status st, const char* fmt, ...) {
 // tracing (per-kernel HIP events)
 // ---------------------------------------------------------------------------
 static const char* kNames[K_COUNT] = {
-    "gemm_ctx_fuse", "setup",      "gemm_ctx_kv", "attn_split_k",
-    "attn_combine",  "block_gemm", "block_rows"};
+    "gemm_ctx_fuse",      "setup",      "gemm_ctx_kv", "attn_split_k",
+    "attn_combine_oproj", "block_gemm", "block_rows"};
 
 const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
 
@@ -84,7 +84,7 @@ struct Plan {
   size_t esz = 4;
   // workspace offsets (bytes)
   size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
-  size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, attn = 0, E = 0, GU = 0;
+  size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, E = 0, GU = 0;
   size_t total = 0;
 };
 
@@ -165,8 +165,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
     p->Q = take(row);
     p->Kd = take(row);
     p->Vd = take(row);
-    p->attn = take(row);
-    p->E = take(row);
+    p->E = take(row * p->kv_layers);   // one accumulator per layer, cleared by the set-up pass
     p->GU = take((size_t)M * 2 * ff * 4);
   }
   p->total = off == 0 ? 256 : off;
@@ -276,6 +275,8 @@ static void setup_block_roles(const dspark_dims* dm, const Plan& p, int A, const
   sa->A = A;
   sa->chunk = p.chunk;
   sa->prefix = at<int32_t>(ws, p.prefix);
+  sa->zero = at<float>(ws, p.E);
+  sa->zero_n = (int64_t)p.kv_layers * p.M * dm->d;
   if (dm->dtype == DSPARK_BF16 && p.T > 0) {
     sa->b = kv_mats(layers, nl, dm->d);
     sa->Bt = at<char>(ws, p.wkvt);
@@ -291,8 +292,7 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   float* Q = at<float>(ws, p.Q);
   float* Kd = at<float>(ws, p.Kd);
   float* Vd = at<float>(ws, p.Vd);
-  float* attn = at<float>(ws, p.attn);
-  float* E = at<float>(ws, p.E);
+  float* E = at<float>(ws, p.E) + (size_t)kv_layer * M * d;   // zeroed by the set-up pass
   float* GU = at<float>(ws, p.GU);
 
   // Q (pre-scaled for the base-2 softmax), K_d, V_d from RMSNorm(D; attn_norm)
@@ -305,6 +305,7 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   r.qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
   DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_QKV, r, s));
   // attention over [context ++ block]: split-K partials, then the combine
+  // with the output projection, E = D + Attn Wo^T
   AttnArgs aa{};
   aa.Q = Q; aa.Kd = Kd; aa.Vd = Vd;
   aa.kv = KVDesc{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
@@ -314,14 +315,10 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   aa.A = A; aa.gamma = G; aa.chunk = p.chunk; aa.total_tiles = p.total_chunks;
   aa.part_o = at<float>(ws, p.po);
   aa.part_ml = at<float>(ws, p.pml);
-  aa.attn = attn;
+  aa.wo = lw.wo;
+  aa.resid = D;
+  aa.out = E;
   DSPARK_HIP(launch_attention(dt, aa, s));
-  // E = D + Attn Wo
-  r = RowGemmArgs{};
-  r.X = attn; r.ldx = d; r.M = M; r.K = d; r.N = d;
-  r.b.mat[0] = lw.wo; r.b.n_per = d; r.b.nmat = 1;
-  r.res = D; r.out = E; r.ldo = d;
-  DSPARK_HIP(launch_rowgemm(dt, RP_NONE, RE_RESID, r, s));
   // H = SiLU(Z Wgate^T) * (Z Wup^T), Z = RMSNorm(E; ff_norm)
   r = RowGemmArgs{};
   r.X = E; r.ldx = d; r.M = M; r.K = d; r.N = 2 * ff;

@@ -64,6 +64,7 @@ struct KVDesc {
 //   h       part != null: h[t] = RMSNorm(sum_z part[z][t]; g), rinv[t] = inverse
 //           RMS of the stored row (rinv nullable); part == null and h_in != null:
 //           only rinv[t] of the given rows
+//   zero    zero[0 .. zero_n) = 0 (zero_n a multiple of 4)
 struct SetupArgs {
   int d = 0;
   float eps = 0.f;
@@ -87,6 +88,9 @@ struct SetupArgs {
   void* h = nullptr;
   const void* h_in = nullptr;
   float* rinv = nullptr;
+  // cleared buffer
+  float* zero = nullptr;
+  int64_t zero_n = 0;
 };
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s);
 
@@ -120,9 +124,11 @@ struct AttnArgs {
   int A, gamma, chunk, total_tiles;
   float* part_o;        // [tiles][n_heads][gamma][hd]
   float* part_ml;       // [tiles][n_heads][gamma][2]
-  float* attn;          // out [A*gamma][d]
+  const void* wo;       // W_o [d][d] ([out, in], storage type)
+  const float* resid;   // D [A*gamma][d]
+  float* out;           // E [A*gamma][d]: zero on entry, D + Attn W_o^T on exit
 };
-// partial kernel, then the combine kernel
+// partial kernel, then the combine + output projection kernel
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 // ---- block side -----------------------------------------------------------

@@ -1,6 +1,6 @@
 // The forward's row passes and independent set-up work, in one launch.
 //
-// After the Eq 2 projection, four pieces of work need nothing but the call's
+// After the Eq 2 projection, these pieces of work need nothing but the call's
 // inputs and that projection, and none needs another:
 //   plan   the split-K attention's tile prefix over the ragged context lengths
 //   D0     block_in + block_pos (the block rows entering the first layer)
@@ -9,6 +9,8 @@
 //   norm   H_ctx = RMSNorm(sum of the projection's K splits; ctx_norm) and the
 //          inverse RMS of each stored row, or, when H_ctx is given, only the
 //          inverse RMS ("DFlash draft layer", `#buildContext` and `#layer`)
+//   zero   clears the per-layer accumulators that the attention output
+//          projection adds its heads' shares into
 // Each is a range of workgroups of one grid (256 threads, one wave per row),
 // so a forward pays one kernel boundary for all of them.
 #include "common.h"
@@ -16,7 +18,6 @@
 
 namespace dspark {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // chunk_prefix[b] = sum_{b' < b} max(1, ceil(L_b' / chunk)) for b = 0..A. An
 // empty sequence still gets one tile, which finds no keys and leaves an empty
@@ -164,16 +165,18 @@ __device__ __forceinline__ void stats_row(const SetupArgs& a, int64_t t, int lan
   if (lane == 0) a.rinv[t] = rsqrtf(ss / (float)d + a.eps);
 }
 
-// Workgroup ranges, in dispatch order: [plan][D0][prep][norm]. The small
-// roles come first so that none of them lands in the grid's tail.
+// Workgroup ranges, in dispatch order: [plan][zero][D0][prep][norm]. The
+// small roles come first so that none of them lands in the grid's tail.
 struct SetupGrid {
-  int plan, d0, prep, norm;
-  int total() const { return plan + d0 + prep + norm; }
+  int plan, zero, d0, prep, norm;
+  int total() const { return plan + zero + d0 + prep + norm; }
 };
+constexpr int kZeroPerBlock = 256 * 4 * 4;   // floats cleared per workgroup
 
 static SetupGrid setup_grid(const SetupArgs& a) {
   SetupGrid g;
   g.plan = a.prefix ? 1 : 0;
+  g.zero = a.zero ? (int)((a.zero_n + kZeroPerBlock - 1) / kZeroPerBlock) : 0;
   g.d0 = a.D0 ? (a.A * a.gamma + 3) / 4 : 0;
   g.prep = a.Bt ? (a.b.n_per * a.b.nmat + 3) / 4 : 0;
   g.norm = (a.part || a.h_in) ? (int)((a.T + 3) / 4) : 0;
@@ -191,6 +194,17 @@ __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
     return;
   }
   blk -= sg.plan;
+  if (blk < sg.zero) {
+    f32x4* z = reinterpret_cast<f32x4*>(a.zero) + (int64_t)blk * (kZeroPerBlock / 4);
+    const int64_t n4 = a.zero_n / 4 - (int64_t)blk * (kZeroPerBlock / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = i * 256 + threadIdx.x;
+      if (e < n4) z[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  blk -= sg.zero;
   if (blk < sg.d0) {
     const int r = blk * 4 + w;
     if (r < a.A * a.gamma) d0_row(a, r, lane);
