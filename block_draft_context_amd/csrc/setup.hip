@@ -96,48 +96,75 @@ __device__ __forceinline__ void prep_row(const SetupArgs& a, int row, int lane) 
 }
 
 // H_ctx row t = RMSNorm(sum_z part[z][t]; g) in the storage type, and the
-// inverse RMS of the row as stored. Each lane owns d / 128 float2 column
-// pairs (d <= 2048); all of a split's loads are issued together.
-template <typename S>
+// inverse RMS of the row as stored. Lane l owns the 8-column chunks l + 64 i,
+// i < CPL = ceil(d / 512); the loads of SB splits are issued together, and
+// a chunk leaves as one 16-byte store (bf16) or two (float32).
+template <typename S, int CPL>
 __device__ __forceinline__ void norm_row(const SetupArgs& a, int64_t t, int lane) {
-  const int d = a.d, T = a.T;
-  const int nv = d / 128;
-  f32x2 v[16];
+  constexpr int SB = 8 / CPL > 0 ? 8 / CPL : 1;   // splits per batch: <= 16 float4 in flight
+  const int d = a.d, nch = d / 8;
+  const int64_t T = a.T;
+  f32x4 acc[CPL][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = f32x2{0.f, 0.f};
-  for (int zz = 0; zz < a.splits; ++zz) {
-    const f32x2* row = reinterpret_cast<const f32x2*>(a.part + ((int64_t)zz * T + t) * d);
-    f32x2 x[16];
+  for (int i = 0; i < CPL; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < a.splits; z0 += SB) {
+    f32x4 x[SB][CPL][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = row[min(i, nv - 1) * 64 + lane];
+    for (int sb = 0; sb < SB; ++sb) {
+      const int zz = min(z0 + sb, a.splits - 1);
+      const f32x4* row = reinterpret_cast<const f32x4*>(a.part + ((int64_t)zz * T + t) * d);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] += x[i];
+      for (int i = 0; i < CPL; ++i) {
+        const int c = min(lane + 64 * i, nch - 1);
+        x[sb][i][0] = row[2 * c];
+        x[sb][i][1] = row[2 * c + 1];
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+      if (z0 + sb < a.splits) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          acc[i][0] += x[sb][i][0];
+          acc[i][1] += x[sb][i][1];
+        }
+      }
   }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (i < nv) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1];
+  for (int i = 0; i < CPL; ++i)
+    if (lane + 64 * i < nch)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += acc[i][h2][e] * acc[i][h2][e];
   ss = wave_sum(ss);
   const float sc = rsqrtf(ss / (float)d + a.eps);
-  const f32x2* g2 = reinterpret_cast<const f32x2*>(a.g);
-  f32x2 gv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) gv[i] = g2[min(i, nv - 1) * 64 + lane];
-  S* __restrict__ h = static_cast<S*>(a.h);
+  const f32x4* g4 = reinterpret_cast<const f32x4*>(a.g);
   float ss2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < nv) {
-      const int c = (i * 64 + lane) * 2;
-      const S o0 = from_f32<S>(v[i][0] * sc * gv[i][0]);
-      const S o1 = from_f32<S>(v[i][1] * sc * gv[i][1]);
-      const float f0 = to_f32(o0), f1 = to_f32(o1);
-      ss2 += f0 * f0 + f1 * f1;
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float o[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f32x4 gv = g4[2 * c + h2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[4 * h2 + e] = to_f32(from_f32<S>(acc[i][h2][e] * sc * gv[e]));
+          ss2 += o[4 * h2 + e] * o[4 * h2 + e];
+        }
+      }
+      S* h = static_cast<S*>(a.h) + t * d + 8 * c;
       if constexpr (sizeof(S) == 2) {
-        *reinterpret_cast<uint32_t*>(h + t * d + c) =
-            (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = from_f32<bf16>(o[e]);
+        *reinterpret_cast<bf16x8*>(h) = v;
       } else {
-        *reinterpret_cast<f32x2*>(h + t * d + c) = f32x2{f0, f1};
+        reinterpret_cast<f32x4*>(h)[0] = f32x4{o[0], o[1], o[2], o[3]};
+        reinterpret_cast<f32x4*>(h)[1] = f32x4{o[4], o[5], o[6], o[7]};
       }
     }
   }
@@ -183,7 +210,7 @@ static SetupGrid setup_grid(const SetupArgs& a) {
   return g;
 }
 
-template <typename S>
+template <typename S, int CPL>
 __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
   __shared__ int32_t sums[256];
   int blk = blockIdx.x;
@@ -222,7 +249,7 @@ __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
   const int64_t t = (int64_t)blk * 4 + w;
   if (t >= a.T) return;
   if (a.part)
-    norm_row<S>(a, t, lane);
+    norm_row<S, CPL>(a, t, lane);
   else
     stats_row<S>(a, t, lane);
 }
@@ -232,10 +259,17 @@ hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s) {
   const SetupGrid sg = setup_grid(a);
   if (sg.total() == 0) return hipSuccess;
   trace_pre(K_SETUP, s);
-  if (dtype == 1)
-    setup_kernel<bf16><<<sg.total(), 256, 0, s>>>(a, sg);
-  else
-    setup_kernel<float><<<sg.total(), 256, 0, s>>>(a, sg);
+  const int cpl = (a.d / 8 + 63) / 64;   // 8-column chunks per lane, d <= 2048
+#define DSPARK_SETUP(C)                                                    \
+  if (cpl == C) {                                                          \
+    if (dtype == 1) setup_kernel<bf16, C><<<sg.total(), 256, 0, s>>>(a, sg); \
+    else setup_kernel<float, C><<<sg.total(), 256, 0, s>>>(a, sg);           \
+  }
+  DSPARK_SETUP(1)
+  DSPARK_SETUP(2)
+  DSPARK_SETUP(3)
+  DSPARK_SETUP(4)
+#undef DSPARK_SETUP
   trace_post(K_SETUP, s);
   return hipGetLastError();
 }
