@@ -59,6 +59,14 @@ CASES = {
     "bf16-3layer-d1024": dict(name="b8", seed_id=19, A=2, m=2, H=128, d=1024, n_heads=8,
                                gamma=4, n_layers=3, ff=2048, dtype="bf16",
                                lengths=[3000, 1096]),
+    # sixteen short ragged sequences (80 block rows: ten 8-row passes of the
+    # block GEMMs, many (sequence, head) combine workgroups)
+    "bf16-16seq": dict(name="b9", seed_id=20, A=16, m=2, H=64, d=256, n_heads=2, gamma=5,
+                       n_layers=2, ff=1024, dtype="bf16",
+                       lengths=[37, 0, 250, 1, 64, 65, 300, 129, 7, 0, 200, 33, 128, 5, 90, 311]),
+    "f32-16seq": dict(name="f2", seed_id=21, A=16, m=1, H=64, d=128, n_heads=4, gamma=5,
+                      n_layers=1, ff=2048, dtype="f32",
+                      lengths=[20, 3, 0, 64, 1, 100, 50, 9, 77, 0, 12, 64, 65, 8, 31, 40]),
 }
 
 
@@ -121,7 +129,8 @@ def _storage(w, a):
     return W.bf16_round(np.asarray(a, dtype=np.float32)) if w.dtype == "bf16" else np.asarray(a, np.float32)
 
 
-@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-gamma16"])
+@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-gamma16",
+                                  "bf16-16seq"])
 def test_block_layer_matches_oracle_and_keeps_context(case):
     """One layer on a given context; H_ctx is bitwise unchanged by the call."""
     w, x = _make(case, gains="random")
@@ -142,7 +151,8 @@ def test_block_layer_matches_oracle_and_keeps_context(case):
 
 
 def test_block_layer_in_place():
-    """d_out may alias d_in."""
+    """d_out may alias d_in (the two runs agree up to the order in which float
+    atomics sum the heads' shares)."""
     w, x = _make("bf16-ragged-hd128")
     u = Uploaded(w, x)
     C = _storage(w, O.ctx_fuse(x["taps"], x["w_c"], x["ctx_norm"], w.eps))
@@ -153,7 +163,7 @@ def test_block_layer_in_place():
     ref = B.block_layer(dims_of(B, w), u.cu, h, d1, u.layers[0], cu_dev=u.cu_dev)
     B.block_layer(dims_of(B, w), u.cu, h, d2, u.layers[0], cu_dev=u.cu_dev, d_out=d2)
     torch.cuda.synchronize()
-    assert torch.equal(ref, d2)
+    assert rel_err(d2.cpu().numpy(), ref.cpu().numpy()) < 1e-6
 
 
 def test_layer_chain_equals_forward():
@@ -172,11 +182,18 @@ def test_layer_chain_equals_forward():
     assert rel_err(out.cpu().numpy(), ref) < 1e-5
 
 
-def test_deterministic():
-    w, x = _make("bf16-ragged-hd128")
-    a, _, u = _forward(w, x)
-    b, _, _ = _forward(w, x, u)
-    assert torch.equal(a, b)
+@pytest.mark.parametrize("case", ["bf16-ragged-hd128", "bf16-16seq"])
+def test_repeatable(case):
+    """Repeat runs: the context side (H_ctx) is bitwise the same; the block
+    rows agree up to float reassociation, since the attention heads' shares
+    of a row are summed with float atomics in arrival order."""
+    w, x = _make(case)
+    a, ha, u = _forward(w, x, h_ctx_out=True)
+    b, hb, _ = _forward(w, x, u, h_ctx_out=True)
+    assert torch.equal(ha, hb)
+    e = rel_err(a.cpu().numpy(), b.cpu().numpy())
+    print(f"{case}: repeat rel diff {e:.2e}")
+    assert e < 1e-6
 
 
 def test_varlen_equals_separate_runs():
