@@ -53,6 +53,39 @@ int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
   return n;
 }
 
+// Sequence and key range [k0, k1) of a split-K tile; false past the plan.
+// The tile prefix (device plan) is searched for the owning sequence; with one
+// sequence the range follows from the tile index and the context length T1,
+// so the K/V loads need no dependent memory access first.
+struct TileRange {
+  int b;
+  int64_t k0, k1;
+};
+DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restrict__ cu,
+                           const int32_t* __restrict__ prefix, int chunk, int total_tiles,
+                           TileRange& r) {
+  if (tile >= total_tiles) return false;
+  if (A == 1) {
+    r.b = 0;
+    r.k0 = min(T1, (int64_t)tile * chunk);
+    r.k1 = min(T1, r.k0 + chunk);
+    return true;
+  }
+  if (tile >= prefix[A]) return false;
+  // sequence owning this tile: largest b with prefix[b] <= tile
+  int lo = 0, hi = A - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  r.b = lo;
+  const int c = tile - prefix[lo];
+  const int64_t kseq0 = cu[lo], kseq1 = cu[lo + 1];
+  r.k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
+  r.k1 = min(kseq1, r.k0 + chunk);
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // partials: grid (total_tiles, n_heads), 256 threads (4 waves)
 // part_o  [total_tiles][n_heads][G][HD]   unnormalised output
@@ -61,7 +94,7 @@ int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
 template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int chunk,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
     int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
@@ -78,20 +111,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int dev_total = prefix[A];
-  if (tile >= total_tiles || tile >= dev_total) return;
-
-  // sequence owning this tile: largest b with prefix[b] <= tile
-  int lo = 0, hi = A - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int b = lo;
-  const int c = tile - prefix[b];
-  const int64_t kseq0 = cu[b], kseq1 = cu[b + 1];
-  const int64_t k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
-  const int64_t k1 = min(kseq1, k0 + chunk);
+  TileRange tr;
+  if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, tr)) return;
+  const int b = tr.b;
+  const int64_t k0 = tr.k0, k1 = tr.k1;
 
   const int d = HD * n_heads;
   for (int i = tid; i < G * HD; i += 256) {
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_hsplit_kernel(
     const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int chunk,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
     int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
@@ -287,18 +310,10 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int dev_total = prefix[A];
-  if (tile >= total_tiles || tile >= dev_total) return;
-  int lo = 0, hi = A - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int b = lo;
-  const int c = tile - prefix[b];
-  const int64_t kseq0 = cu[b], kseq1 = cu[b + 1];
-  const int64_t k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
-  const int64_t k1 = min(kseq1, k0 + chunk);
+  TileRange tr;
+  if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, tr)) return;
+  const int b = tr.b;
+  const int64_t k0 = tr.k0, k1 = tr.k1;
   const int64_t blk0 = k0 >> 6;
   const int nblk = k1 > k0 ? (int)(((k1 - 1) >> 6) - blk0 + 1) : 0;   // 0, 1 or 2
 
@@ -700,12 +715,12 @@ static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
   if (a.chunk == 64) {
     attn_hsplit_kernel<S, HD, G><<<grid, 256, 0, s>>>(
         a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-        a.chunk, a.total_tiles, a.part_o, a.part_ml);
+        a.kv.T, a.chunk, a.total_tiles, a.part_o, a.part_ml);
     return;
   }
   attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(
       a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-      a.chunk, a.total_tiles, a.part_o, a.part_ml);
+      a.kv.T, a.chunk, a.total_tiles, a.part_o, a.part_ml);
 }
 
 template <typename S, int HD>
