@@ -67,6 +67,11 @@ CASES = {
     "f32-16seq": dict(name="f2", seed_id=21, A=16, m=1, H=64, d=128, n_heads=4, gamma=5,
                       n_layers=1, ff=2048, dtype="f32",
                       lengths=[20, 3, 0, 64, 1, 100, 50, 9, 77, 0, 12, 64, 65, 8, 31, 40]),
+    # the most block rows a call takes, A * gamma = 1024 (128 eight-row passes
+    # of the block GEMMs), over short ragged contexts with empty ones
+    "bf16-max-rows": dict(name="b10", seed_id=22, A=64, m=1, H=64, d=128, n_heads=4, gamma=16,
+                          n_layers=1, ff=256, dtype="bf16",
+                          lengths=[(37 * i) % 41 for i in range(64)]),
 }
 
 
