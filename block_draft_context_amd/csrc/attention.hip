@@ -30,20 +30,6 @@ namespace dspark {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// Keys per chunk. Short contexts (at most ~1024 64-key blocks over all
-// heads) use one block per tile and the head-split kernel, whose four waves
-// share each block; longer ones use chunks of >= 256 keys streamed by the
-// four waves of a workgroup, aiming for ~512 (chunk, head) workgroups.
-int attention_chunk(int64_t T, int n_heads, int A) {
-  const int64_t blocks = (T + 63) / 64 + A;   // bound on sum_b ceil(L_b / 64)
-  if (blocks * n_heads <= 1024) return 64;
-  int64_t c = (T * n_heads + 511) / 512;
-  c = ((c + 63) / 64) * 64;
-  if (c < 256) c = 256;
-  if (c > 16384) c = 16384;
-  return (int)c;
-}
-
 int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
   int64_t n = 0;
   for (int b = 0; b < A; ++b) {
@@ -51,6 +37,44 @@ int64_t attention_tiles(const int32_t* cu_host, int A, int chunk) {
     n += L > 0 ? (L + chunk - 1) / chunk : 1;
   }
   return n;
+}
+
+// Keys per chunk. Short contexts (at most ~1024 64-key blocks over all
+// heads) use one block per tile and the head-split kernel, whose four waves
+// share each block. Longer ones use the streaming kernel, aiming first for
+// ~512 (chunk, head) workgroups of at least 256 keys. The streaming kernel
+// holds one 256-thread workgroup per CU at its register use, so kAttnSlots
+// workgroups run at once. Where that aim gives chunks of 1024 keys or more,
+// a last partly filled round of such long chunks costs more than it saves.
+// There the chunk comes from a ladder of sizes: the one with the fewest
+// rounds of kAttnSlots workgroups times the keys a workgroup streams plus a
+// fixed cost of about 256 keys per workgroup, the larger on ties (fewer
+// partials to merge). The per-sequence rounding of ragged lengths is counted
+// exactly. Shorter chunks keep the first aim, which measured faster there.
+constexpr int kAttnSlots = 256;
+
+int attention_chunk(const int32_t* cu_host, int A, int n_heads) {
+  const int64_t T = cu_host[A] - cu_host[0];
+  const int64_t blocks = (T + 63) / 64 + A;   // bound on sum_b ceil(L_b / 64)
+  if (blocks * n_heads <= 1024) return 64;
+  int64_t c = (T * n_heads + 511) / 512;
+  c = ((c + 63) / 64) * 64;
+  if (c < 256) c = 256;
+  if (c > 16384) c = 16384;
+  if (c < 1024) return (int)c;
+  static const int ladder[] = {1024, 1280, 1536, 1792, 2048, 2560, 3072, 3584,
+                               4096, 5120, 6144, 7168, 8192, 10240, 12288, 14336, 16384};
+  int best = ladder[0];
+  int64_t best_cost = -1;
+  for (int lc : ladder) {
+    const int64_t wg = attention_tiles(cu_host, A, lc) * n_heads;
+    const int64_t cost = ((wg + kAttnSlots - 1) / kAttnSlots) * (lc + 256);
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = lc;
+    }
+  }
+  return best;
 }
 
 // Sequence and key range [k0, k1) of a split-K tile; false past the plan.

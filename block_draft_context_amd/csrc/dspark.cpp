@@ -140,7 +140,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   p->M = A * dm->gamma;
   const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
   p->ctx_splits = ctx_gemm_splits(dm->dtype, T, d, mH);
-  p->chunk = attention_chunk(T, dm->n_heads, A);
+  p->chunk = attention_chunk(cu_host, A, dm->n_heads);
   p->total_chunks = (int)attention_tiles(cu_host, A, p->chunk);
   p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;
 

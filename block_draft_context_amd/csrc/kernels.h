@@ -108,7 +108,7 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
                           hipStream_t s);
 
 // ---- attention ------------------------------------------------------------
-int attention_chunk(int64_t T, int n_heads, int A);   // keys per chunk (multiple of 64)
+int attention_chunk(const int32_t* cu_host, int A, int n_heads);   // keys per chunk (multiple of 64)
 // tiles = sum_b max(1, ceil(L_b / chunk)); the device prefix of the same sum
 // comes from the set-up pass
 int64_t attention_tiles(const int32_t* cu_host, int A, int chunk);
