@@ -25,6 +25,20 @@ template <typename S> DSPARK_DEV S from_f32(float x);
 template <> DSPARK_DEV float from_f32<float>(float x) { return x; }
 template <> DSPARK_DEV bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
+// Two floats rounded to bf16 and packed low, high into one dword.
+DSPARK_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(lo)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(hi)) << 16);
+}
+
+// c + a.lo * b.lo + a.hi * b.hi for two bf16 pairs, accumulated in f32
+// (v_dot2_f32_bf16; the bf16 products are exact in f32).
+DSPARK_DEV float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
 // Unpack one 16-byte vector of storage elements into floats.
 // bf16: 8 values; f32: 4 values.
 template <typename S> struct Vec16;

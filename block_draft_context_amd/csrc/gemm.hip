@@ -237,25 +237,51 @@ __global__ __launch_bounds__(256) void gemm_f32(ASegs a, BMats b, int M, int MR,
 // accumulators live in the AGPR file), so each k-substep of 16 issues 16 MFMAs
 // against 8 LDS operand reads and LDS bandwidth stays below the matrix-core
 // rate. Operands move global -> LDS with the gfx950 direct 16-byte loads (no
-// register staging) through a ring of 4 stages of 32-deep k tiles, so a
-// stage's loads have three k-steps to land. Within a k-step the operands of
-// substep 1 are read while substep 0's MFMAs run. Lane l of a load
-// instruction lands at LDS base + 16 l, so each lane fetches the global chunk
-// that its (swizzled) LDS slot stands for.
+// register staging) through a ring of stages of BK-deep k tiles, in 128 KiB
+// of LDS either way:
+//   BK = 32, 4 stages: a row's k tile is half a cache line, and a stage's
+//            loads have about three steps to land;
+//   BK = 64, 2 stages: a row's k tile is one whole 128-byte line, fetched by 8
+//            lanes of one instruction, so the vector memory path looks up
+//            half as many lines per byte; loads have about one step to land.
+// The operands of the next k-substep are read while the MFMAs of the current
+// one run. Lane l of a load instruction lands at LDS base + 16 l, so each lane
+// fetches the global chunk that its (swizzled) LDS slot stands for.
 // ---------------------------------------------------------------------------
-constexpr int BG_M = 256, BG_N = 256, BG_K = 32, BG_NST = 4;
-constexpr int BG_STAGE = (BG_M + BG_N) * BG_K * 2;   // 32 KiB per stage
-constexpr int BG_SROW = 264;                          // bf16 per row of the epilogue stage
+constexpr int BG_M = 256, BG_N = 256;
+constexpr int BG_LDS = 128 * 1024;                    // the stage ring
+
+template <int BK>
+struct BigCfg {
+  static_assert(BK == 32 || BK == 64, "BK");
+  static constexpr int ROWB = BK * 2;                 // bytes per LDS row
+  static constexpr int STAGE = (BG_M + BG_N) * ROWB;  // bytes per stage
+  static constexpr int NST = BG_LDS / STAGE;          // stages in the ring
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                // rows per load instruction
+  static constexpr int LPO = BG_M / (4 * RPI);        // load instructions per operand
+  static constexpr int LPS = 2 * LPO;                 // per stage
+  static constexpr int SUB = BK / 16;                 // MFMA k-substeps per step
+  // Chunk c of row r sits in slot c ^ f(r). An MFMA operand read has lanes
+  // 16g .. 16g+15 read one chunk of 16 consecutive rows; LDS serves a
+  // ds_read_b128 in groups of 16 lanes over 64 four-byte banks, and row r's
+  // chunk lands on bank quad (r * CPR + (c ^ f(r))) % 16, which f makes
+  // distinct over the 16 rows: f(r) = (r >> 2) & 3 for 64-byte rows,
+  // (r >> 1) & 7 for 128-byte rows (measured: no SQ_LDS_BANK_CONFLICT cycles
+  // for the former; patterns that repeat within 16 rows cost about 4 cycles
+  // per read).
+  static DSPARK_DEV int swz_f(int row) { return (row / (16 / CPR)) & (CPR - 1); }
+  static DSPARK_DEV int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_f(row)) << 4); }
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// 64-byte LDS rows (32 bf16 = 4 chunks of 16 B); chunk c of row r sits in slot
-// c ^ f(r), f(r) = (r >> 2) & 3. The MFMA operand reads (lane -> row lane % 32,
-// chunk 2 * ks + lane / 32) then take no bank-conflict cycles on gfx950, as
-// the SQ_LDS_BANK_CONFLICT counter shows; swizzles whose pattern repeats every
-// 8 rows of r >> 1 cost about 4 conflict cycles per ds_read_b128.
-DSPARK_DEV int swz64_f(int row) { return (row >> 2) & 3; }
-DSPARK_DEV int swz64(int row, int chunk) { return row * 64 + ((chunk ^ swz64_f(row)) << 4); }
+// One 16-byte direct global -> LDS load per lane. A plain function, so that
+// kernel templates calling it with template-dependent addresses still
+// instantiate in the host compilation pass, which has no such builtin.
+DSPARK_DEV void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)l, 16, 0, 0);
+}
 
 struct EpiPartialBig {         // out[z][r][n] = acc for r < M
   float* out;
@@ -290,10 +316,10 @@ DSPARK_DEV void wait_vmcnt() {
 }
 DSPARK_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-// Each k-step is two scheduling regions of 16 MFMAs. The first runs the
-// MFMAs of k-substep 0 with the operand reads of substep 1 interleaved; the
-// second, after the stage barrier, runs those of substep 1 with the reads of
-// the next step's substep 0 and the direct loads of a later stage interleaved.
+// Each k-step is one scheduling region of 16 MFMAs per k-substep. The MFMAs
+// of a substep run with the operand reads of the next one interleaved; in
+// the last region, after the stage barrier, with the reads of the next
+// step's first substep and the NL direct loads of the stage NST steps ahead.
 #define DSPARK_BIG_SCHED_A()                                                               \
   do {                                                                                     \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
@@ -302,24 +328,18 @@ DSPARK_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 <<
     }                                                                                      \
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                     \
   } while (0)
-#define DSPARK_BIG_SCHED_B()                                                               \
+#define DSPARK_BIG_SCHED_ISSUE(NL)                                                         \
   do {                                                                                     \
     _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x010, (NL) / 8, 0);                            \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                     \
   } while (0)
-
-// Two floats rounded to bf16 and packed low, high into one dword.
-DSPARK_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(lo)) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(hi)) << 16);
-}
 
 // 4x4 dword transpose among the 4 lanes of a DPP quad: afterwards a[m] of
 // lane k is the a[k] that lane m held. Two exchange stages, lane ^ 2 then
@@ -340,12 +360,13 @@ DSPARK_DEV void transpose4_quad(uint32_t (&a)[4], int k) {
   a[3] = even ? w1 : t3;
 }
 
-template <class Epi, int HD>
+template <class Epi, int HD, int BK>
 __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
                                                        int MR, int N, int K, int k_per_split, Epi epi) {
   // the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
   // so the compiler's tracking of direct LDS loads sees a single target
-  __shared__ __attribute__((aligned(16))) char smem[BG_NST * BG_STAGE + (Epi::kSwap ? BG_M * 4 : 0)];
+  using C = BigCfg<BK>;
+  __shared__ __attribute__((aligned(16))) char smem[BG_LDS + (Epi::kSwap ? BG_M * 4 : 0)];
   const int tiles_m = (MR + BG_M - 1) / BG_M;
   const int tiles_n = N / BG_N;
   const int ntiles = tiles_m * tiles_n;
@@ -366,7 +387,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   const int m0 = tm * BG_M, n0 = tn * BG_N;
   const int kbeg = z * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
-  const int nsteps = kend > kbeg ? (kend - kbeg) / BG_K : 0;
+  const int nsteps = kend > kbeg ? (kend - kbeg) / BK : 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
   const int wm = wave >> 1, wn = wave & 1;
@@ -381,44 +402,44 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
     if (lane == i && i < a.nseg) my_seg = reinterpret_cast<uint64_t>(a.seg[i]);
   const uint32_t seg_lo = (uint32_t)my_seg, seg_hi = (uint32_t)(my_seg >> 32);
 
-  // ---- direct global -> LDS loads of one stage (4 A + 4 B per thread).
-  // Each lane's byte offsets from the stage's scalar base addresses are
-  // fixed for the whole tile, so a load is one instruction on a scalar base
-  // and a 32-bit lane offset (the host guarantees the offsets fit), and the
-  // LDS destinations are scalar values.
-  const int rl = lane >> 2, slot = lane & 3;
-  uint32_t aoff[4], boff[4];
+  // ---- direct global -> LDS loads of one stage (LPO for A, LPO for B per
+  // thread). A wave's load instruction fills RPI LDS rows: lane l takes row
+  // l / CPR and slot l % CPR. Each lane's byte offsets from the stage's scalar
+  // base addresses are fixed for the whole tile, so a load is one
+  // instruction on a scalar base and a 32-bit lane offset (the host
+  // guarantees the offsets fit), and the LDS destinations are scalar values.
+  const int rl = lane / C::CPR, slot = lane % C::CPR;
+  uint32_t aoff[C::LPO], boff[C::LPO];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = i * 64 + wave * 16 + rl;
-    const int ch = slot ^ swz64_f(row);
+  for (int i = 0; i < C::LPO; ++i) {
+    const int row = (i * 4 + wave) * C::RPI + rl;
+    const int ch = slot ^ C::swz_f(row);
     aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(a.ld * 2) + (uint32_t)(ch * 16);
     boff[i] = (uint32_t)(n0 + row) * (uint32_t)(K * 2) + (uint32_t)(ch * 16);
   }
-  auto issue = [&](int step) __attribute__((always_inline)) {
-    const int k0 = kbeg + step * BG_K;
+  auto issue = [&](int step, int stage) __attribute__((always_inline)) {
+    const int k0 = kbeg + step * BK;
     const int sgi = k0 / a.seg_k;
     const int kin = k0 - sgi * a.seg_k;
     const uint64_t ap = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)seg_hi, sgi) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane((int)seg_lo, sgi);
     const char* __restrict__ abase = reinterpret_cast<const char*>(ap) + (int64_t)kin * 2;
     const char* __restrict__ bbase = reinterpret_cast<const char*>(Bt) + (int64_t)k0 * 2;
-    char* base = smem + (step % BG_NST) * BG_STAGE + wave * 16 * 64;
+    char* base = smem + stage * C::STAGE + wave * C::RPI * C::ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(abase + aoff[i], (lds_ptr_t)(base + i * 64 * 64), 16, 0, 0);
+    for (int i = 0; i < C::LPO; ++i)
+      lds_load16(abase + aoff[i], base + i * 4 * C::RPI * C::ROWB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(bbase + boff[i], (lds_ptr_t)(base + BG_M * BG_K * 2 + i * 64 * 64),
-                                       16, 0, 0);
+    for (int i = 0; i < C::LPO; ++i)
+      lds_load16(bbase + boff[i], base + BG_M * C::ROWB + i * 4 * C::RPI * C::ROWB);
   };
-  auto read_ops = [&](int step, int ks, bf16x8 (&av)[4], bf16x8 (&bv)[4]) __attribute__((always_inline)) {
-    const char* As = smem + (step % BG_NST) * BG_STAGE;
-    const char* Bs = As + BG_M * BG_K * 2;
+  auto read_ops = [&](int stage, int ks, bf16x8 (&av)[4], bf16x8 (&bv)[4]) __attribute__((always_inline)) {
+    const char* As = smem + stage * C::STAGE;
+    const char* Bs = As + BG_M * C::ROWB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      av[i] = *reinterpret_cast<const bf16x8*>(As + swz64(wm * 128 + i * 32 + r32, 2 * ks + hi));
-      bv[i] = *reinterpret_cast<const bf16x8*>(Bs + swz64(wn * 128 + i * 32 + r32, 2 * ks + hi));
+      av[i] = *reinterpret_cast<const bf16x8*>(As + C::swz(wm * 128 + i * 32 + r32, 2 * ks + hi));
+      bv[i] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * 128 + i * 32 + r32, 2 * ks + hi));
     }
   };
 
@@ -442,7 +463,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   // Row scales of the K/V epilogue: one direct LDS load per lane (the
   // tile's 256 rows), issued ahead of the stage loads, so they hold no
   // registers through the main loop and are waited for with the first stage.
-  float* rsc_lds = reinterpret_cast<float*>(smem + BG_NST * BG_STAGE);
+  float* rsc_lds = reinterpret_cast<float*>(smem + BG_LDS);
   if constexpr (Epi::kSwap) {
     if (nsteps > 0) {
       const int row = min(m0 + wave * 64 + lane, epi.T - 1);
@@ -450,33 +471,48 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
     }
   }
 
-  // Ring of BG_NST stages (8 direct loads per thread each). All stages are
-  // loaded up front (after the row-scale load, which the first wait covers); the barrier in the middle of step s (everyone has read
-  // stage s, stage s+1 has landed) frees stage s for the load of step
-  // s+BG_NST. Loads past the last step repeat the last one (in bounds, never
-  // read), which keeps every wait count fixed.
+  // Ring of NST stages of LPS direct loads per thread. Steps 0 .. NST-1 are
+  // loaded up front (after the row-scale load, which the first wait covers).
+  // In step s, once every wave has read its last operands of stage s % NST
+  // and stage (s+1) % NST has landed (the barrier), the loads of step s+NST
+  // go into stage s % NST. Near the end those loads repeat the last step
+  // into the freed stage (in bounds, never read), which keeps every wait
+  // count fixed.
   bf16x8 av0[4], bv0[4], av1[4], bv1[4];
-  if (nsteps > 0) {
+  auto run_step = [&](int step, auto last) __attribute__((always_inline)) {
+    const int st = step % C::NST;
 #pragma unroll
-    for (int st = 0; st < BG_NST; ++st) issue(min(st, nsteps - 1));
-    wait_vmcnt<8 * (BG_NST - 1)>();
-    stage_barrier();
-    read_ops(0, 0, av0, bv0);
-    for (int step = 0; step < nsteps - 1; ++step) {
-      read_ops(step, 1, av1, bv1);
-      mfma16(av0, bv0);
+    for (int ks = 1; ks < C::SUB; ++ks) {
+      if (ks & 1) {
+        read_ops(st, ks, av1, bv1);
+        mfma16(av0, bv0);
+      } else {
+        read_ops(st, ks, av0, bv0);
+        mfma16(av1, bv1);
+      }
       DSPARK_BIG_SCHED_A();
-      wait_vmcnt<8 * (BG_NST - 2)>();
+    }
+    // SUB is even: the last substep's operands are in av1 / bv1
+    if constexpr (!decltype(last)::value) {
+      wait_vmcnt<C::LPS * (C::NST - 2)>();
       wait_lgkm0();
       stage_barrier();
-      read_ops(step + 1, 0, av0, bv0);
-      issue(min(step + BG_NST, nsteps - 1));
+      read_ops((step + 1) % C::NST, 0, av0, bv0);
+      issue(min(step + C::NST, nsteps - 1), st);
       mfma16(av1, bv1);
-      DSPARK_BIG_SCHED_B();
+      DSPARK_BIG_SCHED_ISSUE(C::LPS);
+    } else {
+      mfma16(av1, bv1);
     }
-    read_ops(nsteps - 1, 1, av1, bv1);
-    mfma16(av0, bv0);
-    mfma16(av1, bv1);
+  };
+  if (nsteps > 0) {
+#pragma unroll
+    for (int st = 0; st < C::NST; ++st) issue(min(st, nsteps - 1), st);
+    wait_vmcnt<C::LPS * (C::NST - 1)>();
+    stage_barrier();
+    read_ops(0, 0, av0, bv0);
+    for (int step = 0; step < nsteps - 1; ++step) run_step(step, std::false_type{});
+    run_step(nsteps - 1, std::true_type{});
     wait_vmcnt<0>();
   }
 
@@ -555,6 +591,12 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
 }
 
 static int pick_gemm_bm(int M) { return M >= 4096 ? 128 : 64; }
+// k-tile depth of the big-tile kernel per product. Whole-line 64-deep tiles
+// for both: alternating runs on one GPU measured the forward 1-2% faster at
+// T = 2048 and 131072 than with 32-deep tiles (the K/V GEMM gains 3-9%; the
+// fuse GEMM, which streams its taps from HBM, loses up to 4% at T = 131072
+// for the shorter prefetch distance, and gains 5% at T = 2048).
+constexpr int kFuseBK = 64, kKvBK = 64;
 static bool use_big_tiles(int dtype, int64_t M, int N) { return dtype == 1 && N % BG_N == 0 && M >= 512; }
 
 int ctx_gemm_splits(int dtype, int64_t M, int N, int K) {
@@ -564,7 +606,7 @@ int ctx_gemm_splits(int dtype, int64_t M, int N, int K) {
   if (use_big_tiles(dtype, M, N)) {
     tiles = ((M + BG_M - 1) / BG_M) * (N / BG_N);
     target = 256;   // one 128 KiB-LDS workgroup per CU
-    bk = BG_K;
+    bk = kFuseBK;
   } else {
     const int bm = dtype == 1 ? pick_gemm_bm((int)M) : 64;
     const int bn = dtype == 1 ? 128 : 64;
@@ -585,10 +627,10 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
   trace_pre(K_GEMM_CTX, s);
   if (use_big_tiles(dtype, M, N)) {
     EpiPartialBig epi{out, (int64_t)M * N};
-    const int kps = ((K / splits + BG_K - 1) / BG_K) * BG_K;
+    const int kps = ((K / splits + kFuseBK - 1) / kFuseBK) * kFuseBK;
     dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);
-    gemm_big_kernel<EpiPartialBig, 128><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt), M, M,
-                                                             N, K, kps, epi);
+    gemm_big_kernel<EpiPartialBig, 128, kFuseBK><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt), M,
+                                                                      M, N, K, kps, epi);
   } else if (dtype == 1) {
     EpiPartial epi{out, (int64_t)M * N};
     const bf16* B = static_cast<const bf16*>(Bt);
@@ -626,11 +668,11 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
     dim3 grid(((Mrows + BG_M - 1) / BG_M) * (N / BG_N), 1, 1);
     const bf16* B = static_cast<const bf16*>(Bt);
     if (kv.hd == 128)
-      gemm_big_kernel<EpiKVBig<bf16>, 128><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+      gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
     else if (kv.hd == 64)
-      gemm_big_kernel<EpiKVBig<bf16>, 64><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+      gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
     else
-      gemm_big_kernel<EpiKVBig<bf16>, 32><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+      gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
   } else if (dtype == 1) {
     EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
     const bf16* B = static_cast<const bf16*>(Bt);
