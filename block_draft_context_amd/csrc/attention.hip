@@ -19,9 +19,12 @@
 // Q.K^T lane t owns key t and reads its whole key row (hd/E 16-byte vectors,
 // one 1 KiB wave-wide run each, see kv_layout.h). For P.V lane (kg, cp) owns two value
 // columns and R keys per load, so each V load is again one 1 KiB run; the
-// block's probabilities are broadcast through LDS. All arithmetic is float32
-// on the vector ALUs: with gamma <= 16 queries the arithmetic intensity is a
-// few flop per byte, far below the matrix cores'.
+// block's probabilities are broadcast through LDS. All arithmetic runs on the
+// vector ALUs, accumulating in float32: with gamma <= 16 queries the
+// arithmetic intensity is a few flop per byte, far below the matrix cores'.
+// With bf16 storage the long-context kernel multiplies bf16 pairs
+// (v_dot2_f32_bf16), Q and the probabilities rounded to bf16 once; the rest
+// multiplies in float32.
 #include "common.h"
 #include "kernels.h"
 #include "kv_layout.h"
@@ -126,8 +129,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   constexpr int KG = 128 / HD;           // key groups in the P.V lane split
   constexpr int NLD = 64 / (KG * R);     // V loads per 64-key block
 
-  __shared__ __attribute__((aligned(16))) float qs[G][HD];
-  __shared__ __attribute__((aligned(16))) float ps[4][G][64];
+  // bf16 storage multiplies bf16 pairs with v_dot2_f32_bf16 (f32
+  // accumulation): Q and the block's probabilities are rounded to bf16 once,
+  // K and V are used as stored, which halves the vector ALU work that bounds
+  // this kernel. f32 storage keeps f32 products throughout.
+  constexpr bool kDot2 = sizeof(S) == 2;
+  __shared__ __attribute__((aligned(16))) float qs[kDot2 ? 1 : G][HD];
+  __shared__ __attribute__((aligned(16))) float ps[kDot2 ? 1 : 4][G][64];
+  __shared__ __attribute__((aligned(16))) uint32_t qb[kDot2 ? G : 1][HD / 2];   // bf16 pairs
+  __shared__ __attribute__((aligned(16))) uint16_t pb[kDot2 ? 4 : 1][G][64];    // bf16 bits
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
   __shared__ __attribute__((aligned(16))) float red_o[4][G][HD];
@@ -141,9 +151,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int64_t k0 = tr.k0, k1 = tr.k1;
 
   const int d = HD * n_heads;
-  for (int i = tid; i < G * HD; i += 256) {
-    const int j = i / HD, cc = i % HD;
-    qs[j][cc] = Q[(int64_t)(b * G + j) * d + h * HD + cc];
+  if constexpr (kDot2) {
+    for (int i = tid; i < G * HD / 2; i += 256) {
+      const int j = i / (HD / 2), c2 = i % (HD / 2);
+      const float2 q2 = *reinterpret_cast<const float2*>(Q + (int64_t)(b * G + j) * d + h * HD + 2 * c2);
+      qb[j][c2] = pack_bf16x2(q2.x, q2.y);
+    }
+  } else {
+    for (int i = tid; i < G * HD; i += 256) {
+      const int j = i / HD, cc = i % HD;
+      qs[j][cc] = Q[(int64_t)(b * G + j) * d + h * HD + cc];
+    }
   }
   __syncthreads();
 
@@ -191,19 +209,31 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       float s[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) s[j] = 0.f;
+      if constexpr (kDot2) {
+        // kreg[i] dword w holds dims 8i + 2w, 8i + 2w + 1 of this lane's key
 #pragma unroll
-      for (int i = 0; i < NKV; ++i) {
-        float kf[E];
-        Vec16<S>::unpack(kreg[i], kf);
+        for (int i = 0; i < NKV; ++i)
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
+          for (int j = 0; j < G; ++j) {
+            const u32x4 q4 = *reinterpret_cast<const u32x4*>(&qb[j][i * 4]);
 #pragma unroll
-          for (int e = 0; e < E; e += 4) {
-            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qs[j][i * E + e]);
-            s[j] = fmaf(q4[0], kf[e], s[j]);
-            s[j] = fmaf(q4[1], kf[e + 1], s[j]);
-            s[j] = fmaf(q4[2], kf[e + 2], s[j]);
-            s[j] = fmaf(q4[3], kf[e + 3], s[j]);
+            for (int w = 0; w < 4; ++w) s[j] = dot2_bf16(kreg[i][w], q4[w], s[j]);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NKV; ++i) {
+          float kf[E];
+          Vec16<S>::unpack(kreg[i], kf);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+              const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qs[j][i * E + e]);
+              s[j] = fmaf(q4[0], kf[e], s[j]);
+              s[j] = fmaf(q4[1], kf[e + 1], s[j]);
+              s[j] = fmaf(q4[2], kf[e + 2], s[j]);
+              s[j] = fmaf(q4[3], kf[e + 3], s[j]);
+            }
           }
         }
       }
@@ -221,31 +251,56 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
         o[j][0] *= alpha;
         o[j][1] *= alpha;
         m_run[j] = mn;
-        ps[wave][j][lane] = p;
+        if constexpr (kDot2)
+          pb[wave][j][lane] = __builtin_bit_cast(uint16_t, from_f32<bf16>(p));
+        else
+          ps[wave][j][lane] = p;
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // ---- P.V: lane owns columns 2cp, 2cp+1 and R keys per vector
+      if constexpr (kDot2) {
 #pragma unroll
-      for (int ld = 0; ld < NLD; ++ld) {
-        float vf[E];
-        Vec16<S>::unpack(vreg[ld], vf);
-        const int kb = ld * KG * R + kg * R;   // first key of this vector
+        for (int ld = 0; ld < NLD; ++ld) {
+          // vreg dword r = (column 2cp, column 2cp+1) of key kb + r; regroup
+          // into key pairs per column for the dot products
+          const u32x4 v = vreg[ld];
+          const uint32_t c0k01 = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+          const uint32_t c1k01 = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+          const uint32_t c0k23 = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+          const uint32_t c1k23 = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+          const int kb = ld * KG * R + kg * R;   // first key of this vector
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-          float pr[R];
-          if constexpr (R == 4) {
-            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&ps[wave][j][kb]);
-            pr[0] = p4[0]; pr[1] = p4[1]; pr[2] = p4[2]; pr[3] = p4[3];
-          } else {
-#pragma unroll
-            for (int r = 0; r < R; ++r) pr[r] = ps[wave][j][kb + r];
+          for (int j = 0; j < G; ++j) {
+            const uint2 pp = *reinterpret_cast<const uint2*>(&pb[wave][j][kb]);
+            o[j][0] = dot2_bf16(c0k01, pp.x, o[j][0]);
+            o[j][0] = dot2_bf16(c0k23, pp.y, o[j][0]);
+            o[j][1] = dot2_bf16(c1k01, pp.x, o[j][1]);
+            o[j][1] = dot2_bf16(c1k23, pp.y, o[j][1]);
           }
+        }
+      } else {
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            o[j][0] = fmaf(pr[r], vf[2 * r], o[j][0]);
-            o[j][1] = fmaf(pr[r], vf[2 * r + 1], o[j][1]);
+        for (int ld = 0; ld < NLD; ++ld) {
+          float vf[E];
+          Vec16<S>::unpack(vreg[ld], vf);
+          const int kb = ld * KG * R + kg * R;   // first key of this vector
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            float pr[R];
+            if constexpr (R == 4) {
+              const f32x4 p4 = *reinterpret_cast<const f32x4*>(&ps[wave][j][kb]);
+              pr[0] = p4[0]; pr[1] = p4[1]; pr[2] = p4[2]; pr[3] = p4[3];
+            } else {
+#pragma unroll
+              for (int r = 0; r < R; ++r) pr[r] = ps[wave][j][kb + r];
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              o[j][0] = fmaf(pr[r], vf[2 * r], o[j][0]);
+              o[j][1] = fmaf(pr[r], vf[2 * r + 1], o[j][1]);
+            }
           }
         }
       }
