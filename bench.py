@@ -100,6 +100,9 @@ def write_traffic(fetch_csv, write_csv, workload, copy_bytes):
     import statistics
 
     def per_kind(path, counter):
+        # median per kernel name, summed over the names of a kind: one call of
+        # a kind may launch two kernels (the K/V product's 256x256 and 128x128
+        # tiles)
         vals = {}
         with open(path) as f:
             for r in csv.DictReader(f):
@@ -109,8 +112,8 @@ def write_traffic(fetch_csv, write_csv, workload, copy_bytes):
                 kind = CALIBRATION_KERNEL if CALIBRATION_KERNEL in name else next(
                     (k for sub, k in PMC_KINDS if sub in name), None)
                 if kind:
-                    vals.setdefault(kind, []).append(float(r["Counter_Value"]) * 1024.0)
-        return {k: statistics.median(v) for k, v in vals.items()}
+                    vals.setdefault(kind, {}).setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(statistics.median(v) for v in names.values()) for k, names in vals.items()}
 
     fetch = per_kind(fetch_csv, "FETCH_SIZE")
     write = per_kind(write_csv, "WRITE_SIZE")

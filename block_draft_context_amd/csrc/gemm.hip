@@ -248,20 +248,26 @@ __global__ __launch_bounds__(256) void gemm_f32(ASegs a, BMats b, int M, int MR,
 // one run. Lane l of a load instruction lands at LDS base + 16 l, so each lane
 // fetches the global chunk that its (swizzled) LDS slot stands for.
 // ---------------------------------------------------------------------------
-constexpr int BG_M = 256, BG_N = 256;
+constexpr int BG_M = 256, BG_N = 256;                 // the full tile (WT = 4)
 constexpr int BG_LDS = 128 * 1024;                    // the stage ring
 
-template <int BK>
+// BK: k depth of a stage; WT: 32x32 MFMA blocks per wave along each side, so
+// a wave owns a (32 WT)^2 sub-tile and the 2x2 waves a TM x TM tile.
+template <int BK, int WT = 4>
 struct BigCfg {
   static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(WT == 2 || WT == 4, "WT");
+  static constexpr int TM = 64 * WT;                  // tile rows = tile columns
   static constexpr int ROWB = BK * 2;                 // bytes per LDS row
-  static constexpr int STAGE = (BG_M + BG_N) * ROWB;  // bytes per stage
+  static constexpr int STAGE = 2 * TM * ROWB;         // bytes per stage
   static constexpr int NST = BG_LDS / STAGE;          // stages in the ring
   static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                // rows per load instruction
-  static constexpr int LPO = BG_M / (4 * RPI);        // load instructions per operand
+  static constexpr int LPO = TM / (4 * RPI);          // load instructions per operand
   static constexpr int LPS = 2 * LPO;                 // per stage
   static constexpr int SUB = BK / 16;                 // MFMA k-substeps per step
+  static constexpr int NR = 2 * WT;                   // operand reads per substep
+  static constexpr int NM = WT * WT;                  // MFMAs per substep
   // Chunk c of row r sits in slot c ^ f(r). An MFMA operand read has lanes
   // 16g .. 16g+15 read one chunk of 16 consecutive rows; LDS serves a
   // ds_read_b128 in groups of 16 lanes over 64 four-byte banks, and row r's
@@ -296,6 +302,7 @@ struct EpiKVBig {              // all layers' K/V, row scale, attention layout
   const float* rinv;
   int64_t Tpad;
   int T, d, hd, n_heads;
+  int n_base;                  // column of the stacked K/V where this launch's columns start
   static constexpr bool kStaged = true;
   static constexpr bool kSwap = true;     // accumulate C^T: a lane holds one row
 };
@@ -316,29 +323,29 @@ DSPARK_DEV void wait_vmcnt() {
 }
 DSPARK_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-// Each k-step is one scheduling region of 16 MFMAs per k-substep. The MFMAs
-// of a substep run with the operand reads of the next one interleaved; in
+// Each k-step is one scheduling region per k-substep (NM MFMAs). The MFMAs
+// of a substep run with the NR operand reads of the next one interleaved; in
 // the last region, after the stage barrier, with the reads of the next
 // step's first substep and the NL direct loads of the stage NST steps ahead.
-#define DSPARK_BIG_SCHED_A()                                                               \
+#define DSPARK_BIG_SCHED_A(NR, NM)                                                         \
   do {                                                                                     \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
+    _Pragma("unroll") for (int q = 0; q < (NR); ++q) {                                     \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                     \
+    __builtin_amdgcn_sched_group_barrier(0x008, (NM) - (NR), 0);                           \
   } while (0)
-#define DSPARK_BIG_SCHED_ISSUE(NL)                                                         \
+#define DSPARK_BIG_SCHED_ISSUE(NR, NM, NL)                                                 \
   do {                                                                                     \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                   \
+    _Pragma("unroll") for (int q = 0; q < (NM) / 4; ++q) {                                 \
+      __builtin_amdgcn_sched_group_barrier(0x100, (NR) / ((NM) / 4), 0);                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                        \
-      __builtin_amdgcn_sched_group_barrier(0x010, (NL) / 8, 0);                            \
+    _Pragma("unroll") for (int q = 0; q < (NM) / 2; ++q) {                                 \
+      __builtin_amdgcn_sched_group_barrier(0x010, (NL) / ((NM) / 2), 0);                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                     \
+    __builtin_amdgcn_sched_group_barrier(0x008, (NM) / 4, 0);                              \
   } while (0)
 
 // 4x4 dword transpose among the 4 lanes of a DPP quad: afterwards a[m] of
@@ -360,15 +367,16 @@ DSPARK_DEV void transpose4_quad(uint32_t (&a)[4], int k) {
   a[3] = even ? w1 : t3;
 }
 
-template <class Epi, int HD, int BK>
+template <class Epi, int HD, int BK, int WT>
 __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
                                                        int MR, int N, int K, int k_per_split, Epi epi) {
   // the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
   // so the compiler's tracking of direct LDS loads sees a single target
-  using C = BigCfg<BK>;
-  __shared__ __attribute__((aligned(16))) char smem[BG_LDS + (Epi::kSwap ? BG_M * 4 : 0)];
-  const int tiles_m = (MR + BG_M - 1) / BG_M;
-  const int tiles_n = N / BG_N;
+  using C = BigCfg<BK, WT>;
+  constexpr int TM = C::TM, WS = TM / 2;   // tile side, wave sub-tile side
+  __shared__ __attribute__((aligned(16))) char smem[BG_LDS + (Epi::kSwap ? TM * 4 : 0)];
+  const int tiles_m = (MR + TM - 1) / TM;
+  const int tiles_n = N / TM;
   const int ntiles = tiles_m * tiles_n;
   // Work items (split z, tile) are dealt to the 8 XCDs (workgroup i runs on
   // XCD i % 8) in contiguous runs, z-major, so an XCD owns whole K slices;
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   const int grp = t / gsize, first_m = grp * G;
   const int gm = min(tiles_m - first_m, G);
   const int tm = first_m + (t % gsize) % gm, tn = (t % gsize) / gm;
-  const int m0 = tm * BG_M, n0 = tn * BG_N;
+  const int m0 = tm * TM, n0 = tn * TM;
   const int kbeg = z * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
   const int nsteps = kend > kbeg ? (kend - kbeg) / BK : 0;
@@ -431,41 +439,42 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
       lds_load16(abase + aoff[i], base + i * 4 * C::RPI * C::ROWB);
 #pragma unroll
     for (int i = 0; i < C::LPO; ++i)
-      lds_load16(bbase + boff[i], base + BG_M * C::ROWB + i * 4 * C::RPI * C::ROWB);
+      lds_load16(bbase + boff[i], base + TM * C::ROWB + i * 4 * C::RPI * C::ROWB);
   };
-  auto read_ops = [&](int stage, int ks, bf16x8 (&av)[4], bf16x8 (&bv)[4]) __attribute__((always_inline)) {
+  auto read_ops = [&](int stage, int ks, bf16x8 (&av)[WT], bf16x8 (&bv)[WT]) __attribute__((always_inline)) {
     const char* As = smem + stage * C::STAGE;
-    const char* Bs = As + BG_M * C::ROWB;
+    const char* Bs = As + TM * C::ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = *reinterpret_cast<const bf16x8*>(As + C::swz(wm * 128 + i * 32 + r32, 2 * ks + hi));
-      bv[i] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * 128 + i * 32 + r32, 2 * ks + hi));
+    for (int i = 0; i < WT; ++i) {
+      av[i] = *reinterpret_cast<const bf16x8*>(As + C::swz(wm * WS + i * 32 + r32, 2 * ks + hi));
+      bv[i] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * WS + i * 32 + r32, 2 * ks + hi));
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[WT][WT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto mfma16 = [&](const bf16x8 (&av)[4], const bf16x8 (&bv)[4]) __attribute__((always_inline)) {
+  auto mfma16 = [&](const bf16x8 (&av)[WT], const bf16x8 (&bv)[WT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WT; ++j)
         acc[i][j] = Epi::kSwap
                         ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0)
                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
-  // Row scales of the K/V epilogue: one direct LDS load per lane (the
-  // tile's 256 rows), issued ahead of the stage loads, so they hold no
-  // registers through the main loop and are waited for with the first stage.
+  // Row scales of the K/V epilogue: one direct LDS load per lane of the
+  // first TM / 64 waves (the tile's TM rows), issued ahead of the stage
+  // loads, so they hold no registers through the main loop and are waited
+  // for with the first stage.
   float* rsc_lds = reinterpret_cast<float*>(smem + BG_LDS);
   if constexpr (Epi::kSwap) {
-    if (nsteps > 0) {
+    if (nsteps > 0 && wave < TM / 64) {
       const int row = min(m0 + wave * 64 + lane, epi.T - 1);
       __builtin_amdgcn_global_load_lds(epi.rinv + row, (lds_ptr_t)(rsc_lds + wave * 64), 4, 0, 0);
     }
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   // go into stage s % NST. Near the end those loads repeat the last step
   // into the freed stage (in bounds, never read), which keeps every wait
   // count fixed.
-  bf16x8 av0[4], bv0[4], av1[4], bv1[4];
+  bf16x8 av0[WT], bv0[WT], av1[WT], bv1[WT];
   auto run_step = [&](int step, auto last) __attribute__((always_inline)) {
     const int st = step % C::NST;
 #pragma unroll
@@ -490,7 +499,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
         read_ops(st, ks, av0, bv0);
         mfma16(av1, bv1);
       }
-      DSPARK_BIG_SCHED_A();
+      DSPARK_BIG_SCHED_A(C::NR, C::NM);
     }
     // SUB is even: the last substep's operands are in av1 / bv1
     if constexpr (!decltype(last)::value) {
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
       read_ops((step + 1) % C::NST, 0, av0, bv0);
       issue(min(step + C::NST, nsteps - 1), st);
       mfma16(av1, bv1);
-      DSPARK_BIG_SCHED_ISSUE(C::LPS);
+      DSPARK_BIG_SCHED_ISSUE(C::NR, C::NM, C::LPS);
     } else {
       mfma16(av1, bv1);
     }
@@ -517,21 +526,21 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   }
 
   if constexpr (!Epi::kSwap) {
-    // accumulator (i, j, r) of this lane: tile row wm*128 + i*32 + 8*(r/4) +
-    // 4*(lane/32) + r%4, tile column wn*128 + j*32 + lane%32
+    // accumulator (i, j, r) of this lane: tile row wm*WS + i*32 + 8*(r/4) +
+    // 4*(lane/32) + r%4, tile column wn*WS + j*32 + lane%32
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WT; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+          const int row = m0 + wm * WS + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * WS + j * 32 + (lane & 31);
           if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
         }
   } else {
     // Transposed accumulators: (i, j, r) of this lane is tile row (token)
-    // wm*128 + i*32 + lane%32 and tile column wn*128 + j*32 + 8*(r/4) +
+    // wm*WS + i*32 + lane%32 and tile column wn*WS + j*32 + 8*(r/4) +
     // 4*(lane/32) + r%4. After the row scale and rounding, each 32x32 block
     // becomes 16-byte vectors of the attention layout with lane exchanges
     // only: K (one token x 8 columns) pairs lane l with l^32, V (4 tokens x 2
@@ -539,17 +548,17 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
     using S = std::remove_pointer_t<decltype(epi.base)>;
     using L = KVLayout<S>;
     static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
-    const int nw = n0 + wn * 128;     // the wave's 128 columns lie in one K or V block
+    const int nw = epi.n_base + n0 + wn * WS;   // the wave's WS columns lie in one K or V block
     const int layer = nw / (2 * epi.d);
     const int kv = (nw / epi.d) & 1;
     const int k4 = lane & 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tb = (int64_t)m0 + wm * 128 + i * 32;
+    for (int i = 0; i < WT; ++i) {
+      const int64_t tb = (int64_t)m0 + wm * WS + i * 32;
       // padding rows (T <= row < Tpad) are written as zeros
-      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[wm * 128 + i * 32 + r32] : 0.f;
+      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[wm * WS + i * 32 + r32] : 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WT; ++j) {
         const int w = (nw + j * 32) % epi.d;
         const int head = w / HD, c0 = w % HD;
         S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
@@ -599,6 +608,25 @@ static int pick_gemm_bm(int M) { return M >= 4096 ? 128 : 64; }
 constexpr int kFuseBK = 64, kKvBK = 64;
 static bool use_big_tiles(int dtype, int64_t M, int N) { return dtype == 1 && N % BG_N == 0 && M >= 512; }
 
+// Column tiles of the K/V product done with 256x256 tiles; the rest of the
+// columns go to 128x128 tiles of the same kernel (a second launch). With one
+// 128 KiB workgroup per CU the big tiles run in rounds of kCUs; when the last
+// round would be partly filled, its columns as four times as many 128x128
+// tiles (each about half a big tile's time, at their lower operand reuse)
+// finish sooner: at T = 2048 and 5 layers of d = 1024, 320 big tiles take
+// two rounds, 256 big tiles plus 256 small ones about one and a half.
+constexpr int kCUs = 256;
+static int kv_big_columns(int Mrows, int N) {
+  const int64_t tm = (Mrows + BG_M - 1) / BG_M, tn = N / BG_N, total = tm * tn;
+  const int64_t whole = (total / kCUs) * kCUs;
+  if (whole == 0 || whole == total) return (int)tn;
+  const int64_t nb = whole / tm;                                  // big column tiles
+  const int64_t small = ((Mrows + 127) / 128) * ((tn - nb) * 2);  // 128x128 tiles
+  const int64_t cost_big = 2 * ((total + kCUs - 1) / kCUs);       // in half big-tile rounds
+  const int64_t cost_split = 2 * ((tm * nb + kCUs - 1) / kCUs) + (small + kCUs - 1) / kCUs;
+  return cost_split < cost_big ? (int)nb : (int)tn;
+}
+
 int ctx_gemm_splits(int dtype, int64_t M, int N, int K) {
   if (M <= 0) return 1;
   int64_t tiles, target;
@@ -629,8 +657,8 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
     EpiPartialBig epi{out, (int64_t)M * N};
     const int kps = ((K / splits + kFuseBK - 1) / kFuseBK) * kFuseBK;
     dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);
-    gemm_big_kernel<EpiPartialBig, 128, kFuseBK><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt), M,
-                                                                      M, N, K, kps, epi);
+    gemm_big_kernel<EpiPartialBig, 128, kFuseBK, 4><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt),
+                                                                         M, M, N, K, kps, epi);
   } else if (dtype == 1) {
     EpiPartial epi{out, (int64_t)M * N};
     const bf16* B = static_cast<const bf16*>(Bt);
@@ -664,15 +692,31 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
   const int Mrows = (int)kv.Tpad;  // rows T..Tpad-1 are written as zeros
   trace_pre(K_GEMM_KV, s);
   if (use_big_tiles(dtype, M, N)) {
-    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
-    dim3 grid(((Mrows + BG_M - 1) / BG_M) * (N / BG_N), 1, 1);
     const bf16* B = static_cast<const bf16*>(Bt);
-    if (kv.hd == 128)
-      gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
-    else if (kv.hd == 64)
-      gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
-    else
-      gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    const int nb = kv_big_columns(Mrows, N);
+    if (nb > 0) {   // columns [0, nb * 256): 256x256 tiles
+      EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, 0};
+      dim3 grid(((Mrows + BG_M - 1) / BG_M) * nb, 1, 1);
+      const int Nb = nb * BG_N;
+      if (kv.hd == 128)
+        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, Nb, d, d, epi);
+      else if (kv.hd == 64)
+        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, Nb, d, d, epi);
+      else
+        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, Nb, d, d, epi);
+    }
+    if (nb * BG_N < N) {   // the remaining columns: 128x128 tiles
+      const int n_base = nb * BG_N, Nq = N - n_base;
+      EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, n_base};
+      dim3 grid(((Mrows + 127) / 128) * (Nq / 128), 1, 1);
+      const bf16* Bq = B + (int64_t)n_base * d;
+      if (kv.hd == 128)
+        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 2><<<grid, 256, 0, s>>>(a, Bq, M, Mrows, Nq, d, d, epi);
+      else if (kv.hd == 64)
+        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 2><<<grid, 256, 0, s>>>(a, Bq, M, Mrows, Nq, d, d, epi);
+      else
+        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 2><<<grid, 256, 0, s>>>(a, Bq, M, Mrows, Nq, d, d, epi);
+    }
   } else if (dtype == 1) {
     EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
     const bf16* B = static_cast<const bf16*>(Bt);
