@@ -67,6 +67,13 @@ CASES = {
     "f32-16seq": dict(name="f2", seed_id=21, A=16, m=1, H=64, d=128, n_heads=4, gamma=5,
                       n_layers=1, ff=2048, dtype="f32",
                       lengths=[20, 3, 0, 64, 1, 100, 50, 9, 77, 0, 12, 64, 65, 8, 31, 40]),
+    # K/V projections whose 256x256 tiles would leave a last round of the 256
+    # CUs partly filled (320 tiles), so its columns go to 128x128 tiles: head
+    # dims 64 and 32 (the full-size T = 2048 workload covers 128)
+    "bf16-hd64-kv-split": dict(name="b11", seed_id=23, A=1, m=1, H=64, d=512, n_heads=8, gamma=5,
+                               n_layers=10, ff=1024, dtype="bf16", lengths=[2048]),
+    "bf16-hd32-kv-split": dict(name="b12", seed_id=24, A=2, m=1, H=64, d=256, n_heads=8, gamma=3,
+                               n_layers=10, ff=512, dtype="bf16", lengths=[2500, 1596]),
     # the most block rows a call takes, A * gamma = 1024 (128 eight-row passes
     # of the block GEMMs), over short ragged contexts with empty ones
     "bf16-max-rows": dict(name="b10", seed_id=22, A=64, m=1, H=64, d=128, n_heads=4, gamma=16,
