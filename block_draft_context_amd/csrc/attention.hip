@@ -86,7 +86,9 @@ int attention_chunk(const int32_t* cu_host, int A, int n_heads) {
 // so the K/V loads need no dependent memory access first.
 struct TileRange {
   int b;
-  int64_t k0, k1;
+  int64_t k0, k1;   // the tile's chunk of keys
+  int64_t s0, s1;   // the sequence's keys
+  int c, nt;        // the tile's index among its sequence's nt tiles
 };
 DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restrict__ cu,
                            const int32_t* __restrict__ prefix, int chunk, int total_tiles,
@@ -96,6 +98,10 @@ DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restric
     r.b = 0;
     r.k0 = min(T1, (int64_t)tile * chunk);
     r.k1 = min(T1, r.k0 + chunk);
+    r.s0 = 0;
+    r.s1 = T1;
+    r.c = tile;
+    r.nt = total_tiles;
     return true;
   }
   if (tile >= prefix[A]) return false;
@@ -110,6 +116,10 @@ DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restric
   const int64_t kseq0 = cu[lo], kseq1 = cu[lo + 1];
   r.k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
   r.k1 = min(kseq1, r.k0 + chunk);
+  r.s0 = kseq0;
+  r.s1 = kseq1;
+  r.c = c;
+  r.nt = prefix[lo + 1] - prefix[lo];
   return true;
 }
 
@@ -148,7 +158,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   TileRange tr;
   if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, tr)) return;
   const int b = tr.b;
-  const int64_t k0 = tr.k0, k1 = tr.k1;
+  // the sequence's keys; this tile owns every nt-th of its 64-key blocks
+  const int64_t k0 = tr.s0, k1 = tr.s1;
 
   const int d = HD * n_heads;
   if constexpr (kDot2) {
@@ -178,16 +189,21 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   const int kg = lane / (HD / 2), cp = lane % (HD / 2);
 
-  // The wave's 64-key blocks are blk0 + wave, +4, ... <= blk1. A block's K
-  // (NKV vectors) and V (NLD vectors) live in registers; the next block's K
-  // is requested as soon as the scores are done and its V as soon as P.V is
-  // done, so each load's latency hides behind the other half's arithmetic.
-  // On the wave's last block the "next" loads repeat that block (in bounds,
-  // unused), which keeps every wait count static.
+  // The sequence's 64-key blocks blk0 .. blk1 are dealt to its nt tiles in
+  // turn, and a tile's to its four waves in turn: wave w of tile c takes
+  // blocks blk0 + c + (w + 4i) nt. The workgroups of one head thus read one
+  // window of consecutive blocks at a time instead of nt separate streams,
+  // which keeps the HBM accesses local. A block's K (NKV vectors) and V (NLD
+  // vectors) live in registers; the next block's K is requested as soon as
+  // the scores are done and its V as soon as P.V is done, so each load's
+  // latency hides behind the other half's arithmetic. On the wave's last
+  // block the "next" loads repeat that block (in bounds, unused), which keeps
+  // every wait count static.
   const int64_t blk0 = k0 >> 6, blk1 = k1 > k0 ? (k1 - 1) >> 6 : blk0 - 1;
-  const int64_t first = blk0 + wave;
+  const int64_t bstep = 4 * (int64_t)tr.nt;
+  const int64_t first = blk0 + tr.c + (int64_t)wave * tr.nt;
   if (first <= blk1) {
-    const int64_t last = first + ((blk1 - first) / 4) * 4;
+    const int64_t last = first + ((blk1 - first) / bstep) * bstep;
     u32x4 kreg[NKV], vreg[NLD];
     auto load_k = [&](int64_t blk) __attribute__((always_inline)) {
       const S* kp = Kh + blk * 64 * HD + lane * E;
@@ -201,8 +217,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     };
     load_k(first);
     load_v(first);
-    for (int64_t blk = first; blk <= last; blk += 4) {
-      const int64_t nxt = min(blk + 4, last);
+    for (int64_t blk = first; blk <= last; blk += bstep) {
+      const int64_t nxt = min(blk + bstep, last);
       // ---- scores: lane owns key blk*64 + lane
       const int64_t key = blk * 64 + lane;
       const bool valid = key >= k0 && key < k1;
