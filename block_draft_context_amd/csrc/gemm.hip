@@ -367,14 +367,13 @@ DSPARK_DEV void transpose4_quad(uint32_t (&a)[4], int k) {
   a[3] = even ? w1 : t3;
 }
 
+// The body of one big-tile workgroup: work item `logical` of `total` (split
+// z, tile), with `smem` the stage ring followed by the tile's row scales.
 template <class Epi, int HD, int BK, int WT>
-__global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
-                                                       int MR, int N, int K, int k_per_split, Epi epi) {
-  // the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
-  // so the compiler's tracking of direct LDS loads sees a single target
+DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const bf16* __restrict__ Bt,
+                              int M, int MR, int N, int K, int k_per_split, Epi epi) {
   using C = BigCfg<BK, WT>;
   constexpr int TM = C::TM, WS = TM / 2;   // tile side, wave sub-tile side
-  __shared__ __attribute__((aligned(16))) char smem[BG_LDS + (Epi::kSwap ? TM * 4 : 0)];
   const int tiles_m = (MR + TM - 1) / TM;
   const int tiles_n = N / TM;
   const int ntiles = tiles_m * tiles_n;
@@ -382,8 +381,6 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   // XCD i % 8) in contiguous runs, z-major, so an XCD owns whole K slices;
   // inside a slice, tiles go in groups of up to 8 m-tiles swept n by n, so
   // the XCD's L2 holds a few A panels while it walks the B panels.
-  const int total = ntiles * (int)gridDim.y;
-  int logical = blockIdx.x + (int)gridDim.x * (int)blockIdx.y;
   if (total % 8 == 0) logical = (logical % 8) * (total / 8) + logical / 8;
   const int z = logical / ntiles;
   const int t = logical % ntiles;
@@ -599,6 +596,39 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __re
   }
 }
 
+// the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
+// so the compiler's tracking of direct LDS loads sees a single target
+template <class Epi, int WT>
+constexpr int big_lds_bytes() { return BG_LDS + (Epi::kSwap ? 64 * WT * 4 : 0); }
+
+template <class Epi, int HD, int BK, int WT>
+__global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                       int MR, int N, int K, int k_per_split, Epi epi) {
+  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, WT>()];
+  const int ntiles = ((MR + 64 * WT - 1) / (64 * WT)) * (N / (64 * WT));
+  gemm_big_body<Epi, HD, BK, WT>(smem, blockIdx.x + (int)gridDim.x * (int)blockIdx.y, ntiles * (int)gridDim.y,
+                                 a, Bt, M, MR, N, K, k_per_split, epi);
+}
+
+// The K/V product with its partly filled last round of 256x256 tiles done as
+// 128x128 tiles, in one grid: workgroups [0, nbig) take the 256x256 tiles of
+// columns [0, nb), the rest the 128x128 tiles of columns [nb, N). The small
+// tiles start as soon as a CU is free, with no launch boundary between.
+template <class Epi, int HD, int BK>
+__global__ __launch_bounds__(256) void gemm_kv_tail_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                           int MR, int N, int K, int nb, int nbig, Epi epi) {
+  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, 4>()];
+  const int bid = blockIdx.x;
+  if (bid < nbig) {
+    gemm_big_body<Epi, HD, BK, 4>(smem, bid, nbig, a, Bt, M, MR, nb, K, K, epi);
+  } else {
+    Epi e = epi;
+    e.n_base = epi.n_base + nb;
+    gemm_big_body<Epi, HD, BK, 2>(smem, bid - nbig, (int)gridDim.x - nbig, a, Bt + (int64_t)nb * K, M, MR,
+                                  N - nb, K, K, e);
+  }
+}
+
 static int pick_gemm_bm(int M) { return M >= 4096 ? 128 : 64; }
 // k-tile depth of the big-tile kernel per product. Whole-line 64-deep tiles
 // for both: alternating runs on one GPU measured the forward 1-2% faster at
@@ -609,7 +639,7 @@ constexpr int kFuseBK = 64, kKvBK = 64;
 static bool use_big_tiles(int dtype, int64_t M, int N) { return dtype == 1 && N % BG_N == 0 && M >= 512; }
 
 // Column tiles of the K/V product done with 256x256 tiles; the rest of the
-// columns go to 128x128 tiles of the same kernel (a second launch). With one
+// columns go to 128x128 tiles of the same kernel body, in the same grid. With one
 // 128 KiB workgroup per CU the big tiles run in rounds of kCUs; when the last
 // round would be partly filled, its columns as four times as many 128x128
 // tiles (each about half a big tile's time, at their lower operand reuse)
@@ -694,28 +724,29 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
   if (use_big_tiles(dtype, M, N)) {
     const bf16* B = static_cast<const bf16*>(Bt);
     const int nb = kv_big_columns(Mrows, N);
-    if (nb > 0) {   // columns [0, nb * 256): 256x256 tiles
-      EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, 0};
-      dim3 grid(((Mrows + BG_M - 1) / BG_M) * nb, 1, 1);
-      const int Nb = nb * BG_N;
+    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, 0};
+    const int tm = (Mrows + BG_M - 1) / BG_M;
+    if (nb * BG_N == N) {   // 256x256 tiles only
+      dim3 grid(tm * (N / BG_N), 1, 1);
       if (kv.hd == 128)
-        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, Nb, d, d, epi);
+        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
       else if (kv.hd == 64)
-        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, Nb, d, d, epi);
+        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
       else
-        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, Nb, d, d, epi);
-    }
-    if (nb * BG_N < N) {   // the remaining columns: 128x128 tiles
-      const int n_base = nb * BG_N, Nq = N - n_base;
-      EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, n_base};
-      dim3 grid(((Mrows + 127) / 128) * (Nq / 128), 1, 1);
-      const bf16* Bq = B + (int64_t)n_base * d;
+        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    } else {                // columns [0, nb * 256) in 256x256 tiles, the rest in 128x128 tiles
+      const int Nb = nb * BG_N, nbig = tm * nb;
+      const int nsmall = ((Mrows + 127) / 128) * ((N - Nb) / 128);
+      dim3 grid(nbig + nsmall, 1, 1);
       if (kv.hd == 128)
-        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 2><<<grid, 256, 0, s>>>(a, Bq, M, Mrows, Nq, d, d, epi);
+        gemm_kv_tail_kernel<EpiKVBig<bf16>, 128, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
+                                                                               epi);
       else if (kv.hd == 64)
-        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 2><<<grid, 256, 0, s>>>(a, Bq, M, Mrows, Nq, d, d, epi);
+        gemm_kv_tail_kernel<EpiKVBig<bf16>, 64, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
+                                                                               epi);
       else
-        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 2><<<grid, 256, 0, s>>>(a, Bq, M, Mrows, Nq, d, d, epi);
+        gemm_kv_tail_kernel<EpiKVBig<bf16>, 32, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
+                                                                               epi);
     }
   } else if (dtype == 1) {
     EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
