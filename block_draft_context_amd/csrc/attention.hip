@@ -210,10 +210,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 #pragma unroll
       for (int i = 0; i < NKV; ++i) kreg[i] = ld16(kp + i * 64 * E);
     };
+    // V is read once per layer: non-temporal loads (measured 5% faster per
+    // forward at T = 131072 and on a ragged 16-sequence batch; marking K as
+    // well was faster on the first and slower on the second)
     auto load_v = [&](int64_t blk) __attribute__((always_inline)) {
       const S* vp = Vh + blk * 64 * HD + lane * E;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) vreg[i] = ld16(vp + i * 64 * E);
+      for (int i = 0; i < NLD; ++i)
+        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 64 * E));
     };
     load_k(first);
     load_v(first);
