@@ -429,7 +429,8 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
 #pragma unroll
     for (int i = 0; i < NKW; ++i) kreg[bb][i] = ld16(kp + i * 64 * E);
 #pragma unroll
-    for (int i = 0; i < NLW; ++i) vreg[bb][i] = ld16(vp + i * 64 * E);
+    for (int i = 0; i < NLW; ++i)   // V is read once: non-temporal, as in the streaming kernel
+      vreg[bb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 64 * E));
   }
   const int d = HD * n_heads;
   for (int i = tid; i < G * HD; i += 256) {
