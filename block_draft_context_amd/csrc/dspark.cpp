@@ -138,6 +138,16 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   p->Tpad = ((T + 63) / 64) * 64;
   p->hd = dm->d / dm->n_heads;
   p->M = A * dm->gamma;
+  // The context projections address H_ctx (the A operand of the K/V
+  // product) and W_c with 32-bit byte offsets (the taps are checked with
+  // their leading dimension in check_taps).
+  const int64_t kMaxBytes = (int64_t)1 << 32;
+  if (T * dm->d * p->esz >= kMaxBytes)
+    return fail(DSPARK_EUNSUPPORTED, "H_ctx spans %lld bytes (T * d); at most 4 GiB is supported",
+                (long long)(T * dm->d * p->esz));
+  if (op != DSPARK_OP_BLOCK_LAYER && (int64_t)dm->d * dm->m * dm->H * p->esz >= kMaxBytes)
+    return fail(DSPARK_EUNSUPPORTED, "W_c spans %lld bytes (d * m * H); at most 4 GiB is supported",
+                (long long)((int64_t)dm->d * dm->m * dm->H * p->esz));
   const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
   p->ctx_splits = ctx_gemm_splits(dm->dtype, T, d, mH);
   p->chunk = attention_chunk(cu_host, A, dm->n_heads);

@@ -58,7 +58,10 @@
  * - Supported: head_dim = d / n_heads in {32, 64, 128}; 1 <= gamma <= 16;
  *   1 <= m <= 16; 1 <= n_layers <= 16; H a multiple of 64; d a multiple of
  *   128 up to 2048; ff a multiple of 128 up to 16256; A * gamma <= 1024;
- *   each tap spans less than 4 GiB (T * ld_tap elements).
+ *   each tap spans less than 4 GiB (T * ld_tap elements), and so do H_ctx
+ *   (T * d elements) and, for the calls that run Eq 2, W_c (d * m * H
+ *   elements): the context projections address them with 32-bit byte
+ *   offsets. Larger inputs return DSPARK_EUNSUPPORTED.
  */
 #ifndef DSPARK_H
 #define DSPARK_H

@@ -155,6 +155,35 @@ def test_taps_over_4gib_are_rejected(L):
     assert st == L.EUNSUPPORTED and "4 GiB" in lib.dspark_last_error().decode()
 
 
+def test_h_ctx_and_w_c_over_4gib_are_rejected(L):
+    """The context projections address H_ctx and W_c with 32-bit byte
+    offsets; an H_ctx or W_c of 4 GiB or more is refused before anything
+    runs, also where every tap is small."""
+    lib = L.lib()
+    # H = 64, d = 2048: the taps span 1.1e6 * 64 * 2 bytes, H_ctx 1.1e6 * 2048 * 2 > 4 GiB
+    dm = L.Dims(1, 64, 2048, 16, 5, 1, 4096, 1e-6, L.BF16)
+    T = 1100000
+    cu = _cu([0, T])
+    lw = L.LayerWeights(*([0x1000] * 9))
+    st = lib.dspark_block_layer(ctypes.byref(dm), 1, cu, 0x2000, 0x3000, 0x4000, 0x4000,
+                                ctypes.byref(lw), 0x6000, 1 << 50, None)
+    assert st == L.EUNSUPPORTED and "H_ctx" in lib.dspark_last_error().decode()
+    taps = (ctypes.c_void_p * 1)(0x1000)
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps, 64, 0x3000, 0x4000, 0x5000,
+                             0x6000, 1 << 50, None)
+    assert st == L.EUNSUPPORTED and "H_ctx" in lib.dspark_last_error().decode()
+    assert lib.dspark_workspace_size(L.OP_BLOCK_LAYER, ctypes.byref(dm), 1, cu) == 0
+    # W_c = d * m * H = 2048 * 16 * 65536 bf16 elements = 4 GiB, over 64 rows of context
+    dm = L.Dims(16, 65536, 2048, 16, 5, 1, 4096, 1e-6, L.BF16)
+    cu = _cu([0, 64])
+    taps = (ctypes.c_void_p * 16)(*[0x1000] * 16)
+    st = lib.dspark_ctx_fuse(ctypes.byref(dm), 1, cu, 0x2000, taps, 65536, 0x3000, 0x4000, 0x5000,
+                             0x6000, 1 << 50, None)
+    assert st == L.EUNSUPPORTED and "W_c" in lib.dspark_last_error().decode()
+    # the same sizes are fine for a layer, which does not read W_c
+    assert lib.dspark_workspace_size(L.OP_BLOCK_LAYER, ctypes.byref(dm), 1, cu) > 0
+
+
 def test_python_binding_raises_with_message(L):
     import block_draft_context_amd as B
     with pytest.raises(B.DsparkError) as e:
