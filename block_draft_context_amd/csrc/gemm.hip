@@ -251,23 +251,29 @@ __global__ __launch_bounds__(256) void gemm_f32(ASegs a, BMats b, int M, int MR,
 constexpr int BG_M = 256, BG_N = 256;                 // the full tile (WT = 4)
 constexpr int BG_LDS = 128 * 1024;                    // the stage ring
 
-// BK: k depth of a stage; WT: 32x32 MFMA blocks per wave along each side, so
-// a wave owns a (32 WT)^2 sub-tile and the 2x2 waves a TM x TM tile.
-template <int BK, int WT = 4>
+// BK: k depth of a stage; WT: the tile is TM = 64 WT square; NW: waves per
+// workgroup, as 2 x NW/2 (rows x columns), so a wave owns a TM/2 x 2TM/NW
+// sub-tile of FM x FN 32x32 MFMA blocks (WT x WT with 4 waves, one per SIMD;
+// WT x WT/2 with 8 waves, two per SIMD).
+template <int BK, int WT = 4, int NW = 4>
 struct BigCfg {
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(WT == 2 || WT == 4, "WT");
+  static_assert(NW == 4 || NW == 8, "NW");
   static constexpr int TM = 64 * WT;                  // tile rows = tile columns
+  static constexpr int NWN = NW / 2;                  // waves along the columns
+  static constexpr int WSM = TM / 2, WSN = TM / NWN;  // wave sub-tile
+  static constexpr int FM = WSM / 32, FN = WSN / 32;  // MFMA blocks per wave
   static constexpr int ROWB = BK * 2;                 // bytes per LDS row
   static constexpr int STAGE = 2 * TM * ROWB;         // bytes per stage
   static constexpr int NST = BG_LDS / STAGE;          // stages in the ring
   static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                // rows per load instruction
-  static constexpr int LPO = TM / (4 * RPI);          // load instructions per operand
+  static constexpr int LPO = TM / (NW * RPI);         // load instructions per operand
   static constexpr int LPS = 2 * LPO;                 // per stage
   static constexpr int SUB = BK / 16;                 // MFMA k-substeps per step
-  static constexpr int NR = 2 * WT;                   // operand reads per substep
-  static constexpr int NM = WT * WT;                  // MFMAs per substep
+  static constexpr int NR = FM + FN;                  // operand reads per substep
+  static constexpr int NM = FM * FN;                  // MFMAs per substep
   // Chunk c of row r sits in slot c ^ f(r). An MFMA operand read has lanes
   // 16g .. 16g+15 read one chunk of 16 consecutive rows; LDS serves a
   // ds_read_b128 in groups of 16 lanes over 64 four-byte banks, and row r's
@@ -329,23 +335,32 @@ DSPARK_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 <<
 // step's first substep and the NL direct loads of the stage NST steps ahead.
 #define DSPARK_BIG_SCHED_A(NR, NM)                                                         \
   do {                                                                                     \
-    _Pragma("unroll") for (int q = 0; q < (NR); ++q) {                                     \
+    constexpr int kPairs = (NR) < (NM) ? (NR) : (NM);                                     \
+    _Pragma("unroll") for (int q = 0; q < kPairs; ++q) {                                   \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
-    __builtin_amdgcn_sched_group_barrier(0x008, (NM) - (NR), 0);                           \
+    _Pragma("unroll") for (int q = kPairs; q < (NR); ++q)                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+    _Pragma("unroll") for (int q = kPairs; q < (NM); ++q)                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
   } while (0)
+// The first quarter of the MFMAs (at least one) with the operand reads, the
+// next half (at least one) with the direct loads, then the rest.
 #define DSPARK_BIG_SCHED_ISSUE(NR, NM, NL)                                                 \
   do {                                                                                     \
-    _Pragma("unroll") for (int q = 0; q < (NM) / 4; ++q) {                                 \
-      __builtin_amdgcn_sched_group_barrier(0x100, (NR) / ((NM) / 4), 0);                   \
+    constexpr int kQ1 = (NM) / 4 > 0 ? (NM) / 4 : 1;                                       \
+    constexpr int kQ2 = (NM) / 2 > 0 ? (NM) / 2 : 1;                                       \
+    _Pragma("unroll") for (int q = 0; q < kQ1; ++q) {                                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, ((NR) + kQ1 - 1) / kQ1, 0);              \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
-    _Pragma("unroll") for (int q = 0; q < (NM) / 2; ++q) {                                 \
-      __builtin_amdgcn_sched_group_barrier(0x010, (NL) / ((NM) / 2), 0);                   \
+    _Pragma("unroll") for (int q = 0; q < kQ2; ++q) {                                      \
+      __builtin_amdgcn_sched_group_barrier(0x010, ((NL) + kQ2 - 1) / kQ2, 0);              \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
     }                                                                                      \
-    __builtin_amdgcn_sched_group_barrier(0x008, (NM) / 4, 0);                              \
+    _Pragma("unroll") for (int q = kQ1 + kQ2; q < (NM); ++q)                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
   } while (0)
 
 // 4x4 dword transpose among the 4 lanes of a DPP quad: afterwards a[m] of
@@ -369,11 +384,11 @@ DSPARK_DEV void transpose4_quad(uint32_t (&a)[4], int k) {
 
 // The body of one big-tile workgroup: work item `logical` of `total` (split
 // z, tile), with `smem` the stage ring followed by the tile's row scales.
-template <class Epi, int HD, int BK, int WT>
+template <class Epi, int HD, int BK, int WT, int NW>
 DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const bf16* __restrict__ Bt,
                               int M, int MR, int N, int K, int k_per_split, Epi epi) {
-  using C = BigCfg<BK, WT>;
-  constexpr int TM = C::TM, WS = TM / 2;   // tile side, wave sub-tile side
+  using C = BigCfg<BK, WT, NW>;
+  constexpr int TM = C::TM, WSM = C::WSM, WSN = C::WSN, FM = C::FM, FN = C::FN;
   const int tiles_m = (MR + TM - 1) / TM;
   const int tiles_n = N / TM;
   const int ntiles = tiles_m * tiles_n;
@@ -395,7 +410,7 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   const int nsteps = kend > kbeg ? (kend - kbeg) / BK : 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::NWN, wn = wave % C::NWN;
   const int r32 = lane & 31, hi = lane >> 5;
 
   // lane i holds the address of A segment i; the loop reads it with a lane
@@ -417,7 +432,7 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   uint32_t aoff[C::LPO], boff[C::LPO];
 #pragma unroll
   for (int i = 0; i < C::LPO; ++i) {
-    const int row = (i * 4 + wave) * C::RPI + rl;
+    const int row = (i * NW + wave) * C::RPI + rl;
     const int ch = slot ^ C::swz_f(row);
     aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(a.ld * 2) + (uint32_t)(ch * 16);
     boff[i] = (uint32_t)(n0 + row) * (uint32_t)(K * 2) + (uint32_t)(ch * 16);
@@ -433,33 +448,34 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
     char* base = smem + stage * C::STAGE + wave * C::RPI * C::ROWB;
 #pragma unroll
     for (int i = 0; i < C::LPO; ++i)
-      lds_load16(abase + aoff[i], base + i * 4 * C::RPI * C::ROWB);
+      lds_load16(abase + aoff[i], base + i * NW * C::RPI * C::ROWB);
 #pragma unroll
     for (int i = 0; i < C::LPO; ++i)
-      lds_load16(bbase + boff[i], base + TM * C::ROWB + i * 4 * C::RPI * C::ROWB);
+      lds_load16(bbase + boff[i], base + TM * C::ROWB + i * NW * C::RPI * C::ROWB);
   };
-  auto read_ops = [&](int stage, int ks, bf16x8 (&av)[WT], bf16x8 (&bv)[WT]) __attribute__((always_inline)) {
+  auto read_ops = [&](int stage, int ks, bf16x8 (&av)[FM], bf16x8 (&bv)[FN]) __attribute__((always_inline)) {
     const char* As = smem + stage * C::STAGE;
     const char* Bs = As + TM * C::ROWB;
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
-      av[i] = *reinterpret_cast<const bf16x8*>(As + C::swz(wm * WS + i * 32 + r32, 2 * ks + hi));
-      bv[i] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * WS + i * 32 + r32, 2 * ks + hi));
-    }
+    for (int i = 0; i < FM; ++i)
+      av[i] = *reinterpret_cast<const bf16x8*>(As + C::swz(wm * WSM + i * 32 + r32, 2 * ks + hi));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bv[j] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * WSN + j * 32 + r32, 2 * ks + hi));
   };
 
-  f32x16 acc[WT][WT];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < WT; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < WT; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto mfma16 = [&](const bf16x8 (&av)[WT], const bf16x8 (&bv)[WT]) __attribute__((always_inline)) {
+  auto mfma16 = [&](const bf16x8 (&av)[FM], const bf16x8 (&bv)[FN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < WT; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < WT; ++j)
+      for (int j = 0; j < FN; ++j)
         acc[i][j] = Epi::kSwap
                         ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0)
                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
@@ -484,7 +500,7 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   // go into stage s % NST. Near the end those loads repeat the last step
   // into the freed stage (in bounds, never read), which keeps every wait
   // count fixed.
-  bf16x8 av0[WT], bv0[WT], av1[WT], bv1[WT];
+  bf16x8 av0[FM], bv0[FN], av1[FM], bv1[FN];
   auto run_step = [&](int step, auto last) __attribute__((always_inline)) {
     const int st = step % C::NST;
 #pragma unroll
@@ -523,21 +539,21 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   }
 
   if constexpr (!Epi::kSwap) {
-    // accumulator (i, j, r) of this lane: tile row wm*WS + i*32 + 8*(r/4) +
-    // 4*(lane/32) + r%4, tile column wn*WS + j*32 + lane%32
+    // accumulator (i, j, r) of this lane: tile row wm*WSM + i*32 + 8*(r/4) +
+    // 4*(lane/32) + r%4, tile column wn*WSN + j*32 + lane%32
 #pragma unroll
-    for (int i = 0; i < WT; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < WT; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WS + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * WS + j * 32 + (lane & 31);
+          const int row = m0 + wm * WSM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * WSN + j * 32 + (lane & 31);
           if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
         }
   } else {
     // Transposed accumulators: (i, j, r) of this lane is tile row (token)
-    // wm*WS + i*32 + lane%32 and tile column wn*WS + j*32 + 8*(r/4) +
+    // wm*WSM + i*32 + lane%32 and tile column wn*WSN + j*32 + 8*(r/4) +
     // 4*(lane/32) + r%4. After the row scale and rounding, each 32x32 block
     // becomes 16-byte vectors of the attention layout with lane exchanges
     // only: K (one token x 8 columns) pairs lane l with l^32, V (4 tokens x 2
@@ -545,17 +561,17 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
     using S = std::remove_pointer_t<decltype(epi.base)>;
     using L = KVLayout<S>;
     static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
-    const int nw = epi.n_base + n0 + wn * WS;   // the wave's WS columns lie in one K or V block
+    const int nw = epi.n_base + n0 + wn * WSN;   // the wave's WSN columns lie in one K or V block
     const int layer = nw / (2 * epi.d);
     const int kv = (nw / epi.d) & 1;
     const int k4 = lane & 3;
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
-      const int64_t tb = (int64_t)m0 + wm * WS + i * 32;
+    for (int i = 0; i < FM; ++i) {
+      const int64_t tb = (int64_t)m0 + wm * WSM + i * 32;
       // padding rows (T <= row < Tpad) are written as zeros
-      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[wm * WS + i * 32 + r32] : 0.f;
+      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[wm * WSM + i * 32 + r32] : 0.f;
 #pragma unroll
-      for (int j = 0; j < WT; ++j) {
+      for (int j = 0; j < FN; ++j) {
         const int w = (nw + j * 32) % epi.d;
         const int head = w / HD, c0 = w % HD;
         S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
@@ -601,31 +617,32 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
 template <class Epi, int WT>
 constexpr int big_lds_bytes() { return BG_LDS + (Epi::kSwap ? 64 * WT * 4 : 0); }
 
-template <class Epi, int HD, int BK, int WT>
-__global__ __launch_bounds__(256) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
-                                                       int MR, int N, int K, int k_per_split, Epi epi) {
+template <class Epi, int HD, int BK, int WT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                           int MR, int N, int K, int k_per_split, Epi epi) {
   __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, WT>()];
   const int ntiles = ((MR + 64 * WT - 1) / (64 * WT)) * (N / (64 * WT));
-  gemm_big_body<Epi, HD, BK, WT>(smem, blockIdx.x + (int)gridDim.x * (int)blockIdx.y, ntiles * (int)gridDim.y,
-                                 a, Bt, M, MR, N, K, k_per_split, epi);
+  gemm_big_body<Epi, HD, BK, WT, NW>(smem, blockIdx.x + (int)gridDim.x * (int)blockIdx.y,
+                                     ntiles * (int)gridDim.y, a, Bt, M, MR, N, K, k_per_split, epi);
 }
 
 // The K/V product with its partly filled last round of 256x256 tiles done as
 // 128x128 tiles, in one grid: workgroups [0, nbig) take the 256x256 tiles of
 // columns [0, nb), the rest the 128x128 tiles of columns [nb, N). The small
 // tiles start as soon as a CU is free, with no launch boundary between.
-template <class Epi, int HD, int BK>
-__global__ __launch_bounds__(256) void gemm_kv_tail_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
-                                                           int MR, int N, int K, int nb, int nbig, Epi epi) {
+template <class Epi, int HD, int BK, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_kv_tail_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                               int MR, int N, int K, int nb, int nbig,
+                                                               Epi epi) {
   __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, 4>()];
   const int bid = blockIdx.x;
   if (bid < nbig) {
-    gemm_big_body<Epi, HD, BK, 4>(smem, bid, nbig, a, Bt, M, MR, nb, K, K, epi);
+    gemm_big_body<Epi, HD, BK, 4, NW>(smem, bid, nbig, a, Bt, M, MR, nb, K, K, epi);
   } else {
     Epi e = epi;
     e.n_base = epi.n_base + nb;
-    gemm_big_body<Epi, HD, BK, 2>(smem, bid - nbig, (int)gridDim.x - nbig, a, Bt + (int64_t)nb * K, M, MR,
-                                  N - nb, K, K, e);
+    gemm_big_body<Epi, HD, BK, 2, NW>(smem, bid - nbig, (int)gridDim.x - nbig, a, Bt + (int64_t)nb * K, M,
+                                      MR, N - nb, K, K, e);
   }
 }
 
@@ -636,6 +653,7 @@ static int pick_gemm_bm(int M) { return M >= 4096 ? 128 : 64; }
 // fuse GEMM, which streams its taps from HBM, loses up to 4% at T = 131072
 // for the shorter prefetch distance, and gains 5% at T = 2048).
 constexpr int kFuseBK = 64, kKvBK = 64;
+constexpr int kBigWaves = 8;   // waves per big-tile workgroup
 static bool use_big_tiles(int dtype, int64_t M, int N) { return dtype == 1 && N % BG_N == 0 && M >= 512; }
 
 // Column tiles of the K/V product done with 256x256 tiles; the rest of the
@@ -687,7 +705,7 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
     EpiPartialBig epi{out, (int64_t)M * N};
     const int kps = ((K / splits + kFuseBK - 1) / kFuseBK) * kFuseBK;
     dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);
-    gemm_big_kernel<EpiPartialBig, 128, kFuseBK, 4><<<grid, 256, 0, s>>>(a, static_cast<const bf16*>(Bt),
+    gemm_big_kernel<EpiPartialBig, 128, kFuseBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, static_cast<const bf16*>(Bt),
                                                                          M, M, N, K, kps, epi);
   } else if (dtype == 1) {
     EpiPartial epi{out, (int64_t)M * N};
@@ -729,23 +747,23 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
     if (nb * BG_N == N) {   // 256x256 tiles only
       dim3 grid(tm * (N / BG_N), 1, 1);
       if (kv.hd == 128)
-        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
       else if (kv.hd == 64)
-        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
       else
-        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
     } else {                // columns [0, nb * 256) in 256x256 tiles, the rest in 128x128 tiles
       const int Nb = nb * BG_N, nbig = tm * nb;
       const int nsmall = ((Mrows + 127) / 128) * ((N - Nb) / 128);
       dim3 grid(nbig + nsmall, 1, 1);
       if (kv.hd == 128)
-        gemm_kv_tail_kernel<EpiKVBig<bf16>, 128, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
+        gemm_kv_tail_kernel<EpiKVBig<bf16>, 128, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
                                                                                epi);
       else if (kv.hd == 64)
-        gemm_kv_tail_kernel<EpiKVBig<bf16>, 64, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
+        gemm_kv_tail_kernel<EpiKVBig<bf16>, 64, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
                                                                                epi);
       else
-        gemm_kv_tail_kernel<EpiKVBig<bf16>, 32, kKvBK><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
+        gemm_kv_tail_kernel<EpiKVBig<bf16>, 32, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, Nb, nbig,
                                                                                epi);
     }
   } else if (dtype == 1) {
