@@ -553,6 +553,9 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
           if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
         }
   } else {
+    // The K/V vectors are stored non-temporally: the attention that reads
+    // them later streams about 12% faster (T = 131072 and a ragged batch;
+    // the forward 1-3% faster at T >= 8192, neutral at T = 2048).
     // Transposed accumulators: (i, j, r) of this lane is tile row (token)
     // wm*WSM + i*32 + lane%32 and tile column wn*WSN + j*32 + 8*(r/4) +
     // 4*(lane/32) + r%4. After the row scale and rounding, each 32x32 block
@@ -592,7 +595,8 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
             const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
             const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
             const int g = qq + 2 * hi;
-            if (t < epi.Tpad) *reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)) = v;
+            if (t < epi.Tpad)
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)));
           }
         } else {
           const int64_t t0 = tb + (r32 & ~3);
@@ -605,7 +609,8 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
             transpose4_quad(a, k4);
             const int p = 4 * (2 * set + (k4 >> 1)) + 2 * hi + (k4 & 1);
             const u32x4 v = {a[0], a[1], a[2], a[3]};
-            if (t0 < epi.Tpad) *reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)) = v;
+            if (t0 < epi.Tpad)
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)));
           }
         }
       }
