@@ -416,10 +416,485 @@ def pin_split_combine(O, seed=12):
         assert rel_err(split_combine_attention(Q[0], k, v, chunk), ref) < 1e-13, chunk
 
 
+# ---------------------------------------------------------------------------
+# 5. tanh-GELU (the gated FFN activation of module-dflash.ts, #layer)
+# ---------------------------------------------------------------------------
+
+def pin_gelu_tanh(O):
+    """tanh-GELU against torch's independent implementation (float64,
+    approximate="tanh"), and its closed forms: gelu(0) = 0, gelu(x) -> x for
+    large x and -> 0 for large -x, gelu(x) - gelu(-x) = x (it is x * an odd
+    sigmoid-like factor 0.5 (1 + tanh(.))), slope 1/2 at 0."""
+    import torch
+    import torch.nn.functional as F
+    x = np.linspace(-8.0, 8.0, 2001)
+    ref = F.gelu(torch.as_tensor(x, dtype=torch.float64), approximate="tanh").numpy()
+    assert rel_err(O.gelu_tanh(x), ref) < 1e-14, "gelu vs torch"
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    big = np.array([30.0, 60.0])
+    assert np.all(np.abs(O.gelu_tanh(big) - big) < 1e-12)
+    assert np.all(np.abs(O.gelu_tanh(-big)) < 1e-12)
+    assert np.max(np.abs(O.gelu_tanh(x) - O.gelu_tanh(-x) - x)) < 1e-12, "odd part"
+    h = 1e-6
+    slope = (O.gelu_tanh(np.array([h]))[0] - O.gelu_tanh(np.array([-h]))[0]) / (2 * h)
+    assert abs(slope - 0.5) < 1e-9, slope
+
+
+# ---------------------------------------------------------------------------
+# 6. incremental context (dspark-runtime.js updateContext / store / propose)
+# ---------------------------------------------------------------------------
+
+def _append_in_pieces(O, p, pieces, dtype=np.float64):
+    """Fill a cache through cache_append calls: ``pieces`` is a list of
+    per-sequence row counts, consumed in order from each sequence's rows."""
+    A, d = p["A"], p["d"]
+    cache = O.DraftCache(A, len(p["layers"]), d, dtype=dtype)
+    cu = [int(c) for c in p["cu"]]
+    done = [0] * A
+    for counts in pieces:
+        rows = []
+        cu_new = [0]
+        for b in range(A):
+            r0 = cu[b] + done[b]
+            rows.append((r0, r0 + counts[b]))
+            cu_new.append(cu_new[-1] + counts[b])
+            done[b] += counts[b]
+        taps_new = [np.concatenate([t[r0:r1] for r0, r1 in rows], axis=0) for t in p["taps"]]
+        O.cache_append(cache, taps_new, cu_new, p["w_c"], p["ctx_norm"], p["layers"], p["eps"])
+    assert done == [cu[b + 1] - cu[b] for b in range(A)]
+    return cache
+
+
+def pin_cache_equals_full_context(O, seed=20):
+    """The context is read-only memory that every layer re-projects (the
+    module-dflash.ts header): a cache filled by several appends of any sizes,
+    empty ones included, gives the same draft block as the scalar-loop
+    forward over the whole context."""
+    rs = np.random.default_rng(seed)
+    p = _rand_problem(rs, lengths=[5, 0, 3])
+    cache = _append_in_pieces(O, p, [[2, 0, 0], [0, 0, 3], [3, 0, 0], [0, 0, 0]])
+    assert list(cache.lengths()) == [5, 0, 3]
+    out = O.block_propose(cache, p["block_in"], p["block_pos"], p["layers"], p["out_norm"],
+                          p["n_heads"], p["eps"])
+    _, out_bf = brute_force_forward(p)
+    assert rel_err(out, out_bf) < TIGHT, "incremental vs brute force"
+
+
+def pin_cache_rows_are_row_local(O, seed=21):
+    """Each cached row depends on its own context row only: appending rows
+    one at a time fills the cache with the same keys and values as one
+    append of all of them, and a sequence's rows are unaffected by the rows
+    appended to the other sequences."""
+    rs = np.random.default_rng(seed)
+    p = _rand_problem(rs, lengths=[4, 2], n_layers=2)
+    whole = _append_in_pieces(O, p, [[4, 2]])
+    single = _append_in_pieces(O, p, [[1, 0]] * 4 + [[0, 1]] * 2)
+    for b in range(2):
+        for i in range(2):
+            assert rel_err(single.K[b][i], whole.K[b][i]) < TIGHT
+            assert rel_err(single.V[b][i], whole.V[b][i]) < TIGHT
+    alone = O.DraftCache(1, 2, p["d"])
+    O.cache_append(alone, [t[:4] for t in p["taps"]], [0, 4], p["w_c"], p["ctx_norm"],
+                   p["layers"], p["eps"])
+    assert rel_err(alone.K[0][1], whole.K[0][1]) < TIGHT
+
+
+# ---------------------------------------------------------------------------
+# 7. Markov head, confidence head, greedy loop (module-dflash.ts forwardInfer)
+# ---------------------------------------------------------------------------
+
+def _markov_problem(rs, A=2, G=4, d=6, r=3, V=11):
+    return dict(block=rs.standard_normal((A, G, d)), U=rs.standard_normal((A, G, V)),
+                anchor=rs.integers(0, V, size=A), w1=rs.standard_normal((V, r)),
+                w2=rs.standard_normal((r, V)), cw=rs.standard_normal(d + r) * 0.5, cb=0.3)
+
+
+def _markov_brute(q):
+    """Scalar loops over forwardInfer's per-position steps."""
+    A, G, d = q["block"].shape
+    V, r = q["w1"].shape
+    toks, conf = [], []
+    for b in range(A):
+        prev = int(q["anchor"][b])
+        tb, cb = [], []
+        for k in range(G):
+            e1 = [q["w1"][prev][i] for i in range(r)]
+            lg = [q["U"][b][k][v] + sum(e1[i] * q["w2"][i][v] for i in range(r)) for v in range(V)]
+            best = 0
+            for v in range(1, V):
+                if lg[v] > lg[best]:
+                    best = v
+            z = sum(q["block"][b][k][i] * q["cw"][i] for i in range(d))
+            z += sum(e1[i] * q["cw"][d + i] for i in range(r)) + q["cb"]
+            cb.append(1.0 / (1.0 + math.exp(-z)))
+            tb.append(best)
+            prev = best
+        toks.append(tb)
+        conf.append(cb)
+    return np.array(toks), np.array(conf)
+
+
+def _markov(O, q, **kw):
+    return O.markov_draft(q["block"], q["U"], q["anchor"], q["w1"], q["w2"], q["cw"], q["cb"], **kw)
+
+
+def pin_markov_brute_force(O, seed=30):
+    rs = np.random.default_rng(seed)
+    q = _markov_problem(rs)
+    toks, conf, _ = _markov(O, q)
+    bt, bc = _markov_brute(q)
+    assert np.array_equal(toks, bt), (toks, bt)
+    assert rel_err(conf, bc) < TIGHT
+
+
+def pin_markov_closed_forms(O, seed=31):
+    """W2 = 0 (the initialisation of initFromDims, "pure parallel DFlash")
+    gives token k = argmax of the base logits at position k; conf.w = 0 and
+    conf.b = 0 give confidence sigmoid(0) = 1/2 exactly; equal maxima resolve
+    to the lowest index."""
+    rs = np.random.default_rng(seed)
+    q = _markov_problem(rs)
+    q["w2"] = np.zeros_like(q["w2"])
+    toks, _, logits = _markov(O, q)
+    assert np.array_equal(toks, np.argmax(q["U"], axis=-1))
+    assert np.array_equal(logits, q["U"])
+    q["cw"] = np.zeros_like(q["cw"])
+    q["cb"] = 0.0
+    assert np.all(_markov(O, q)[1] == 0.5)
+    U = np.zeros_like(q["U"])
+    U[..., 7] = 2.0
+    U[..., 3] = 2.0
+    U[..., 9] = 1.0
+    q["U"] = U
+    assert np.all(_markov(O, q)[0] == 3), "ties go to the lowest index"
+
+
+def pin_markov_chain_feeds_back(O, seed=32):
+    """The previous token drives the next position: with zero base logits,
+    one-hot Markov embeddings (w1 = identity, r = V) and w2 the cyclic shift
+    v -> v + 1, the greedy draft counts up from the anchor token."""
+    rs = np.random.default_rng(seed)
+    V, A, G, d = 9, 3, 6, 4
+    q = dict(block=rs.standard_normal((A, G, d)), U=np.zeros((A, G, V)),
+             anchor=np.array([0, 4, 8]), w1=np.eye(V), w2=np.roll(np.eye(V), 1, axis=1),
+             cw=np.zeros(d + V), cb=0.0)
+    toks, _, _ = _markov(O, q)
+    want = (q["anchor"][:, None] + np.arange(1, G + 1)[None, :]) % V
+    assert np.array_equal(toks, want), (toks, want)
+
+
+def pin_markov_confidence_torch(O, seed=33):
+    """The confidence head against torch (float64 sigmoid of a linear map of
+    [block row, Markov embedding of the previous token])."""
+    import torch
+    rs = np.random.default_rng(seed)
+    q = _markov_problem(rs)
+    toks, conf, _ = _markov(O, q)
+    prev = np.concatenate([q["anchor"][:, None], toks[:, :-1]], axis=1)
+    x = np.concatenate([q["block"], q["w1"][prev]], axis=-1)
+    ref = torch.sigmoid(torch.as_tensor(x) @ torch.as_tensor(q["cw"]) + q["cb"]).numpy()
+    assert rel_err(conf, ref) < TIGHT
+
+
+# ---------------------------------------------------------------------------
+# 8. block construction and the padded-batch mask (#buildBlock, #maskBias)
+# ---------------------------------------------------------------------------
+
+def pin_build_block_brute_force(O, seed=40):
+    rs = np.random.default_rng(seed)
+    A, H, d, G = 3, 5, 4, 4
+    ae, tp = rs.standard_normal((A, H)), rs.standard_normal((H, d))
+    me, bp = rs.standard_normal((G - 1, d)), rs.standard_normal((G, d))
+    Hd = O.build_block(ae, tp, me, bp)
+    for b in range(A):
+        for k in range(d):
+            v = sum(ae[b][i] * tp[i][k] for i in range(H)) + bp[0][k]
+            assert abs(Hd[b, 0, k] - v) < 1e-12
+            for j in range(1, G):
+                assert abs(Hd[b, j, k] - (me[j - 1][k] + bp[j][k])) < 1e-15
+    one = O.build_block(ae, tp, me[:0], bp[:1])
+    assert one.shape == (A, 1, d)
+
+
+def _padded_from_packed(p, rs, Lctx, real_rows_first=False):
+    """A padded batch [A, Lctx, H] holding each sequence's real rows at
+    random (or leading) positions, padding rows filled with noise."""
+    A, m = p["A"], p["m"]
+    cu = [int(c) for c in p["cu"]]
+    mask = np.zeros((A, Lctx))
+    taps = [rs.standard_normal((A, Lctx, p["H"])) * 3.0 for _ in range(m)]
+    for b in range(A):
+        L = cu[b + 1] - cu[b]
+        pos = np.arange(L) if real_rows_first else np.sort(rs.choice(Lctx, size=L, replace=False))
+        mask[b, pos] = 1
+        for j in range(m):
+            taps[j][b, pos] = p["taps"][j][cu[b]:cu[b + 1]]
+    return taps, mask
+
+
+def pin_padded_mask_equals_packed(O, seed=41):
+    """#maskBias: padding rows get a -1e9 bias, so a padded batch gives the
+    packed (varlen) result of its real rows, wherever the padding sits (the
+    context carries no position); an all-ones mask adds nothing."""
+    rs = np.random.default_rng(seed)
+    p = _rand_problem(rs, lengths=[3, 0, 5])
+    ref = _fwd(O, p)
+    for lead in (True, False):
+        taps, mask = _padded_from_packed(p, rs, 7, real_rows_first=lead)
+        out = O.block_forward_padded(taps, p["w_c"], p["ctx_norm"], mask, p["block_in"],
+                                     p["block_pos"], p["layers"], p["out_norm"], p["n_heads"],
+                                     p["eps"])
+        assert rel_err(out, ref) < TIGHT, lead
+    assert np.all(O.mask_bias(np.ones((2, 5)), 3) == 0.0)
+    b = O.mask_bias(np.array([[1, 0, 1]]), 2)
+    assert b.tolist() == [[0.0, -1e9, 0.0, 0.0, 0.0]]
+
+
+def pin_padded_bias_is_exact_in_float32(O, seed=42):
+    """In float32 the -1e9 bias makes a padding key's weight exactly 0
+    (exp underflows), so the float32 padded forward equals the float32
+    packed forward up to float32 rounding."""
+    rs = np.random.default_rng(seed)
+    p = _rand_problem(rs, lengths=[4, 6])
+    taps, mask = _padded_from_packed(p, rs, 9)
+    out = O.block_forward_padded(taps, p["w_c"], p["ctx_norm"], mask, p["block_in"],
+                                 p["block_pos"], p["layers"], p["out_norm"], p["n_heads"],
+                                 p["eps"], dtype=np.float32)
+    assert rel_err(out, _fwd(O, p)) < 1e-5
+    assert np.exp(np.float32(-1e9) + np.float32(50.0) - np.float32(60.0)) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# 9. the page-1 layer variant (q/k norms, RoPE, grouped K/V heads, plain
+#    context K/V)
+# ---------------------------------------------------------------------------
+
+def _variant_problem(rs, lengths, n_heads=4, n_kv=2, hd=4, n_layers=2, m=2, H=3, gamma=3, ff=6):
+    d = n_heads * hd
+    kvd = n_kv * hd
+    p = _rand_problem(rs, lengths=lengths, m=m, H=H, d=d, n_heads=n_heads, gamma=gamma,
+                      n_layers=n_layers, ff=ff)
+    for lw in p["layers"]:
+        lw["wk"] = rs.standard_normal((d, kvd)) * 0.5
+        lw["wv"] = rs.standard_normal((d, kvd)) * 0.5
+        lw["q_norm"] = rs.uniform(0.5, 1.5, size=hd)
+        lw["k_norm"] = rs.uniform(0.5, 1.5, size=hd)
+    p["n_kv"] = n_kv
+    return p
+
+
+def _vfwd(O, p, **kw):
+    return O.variant_forward(p["taps"], p["w_c"], p["ctx_norm"], p["cu"], p["block_in"],
+                             p["block_pos"], p["layers"], p["out_norm"], p["n_heads"],
+                             p["n_kv"], p["eps"], **kw)
+
+
+def pin_variant_reduces_to_layer(O, seed=50):
+    """With every variant switch off (context norm on, no q/k norms, no RoPE,
+    as many K/V heads as query heads) the variant is #layer itself."""
+    rs = np.random.default_rng(seed)
+    p = _rand_problem(rs, lengths=[4, 0, 2])
+    p["n_kv"] = p["n_heads"]
+    assert rel_err(_vfwd(O, p), _fwd(O, p)) < TIGHT
+
+
+def pin_rope_closed_forms(O, seed=51):
+    """RoPE as complex multiplication: the pair (x_c, x_{c+hd/2}) is the
+    complex number x_c + i x_{c+hd/2} times exp(i pos theta^(-2c/hd)). So it is
+    the identity at position 0, keeps norms, and q.k after rotation depends
+    only on the difference of the two positions."""
+    rs = np.random.default_rng(seed)
+    hd, n, theta = 8, 5, 10000.0
+    x = rs.standard_normal((n, hd))
+    pos = rs.integers(0, 5000, size=n)
+    z = x[:, :hd // 2] + 1j * x[:, hd // 2:]
+    w = np.exp(1j * pos[:, None] * theta ** (-2.0 * np.arange(hd // 2) / hd)[None, :])
+    zr = z * w
+    ref = np.concatenate([zr.real, zr.imag], axis=1)
+    assert rel_err(O.rope(x, pos, theta), ref) < 1e-12
+    assert rel_err(O.rope(x, np.zeros(n, dtype=np.int64), theta), x) == 0.0
+    assert rel_err(np.linalg.norm(O.rope(x, pos, theta), axis=1), np.linalg.norm(x, axis=1)) < 1e-13
+    q, k = rs.standard_normal((1, hd)), rs.standard_normal((1, hd))
+    for shift in (0, 7, 1234):
+        a = O.rope(q, np.array([10 + shift]), theta) @ O.rope(k, np.array([3 + shift]), theta).T
+        if shift == 0:
+            a0 = a
+        assert abs(a - a0).max() < 1e-10
+
+
+def pin_variant_rope_shift_invariance(O, seed=52):
+    """Positions count from each sequence's own start (context row t at t,
+    block row j at L_b + j), and RoPE depends on position differences only:
+    two sequences with equal contexts and blocks get equal drafts wherever
+    they sit in the packed batch. Unlike the base method, the context then
+    carries position: reordering a sequence's context rows changes its
+    draft."""
+    rs = np.random.default_rng(seed)
+    p = _variant_problem(rs, lengths=[3, 3])
+    for j in range(p["m"]):
+        p["taps"][j][3:6] = p["taps"][j][0:3]
+    p["block_in"][1] = p["block_in"][0]
+    out = _vfwd(O, p, qk_norm=True, theta=100.0, ctx_norm_kv=False)
+    assert rel_err(out[1], out[0]) < TIGHT
+    # and RoPE does matter: a context row moved within its sequence changes the draft
+    q = _variant_problem(np.random.default_rng(seed), lengths=[3, 3])
+    for j in range(q["m"]):
+        q["taps"][j][3:6] = q["taps"][j][[1, 0, 2]]
+    q["block_in"][1] = q["block_in"][0]
+    out2 = _vfwd(O, q, qk_norm=True, theta=100.0, ctx_norm_kv=False)
+    assert rel_err(out2[1], out2[0]) > 1e-6
+
+
+def pin_variant_gqa_is_repeated_heads(O, seed=53):
+    """Grouped K/V heads (query head h reads K/V head h // (n / n_kv)) equal
+    the full-head layer whose W_K / W_V repeat each K/V head's columns for
+    the query heads of its group; likewise with q/k norms and RoPE."""
+    rs = np.random.default_rng(seed)
+    p = _variant_problem(rs, lengths=[4, 1], n_heads=4, n_kv=2, hd=4)
+    full = {k: (v if not isinstance(v, list) else v) for k, v in p.items()}
+    grp = p["n_heads"] // p["n_kv"]
+    hd = p["d"] // p["n_heads"]
+    full["layers"] = []
+    for lw in p["layers"]:
+        f = dict(lw)
+        cols = np.concatenate([np.arange((h // grp) * hd, (h // grp + 1) * hd) for h in range(p["n_heads"])])
+        f["wk"], f["wv"] = lw["wk"][:, cols], lw["wv"][:, cols]
+        full["layers"].append(f)
+    full["n_kv"] = p["n_heads"]
+    for kw in (dict(), dict(qk_norm=True, theta=500.0)):
+        assert rel_err(_vfwd(O, p, **kw), _vfwd(O, full, **kw)) < TIGHT, kw
+
+
+def pin_variant_head_norm_torch(O, seed=54):
+    """q_norm / k_norm are RMSNorms over each head (torch rms_norm over the
+    last axis of the [.., heads, hd] view); with them, scaling W_Q and W_K
+    by any positive factor leaves the draft unchanged (eps = 0)."""
+    import torch
+    import torch.nn.functional as F
+    rs = np.random.default_rng(seed)
+    x, g = rs.standard_normal((5, 12)), rs.uniform(0.5, 1.5, size=4)
+    ref = F.rms_norm(torch.as_tensor(x).view(5, 3, 4), (4,), weight=torch.as_tensor(g), eps=1e-6)
+    assert rel_err(O.head_rmsnorm(x, g, 3, 1e-6), ref.reshape(5, 12).numpy()) < 1e-14
+    p = _variant_problem(rs, lengths=[3, 2])
+    p["eps"] = 0.0
+    out = _vfwd(O, p, qk_norm=True, theta=50.0)
+    for lw in p["layers"]:
+        lw["wq"] = lw["wq"] * 3.7
+        lw["wk"] = lw["wk"] * 0.21
+    assert rel_err(_vfwd(O, p, qk_norm=True, theta=50.0), out) < 1e-10
+
+
+def pin_variant_plain_context_kv(O, seed=55):
+    """Without the per-layer context norm the context rows enter W_K / W_V as
+    Eq 2 leaves them. Eq 2's rows have RMS 1 (eps = 0, gain 1), so with unit
+    attention-norm gains the two readings agree; with other gains they do
+    not."""
+    rs = np.random.default_rng(seed)
+    p = _variant_problem(rs, lengths=[3, 4])
+    p["eps"] = 0.0
+    p["ctx_norm"] = np.ones(p["d"])
+    for lw in p["layers"]:
+        lw["attn_norm"] = np.ones(p["d"])
+    a = _vfwd(O, p, ctx_norm_kv=True, qk_norm=True, theta=30.0)
+    b = _vfwd(O, p, ctx_norm_kv=False, qk_norm=True, theta=30.0)
+    assert rel_err(a, b) < 1e-12
+    for lw in p["layers"]:
+        lw["attn_norm"] = rs.uniform(0.5, 1.5, size=p["d"])
+    a = _vfwd(O, p, ctx_norm_kv=True)
+    b = _vfwd(O, p, ctx_norm_kv=False)
+    assert rel_err(a, b) > 1e-6
+
+
+def _variant_brute(p, *, qk_norm, theta, ctx_norm_kv):
+    """Scalar loops over the variant forward, with RoPE as a rotation of the
+    complex number x_c + i x_{c+hd/2} by the angle pos * theta^(-2c/hd) at
+    explicit positions (context row t of a sequence at t, block row j at
+    L_b + j)."""
+    A, G, d, n, nkv = p["A"], p["gamma"], p["d"], p["n_heads"], p["n_kv"]
+    hd, grp, eps = d // n, n // nkv, p["eps"]
+    cu = [int(c) for c in p["cu"]]
+    C, _ = brute_force_forward(dict(p, layers=[]))
+    C = C.tolist()
+    D = [[[p["block_in"][b, j, k] + p["block_pos"][j, k] for k in range(d)] for j in range(G)]
+         for b in range(A)]
+
+    def head_norm(row, g, heads):
+        out = []
+        for h in range(heads):
+            out += _bf_rms(row[h * hd:(h + 1) * hd], list(g), eps)
+        return out
+
+    def rot(row, pos, heads):
+        out = list(row)
+        for h in range(heads):
+            for c in range(hd // 2):
+                z = complex(row[h * hd + c], row[h * hd + c + hd // 2])
+                ang = pos * theta ** (-2.0 * c / hd)
+                z *= complex(math.cos(ang), math.sin(ang))
+                out[h * hd + c], out[h * hd + c + hd // 2] = z.real, z.imag
+        return out
+
+    for lw in p["layers"]:
+        L_ = {k: np.asarray(v).tolist() for k, v in lw.items()}
+        newD = []
+        for b in range(A):
+            ctx = C[cu[b]:cu[b + 1]]
+            xc = [_bf_rms(r, L_["attn_norm"], eps) for r in ctx] if ctx_norm_kv else ctx
+            Kc = _bf_matmul(xc, L_["wk"]) if xc else []
+            Vc = _bf_matmul(xc, L_["wv"]) if xc else []
+            U = [_bf_rms(D[b][j], L_["attn_norm"], eps) for j in range(G)]
+            Q, Kd, Vd = _bf_matmul(U, L_["wq"]), _bf_matmul(U, L_["wk"]), _bf_matmul(U, L_["wv"])
+            if qk_norm:
+                Kc = [head_norm(r, L_["k_norm"], nkv) for r in Kc]
+                Q = [head_norm(r, L_["q_norm"], n) for r in Q]
+                Kd = [head_norm(r, L_["k_norm"], nkv) for r in Kd]
+            Lb = len(ctx)
+            if theta > 0:
+                Kc = [rot(r, t, nkv) for t, r in enumerate(Kc)]
+                Q = [rot(r, Lb + j, n) for j, r in enumerate(Q)]
+                Kd = [rot(r, Lb + j, nkv) for j, r in enumerate(Kd)]
+            keys, vals = Kc + Kd, Vc + Vd
+            att = [[0.0] * d for _ in range(G)]
+            for h in range(n):
+                qo, ko = h * hd, (h // grp) * hd
+                for j in range(G):
+                    sc = [sum(Q[j][qo + c] * kk[ko + c] for c in range(hd)) / math.sqrt(hd) for kk in keys]
+                    mx = max(sc)
+                    e = [math.exp(v - mx) for v in sc]
+                    z = sum(e)
+                    for c in range(hd):
+                        att[j][qo + c] = sum(e[t] * vals[t][ko + c] for t in range(len(e))) / z
+            ao = _bf_matmul(att, L_["wo"])
+            E = [[D[b][j][k] + ao[j][k] for k in range(d)] for j in range(G)]
+            Z = [_bf_rms(E[j], L_["ff_norm"], eps) for j in range(G)]
+            Gt, Up = _bf_matmul(Z, L_["w_gate"]), _bf_matmul(Z, L_["w_up"])
+            Hh = [[Gt[j][f] / (1.0 + math.exp(-Gt[j][f])) * Up[j][f] for f in range(len(Gt[j]))]
+                  for j in range(G)]
+            dn = _bf_matmul(Hh, L_["w_down"])
+            newD.append([[E[j][k] + dn[j][k] for k in range(d)] for j in range(G)])
+        D = newD
+    return np.array([[_bf_rms(D[b][j], p["out_norm"].tolist(), eps) for j in range(G)] for b in range(A)])
+
+
+def pin_variant_brute_force(O, seed=56):
+    rs = np.random.default_rng(seed)
+    p = _variant_problem(rs, lengths=[3, 0, 2], n_heads=4, n_kv=2, hd=4)
+    for kw in (dict(qk_norm=True, theta=1000.0, ctx_norm_kv=False),
+               dict(qk_norm=False, theta=77.0, ctx_norm_kv=True),
+               dict(qk_norm=True, theta=0.0, ctx_norm_kv=True)):
+        assert rel_err(_vfwd(O, p, **kw), _variant_brute(p, **kw)) < TIGHT, kw
+
+
 ALL_PINS = [
     pin_brute_force, pin_torch_library, pin_wq_zero_is_mean_of_values,
     pin_two_key_logistic, pin_residual_passthrough, pin_hand_example,
     pin_scale_invariance, pin_block_permutation, pin_context_permutation,
     pin_varlen_equals_separate, pin_readonly_context, pin_empty_context_textbook,
-    pin_fp32_close_to_fp64, pin_split_combine,
+    pin_fp32_close_to_fp64, pin_split_combine, pin_gelu_tanh,
+    pin_cache_equals_full_context, pin_cache_rows_are_row_local,
+    pin_markov_brute_force, pin_markov_closed_forms, pin_markov_chain_feeds_back,
+    pin_markov_confidence_torch, pin_build_block_brute_force, pin_padded_mask_equals_packed,
+    pin_padded_bias_is_exact_in_float32, pin_variant_reduces_to_layer, pin_rope_closed_forms,
+    pin_variant_rope_shift_invariance, pin_variant_gqa_is_repeated_heads,
+    pin_variant_head_norm_torch, pin_variant_plain_context_kv, pin_variant_brute_force,
 ]
