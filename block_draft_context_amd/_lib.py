@@ -15,8 +15,10 @@ EXPORTS = [
     "dspark_workspace_size", "dspark_ctx_fuse", "dspark_block_layer",
     "dspark_block_forward", "dspark_last_error", "dspark_version",
     "dspark_kernel_kinds", "dspark_kernel_name", "dspark_trace_begin",
-    "dspark_trace_end",
+    "dspark_trace_end", "dspark_plan_info",
 ]
+PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "attn_streaming",
+               "workspace_bytes")
 
 
 class Dims(ctypes.Structure):
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.dspark_trace_begin.restype = i32
     L.dspark_trace_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32]
     L.dspark_trace_end.restype = i32
+    L.dspark_plan_info.argtypes = [i32, ctypes.POINTER(Dims), i32, pi32, ctypes.POINTER(ctypes.c_int64), i32]
+    L.dspark_plan_info.restype = i32
     _lib = L
     return L
 

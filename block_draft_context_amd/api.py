@@ -21,6 +21,7 @@ from . import _lib as L
 __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
     "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
+    "plan_info",
 ]
 
 DsparkError = L.DsparkError
@@ -63,10 +64,22 @@ def _cu_host(cu) -> ctypes.Array:
     return (ctypes.c_int32 * len(vals))(*vals)
 
 
-def _stream(stream) -> int:
+def _torch_stream(stream) -> "torch.cuda.Stream":
+    """The stream the library enqueues on, as a torch stream object: the
+    current one for None, the given one, or a raw hipStream_t handle wrapped
+    as an external stream. Outputs and workspaces that this module allocates
+    are allocated on it (``with torch.cuda.stream``), so the caching
+    allocator never hands their memory to other work before the library's
+    kernels on that stream are done with it."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _stream(stream) -> int:
+    return _torch_stream(stream).cuda_stream
 
 
 def version() -> str:
@@ -88,6 +101,17 @@ def workspace_size(op: int, dims: DsparkDims, cu) -> int:
     return int(n)
 
 
+def plan_info(op: int, dims: DsparkDims, cu) -> Dict[str, int]:
+    """The launch plan the library takes for these sizes (host arithmetic)."""
+    cu_h = _cu_host(cu)
+    dm = dims.c()
+    out = (ctypes.c_int64 * len(L.PLAN_FIELDS))()
+    n = L.lib().dspark_plan_info(op, ctypes.byref(dm), len(cu_h) - 1, cu_h, out, len(out))
+    if n == 0:
+        raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+    return {k: int(out[i]) for i, k in enumerate(L.PLAN_FIELDS[:n])}
+
+
 def _workspace(op, dims, cu, ws, device):
     need = workspace_size(op, dims, cu)
     if ws is None:
@@ -95,15 +119,29 @@ def _workspace(op, dims, cu, ws, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def _tap_ptrs(taps) -> ctypes.Array:
+def _tap_list(taps, dims: "DsparkDims") -> List[torch.Tensor]:
+    """The m taps as [T, H] views; they must share the storage dtype and one
+    row stride (the library takes a single leading dimension)."""
     if isinstance(taps, torch.Tensor):
         taps = list(taps.unbind(0))
+    taps = list(taps)
+    if len(taps) != dims.m:
+        raise ValueError(f"{len(taps)} taps given, dims.m = {dims.m}")
+    ld = int(taps[0].stride(0))
+    for j, t in enumerate(taps):
+        if t.dtype != dims.torch_dtype:
+            raise ValueError(f"taps[{j}] is {t.dtype}, the storage dtype is {dims.torch_dtype}")
+        if t.dim() != 2 or t.stride(1) != 1 or int(t.stride(0)) != ld:
+            raise ValueError(f"taps[{j}] must be a row-major [T, H] view with row stride {ld}")
+    return taps
+
+
+def _tap_ptrs(taps) -> ctypes.Array:
     return (ctypes.c_void_p * len(taps))(*[t.data_ptr() for t in taps])
 
 
 def _tap_ld(taps) -> int:
-    t0 = taps[0] if not isinstance(taps, torch.Tensor) else taps[0]
-    return int(t0.stride(0))
+    return int(taps[0].stride(0))
 
 
 def _cu_dev(cu, cu_dev, device):
@@ -123,14 +161,17 @@ def ctx_fuse(dims: DsparkDims, cu, taps, w_c, ctx_norm, *, cu_dev=None, h_ctx=No
     device = w_c.device
     cu_h = _cu_host(cu)
     T = cu_h[len(cu_h) - 1]
-    if h_ctx is None:
-        h_ctx = torch.empty((T, dims.d), dtype=dims.torch_dtype, device=device)
-    cu_dev = _cu_dev(cu, cu_dev, device)
-    ws, nbytes = _workspace(L.OP_CTX_FUSE, dims, cu, ws, device)
+    taps = _tap_list(taps, dims)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if h_ctx is None:
+            h_ctx = torch.empty((T, dims.d), dtype=dims.torch_dtype, device=device)
+        cu_dev = _cu_dev(cu, cu_dev, device)
+        ws, nbytes = _workspace(L.OP_CTX_FUSE, dims, cu, ws, device)
     dm = dims.c()
     L.check(L.lib().dspark_ctx_fuse(ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev),
                                     _tap_ptrs(taps), _tap_ld(taps), _ptr(w_c), _ptr(ctx_norm),
-                                    _ptr(h_ctx), _ptr(ws), nbytes, _stream(stream)))
+                                    _ptr(h_ctx), _ptr(ws), nbytes, ts.cuda_stream))
     return h_ctx
 
 
@@ -139,15 +180,17 @@ def block_layer(dims: DsparkDims, cu, h_ctx, d_in, lw: Dict[str, torch.Tensor], 
     """Eq 3 + FFN for one draft layer: block rows [A, gamma, d] float32 in and out."""
     device = d_in.device
     cu_h = _cu_host(cu)
-    if d_out is None:
-        d_out = torch.empty_like(d_in)
-    cu_dev = _cu_dev(cu, cu_dev, device)
-    ws, nbytes = _workspace(L.OP_BLOCK_LAYER, dims, cu, ws, device)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if d_out is None:
+            d_out = torch.empty_like(d_in)
+        cu_dev = _cu_dev(cu, cu_dev, device)
+        ws, nbytes = _workspace(L.OP_BLOCK_LAYER, dims, cu, ws, device)
     dm = dims.c()
     lws = _layer_struct(lw)
     L.check(L.lib().dspark_block_layer(ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev),
                                        _ptr(h_ctx), _ptr(d_in), _ptr(d_out), ctypes.byref(lws),
-                                       _ptr(ws), nbytes, _stream(stream)))
+                                       _ptr(ws), nbytes, ts.cuda_stream))
     return d_out
 
 
@@ -157,16 +200,19 @@ def block_forward(dims: DsparkDims, cu, taps, w_c, ctx_norm, block_in, block_pos
     """The whole draft block (Eq 2, block init, every layer, output norm)."""
     device = block_in.device
     cu_h = _cu_host(cu)
-    if block_out is None:
-        block_out = torch.empty_like(block_in)
-    cu_dev = _cu_dev(cu, cu_dev, device)
-    ws, nbytes = _workspace(L.OP_BLOCK_FORWARD, dims, cu, ws, device)
+    taps = _tap_list(taps, dims)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if block_out is None:
+            block_out = torch.empty_like(block_in)
+        cu_dev = _cu_dev(cu, cu_dev, device)
+        ws, nbytes = _workspace(L.OP_BLOCK_FORWARD, dims, cu, ws, device)
     dm = dims.c()
     arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
     L.check(L.lib().dspark_block_forward(
         ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev), _tap_ptrs(taps), _tap_ld(taps),
         _ptr(w_c), _ptr(ctx_norm), _ptr(block_in), _ptr(block_pos), arr, _ptr(out_norm),
-        _ptr(h_ctx_out), _ptr(block_out), _ptr(ws), nbytes, _stream(stream)))
+        _ptr(h_ctx_out), _ptr(block_out), _ptr(ws), nbytes, ts.cuda_stream))
     return block_out
 
 
@@ -180,9 +226,13 @@ class PreparedForward:
                  ws=None, stream=None):
         device = block_in.device
         self.cu_h = _cu_host(cu)
-        self.block_out = torch.empty_like(block_in) if block_out is None else block_out
-        self.cu_dev = _cu_dev(cu, cu_dev, device)
-        self.ws, nbytes = _workspace(L.OP_BLOCK_FORWARD, dims, cu, ws, device)
+        taps = _tap_list(taps, dims)
+        ts = _torch_stream(stream)
+        self.stream = ts
+        with torch.cuda.stream(ts):
+            self.block_out = torch.empty_like(block_in) if block_out is None else block_out
+            self.cu_dev = _cu_dev(cu, cu_dev, device)
+            self.ws, nbytes = _workspace(L.OP_BLOCK_FORWARD, dims, cu, ws, device)
         self.dm = dims.c()
         self.layers = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
         self.taps = _tap_ptrs(taps)
@@ -190,7 +240,7 @@ class PreparedForward:
         self.args = (ctypes.byref(self.dm), len(self.cu_h) - 1, self.cu_h, _ptr(self.cu_dev),
                      self.taps, _tap_ld(taps), _ptr(w_c), _ptr(ctx_norm), _ptr(block_in),
                      _ptr(block_pos), self.layers, _ptr(out_norm), _ptr(h_ctx_out),
-                     _ptr(self.block_out), _ptr(self.ws), nbytes, _stream(stream))
+                     _ptr(self.block_out), _ptr(self.ws), nbytes, ts.cuda_stream)
         self.fn = L.lib().dspark_block_forward
 
     def __call__(self) -> torch.Tensor:

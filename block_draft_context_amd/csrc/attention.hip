@@ -417,20 +417,24 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
   const int nblk = k1 > k0 ? (int)(((k1 - 1) >> 6) - blk0 + 1) : 0;   // 0, 1 or 2
 
   // both blocks' slices are requested first (the second repeats the first
-  // when there is only one), then the queries are staged
+  // when there is only one), then the queries are staged. A tile with no
+  // keys (an empty sequence) loads nothing: its block index may lie past the
+  // last block of the slab, or the K/V region may be empty altogether.
   const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, h, n_heads, Tpad, HD);
   const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, h, n_heads, Tpad, HD);
   u32x4 kreg[2][NKW], vreg[2][NLW];
+  if (nblk > 0) {
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-    const int64_t blk = blk0 + min(bb, max(nblk - 1, 0));
-    const S* kp = Kh + blk * 64 * HD + (wave * NKW) * 64 * E + lane * E;
-    const S* vp = Vh + blk * 64 * HD + (wave * NLW) * 64 * E + lane * E;
+    for (int bb = 0; bb < 2; ++bb) {
+      const int64_t blk = blk0 + min(bb, nblk - 1);
+      const S* kp = Kh + blk * 64 * HD + (wave * NKW) * 64 * E + lane * E;
+      const S* vp = Vh + blk * 64 * HD + (wave * NLW) * 64 * E + lane * E;
 #pragma unroll
-    for (int i = 0; i < NKW; ++i) kreg[bb][i] = ld16(kp + i * 64 * E);
+      for (int i = 0; i < NKW; ++i) kreg[bb][i] = ld16(kp + i * 64 * E);
 #pragma unroll
-    for (int i = 0; i < NLW; ++i)   // V is read once: non-temporal, as in the streaming kernel
-      vreg[bb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 64 * E));
+      for (int i = 0; i < NLW; ++i)   // V is read once: non-temporal, as in the streaming kernel
+        vreg[bb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 64 * E));
+    }
   }
   const int d = HD * n_heads;
   for (int i = tid; i < G * HD; i += 256) {

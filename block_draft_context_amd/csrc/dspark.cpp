@@ -80,7 +80,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
   int64_t T = 0, Tpad = 0;
-  int hd = 0, M = 0, chunk = 0, total_chunks = 0, ctx_splits = 1, kv_layers = 0;
+  int hd = 0, M = 0, chunk = 0, total_chunks = 0, kv_layers = 0;
+  CtxSplit ctx;   // K splits of the Eq 2 projection
   size_t esz = 4;
   // workspace offsets (bytes)
   size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
@@ -149,7 +150,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
     return fail(DSPARK_EUNSUPPORTED, "W_c spans %lld bytes (d * m * H); at most 4 GiB is supported",
                 (long long)((int64_t)dm->d * dm->m * dm->H * p->esz));
   const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
-  p->ctx_splits = ctx_gemm_splits(dm->dtype, T, d, mH);
+  p->ctx = ctx_gemm_split(dm->dtype, T, d, mH);
   p->chunk = attention_chunk(cu_host, A, dm->n_heads);
   p->total_chunks = (int)attention_tiles(cu_host, A, p->chunk);
   p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;
@@ -159,7 +160,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   const bool need_ctx = op != DSPARK_OP_BLOCK_LAYER;
   const bool need_block = op != DSPARK_OP_CTX_FUSE;
   if (need_ctx) {
-    p->ppart = take((size_t)p->ctx_splits * T * d * 4);
+    p->ppart = take((size_t)p->ctx.splits * T * d * 4);
   }
   if (need_block) {
     if (bf) p->wkvt = take((size_t)2 * p->kv_layers * d * d * 2);
@@ -246,7 +247,7 @@ static dspark_status run_ctx_gemm(const dspark_dims* dm, const Plan& p, const vo
   b.nmat = 1;
   // W_c [d, m*H] is already the K-contiguous B operand
   DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, w_c, at<float>(ws, p.ppart), (int)p.T, d, mH,
-                             p.ctx_splits, s));
+                             p.ctx, s));
   return DSPARK_OK;
 }
 
@@ -386,7 +387,7 @@ dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A, const int32_t*
   sa.eps = dims->eps;
   sa.T = p.T;
   sa.part = at<float>(ws, p.ppart);
-  sa.splits = p.ctx_splits;
+  sa.splits = p.ctx.splits;
   sa.g = ctx_norm;
   sa.h = h_ctx;
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
@@ -472,7 +473,7 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   if (p.T > 0) {
     sa.T = p.T;
     sa.part = at<float>(ws, p.ppart);
-    sa.splits = p.ctx_splits;
+    sa.splits = p.ctx.splits;
     sa.g = ctx_norm;
     sa.h = h_ctx;
     sa.rinv = rinv;
@@ -491,6 +492,25 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
     DSPARK_HIP(launch_block_rows(Da, nullptr, A, dims->gamma, dims->d, out_norm, dims->eps, nullptr,
                                  block_out, s));
   return DSPARK_OK;
+}
+
+int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                         int64_t* out, int32_t n) {
+  if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_FORWARD) {
+    fail(DSPARK_EINVAL, "unknown op %d", op);
+    return 0;
+  }
+  if (!out || n < 1) {
+    fail(DSPARK_EINVAL, "out is NULL or n < 1");
+    return 0;
+  }
+  Plan p;
+  if (make_plan(op, dims, A, cu_host, &p) != DSPARK_OK) return 0;
+  const int64_t v[DSPARK_PLAN_COUNT] = {p.ctx.splits, p.ctx.k_per_split, p.chunk, p.total_chunks,
+                                        p.chunk != 64 ? 1 : 0, (int64_t)p.total};
+  const int k = std::min<int32_t>(n, DSPARK_PLAN_COUNT);
+  for (int i = 0; i < k; ++i) out[i] = v[i];
+  return k;
 }
 
 const char* dspark_last_error(void) { return g_err.c_str(); }

@@ -15,6 +15,7 @@
 #include "kernels.h"
 #include "kv_layout.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace dspark {
@@ -681,8 +682,10 @@ static int kv_big_columns(int Mrows, int N) {
   return cost_split < cost_big ? (int)nb : (int)tn;
 }
 
-int ctx_gemm_splits(int dtype, int64_t M, int N, int K) {
-  if (M <= 0) return 1;
+// K splits of the Eq 2 projection and the columns each covers. The width is
+// a whole number of k tiles and the count is recomputed from it, so that
+// splits * k_per_split >= K and no split is empty, whatever the sizes.
+CtxSplit ctx_gemm_split(int dtype, int64_t M, int N, int K) {
   int64_t tiles, target;
   int bk;
   if (use_big_tiles(dtype, M, N)) {
@@ -690,26 +693,30 @@ int ctx_gemm_splits(int dtype, int64_t M, int N, int K) {
     target = 256;   // one 128 KiB-LDS workgroup per CU
     bk = kFuseBK;
   } else {
-    const int bm = dtype == 1 ? pick_gemm_bm((int)M) : 64;
+    const int bm = dtype == 1 ? pick_gemm_bm((int)std::max<int64_t>(M, 1)) : 64;
     const int bn = dtype == 1 ? 128 : 64;
-    tiles = ((M + bm - 1) / bm) * (N / bn);
+    tiles = ((std::max<int64_t>(M, 1) + bm - 1) / bm) * (N / bn);
     target = 512;
     bk = dtype == 1 ? BK : 16;
   }
-  int64_t sp = (target + tiles - 1) / tiles;
+  int64_t sp = M <= 0 ? 1 : (target + tiles - 1) / tiles;
   const int64_t max_s = K / (4 * bk);
   if (sp > max_s) sp = max_s;
   if (sp < 1) sp = 1;
-  return (int)sp;
+  const int64_t kps = ((K + sp * bk - 1) / (sp * bk)) * bk;   // ceil(K / sp), whole k tiles
+  CtxSplit r;
+  r.k_per_split = (int)kps;
+  r.splits = (int)((K + kps - 1) / kps);
+  return r;
 }
 
 hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, float* out,
-                           int M, int N, int K, int splits, hipStream_t s) {
-  const int kps = ((K / splits + BK - 1) / BK) * BK;
+                           int M, int N, int K, const CtxSplit& sp, hipStream_t s) {
+  const int splits = sp.splits, kps = sp.k_per_split;
+  if ((int64_t)splits * kps < K || (int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   trace_pre(K_GEMM_CTX, s);
   if (use_big_tiles(dtype, M, N)) {
     EpiPartialBig epi{out, (int64_t)M * N};
-    const int kps = ((K / splits + kFuseBK - 1) / kFuseBK) * kFuseBK;
     dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);
     gemm_big_kernel<EpiPartialBig, 128, kFuseBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, static_cast<const bf16*>(Bt),
                                                                          M, M, N, K, kps, epi);
@@ -725,9 +732,8 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
     }
   } else {
     EpiPartial epi{out, (int64_t)M * N};
-    const int kps16 = ((K / splits + 15) / 16) * 16;
     dim3 grid(((M + 63) / 64) * (N / 64), 1, splits);
-    gemm_f32<EpiPartial><<<grid, 256, 0, s>>>(a, b, M, M, N, K, kps16, epi);
+    gemm_f32<EpiPartial><<<grid, 256, 0, s>>>(a, b, M, M, N, K, kps, epi);
   }
   trace_post(K_GEMM_CTX, s);
   return hipGetLastError();

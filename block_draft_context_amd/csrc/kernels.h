@@ -95,11 +95,17 @@ struct SetupArgs {
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s);
 
 // ---- context side -------------------------------------------------------
-// K splits of the Eq 2 projection for these sizes (sizes the partial buffer)
-int ctx_gemm_splits(int dtype, int64_t M, int N, int K);
+// K splits of the Eq 2 projection for these sizes (sizes the partial
+// buffer): split z covers columns [z * k_per_split, min(K, (z+1) * k_per_split)),
+// with splits * k_per_split >= K and every split non-empty.
+struct CtxSplit {
+  int splits = 1;
+  int k_per_split = 0;
+};
+CtxSplit ctx_gemm_split(int dtype, int64_t M, int N, int K);
 // out[z][r][n] = sum_{k in split z} A(r,k) B(k,n); float32 partials.
 hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt,
-                           float* out, int M, int N, int K, int splits, hipStream_t s);
+                           float* out, int M, int N, int K, const CtxSplit& sp, hipStream_t s);
 
 // K/V for all layers of `b` (2 matrices per layer: K then V) from H_ctx with
 // the row scale rinv, written in the attention layout of `kv`.

@@ -21,12 +21,14 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Every matrix is row-major [out, in] and applied as y = x W^T: the layout
- *   checkpoints store and the page "src/dspark-runtime.js" multiplies with a
- *   transposed B operand. (module-dflash.ts, initFromDims, keeps the same
- *   parameters as [in, out] and computes x @ W; its W is this W^T.) An
- *   output feature's weights are then one contiguous run over the input,
- *   which is what the kernels stream. Norm gains are float32 [d].
+ * - Every matrix is row-major [out, in] and applied as y = x W^T. This is
+ *   this library's own choice, not the pages': module-dflash.ts
+ *   (initFromDims) keeps the parameters as [in, out] and computes x @ W, so
+ *   its W is this W^T. With [out, in] an output feature's weights are one
+ *   contiguous run over the input: the block-side products then read 1 KiB
+ *   per wave load instead of 64 scattered lines, and W_c is directly the
+ *   K-contiguous operand of the Eq 2 matrix-core product, with no per-call
+ *   transpose. Norm gains are float32 [d].
  * - dims->dtype is the storage type of the long tensors: the taps, W_c, every
  *   layer matrix and H_ctx. DSPARK_BF16 means bfloat16 storage with float32
  *   accumulation; DSPARK_F32 means float32 everywhere.
@@ -159,6 +161,24 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A,
                                    const float* out_norm, void* h_ctx_out,
                                    float* block_out, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* The launch plan that `op` takes for these sizes: pure host arithmetic, for
+ * tests and tools. Writes min(n, DSPARK_PLAN_COUNT) values to out, indexed by
+ * dspark_plan_field, and returns that count (0 with a message in
+ * dspark_last_error() when the arguments are invalid). */
+typedef enum {
+  DSPARK_PLAN_CTX_SPLITS = 0,     /* K splits of the Eq 2 projection */
+  DSPARK_PLAN_CTX_K_PER_SPLIT,    /* columns of m*H per split (the last may cover fewer) */
+  DSPARK_PLAN_ATTN_CHUNK,         /* context keys per attention tile */
+  DSPARK_PLAN_ATTN_TILES,         /* attention tiles over all sequences */
+  DSPARK_PLAN_ATTN_STREAMING,     /* 1: chunks of several 64-key blocks, one wave
+                                     per block (long contexts); 0: one block per tile,
+                                     four waves share it (short contexts) */
+  DSPARK_PLAN_WORKSPACE_BYTES,    /* dspark_workspace_size for the same arguments */
+  DSPARK_PLAN_COUNT
+} dspark_plan_field;
+int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                         int64_t* out, int32_t n);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* dspark_last_error(void);

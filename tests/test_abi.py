@@ -190,3 +190,45 @@ def test_python_binding_raises_with_message(L):
         B.workspace_size(B.OP_BLOCK_FORWARD, B.DsparkDims(m=2, H=64, d=128, n_heads=3, gamma=2,
                                                           n_layers=1, ff=128), [0, 4])
     assert "not divisible" in str(e.value)
+
+
+def _plan(L, op, dm, cu):
+    out = (ctypes.c_int64 * 6)()
+    n = L.lib().dspark_plan_info(op, ctypes.byref(dm), len(cu) - 1, _cu(cu), out, 6)
+    assert n == 6, L.lib().dspark_last_error().decode()
+    return dict(zip(L.PLAN_FIELDS, list(out)))
+
+
+def test_ctx_splits_cover_every_column(L):
+    """The Eq 2 projection's K splits cover all m*H columns with no empty
+    split, for every storage type and kernel choice (K / splits need not be
+    whole: e.g. float32 m=3, H=2304 once split 43 ways at 160 columns left 32
+    columns out)."""
+    checked = 0
+    for dtype in (L.F32, L.BF16):
+        for m in (1, 2, 3, 4, 5, 7, 16):
+            for H in (64, 192, 2304, 2560, 3584, 5568):
+                for d in (128, 384, 768, 1024, 2048):
+                    for T in (1, 64, 100, 511, 512, 2048, 9000, 131072):
+                        dm = _dims(L, m=m, H=H, d=d, n_heads=d // 128, dtype=dtype)
+                        if d * m * H * (2 if dtype == L.BF16 else 4) >= 1 << 32:
+                            continue
+                        p = _plan(L, L.OP_CTX_FUSE, dm, [0, T])
+                        K = m * H
+                        s, kps = p["ctx_splits"], p["ctx_k_per_split"]
+                        bk = 16 if dtype == L.F32 else 64
+                        assert s >= 1 and kps % bk == 0, (dtype, m, H, d, T, p)
+                        assert s * kps >= K and (s - 1) * kps < K, (dtype, m, H, d, T, p)
+                        checked += 1
+    assert checked > 1000
+
+
+def test_plan_reports_the_attention_path(L):
+    """Long contexts take the streaming split-K kernel (more than 1024 64-key
+    blocks over the heads), short ones the head-split kernel."""
+    dm = _dims(L, m=2, H=128, d=256, n_heads=2, gamma=6)
+    assert _plan(L, L.OP_BLOCK_FORWARD, dm, [0, 1000])["attn_streaming"] == 0
+    p = _plan(L, L.OP_BLOCK_FORWARD, dm, [0, 30011, 30011, 41122])
+    assert p["attn_streaming"] == 1 and p["attn_chunk"] > 64
+    need = L.lib().dspark_workspace_size(L.OP_BLOCK_FORWARD, ctypes.byref(dm), 3, _cu([0, 30011, 30011, 41122]))
+    assert p["workspace_bytes"] == need
