@@ -29,7 +29,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 import workloads as W  # noqa: E402
 
-DEFAULT_WORKLOAD = "bf16-L2048-d1024"
+DEFAULT_WORKLOAD = "bf16-ragged16-L512..16384"
 METRIC = "context tokens/s through Eq2+Eq3 and draft blocks/s; % MFMA / HBM peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
@@ -140,28 +140,78 @@ def write_traffic(fetch_csv, write_csv, workload, copy_bytes):
     print(json.dumps(rec[workload], indent=1))
 
 
-def cpu_baseline(w, x, seconds):
-    """The oracle (float32 mode) on full forwards of the same workload, repeated
-    until `seconds` of host time have passed."""
-    import oracle as O
+def host_cpu():
+    """The host CPU model and the threads the oracle's BLAS uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    return model, int(threads)
+
+
+def cpu_baseline(w, x, seconds, max_rows=32768):
+    """The oracle (float32 mode) on a bounded sample of the workload: its
+    first sequences up to about max_rows context rows (all of it when
+    smaller), full forwards repeated until `seconds` of host time passed."""
+    import oracle as O
+    import numpy as np
+    cu = [int(c) for c in x["cu"]]
+    nb = 1
+    while nb < w.A and cu[nb] < max_rows:
+        nb += 1
+    Ts = cu[nb]
+    taps = [t[:Ts] for t in x["taps"]]
+    cu_s = cu[:nb + 1]
+    block_in = x["block_in"][:nb]
+    model, threads = host_cpu()
     reps = 0
+    O.block_forward(taps, x["w_c"], x["ctx_norm"], cu_s, block_in, x["block_pos"], x["layers"],
+                    x["out_norm"], w.n_heads, w.eps, dtype=np.float32)   # untimed: page-in
     t0 = time.perf_counter()
     while True:
-        O.block_forward(x["taps"], x["w_c"], x["ctx_norm"], x["cu"], x["block_in"],
-                        x["block_pos"], x["layers"], x["out_norm"], w.n_heads, w.eps,
-                        dtype=np.float32)
+        O.block_forward(taps, x["w_c"], x["ctx_norm"], cu_s, block_in, x["block_pos"], x["layers"],
+                        x["out_norm"], w.n_heads, w.eps, dtype=np.float32)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": reps * x["T"] / el, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{reps} full forwards of {w.name} (T={x['T']}) in float32 numpy, {el:.1f} s"}
+    return {"value": round(reps * Ts / el, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": model,
+            "draft_blocks_per_s": round(reps * nb / el, 3),
+            "sample": (f"{reps} float32 numpy forwards of the first {nb} of {w.A} sequences of "
+                       f"{w.name} (T={Ts} of {x['T']} context rows), {el:.1f} s")}
+
+
+ROOF_KINDS = ("gemm_ctx_fuse", "gemm_ctx_kv", "attn_split_k")
+
+
+def roofline_of(kind, w, T, A, total_ms, launches):
+    """Roofline object of one kernel kind from its HIP-event totals."""
+    amount, unit, bound = kernel_work(kind, w, T, A)
+    avg_s = total_ms / launches / 1e3
+    if unit == "flop":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = amount / avg_s / 1e12
+        runit = "TFLOP/s"
+    else:
+        peak = PEAK_HBM_GBS
+        achieved = amount / avg_s / 1e9
+        runit = "GB/s"
+    return {"bound": bound, "kernel": kind, "achieved": round(achieved, 2), "peak": peak,
+            "unit": runit, "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(kind, w.name),
+            "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step": None,
+            "work_per_launch": amount, "work_unit": unit}
 
 
 def main():
@@ -220,35 +270,33 @@ def main():
     fwd()
     torch.cuda.synchronize()
     per_kind = B.trace_end()
-    candidates = {k: v for k, v in per_kind.items() if kernel_work(k, w, T, A)}
+    candidates = {k: v for k, v in per_kind.items() if k in ROOF_KINDS}
     dominant = max(candidates, key=lambda k: candidates[k][0])
 
-    # timed region: K steps, events only around the dominant kernel's launches
-    B.trace_begin([dominant], capacity=args.steps * 16)
+    # timed region: K steps; HIP events around every launch of the three
+    # roofline kernels (on the library's stream) and around each step
+    roof_kinds = [k for k in ROOF_KINDS if k in per_kind]
+    B.trace_begin(roof_kinds, capacity=args.steps * 32)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i][0].record(fwd.stream)
         fwd()
+        ev[i][1].record(fwd.stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    dom = B.trace_end()[dominant]
+    traced = B.trace_end()
     ms_per_step = el * 1e3 / args.steps
+    step_ms = sorted(a.elapsed_time(b) for a, b in ev)
 
-    amount, unit, bound = kernel_work(dominant, w, T, A)
-    avg_s = dom[0] / dom[1] / 1e3
-    if unit == "flop":
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        achieved = amount / avg_s / 1e12
-        runit = "TFLOP/s"
-    else:
-        peak = PEAK_HBM_GBS
-        achieved = amount / avg_s / 1e9
-        runit = "GB/s"
-    roofline = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
-                "unit": runit, "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(dominant, w.name),
-                "avg_launch_us": round(avg_s * 1e6, 2),
-                "work_per_launch": amount, "work_unit": unit}
+    rooflines = {}
+    for k in roof_kinds:
+        tot, n = traced[k]
+        r = roofline_of(k, w, T, A, tot, n)
+        r["launches_per_step"] = n // args.steps
+        rooflines[k] = r
 
     res = {
         "metric": METRIC,
@@ -258,6 +306,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -266,7 +316,8 @@ def main():
         "config": {"workload": w.name, "A": A, "T": T, "m": w.m, "H": w.H, "d": w.d,
                    "n_heads": w.n_heads, "gamma": w.gamma, "n_layers": w.n_layers, "ff": w.ff},
         "draft_blocks_per_s": round(A / (ms_per_step / 1e3), 2),
-        "roofline": roofline,
+        "roofline": rooflines[dominant],
+        "rooflines": rooflines,
     }
     # the context / block split of the step, from the event-traced pass
     ctx_kinds = ("gemm_ctx_fuse", "setup", "gemm_ctx_kv")
@@ -274,6 +325,11 @@ def main():
     t_blk = sum(v[0] for k, v in per_kind.items() if k not in ctx_kinds) / 1e3
     res["context_side_tokens_per_s"] = round(T / t_ctx, 1) if t_ctx > 0 else None
     res["block_side_blocks_per_s"] = round(A / t_blk, 2) if t_blk > 0 else None
+    proj = [k for k in ("gemm_ctx_fuse", "gemm_ctx_kv") if k in traced]
+    if proj:
+        flop = sum(kernel_work(k, w, T, A)[0] * traced[k][1] for k in proj)
+        t_proj = sum(traced[k][0] for k in proj) / 1e3
+        res["projections_frac_of_bf16_peak"] = round(flop / t_proj / 1e12 / PEAK_BF16_TFLOPS, 4)
     if args.kernels:
         res["kernels_us_per_step"] = {k: round(v[0] * 1e3, 2) for k, v in
                                       sorted(per_kind.items(), key=lambda kv: -kv[1][0])}

@@ -14,6 +14,15 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
+def elem_rel_err(got, ref) -> float:
+    """Elementwise relative error max |y - r| / max(|r|, 1e-3 ||r||_inf),
+    reported for information next to the normwise bound."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    floor = 1e-3 * max(np.max(np.abs(ref)), 1e-30)
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor)))
+
+
 def dims_of(B, w):
     return B.DsparkDims(m=w.m, H=w.H, d=w.d, n_heads=w.n_heads, gamma=w.gamma,
                         n_layers=w.n_layers, ff=w.ff, eps=w.eps, dtype=w.dtype)

@@ -13,7 +13,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_helpers import TOL, Uploaded, dims_of, oracle_forward, rel_err
+from gpu_helpers import TOL, Uploaded, dims_of, elem_rel_err, oracle_forward, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -82,8 +82,36 @@ CASES = {
 }
 
 
+# Cases that must take the streaming split-K attention kernel (more than 1024
+# 64-key blocks over the heads): every storage type, head dim and the gamma
+# extremes on that path. The host asserts the plan before the run.
+STREAMING_CASES = {
+    "stream-bf16-hd64": dict(name="s1", seed_id=31, A=2, m=1, H=64, d=256, n_heads=4, gamma=3,
+                             n_layers=1, ff=512, dtype="bf16", lengths=[17000, 333]),
+    "stream-bf16-hd32-gamma16": dict(name="s2", seed_id=32, A=3, m=1, H=64, d=256, n_heads=8,
+                                     gamma=16, n_layers=1, ff=512, dtype="bf16",
+                                     lengths=[9000, 50, 0]),
+    "stream-bf16-hd128-gamma1": dict(name="s3", seed_id=33, A=1, m=2, H=64, d=256, n_heads=2,
+                                     gamma=1, n_layers=1, ff=256, dtype="bf16", lengths=[33000]),
+    "stream-f32-hd128": dict(name="s4", seed_id=34, A=1, m=1, H=64, d=256, n_heads=2, gamma=5,
+                             n_layers=1, ff=256, dtype="f32", lengths=[33100]),
+    "stream-f32-hd32": dict(name="s5", seed_id=35, A=3, m=1, H=64, d=128, n_heads=4, gamma=4,
+                            n_layers=1, ff=256, dtype="f32", lengths=[17000, 5, 0]),
+    "stream-f32-hd64-gamma16": dict(name="s6", seed_id=36, A=1, m=1, H=64, d=128, n_heads=2,
+                                    gamma=16, n_layers=1, ff=256, dtype="f32", lengths=[33000]),
+    "stream-bf16-hd64-gamma7": dict(name="s7", seed_id=37, A=2, m=1, H=64, d=256, n_heads=4,
+                                    gamma=7, n_layers=2, ff=256, dtype="bf16",
+                                    lengths=[12000, 6000]),
+}
+# Eq 2 with a K split count that does not divide m*H (float32, m = 3,
+# H = 2304: 6912 columns over 40 splits of 176)
+CASES["f32-uneven-splits"] = dict(name="f3", seed_id=38, A=1, m=3, H=2304, d=768, n_heads=6,
+                                  gamma=5, n_layers=1, ff=256, dtype="f32", lengths=[64])
+ALL_CASES = {**CASES, **STREAMING_CASES}
+
+
 def _make(case, gains="unit"):
-    kw = dict(CASES[case])
+    kw = dict(ALL_CASES[case])
     lengths = kw.pop("lengths", None)
     for k in ("L_range", "outlier_scale"):
         kw.pop(k, None)
@@ -96,17 +124,20 @@ def _make(case, gains="unit"):
     return w, x
 
 
-@pytest.mark.parametrize("case", sorted(CASES))
+@pytest.mark.parametrize("case", sorted(ALL_CASES))
 def test_block_forward_matches_oracle(case):
     w, x = _make(case)
+    plan = B.plan_info(B.OP_BLOCK_FORWARD, dims_of(B, w), x["cu"])
+    if case in STREAMING_CASES:
+        assert plan["attn_streaming"] == 1 and plan["attn_chunk"] > 64, plan
+    print(f"{case}: lengths={x['lengths'].tolist()} plan={plan}", flush=True)
     out, h, _ = _forward(w, x, h_ctx_out=True)
     tr = {}
     ref = oracle_forward(O, w, x, trace=tr)
     got = out.cpu().numpy()
-    print(f"{case}: lengths={x['lengths'].tolist()}")
     assert np.all(np.isfinite(got))
     e = rel_err(got, ref)
-    print(f"  block_out rel err {e:.3e}")
+    print(f"  block_out rel err {e:.3e} (elementwise {elem_rel_err(got, ref):.3e})")
     assert e < TOL[w.dtype]
     if x["T"] > 0:
         eh = rel_err(h.float().cpu().numpy(), tr["C"])
@@ -270,5 +301,11 @@ def test_full_size_against_stored_oracle(name):
     e = rel_err(out.cpu().numpy(), g["out"])
     idx = torch.as_tensor(g["C_idx"], device="cuda:0")
     eh = rel_err(h.index_select(0, idx).float().cpu().numpy(), g["C_rows"])
-    print(f"  block_out rel err {e:.3e}, sampled H_ctx rel err {eh:.3e}")
-    assert e < TOL["bf16"] and eh < TOL["bf16"]
+    # the block rows after the first layer: that layer alone over the same H_ctx
+    d0 = (u.block_in + u.block_pos[None]).contiguous()
+    d1 = B.block_layer(dims_of(B, w), u.cu, h, d0, u.layers[0], cu_dev=u.cu_dev)
+    torch.cuda.synchronize()
+    e1 = rel_err(d1.cpu().numpy(), g["D1"])
+    print(f"  block_out rel err {e:.3e} (elementwise {elem_rel_err(out.cpu().numpy(), g['out']):.3e}), "
+          f"D1 rel err {e1:.3e}, sampled H_ctx rel err {eh:.3e}")
+    assert e < TOL["bf16"] and eh < TOL["bf16"] and e1 < TOL["bf16"]
