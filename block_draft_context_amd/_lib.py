@@ -9,13 +9,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.s
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_CTX_FUSE, OP_BLOCK_LAYER, OP_BLOCK_FORWARD = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the no-allocation entry point's device array
 
 # every function the header declares
 EXPORTS = [
     "dspark_workspace_size", "dspark_ctx_fuse", "dspark_block_layer",
     "dspark_block_forward", "dspark_last_error", "dspark_version",
     "dspark_kernel_kinds", "dspark_kernel_name", "dspark_trace_begin",
-    "dspark_trace_end", "dspark_plan_info",
+    "dspark_trace_end", "dspark_plan_info", "dspark_block_layer_noalloc",
 ]
 PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "attn_streaming",
                "workspace_bytes")
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.dspark_trace_begin.restype = i32
     L.dspark_trace_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32]
     L.dspark_trace_end.restype = i32
+    L.dspark_block_layer_noalloc.argtypes = [ctypes.POINTER(Dims), i32, pi32, vp, vp, vp, vp,
+                                             ctypes.POINTER(LayerWeights), vp]
+    L.dspark_block_layer_noalloc.restype = i32
     L.dspark_plan_info.argtypes = [i32, ctypes.POINTER(Dims), i32, pi32, ctypes.POINTER(ctypes.c_int64), i32]
     L.dspark_plan_info.restype = i32
     _lib = L

@@ -21,7 +21,7 @@ from . import _lib as L
 __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
     "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
-    "plan_info",
+    "plan_info", "block_layer_noalloc",
 ]
 
 DsparkError = L.DsparkError
@@ -191,6 +191,20 @@ def block_layer(dims: DsparkDims, cu, h_ctx, d_in, lw: Dict[str, torch.Tensor], 
     L.check(L.lib().dspark_block_layer(ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev),
                                        _ptr(h_ctx), _ptr(d_in), _ptr(d_out), ctypes.byref(lws),
                                        _ptr(ws), nbytes, ts.cuda_stream))
+    return d_out
+
+
+def block_layer_noalloc(dims: DsparkDims, cu, h_ctx, d_in, lw: Dict[str, torch.Tensor], *,
+                        cu_dev, d_out, stream=None) -> torch.Tensor:
+    """block_layer with the library's own device scratch: the library call
+    allocates nothing. The caller passes the device copy of cu and the
+    output; calls on one GPU must not overlap."""
+    cu_h = _cu_host(cu)
+    dm = dims.c()
+    lws = _layer_struct(lw)
+    L.check(L.lib().dspark_block_layer_noalloc(ctypes.byref(dm), len(cu_h) - 1, cu_h, _ptr(cu_dev),
+                                               _ptr(h_ctx), _ptr(d_in), _ptr(d_out),
+                                               ctypes.byref(lws), _stream(stream)))
     return d_out
 
 

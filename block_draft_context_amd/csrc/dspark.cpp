@@ -394,13 +394,11 @@ dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A, const int32_t*
   return DSPARK_OK;
 }
 
-dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
-                                 const int32_t* cu_dev, const void* h_ctx, const float* d_in,
-                                 float* d_out, const dspark_layer_weights* lw, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  Plan p;
-  dspark_status st = make_plan(DSPARK_OP_BLOCK_LAYER, dims, A, cu_host, &p);
-  if (st != DSPARK_OK) return st;
+static dspark_status block_layer_impl(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                                      const int32_t* cu_dev, const void* h_ctx, const float* d_in,
+                                      float* d_out, const dspark_layer_weights* lw, void* ws,
+                                      size_t ws_bytes, void* stream, const Plan& p) {
+  dspark_status st;
   NEED_PTR(cu_dev);
   if (p.T > 0) NEED_PTR(h_ctx);
   NEED_PTR(d_in);
@@ -425,6 +423,33 @@ dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32
   st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, ws, s);
   if (st != DSPARK_OK) return st;
   return run_layer(dims, p, A, cu_dev, *lw, 0, d_in, d_out, ws, s);
+}
+
+dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                                 const int32_t* cu_dev, const void* h_ctx, const float* d_in,
+                                 float* d_out, const dspark_layer_weights* lw, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_LAYER, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  return block_layer_impl(dims, A, cu_host, cu_dev, h_ctx, d_in, d_out, lw, ws, ws_bytes, stream, p);
+}
+
+dspark_status dspark_block_layer_noalloc(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                                         const int32_t* cu_dev, const void* h_ctx, const float* d_in,
+                                         float* d_out, const dspark_layer_weights* lw, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_LAYER, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  if (p.total > kNoAllocScratchBytes)
+    return fail(DSPARK_EUNSUPPORTED,
+                "this layer needs %zu bytes of scratch; dspark_block_layer_noalloc holds at most %zu "
+                "(use dspark_block_layer with a workspace)",
+                p.total, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  DSPARK_HIP(noalloc_scratch(&ws));
+  return block_layer_impl(dims, A, cu_host, cu_dev, h_ctx, d_in, d_out, lw, ws, kNoAllocScratchBytes,
+                          stream, p);
 }
 
 dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int32_t* cu_host,

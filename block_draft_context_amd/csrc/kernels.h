@@ -23,6 +23,12 @@ enum KernelKind : int {
   K_COUNT
 };
 
+// Scratch of the no-allocation entry point: a file-scope device array of
+// this many bytes (noalloc.hip); noalloc_scratch gives its device address on
+// the current device (taken once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 const char* kernel_name(int kind);
 void trace_pre(int kind, hipStream_t s);
 void trace_post(int kind, hipStream_t s);

@@ -144,6 +144,27 @@ dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A,
                                  const dspark_layer_weights* lw,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* dspark_block_layer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, with the scratch in a
+ * file-scope device array of 64 MiB inside the library instead of a
+ * caller workspace. The array exists once per GPU for the life of the
+ * process; its device address is resolved on the first call on each device.
+ * The call allocates nothing and calls no allocating routine.
+ *   - Arguments as for dspark_block_layer, without ws / ws_bytes; the
+ *     stream must belong to the current device.
+ *   - Sizes whose workspace (dspark_workspace_size, DSPARK_OP_BLOCK_LAYER)
+ *     exceeds 64 MiB return DSPARK_EUNSUPPORTED with a message, before
+ *     anything is enqueued (about 14k context rows at d = 1024 in bf16).
+ *   - Every call on one GPU shares that GPU's array, so calls that overlap
+ *     on one GPU (several streams, several host threads) race: serialise
+ *     them. The array keeps the last call's contents; every value a call
+ *     reads from it is written earlier in the same call. */
+dspark_status dspark_block_layer_noalloc(const dspark_dims* dims, int32_t A,
+                                         const int32_t* cu_host, const int32_t* cu_dev,
+                                         const void* h_ctx, const float* d_in, float* d_out,
+                                         const dspark_layer_weights* lw, void* stream);
+
 /* The whole draft block (#backbone): Eq 2, D0 = block_in + block_pos,
  * dims->n_layers x (Eq 3 + FFN), then the output norm.
  *   block_in   [A, gamma, d] float32 token rows (anchor row, mask rows)
