@@ -8,7 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.s
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-OP_CTX_FUSE, OP_BLOCK_LAYER, OP_BLOCK_FORWARD = 0, 1, 2
+OP_CTX_FUSE, OP_BLOCK_LAYER, OP_BLOCK_FORWARD, OP_CTX_APPEND, OP_BLOCK_PROPOSE = 0, 1, 2, 3, 4
 NOALLOC_SCRATCH_BYTES = 64 << 20   # the no-allocation entry point's device array
 
 # every function the header declares
@@ -17,6 +17,7 @@ EXPORTS = [
     "dspark_block_forward", "dspark_last_error", "dspark_version",
     "dspark_kernel_kinds", "dspark_kernel_name", "dspark_trace_begin",
     "dspark_trace_end", "dspark_plan_info", "dspark_block_layer_noalloc",
+    "dspark_cache_bytes", "dspark_cache_reset", "dspark_ctx_append", "dspark_block_propose",
 ]
 PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "attn_streaming",
                "workspace_bytes")
@@ -83,6 +84,17 @@ def lib() -> ctypes.CDLL:
     L.dspark_block_layer_noalloc.argtypes = [ctypes.POINTER(Dims), i32, pi32, vp, vp, vp, vp,
                                              ctypes.POINTER(LayerWeights), vp]
     L.dspark_block_layer_noalloc.restype = i32
+    L.dspark_cache_bytes.argtypes = [ctypes.POINTER(Dims), i32, i32]
+    L.dspark_cache_bytes.restype = sz
+    L.dspark_cache_reset.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, vp]
+    L.dspark_cache_reset.restype = i32
+    L.dspark_ctx_append.argtypes = [ctypes.POINTER(Dims), i32, i32, pi32, vp, pi32, vp,
+                                    ctypes.POINTER(vp), i64, vp, vp, ctypes.POINTER(LayerWeights),
+                                    vp, vp, sz, vp]
+    L.dspark_ctx_append.restype = i32
+    L.dspark_block_propose.argtypes = [ctypes.POINTER(Dims), i32, i32, pi32, vp, vp, vp, vp,
+                                       ctypes.POINTER(LayerWeights), vp, vp, vp, sz, vp]
+    L.dspark_block_propose.restype = i32
     L.dspark_plan_info.argtypes = [i32, ctypes.POINTER(Dims), i32, pi32, ctypes.POINTER(ctypes.c_int64), i32]
     L.dspark_plan_info.restype = i32
     _lib = L

@@ -21,7 +21,7 @@ from . import _lib as L
 __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
     "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
-    "plan_info", "block_layer_noalloc",
+    "plan_info", "block_layer_noalloc", "cache_bytes", "DraftCache",
 ]
 
 DsparkError = L.DsparkError
@@ -228,6 +228,90 @@ def block_forward(dims: DsparkDims, cu, taps, w_c, ctx_norm, block_in, block_pos
         _ptr(w_c), _ptr(ctx_norm), _ptr(block_in), _ptr(block_pos), arr, _ptr(out_norm),
         _ptr(h_ctx_out), _ptr(block_out), _ptr(ws), nbytes, ts.cuda_stream))
     return block_out
+
+
+def cache_bytes(dims: DsparkDims, A: int, cap: int) -> int:
+    dm = dims.c()
+    n = L.lib().dspark_cache_bytes(ctypes.byref(dm), A, cap)
+    if n == 0:
+        raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+    return int(n)
+
+
+class DraftCache:
+    """A draft cache (include/dspark.h, incremental context) for A sequences
+    of up to ``cap`` context rows each: the device buffer, cleared on
+    creation, and the sequences' lengths kept on the host. ``append`` runs
+    dspark_ctx_append (Eq 2 + every layer's context K/V of the new rows into
+    the cache), ``propose`` runs dspark_block_propose (the draft block over
+    the cached rows)."""
+
+    def __init__(self, dims: DsparkDims, A: int, cap: int, device="cuda:0", stream=None):
+        self.dims, self.A, self.cap = dims, A, cap
+        self.device = torch.device(device)
+        ts = _torch_stream(stream)
+        with torch.cuda.stream(ts):
+            self.buf = torch.empty(cache_bytes(dims, A, cap), dtype=torch.uint8, device=self.device)
+        self.lengths = [0] * A
+        self.reset(stream=stream)
+
+    def reset(self, stream=None) -> None:
+        dm = self.dims.c()
+        L.check(L.lib().dspark_cache_reset(ctypes.byref(dm), self.A, self.cap, _ptr(self.buf),
+                                           _stream(stream)))
+        self.lengths = [0] * self.A
+
+    def cu(self) -> List[int]:
+        """Prefix offsets of the cached lengths."""
+        out = [0]
+        for n in self.lengths:
+            out.append(out[-1] + n)
+        return out
+
+    def append(self, taps, counts: Sequence[int], w_c, ctx_norm, layers, *, ws=None,
+               stream=None) -> None:
+        """Append counts[b] new context rows to sequence b; the new rows of
+        all sequences are packed in the taps in sequence order."""
+        counts = [int(c) for c in counts]
+        if len(counts) != self.A:
+            raise ValueError(f"{len(counts)} counts for {self.A} sequences")
+        ncu = [0]
+        for c in counts:
+            ncu.append(ncu[-1] + c)
+        taps = _tap_list(taps, self.dims)
+        ncu_h = _cu_host(ncu)
+        pos_h = (ctypes.c_int32 * self.A)(*self.lengths)
+        ts = _torch_stream(stream)
+        with torch.cuda.stream(ts):
+            ncu_d = torch.as_tensor(ncu, dtype=torch.int32, device=self.device)
+            pos_d = torch.as_tensor(self.lengths, dtype=torch.int32, device=self.device)
+            ws, nbytes = _workspace(L.OP_CTX_APPEND, self.dims, ncu, ws, self.device)
+        dm = self.dims.c()
+        arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+        L.check(L.lib().dspark_ctx_append(ctypes.byref(dm), self.A, self.cap, ncu_h, _ptr(ncu_d), pos_h,
+                                          _ptr(pos_d), _tap_ptrs(taps), _tap_ld(taps), _ptr(w_c),
+                                          _ptr(ctx_norm), arr, _ptr(self.buf), _ptr(ws), nbytes,
+                                          ts.cuda_stream))
+        self.lengths = [n + c for n, c in zip(self.lengths, counts)]
+
+    def propose(self, block_in, block_pos, layers, out_norm=None, *, block_out=None, ws=None,
+                cu_dev=None, stream=None) -> torch.Tensor:
+        """The draft block [A, gamma, d] over the cached context."""
+        cu = self.cu()
+        cu_h = _cu_host(cu)
+        ts = _torch_stream(stream)
+        with torch.cuda.stream(ts):
+            if block_out is None:
+                block_out = torch.empty_like(block_in)
+            cu_dev = _cu_dev(cu, cu_dev, self.device)
+            ws, nbytes = _workspace(L.OP_BLOCK_PROPOSE, self.dims, cu, ws, self.device)
+        dm = self.dims.c()
+        arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+        L.check(L.lib().dspark_block_propose(ctypes.byref(dm), self.A, self.cap, cu_h, _ptr(cu_dev),
+                                             _ptr(self.buf), _ptr(block_in), _ptr(block_pos), arr,
+                                             _ptr(out_norm), _ptr(block_out), _ptr(ws), nbytes,
+                                             ts.cuda_stream))
+        return block_out
 
 
 class PreparedForward:

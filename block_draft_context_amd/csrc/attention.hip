@@ -83,7 +83,9 @@ int attention_chunk(const int32_t* cu_host, int A, int n_heads) {
 // Sequence and key range [k0, k1) of a split-K tile; false past the plan.
 // The tile prefix (device plan) is searched for the owning sequence; with one
 // sequence the range follows from the tile index and the context length T1,
-// so the K/V loads need no dependent memory access first.
+// so the K/V loads need no dependent memory access first. Sequence b's keys
+// start at row cu[b] of the slab (a packed context) or at b * seq_stride (a
+// draft cache of seq_stride rows per sequence); there are cu[b+1] - cu[b].
 struct TileRange {
   int b;
   int64_t k0, k1;   // the tile's chunk of keys
@@ -92,7 +94,7 @@ struct TileRange {
 };
 DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restrict__ cu,
                            const int32_t* __restrict__ prefix, int chunk, int total_tiles,
-                           TileRange& r) {
+                           int64_t seq_stride, TileRange& r) {
   if (tile >= total_tiles) return false;
   if (A == 1) {
     r.b = 0;
@@ -113,7 +115,8 @@ DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restric
   }
   r.b = lo;
   const int c = tile - prefix[lo];
-  const int64_t kseq0 = cu[lo], kseq1 = cu[lo + 1];
+  const int64_t kseq0 = seq_stride > 0 ? (int64_t)lo * seq_stride : cu[lo];
+  const int64_t kseq1 = kseq0 + (cu[lo + 1] - cu[lo]);
   r.k0 = min(kseq1, kseq0 + (int64_t)c * chunk);
   r.k1 = min(kseq1, r.k0 + chunk);
   r.s0 = kseq0;
@@ -132,7 +135,7 @@ template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
-    int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int total_tiles, int64_t seq_stride, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
   constexpr int NKV = HD / E;            // K vectors per key row
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   TileRange tr;
-  if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, tr)) return;
+  if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, seq_stride, tr)) return;
   const int b = tr.b;
   // the sequence's keys; this tile owns every nt-th of its 64-key blocks
   const int64_t k0 = tr.s0, k1 = tr.s1;
@@ -391,7 +394,7 @@ template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_hsplit_kernel(
     const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
-    int total_tiles, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int total_tiles, int64_t seq_stride, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
   constexpr int NKV = HD / E;            // K vectors per key row
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   TileRange tr;
-  if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, tr)) return;
+  if (!tile_range(tile, A, T1, cu, prefix, chunk, total_tiles, seq_stride, tr)) return;
   const int b = tr.b;
   const int64_t k0 = tr.k0, k1 = tr.k1;
   const int64_t blk0 = k0 >> 6;
@@ -819,12 +822,12 @@ static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
   if (a.chunk == 64) {
     attn_hsplit_kernel<S, HD, G><<<grid, 256, 0, s>>>(
         a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-        a.kv.T, a.chunk, a.total_tiles, a.part_o, a.part_ml);
+        a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.part_o, a.part_ml);
     return;
   }
   attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(
       a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-      a.kv.T, a.chunk, a.total_tiles, a.part_o, a.part_ml);
+      a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.part_o, a.part_ml);
 }
 
 template <typename S, int HD>

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -84,7 +85,7 @@ struct Plan {
   CtxSplit ctx;   // K splits of the Eq 2 projection
   size_t esz = 4;
   // workspace offsets (bytes)
-  size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0;
+  size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0, rowmap = 0;
   size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, E = 0, GU = 0;
   size_t total = 0;
 };
@@ -109,7 +110,8 @@ static dspark_status check_dims(const dspark_dims* dm, int op) {
   if (dm->ff % 128 != 0) return fail(DSPARK_EUNSUPPORTED, "ff %d must be a multiple of 128", dm->ff);
   if (dm->ff > 16256) return fail(DSPARK_EUNSUPPORTED, "ff %d above the supported 16256", dm->ff);
   if (!(dm->eps >= 0.f) || !std::isfinite(dm->eps)) return fail(DSPARK_EINVAL, "eps must be finite and >= 0");
-  if (op == DSPARK_OP_BLOCK_FORWARD && (dm->n_layers < 1 || dm->n_layers > 16))
+  if ((op == DSPARK_OP_BLOCK_FORWARD || op == DSPARK_OP_CTX_APPEND || op == DSPARK_OP_BLOCK_PROPOSE) &&
+      (dm->n_layers < 1 || dm->n_layers > 16))
     return fail(dm->n_layers < 1 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "n_layers %d not in [1, 16]",
                 dm->n_layers);
   return DSPARK_OK;
@@ -142,31 +144,37 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   // The context projections address H_ctx (the A operand of the K/V
   // product) and W_c with 32-bit byte offsets (the taps are checked with
   // their leading dimension in check_taps).
+  // The ops' parts: Eq 2 (the fuse product), the context K/V product (over
+  // H_ctx rows), and the block side (attention over context K/V in the
+  // workspace or in a draft cache).
+  const bool runs_eq2 = op == DSPARK_OP_CTX_FUSE || op == DSPARK_OP_BLOCK_FORWARD || op == DSPARK_OP_CTX_APPEND;
+  const bool runs_kv = op == DSPARK_OP_BLOCK_LAYER || op == DSPARK_OP_BLOCK_FORWARD || op == DSPARK_OP_CTX_APPEND;
+  const bool runs_block = op == DSPARK_OP_BLOCK_LAYER || op == DSPARK_OP_BLOCK_FORWARD ||
+                          op == DSPARK_OP_BLOCK_PROPOSE;
   const int64_t kMaxBytes = (int64_t)1 << 32;
-  if (T * dm->d * p->esz >= kMaxBytes)
+  if (op != DSPARK_OP_BLOCK_PROPOSE && T * dm->d * p->esz >= kMaxBytes)
     return fail(DSPARK_EUNSUPPORTED, "H_ctx spans %lld bytes (T * d); at most 4 GiB is supported",
                 (long long)(T * dm->d * p->esz));
-  if (op != DSPARK_OP_BLOCK_LAYER && (int64_t)dm->d * dm->m * dm->H * p->esz >= kMaxBytes)
+  if (runs_eq2 && (int64_t)dm->d * dm->m * dm->H * p->esz >= kMaxBytes)
     return fail(DSPARK_EUNSUPPORTED, "W_c spans %lld bytes (d * m * H); at most 4 GiB is supported",
                 (long long)((int64_t)dm->d * dm->m * dm->H * p->esz));
   const int d = dm->d, mH = dm->m * dm->H, ff = dm->ff, M = p->M;
   p->ctx = ctx_gemm_split(dm->dtype, T, d, mH);
   p->chunk = attention_chunk(cu_host, A, dm->n_heads);
   p->total_chunks = (int)attention_tiles(cu_host, A, p->chunk);
-  p->kv_layers = op == DSPARK_OP_BLOCK_FORWARD ? dm->n_layers : 1;
+  p->kv_layers = op == DSPARK_OP_BLOCK_LAYER ? 1 : dm->n_layers;
 
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const bool need_ctx = op != DSPARK_OP_BLOCK_LAYER;
-  const bool need_block = op != DSPARK_OP_CTX_FUSE;
-  if (need_ctx) {
-    p->ppart = take((size_t)p->ctx.splits * T * d * 4);
-  }
-  if (need_block) {
+  if (runs_eq2) p->ppart = take((size_t)p->ctx.splits * T * d * 4);
+  if (runs_kv) {
     if (bf) p->wkvt = take((size_t)2 * p->kv_layers * d * d * 2);
-    if (op == DSPARK_OP_BLOCK_FORWARD) p->hctx = take((size_t)T * d * p->esz);
+    if (op != DSPARK_OP_BLOCK_LAYER) p->hctx = take((size_t)T * d * p->esz);
     p->rinv = take((size_t)T * 4);
-    p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * d * p->esz);
+    if (op == DSPARK_OP_CTX_APPEND) p->rowmap = take((size_t)T * 4);
+    else p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * d * p->esz);
+  }
+  if (runs_block) {
     p->prefix = take((size_t)(A + 1) * 4);
     p->po = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * p->hd * 4);
     p->pml = take((size_t)p->total_chunks * dm->n_heads * dm->gamma * 2 * 4);
@@ -268,26 +276,57 @@ static BMats kv_mats(const dspark_layer_weights* layers, int nl, int d) {
 // Context K/V of `nl` layers from H_ctx (rinv, and for bf16 the stacked
 // weights, already written by the set-up pass).
 static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void* h_ctx, const float* rinv,
-                                const dspark_layer_weights* layers, int nl, void* ws, hipStream_t s) {
+                                const dspark_layer_weights* layers, int nl, const KVDesc& kv, void* ws,
+                                hipStream_t s) {
   if (p.T == 0) return DSPARK_OK;
   const int d = dm->d;
   const BMats b = kv_mats(layers, nl, d);
   void* wkvt = dm->dtype == DSPARK_BF16 ? at<char>(ws, p.wkvt) : nullptr;
-  KVDesc kv{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
   DSPARK_HIP(launch_gemm_kv(dm->dtype, h_ctx, b, wkvt, rinv, kv, d, nl, s));
   return DSPARK_OK;
+}
+
+// The context K/V of a forward or a layer: packed rows in the workspace.
+static KVDesc ws_kv(const dspark_dims* dm, const Plan& p, void* ws) {
+  KVDesc kv{};
+  kv.base = at<char>(ws, p.kv);
+  kv.Tpad = p.Tpad;
+  kv.T = (int)p.T;
+  kv.hd = p.hd;
+  kv.n_heads = dm->n_heads;
+  return kv;
+}
+
+// A draft cache of A sequences with `cap` rows each; T = cached rows in
+// total (the attention side) or the new rows of an append (the K/V side).
+static KVDesc cache_kv(const dspark_dims* dm, const Plan& p, int A, int cap, void* cache,
+                       const int32_t* dst_row) {
+  KVDesc kv{};
+  kv.base = cache;
+  kv.Tpad = (int64_t)A * cap;
+  kv.T = (int)p.T;
+  kv.hd = p.hd;
+  kv.n_heads = dm->n_heads;
+  kv.seq_stride = cap;
+  kv.dst_row = dst_row;
+  return kv;
 }
 
 // Set-up roles shared by the block ops: tile plan and, for bf16, the stacked
 // K/V weights.
 static void setup_block_roles(const dspark_dims* dm, const Plan& p, int A, const int32_t* cu_dev,
-                              const dspark_layer_weights* layers, int nl, void* ws, SetupArgs* sa) {
+                              void* ws, SetupArgs* sa) {
   sa->cu = cu_dev;
   sa->A = A;
   sa->chunk = p.chunk;
   sa->prefix = at<int32_t>(ws, p.prefix);
   sa->zero = at<float>(ws, p.E);
   sa->zero_n = (int64_t)p.kv_layers * p.M * dm->d;
+}
+
+// The K/V product's stacked, gain-folded weights (bf16 only).
+static void setup_prep_role(const dspark_dims* dm, const Plan& p, const dspark_layer_weights* layers, int nl,
+                            void* ws, SetupArgs* sa) {
   if (dm->dtype == DSPARK_BF16 && p.T > 0) {
     sa->b = kv_mats(layers, nl, dm->d);
     sa->Bt = at<char>(ws, p.wkvt);
@@ -296,8 +335,8 @@ static void setup_block_roles(const dspark_dims* dm, const Plan& p, int A, const
 
 // One draft layer on the block rows D (float32 [M][d]); writes D_next.
 static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, const int32_t* cu_dev,
-                               const dspark_layer_weights& lw, int kv_layer, const float* D,
-                               float* D_next, void* ws, hipStream_t s) {
+                               const dspark_layer_weights& lw, int kv_layer, const KVDesc& kv,
+                               const float* D, float* D_next, void* ws, hipStream_t s) {
   const int d = dm->d, ff = dm->ff, M = p.M, G = dm->gamma;
   const int dt = dm->dtype;
   float* Q = at<float>(ws, p.Q);
@@ -319,7 +358,7 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   // with the output projection, E = D + Attn Wo^T
   AttnArgs aa{};
   aa.Q = Q; aa.Kd = Kd; aa.Vd = Vd;
-  aa.kv = KVDesc{at<char>(ws, p.kv), p.Tpad, (int)p.T, p.hd, dm->n_heads};
+  aa.kv = kv;
   aa.layer = kv_layer;
   aa.cu = cu_dev;
   aa.prefix = at<int32_t>(ws, p.prefix);
@@ -353,7 +392,7 @@ using namespace dspark;
 extern "C" {
 
 size_t dspark_workspace_size(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host) {
-  if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_FORWARD) {
+  if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_PROPOSE) {
     fail(DSPARK_EINVAL, "unknown op %d", op);
     return 0;
   }
@@ -413,16 +452,18 @@ static dspark_status block_layer_impl(const dspark_dims* dims, int32_t A, const 
   SetupArgs sa{};
   sa.d = dims->d;
   sa.eps = dims->eps;
-  setup_block_roles(dims, p, A, cu_dev, lw, 1, ws, &sa);
+  setup_block_roles(dims, p, A, cu_dev, ws, &sa);
+  setup_prep_role(dims, p, lw, 1, ws, &sa);
   if (p.T > 0) {
     sa.T = p.T;
     sa.h_in = h_ctx;
     sa.rinv = rinv;
   }
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
-  st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, ws, s);
+  const KVDesc kv = ws_kv(dims, p, ws);
+  st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, kv, ws, s);
   if (st != DSPARK_OK) return st;
-  return run_layer(dims, p, A, cu_dev, *lw, 0, d_in, d_out, ws, s);
+  return run_layer(dims, p, A, cu_dev, *lw, 0, kv, d_in, d_out, ws, s);
 }
 
 dspark_status dspark_block_layer(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
@@ -490,7 +531,8 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   SetupArgs sa{};
   sa.d = dims->d;
   sa.eps = dims->eps;
-  setup_block_roles(dims, p, A, cu_dev, layers, dims->n_layers, ws, &sa);
+  setup_block_roles(dims, p, A, cu_dev, ws, &sa);
+  setup_prep_role(dims, p, layers, dims->n_layers, ws, &sa);
   sa.block_in = block_in;
   sa.block_pos = block_pos;
   sa.gamma = dims->gamma;
@@ -504,12 +546,13 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
     sa.rinv = rinv;
   }
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
-  st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, ws, s);
+  const KVDesc kv = ws_kv(dims, p, ws);
+  st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, kv, ws, s);
   if (st != DSPARK_OK) return st;
   const int N = dims->n_layers;
   for (int i = 0; i < N; ++i) {
     float* Dn = (i == N - 1 && !out_norm) ? block_out : Db;
-    st = run_layer(dims, p, A, cu_dev, layers[i], i, Da, Dn, ws, s);
+    st = run_layer(dims, p, A, cu_dev, layers[i], i, kv, Da, Dn, ws, s);
     if (st != DSPARK_OK) return st;
     std::swap(Da, Db);
   }
@@ -519,9 +562,160 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   return DSPARK_OK;
 }
 
+// ---------------------------------------------------------------------------
+// incremental context: a draft cache, appends, and the block side over it
+// ---------------------------------------------------------------------------
+static dspark_status check_cache(const dspark_dims* dims, int32_t A, int32_t cap, size_t* bytes) {
+  dspark_status st = check_dims(dims, DSPARK_OP_BLOCK_PROPOSE);
+  if (st != DSPARK_OK) return st;
+  if (A < 1) return fail(DSPARK_EINVAL, "A = %d < 1", A);
+  if (cap < 64 || cap % 64 != 0) return fail(DSPARK_EINVAL, "cap %d must be a positive multiple of 64", cap);
+  if ((int64_t)A * cap > (int64_t)INT32_MAX)
+    return fail(DSPARK_EUNSUPPORTED, "A * cap = %lld rows; at most 2^31 - 1 are supported",
+                (long long)A * cap);
+  const size_t esz = dims->dtype == DSPARK_BF16 ? 2 : 4;
+  *bytes = (size_t)dims->n_layers * 2 * (size_t)A * cap * dims->d * esz;
+  return DSPARK_OK;
+}
+
+size_t dspark_cache_bytes(const dspark_dims* dims, int32_t A, int32_t cap) {
+  size_t bytes = 0;
+  if (check_cache(dims, A, cap, &bytes) != DSPARK_OK) return 0;
+  return bytes;
+}
+
+dspark_status dspark_cache_reset(const dspark_dims* dims, int32_t A, int32_t cap, void* cache,
+                                 void* stream) {
+  size_t bytes = 0;
+  dspark_status st = check_cache(dims, A, cap, &bytes);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(cache);
+  SetupArgs sa{};
+  sa.d = dims->d;
+  sa.zero = static_cast<float*>(cache);
+  sa.zero_n = (int64_t)(bytes / 4);
+  DSPARK_HIP(launch_setup(dims->dtype, sa, static_cast<hipStream_t>(stream)));
+  return DSPARK_OK;
+}
+
+dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap, const int32_t* ncu_host,
+                                const int32_t* ncu_dev, const int32_t* pos_host, const int32_t* pos_dev,
+                                const void* const* taps, int64_t ld_tap, const void* w_c,
+                                const float* ctx_norm, const dspark_layer_weights* layers, void* cache,
+                                void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_CTX_APPEND, dims, A, ncu_host, &p);
+  if (st != DSPARK_OK) return st;
+  size_t bytes = 0;
+  st = check_cache(dims, A, cap, &bytes);
+  if (st != DSPARK_OK) return st;
+  if (!pos_host) return fail(DSPARK_EINVAL, "pos_host is NULL");
+  for (int b = 0; b < A; ++b) {
+    const int64_t n = ncu_host[b + 1] - ncu_host[b];
+    if (pos_host[b] < 0 || (int64_t)pos_host[b] + n > cap)
+      return fail(DSPARK_EINVAL, "sequence %d: %lld rows at position %d do not fit a cache of %d rows", b,
+                  (long long)n, pos_host[b], cap);
+  }
+  NEED_PTR(ncu_dev);
+  NEED_PTR(pos_dev);
+  st = check_taps(dims, taps, ld_tap, p.T);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(w_c);
+  NEED_PTR(ctx_norm);
+  if (!layers) return fail(DSPARK_EINVAL, "layers is NULL");
+  for (int i = 0; i < dims->n_layers; ++i) {
+    st = check_layer(&layers[i], i);
+    if (st != DSPARK_OK) return st;
+  }
+  NEED_PTR(cache);
+  NEED_PTR(ws);
+  if (ws_bytes < p.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
+  if (p.T == 0) return DSPARK_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ws, s);
+  if (st != DSPARK_OK) return st;
+  // Eq 2's row norm of the new rows, the stacked K/V weights, the row map
+  SetupArgs sa{};
+  sa.d = dims->d;
+  sa.eps = dims->eps;
+  sa.A = A;
+  setup_prep_role(dims, p, layers, dims->n_layers, ws, &sa);
+  sa.T = p.T;
+  sa.part = at<float>(ws, p.ppart);
+  sa.splits = p.ctx.splits;
+  sa.g = ctx_norm;
+  sa.h = at<char>(ws, p.hctx);
+  sa.rinv = at<float>(ws, p.rinv);
+  sa.ncu = ncu_dev;
+  sa.pos = pos_dev;
+  sa.cap = cap;
+  sa.map_T = p.T;
+  sa.dst_row = at<int32_t>(ws, p.rowmap);
+  DSPARK_HIP(launch_setup(dims->dtype, sa, s));
+  const KVDesc kv = cache_kv(dims, p, A, cap, cache, at<int32_t>(ws, p.rowmap));
+  return run_ctx_kv(dims, p, at<char>(ws, p.hctx), at<float>(ws, p.rinv), layers, dims->n_layers, kv, ws, s);
+}
+
+dspark_status dspark_block_propose(const dspark_dims* dims, int32_t A, int32_t cap, const int32_t* cu_host,
+                                   const int32_t* cu_dev, const void* cache, const float* block_in,
+                                   const float* block_pos, const dspark_layer_weights* layers,
+                                   const float* out_norm, float* block_out, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_PROPOSE, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  size_t bytes = 0;
+  st = check_cache(dims, A, cap, &bytes);
+  if (st != DSPARK_OK) return st;
+  for (int b = 0; b < A; ++b)
+    if (cu_host[b + 1] - cu_host[b] > cap)
+      return fail(DSPARK_EINVAL, "sequence %d has %d cached rows, more than the cache's %d", b,
+                  cu_host[b + 1] - cu_host[b], cap);
+  NEED_PTR(cu_dev);
+  NEED_PTR(cache);
+  NEED_PTR(block_in);
+  NEED_PTR(block_pos);
+  if (!layers) return fail(DSPARK_EINVAL, "layers is NULL");
+  for (int i = 0; i < dims->n_layers; ++i) {
+    st = check_layer(&layers[i], i);
+    if (st != DSPARK_OK) return st;
+  }
+  OPT_PTR(out_norm);
+  NEED_PTR(block_out);
+  NEED_PTR(ws);
+  if (ws_bytes < p.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* Da = at<float>(ws, p.D);
+  float* Db = at<float>(ws, p.D2);
+  // tile plan, cleared accumulators, D0 = block_in + block_pos
+  SetupArgs sa{};
+  sa.d = dims->d;
+  sa.eps = dims->eps;
+  setup_block_roles(dims, p, A, cu_dev, ws, &sa);
+  sa.block_in = block_in;
+  sa.block_pos = block_pos;
+  sa.gamma = dims->gamma;
+  sa.D0 = Da;
+  DSPARK_HIP(launch_setup(dims->dtype, sa, s));
+  const KVDesc kv = cache_kv(dims, p, A, cap, const_cast<void*>(cache), nullptr);
+  const int N = dims->n_layers;
+  for (int i = 0; i < N; ++i) {
+    float* Dn = (i == N - 1 && !out_norm) ? block_out : Db;
+    st = run_layer(dims, p, A, cu_dev, layers[i], i, kv, Da, Dn, ws, s);
+    if (st != DSPARK_OK) return st;
+    std::swap(Da, Db);
+  }
+  if (out_norm)
+    DSPARK_HIP(launch_block_rows(Da, nullptr, A, dims->gamma, dims->d, out_norm, dims->eps, nullptr,
+                                 block_out, s));
+  return DSPARK_OK;
+}
+
 int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host,
                          int64_t* out, int32_t n) {
-  if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_FORWARD) {
+  if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_PROPOSE) {
     fail(DSPARK_EINVAL, "unknown op %d", op);
     return 0;
   }

@@ -44,15 +44,25 @@ struct EpiKV {                 // K/V of every layer, row scale, tiled layout
   const float* rinv;
   int64_t Tpad;
   int T, d, hd, n_heads;
+  const int32_t* dst_row;      // null: row r at r (zeros at T .. Tpad-1); else row r < T at dst_row[r]
   DSPARK_DEV void store(int /*z*/, int r, int n, float v, int /*M*/, int /*N*/) const {
-    if (r >= Tpad) return;
+    int64_t t;
+    float val;
+    if (dst_row) {
+      if (r >= T) return;
+      t = dst_row[r];
+      val = v * rinv[r];
+    } else {
+      if (r >= Tpad) return;
+      t = r;
+      val = (r < T) ? v * rinv[r] : 0.f;
+    }
     const int layer = n / (2 * d);
     const int kv = (n / d) & 1;
     const int w = n % d;
     const int head = w / hd, c = w % hd;
-    const float val = (r < T) ? v * rinv[r] : 0.f;
     const int64_t hb = KVLayout<S>::head_base(layer, kv, head, n_heads, Tpad, hd);
-    const int64_t off = kv == 0 ? KVLayout<S>::k_off(r, c, hd) : KVLayout<S>::v_off(r, c, hd);
+    const int64_t off = kv == 0 ? KVLayout<S>::k_off(t, c, hd) : KVLayout<S>::v_off(t, c, hd);
     base[hb + off] = from_f32<S>(val);
   }
 };
@@ -310,6 +320,7 @@ struct EpiKVBig {              // all layers' K/V, row scale, attention layout
   int64_t Tpad;
   int T, d, hd, n_heads;
   int n_base;                  // column of the stacked K/V where this launch's columns start
+  const int32_t* dst_row;      // null: row r at r (zeros at T .. Tpad-1); else row r < T at dst_row[r]
   static constexpr bool kStaged = true;
   static constexpr bool kSwap = true;     // accumulate C^T: a lane holds one row
 };
@@ -487,11 +498,15 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   // first TM / 64 waves (the tile's TM rows), issued ahead of the stage
   // loads, so they hold no registers through the main loop and are waited
   // for with the first stage.
+  // A cache target also stages each row's slab row (the row map) the same way.
   float* rsc_lds = reinterpret_cast<float*>(smem + BG_LDS);
+  int32_t* dst_lds = reinterpret_cast<int32_t*>(smem + BG_LDS + TM * 4);
   if constexpr (Epi::kSwap) {
     if (nsteps > 0 && wave < TM / 64) {
       const int row = min(m0 + wave * 64 + lane, epi.T - 1);
       __builtin_amdgcn_global_load_lds(epi.rinv + row, (lds_ptr_t)(rsc_lds + wave * 64), 4, 0, 0);
+      if (epi.dst_row)
+        __builtin_amdgcn_global_load_lds(epi.dst_row + row, (lds_ptr_t)(dst_lds + wave * 64), 4, 0, 0);
     }
   }
 
@@ -563,6 +578,10 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
     // becomes 16-byte vectors of the attention layout with lane exchanges
     // only: K (one token x 8 columns) pairs lane l with l^32, V (4 tokens x 2
     // columns) transposes dwords among the 4 lanes of consecutive tokens.
+    // With a row map (a cache target) row r < T goes to slab row dst_row[r]
+    // and no padding rows are written; a V vector whose four rows land on
+    // four consecutive slab rows starting at a multiple of 4 is stored
+    // whole, any other as four dwords.
     using S = std::remove_pointer_t<decltype(epi.base)>;
     using L = KVLayout<S>;
     static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
@@ -570,11 +589,13 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
     const int layer = nw / (2 * epi.d);
     const int kv = (nw / epi.d) & 1;
     const int k4 = lane & 3;
+    const bool mapped = epi.dst_row != nullptr;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int64_t tb = (int64_t)m0 + wm * WSM + i * 32;
+      const int lr = wm * WSM + i * 32;   // the block's first row within the tile
       // padding rows (T <= row < Tpad) are written as zeros
-      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[wm * WSM + i * 32 + r32] : 0.f;
+      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[lr + r32] : 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int w = (nw + j * 32) % epi.d;
@@ -588,7 +609,8 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
           for (int x = 0; x < 2; ++x)
             P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rs, acc[i][j][4 * q + 2 * x + 1] * rs);
         if (kv == 0) {
-          const int64_t t = tb + r32;
+          const int64_t t = mapped ? (int64_t)dst_lds[lr + r32] : tb + r32;
+          const bool live = mapped ? tb + r32 < epi.T : t < epi.Tpad;
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
             // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
@@ -596,11 +618,12 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
             const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
             const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
             const int g = qq + 2 * hi;
-            if (t < epi.Tpad)
+            if (live)
               __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)));
           }
         } else {
           const int64_t t0 = tb + (r32 & ~3);
+          const int q0 = lr + (r32 & ~3);   // the quad's first row within the tile
 #pragma unroll
           for (int set = 0; set < 2; ++set) {
             // a[c] = column pair 4*(2*set + c/2) + 2*(lane/32) + c%2 of this
@@ -610,8 +633,22 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
             transpose4_quad(a, k4);
             const int p = 4 * (2 * set + (k4 >> 1)) + 2 * hi + (k4 & 1);
             const u32x4 v = {a[0], a[1], a[2], a[3]};
-            if (t0 < epi.Tpad)
-              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)));
+            if (!mapped) {
+              if (t0 < epi.Tpad)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)));
+            } else {
+              const int64_t d0 = dst_lds[q0];
+              const bool whole = t0 + 3 < epi.T && (d0 & 3) == 0 && dst_lds[q0 + 3] == d0 + 3;
+              if (whole) {
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(d0, c0 + 2 * p, HD)));
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (t0 + e < epi.T)
+                    __builtin_nontemporal_store(
+                        a[e], reinterpret_cast<uint32_t*>(hb + L::v_off(dst_lds[q0 + e], c0 + 2 * p, HD)));
+              }
+            }
           }
         }
       }
@@ -622,7 +659,7 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
 // the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
 // so the compiler's tracking of direct LDS loads sees a single target
 template <class Epi, int WT>
-constexpr int big_lds_bytes() { return BG_LDS + (Epi::kSwap ? 64 * WT * 4 : 0); }
+constexpr int big_lds_bytes() { return BG_LDS + (Epi::kSwap ? 2 * 64 * WT * 4 : 0); }
 
 template <class Epi, int HD, int BK, int WT, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
@@ -749,12 +786,14 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
   a.nseg = 1;
   const int N = 2 * n_layers * d;
   const int M = kv.T;
-  const int Mrows = (int)kv.Tpad;  // rows T..Tpad-1 are written as zeros
+  // packed: rows T..Tpad-1 are written as zeros; cache: only the T new rows
+  const int Mrows = kv.dst_row ? M : (int)kv.Tpad;
   trace_pre(K_GEMM_KV, s);
   if (use_big_tiles(dtype, M, N)) {
     const bf16* B = static_cast<const bf16*>(Bt);
     const int nb = kv_big_columns(Mrows, N);
-    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, 0};
+    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, 0,
+                       kv.dst_row};
     const int tm = (Mrows + BG_M - 1) / BG_M;
     if (nb * BG_N == N) {   // 256x256 tiles only
       dim3 grid(tm * (N / BG_N), 1, 1);
@@ -779,7 +818,7 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
                                                                                epi);
     }
   } else if (dtype == 1) {
-    EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
+    EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, kv.dst_row};
     const bf16* B = static_cast<const bf16*>(Bt);
     if (pick_gemm_bm(M) == 128) {
       dim3 grid(((Mrows + 127) / 128) * (N / 128), 1, 1);
@@ -789,7 +828,7 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
       gemm_bf16_nt<64, 128, 2, 2, EpiKV<bf16>><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
     }
   } else {
-    EpiKV<float> epi{static_cast<float*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads};
+    EpiKV<float> epi{static_cast<float*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, kv.dst_row};
     dim3 grid(((Mrows + 63) / 64) * (N / 64), 1, 1);
     gemm_f32<EpiKV<float>><<<grid, 256, 0, s>>>(a, b, M, Mrows, N, d, d, epi);
   }

@@ -53,12 +53,21 @@ struct BMats {
 
 // Attention-side layout of the context K and V (per layer, per head):
 // see kv_layout.h. Tpad is T rounded up to 64.
+// Two ways of placing context rows in a slab:
+//   packed (seq_stride = 0): sequence b owns rows cu[b] .. cu[b+1]-1, as the
+//     packed context of one forward; the K/V product writes row r at r and
+//     zeros at T .. Tpad-1;
+//   cache (seq_stride = cap): sequence b owns rows b*cap .. b*cap + L_b - 1
+//     of an append-only draft cache; the K/V product writes new row r at
+//     dst_row[r] and nothing past its T new rows.
 struct KVDesc {
   void* base;        // [n_layers][2][n_heads][Tpad][hd] in tiled order
-  int64_t Tpad;
-  int32_t T;
+  int64_t Tpad;      // rows per slab (A * cap for a cache)
+  int32_t T;         // rows the K/V product writes (packed: context rows; cache: new rows)
   int32_t hd;
   int32_t n_heads;
+  int64_t seq_stride = 0;          // attention: 0 = packed by cu, else cache rows per sequence
+  const int32_t* dst_row = nullptr;  // K/V product into a cache: slab row of each new row
 };
 
 // ---- set-up pass ----------------------------------------------------------
@@ -97,6 +106,13 @@ struct SetupArgs {
   // cleared buffer
   float* zero = nullptr;
   int64_t zero_n = 0;
+  // cache row map: new row r of sequence b (rows ncu[b] .. ncu[b+1]-1) goes
+  // to slab row b * cap + pos[b] + (r - ncu[b]); map_T new rows
+  const int32_t* ncu = nullptr;
+  const int32_t* pos = nullptr;
+  int32_t cap = 0;
+  int64_t map_T = 0;
+  int32_t* dst_row = nullptr;
 };
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s);
 

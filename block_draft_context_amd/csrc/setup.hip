@@ -192,17 +192,30 @@ __device__ __forceinline__ void stats_row(const SetupArgs& a, int64_t t, int lan
   if (lane == 0) a.rinv[t] = rsqrtf(ss / (float)d + a.eps);
 }
 
-// Workgroup ranges, in dispatch order: [plan][zero][D0][prep][norm]. The
-// small roles come first so that none of them lands in the grid's tail.
+// Cache row map: new row r belongs to the sequence b with ncu[b] <= r <
+// ncu[b+1] (the last b with ncu[b] <= r, which skips empty sequences) and
+// lands at slab row b * cap + pos[b] + (r - ncu[b]). One thread per row.
+__device__ __forceinline__ void map_rows(const SetupArgs& a, int64_t r) {
+  int lo = 0, hi = a.A - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.ncu[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  a.dst_row[r] = (int32_t)((int64_t)lo * a.cap + a.pos[lo] + (r - a.ncu[lo]));
+}
+
+// Workgroup ranges, in dispatch order: [plan][map][zero][D0][prep][norm].
+// The small roles come first so that none of them lands in the grid's tail.
 struct SetupGrid {
-  int plan, zero, d0, prep, norm;
-  int total() const { return plan + zero + d0 + prep + norm; }
+  int plan, map, zero, d0, prep, norm;
+  int total() const { return plan + map + zero + d0 + prep + norm; }
 };
 constexpr int kZeroPerBlock = 256 * 4 * 4;   // floats cleared per workgroup
 
 static SetupGrid setup_grid(const SetupArgs& a) {
   SetupGrid g;
   g.plan = a.prefix ? 1 : 0;
+  g.map = a.dst_row ? (int)((a.map_T + 255) / 256) : 0;
   g.zero = a.zero ? (int)((a.zero_n + kZeroPerBlock - 1) / kZeroPerBlock) : 0;
   g.d0 = a.D0 ? (a.A * a.gamma + 3) / 4 : 0;
   g.prep = a.Bt ? (a.b.n_per * a.b.nmat + 3) / 4 : 0;
@@ -221,6 +234,12 @@ __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
     return;
   }
   blk -= sg.plan;
+  if (blk < sg.map) {
+    const int64_t r = (int64_t)blk * 256 + threadIdx.x;
+    if (r < a.map_T) map_rows(a, r);
+    return;
+  }
+  blk -= sg.map;
   if (blk < sg.zero) {
     f32x4* z = reinterpret_cast<f32x4*>(a.zero) + (int64_t)blk * (kZeroPerBlock / 4);
     const int64_t n4 = a.zero_n / 4 - (int64_t)blk * (kZeroPerBlock / 4);

@@ -88,7 +88,9 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 typedef enum {
   DSPARK_OP_CTX_FUSE = 0,
   DSPARK_OP_BLOCK_LAYER = 1,
-  DSPARK_OP_BLOCK_FORWARD = 2
+  DSPARK_OP_BLOCK_FORWARD = 2,
+  DSPARK_OP_CTX_APPEND = 3,     /* cu_host = offsets of the new rows (ncu_host) */
+  DSPARK_OP_BLOCK_PROPOSE = 4   /* cu_host = offsets of the cached lengths */
 } dspark_op;
 
 /* Problem sizes (DflashConfig and TargetDims of module-dflash.ts). */
@@ -200,6 +202,72 @@ typedef enum {
 } dspark_plan_field;
 int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host,
                          int64_t* out, int32_t n);
+
+/* ---- incremental context ------------------------------------------------
+ * The steady-state drafting loop of the page "src/dspark-runtime.js":
+ * updateContext(position, count) runs Eq 2 on `count` new context rows and,
+ * for every draft layer, projects them with that layer's W_K / W_V and
+ * stores them in the layer's key/value cache; propose() then runs the block
+ * side of every layer over the cached keys and values. The context rows are
+ * normalised with each layer's attn_norm before W_K / W_V (#layer of
+ * module-dflash.ts), so a cache filled by appends holds exactly the K_c / V_c
+ * that dspark_block_forward computes from the whole context, and
+ * dspark_block_propose over it gives the same draft block.
+ *
+ * The draft cache is caller-owned device memory of dspark_cache_bytes
+ * bytes for A sequences of up to `cap` context rows each (cap a multiple of
+ * 64), in the layout the attention kernels stream:
+ *   cache[layer][K or V][head] is a slab of A * cap rows of head_dim values;
+ *   sequence b owns slab rows b * cap .. b * cap + cap - 1, and its context
+ *   row t (t = 0, 1, ... in append order) is slab row b * cap + t;
+ *   within a slab, row t's values sit in 64-row blocks: for K, value c of row
+ *   t is element ((t / 64) * (hd / E) + c / E) * 64 * E + (t % 64) * E + c % E
+ *   with E = 16 / element size; for V the block is regrouped for the
+ *   probability-times-value product (KG = 128 / hd key groups of R = E / 2
+ *   keys and 2 columns per 16-byte vector).
+ * Rows not yet appended must hold finite values: dspark_cache_reset clears
+ * the cache to zeros, and appends write only the rows they add. The caller
+ * keeps each sequence's length (its number of appended rows). */
+
+/* Bytes of a draft cache (0 with a message when the arguments are invalid):
+ * n_layers * 2 * A * cap * d * element size. */
+size_t dspark_cache_bytes(const dspark_dims* dims, int32_t A, int32_t cap);
+
+/* Clear the whole cache to zeros (a fill kernel on `stream`). */
+dspark_status dspark_cache_reset(const dspark_dims* dims, int32_t A, int32_t cap, void* cache,
+                                 void* stream);
+
+/* updateContext for every sequence at once: the new context rows of sequence
+ * b are rows ncu[b] .. ncu[b+1]-1 of the taps (ncu: A+1 prefix offsets, as cu
+ * elsewhere; a sequence may add none); they are appended at rows pos[b] ..
+ * pos[b] + n_b - 1 of that sequence, where pos[b] is its current length.
+ * Runs Eq 2 on the new rows only, then every layer's context K/V of them,
+ * written straight into the cache. Rows outside the appended ranges are not
+ * touched.
+ *   ncu_host / ncu_dev, pos_host / pos_dev   the same values in host and device memory
+ *   taps, ld_tap, w_c, ctx_norm               as for dspark_ctx_fuse, T = ncu[A] new rows
+ *   layers                                    host array of dims->n_layers parameter sets
+ *   ws, ws_bytes                              dspark_workspace_size(DSPARK_OP_CTX_APPEND, dims, A, ncu_host)
+ * Errors: pos[b] + n_b > cap returns DSPARK_EINVAL (nothing is written). */
+dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
+                                const int32_t* ncu_host, const int32_t* ncu_dev,
+                                const int32_t* pos_host, const int32_t* pos_dev,
+                                const void* const* taps, int64_t ld_tap, const void* w_c,
+                                const float* ctx_norm, const dspark_layer_weights* layers,
+                                void* cache, void* ws, size_t ws_bytes, void* stream);
+
+/* propose(): the draft block over the cache. Sequence b attends to its first
+ * L_b = cu[b+1] - cu[b] cached rows (cu: A+1 prefix offsets of the cached
+ * lengths; L_b <= cap) and to its own gamma block rows.
+ *   block_in, block_pos, layers, out_norm, block_out   as for dspark_block_forward
+ *   ws, ws_bytes   dspark_workspace_size(DSPARK_OP_BLOCK_PROPOSE, dims, A, cu_host)
+ * The cache is only read. */
+dspark_status dspark_block_propose(const dspark_dims* dims, int32_t A, int32_t cap,
+                                   const int32_t* cu_host, const int32_t* cu_dev,
+                                   const void* cache, const float* block_in,
+                                   const float* block_pos, const dspark_layer_weights* layers,
+                                   const float* out_norm, float* block_out, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* dspark_last_error(void);
