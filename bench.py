@@ -11,6 +11,11 @@ inside the timed region), and the CPU oracle timed on a bounded sample of the
 same workload on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-incremental]
+
+The line also carries, under "incremental", the steady-state drafting regime
+of the draft cache: one draft block over a cache of 8192 and of 131072
+context rows (dspark_block_propose) and an 8-row append (dspark_ctx_append).
 """
 from __future__ import annotations
 
@@ -195,6 +200,66 @@ def cpu_baseline(w, x, seconds, max_rows=32768):
 ROOF_KINDS = ("gemm_ctx_fuse", "gemm_ctx_kv", "attn_split_k")
 
 
+def _time_calls(torch, call, stream, steps, warmup=3):
+    """Per-call milliseconds (sorted) of `steps` back-to-back calls, from
+    HIP events on the library's stream."""
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def bench_incremental(B, torch, steps, lengths=(8192, 131072), new_rows=8):
+    """The steady-state drafting regime of the incremental context: one
+    sequence of the 5-layer d = 1024 drafter (the long-context workload's
+    model), its draft cache filled to L context rows by dspark_ctx_append;
+    then dspark_block_propose (one draft block over the cache) and an
+    append of `new_rows` rows (the accepted tokens of a step) are timed at
+    that length. Draft blocks/s = 1 / propose time."""
+    from gpu_helpers import Uploaded, dims_of
+    w = W.get_workload("bf16-L131072")
+    x = W.make_inputs(w)
+    u = Uploaded(w, x)
+    del x
+    dims = dims_of(B, w)
+    cap = ((max(lengths) + new_rows + 63) // 64) * 64
+    cache = B.DraftCache(dims, 1, cap)
+    stream = torch.cuda.current_stream()
+    out = {"workload": f"{w.name} drafter, one sequence", "new_rows_per_append": new_rows}
+    done = 0
+    for L in lengths:
+        cache.append(u.taps[:, done:L], [L - done], u.w_c, u.ctx_norm, u.layers)
+        done = L
+        prop = B.prepared_propose(cache, u.block_in, u.block_pos, u.layers, u.out_norm)
+        B.trace_begin(["attn_split_k"], capacity=(steps + 3) * 8)
+        t = _time_calls(torch, prop, stream, steps)
+        tr = B.trace_end().get("attn_split_k")
+        app = B.prepared_append(cache, u.taps[:, 0:new_rows], [new_rows], u.w_c, u.ctx_norm, u.layers)
+        ta = _time_calls(torch, app, stream, steps)
+        rec = {"propose_ms_median": round(t[len(t) // 2], 4), "propose_ms_min": round(t[0], 4),
+               "draft_blocks_per_s": round(1e3 / t[len(t) // 2], 1),
+               "append_ms_median": round(ta[len(ta) // 2], 4),
+               "draft_steps_per_s": round(1e3 / (t[len(t) // 2] + ta[len(ta) // 2]), 1)}
+        if tr:
+            amount = 2.0 * L * w.d * 2 + 4.0 * w.gamma * w.d * 4
+            avg_s = tr[0] / tr[1] / 1e3
+            rec["attention"] = {"bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(amount / avg_s / 1e9 / PEAK_HBM_GBS, 4),
+                                "avg_launch_us": round(avg_s * 1e6, 2)}
+        out[f"L{L}"] = rec
+    del cache, u
+    torch.cuda.empty_cache()
+    return out
+
+
 def roofline_of(kind, w, T, A, total_ms, launches):
     """Roofline object of one kernel kind from its HIP-event totals."""
     amount, unit, bound = kernel_work(kind, w, T, A)
@@ -221,6 +286,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-incremental", action="store_true",
+                    help="skip the draft-cache measurement (propose / append at L = 8192, 131072)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernels", action="store_true", help="also print per-kernel times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -337,6 +404,10 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    if not args.no_incremental:
+        del fwd, u, x
+        torch.cuda.empty_cache()
+        res["incremental"] = bench_incremental(B, torch, max(args.steps, 20))
     print(json.dumps(res), flush=True)
 
 

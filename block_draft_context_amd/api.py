@@ -21,7 +21,8 @@ from . import _lib as L
 __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
     "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
-    "plan_info", "block_layer_noalloc", "cache_bytes", "DraftCache",
+    "plan_info", "block_layer_noalloc", "cache_bytes", "DraftCache", "PreparedCall",
+    "prepared_propose", "prepared_append",
 ]
 
 DsparkError = L.DsparkError
@@ -312,6 +313,67 @@ class DraftCache:
                                              _ptr(out_norm), _ptr(block_out), _ptr(ws), nbytes,
                                              ts.cuda_stream))
         return block_out
+
+
+class PreparedCall:
+    """A library call with every argument marshalled once (outputs and
+    workspace allocated up front); calling it only enqueues the call. Used
+    to time the library without Python overhead. The tensors it was built
+    from must stay alive while it is used."""
+
+    def __init__(self, fn, args, keep, out=None):
+        self.fn, self.args, self._keep, self.out = fn, args, keep, out
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != L.OK:
+            L.check(st)
+        return self.out
+
+
+def prepared_propose(cache: "DraftCache", block_in, block_pos, layers, out_norm=None, *,
+                     stream=None) -> PreparedCall:
+    """dspark_block_propose over the cache's current lengths, prepared."""
+    cu = cache.cu()
+    cu_h = _cu_host(cu)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        out = torch.empty_like(block_in)
+        cu_dev = _cu_dev(cu, None, cache.device)
+        ws, nbytes = _workspace(L.OP_BLOCK_PROPOSE, cache.dims, cu, None, cache.device)
+    dm = cache.dims.c()
+    arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+    args = (ctypes.byref(dm), cache.A, cache.cap, cu_h, _ptr(cu_dev), _ptr(cache.buf), _ptr(block_in),
+            _ptr(block_pos), arr, _ptr(out_norm), _ptr(out), _ptr(ws), nbytes, ts.cuda_stream)
+    return PreparedCall(L.lib().dspark_block_propose, args,
+                        (dm, cu_h, cu_dev, ws, arr, block_in, block_pos, layers, out_norm), out)
+
+
+def prepared_append(cache: "DraftCache", taps, counts: Sequence[int], w_c, ctx_norm, layers, *,
+                    stream=None) -> PreparedCall:
+    """dspark_ctx_append of counts[b] rows at the cache's current lengths,
+    prepared; repeated calls rewrite the same rows (the host lengths are
+    not advanced), which is what a timing loop wants."""
+    counts = [int(c) for c in counts]
+    ncu = [0]
+    for c in counts:
+        ncu.append(ncu[-1] + c)
+    taps = _tap_list(taps, cache.dims)
+    ncu_h = _cu_host(ncu)
+    pos_h = (ctypes.c_int32 * cache.A)(*cache.lengths)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        ncu_d = torch.as_tensor(ncu, dtype=torch.int32, device=cache.device)
+        pos_d = torch.as_tensor(cache.lengths, dtype=torch.int32, device=cache.device)
+        ws, nbytes = _workspace(L.OP_CTX_APPEND, cache.dims, ncu, None, cache.device)
+    dm = cache.dims.c()
+    arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+    tp = _tap_ptrs(taps)
+    args = (ctypes.byref(dm), cache.A, cache.cap, ncu_h, _ptr(ncu_d), pos_h, _ptr(pos_d), tp,
+            _tap_ld(taps), _ptr(w_c), _ptr(ctx_norm), arr, _ptr(cache.buf), _ptr(ws), nbytes,
+            ts.cuda_stream)
+    return PreparedCall(L.lib().dspark_ctx_append, args,
+                        (dm, ncu_h, pos_h, ncu_d, pos_d, ws, arr, tp, taps, w_c, ctx_norm, layers))
 
 
 class PreparedForward:
