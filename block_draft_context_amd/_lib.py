@@ -18,6 +18,7 @@ EXPORTS = [
     "dspark_kernel_kinds", "dspark_kernel_name", "dspark_trace_begin",
     "dspark_trace_end", "dspark_plan_info", "dspark_block_layer_noalloc",
     "dspark_cache_bytes", "dspark_cache_reset", "dspark_ctx_append", "dspark_block_propose",
+    "dspark_markov_workspace_size", "dspark_markov_draft",
 ]
 PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "attn_streaming",
                "workspace_bytes")
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
     L.dspark_block_propose.argtypes = [ctypes.POINTER(Dims), i32, i32, pi32, vp, vp, vp, vp,
                                        ctypes.POINTER(LayerWeights), vp, vp, vp, sz, vp]
     L.dspark_block_propose.restype = i32
+    L.dspark_markov_workspace_size.argtypes = [ctypes.POINTER(Dims), i32, i32, i32]
+    L.dspark_markov_workspace_size.restype = sz
+    L.dspark_markov_draft.argtypes = [ctypes.POINTER(Dims), i32, i32, i32] + [vp] * 11 + [sz, vp]
+    L.dspark_markov_draft.restype = i32
     L.dspark_plan_info.argtypes = [i32, ctypes.POINTER(Dims), i32, pi32, ctypes.POINTER(ctypes.c_int64), i32]
     L.dspark_plan_info.restype = i32
     _lib = L

@@ -22,7 +22,7 @@ __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
     "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
     "plan_info", "block_layer_noalloc", "cache_bytes", "DraftCache", "PreparedCall",
-    "prepared_propose", "prepared_append",
+    "prepared_propose", "prepared_append", "markov_draft",
 ]
 
 DsparkError = L.DsparkError
@@ -313,6 +313,35 @@ class DraftCache:
                                              _ptr(out_norm), _ptr(block_out), _ptr(ws), nbytes,
                                              ts.cuda_stream))
         return block_out
+
+
+def markov_draft(dims: DsparkDims, block, base_logits, anchor, w1, w2, conf_w, conf_b, *,
+                 tokens=None, conf=None, draft_logits=None, ws=None, stream=None):
+    """The greedy draft loop after the backbone: (tokens [A, gamma] int32,
+    confidences [A, gamma], draft logits [A, gamma, vocab]). w1 and w2 are
+    [vocab, rank] in the storage dtype; anchor [A] int32 and conf_b [1] on
+    the device."""
+    A, G, _ = block.shape
+    vocab, rank = int(w1.shape[0]), int(w1.shape[1])
+    dm = dims.c()
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if tokens is None:
+            tokens = torch.empty((A, G), dtype=torch.int32, device=block.device)
+        if conf is None:
+            conf = torch.empty((A, G), dtype=torch.float32, device=block.device)
+        if draft_logits is None:
+            draft_logits = torch.empty((A, G, vocab), dtype=torch.float32, device=block.device)
+        need = L.lib().dspark_markov_workspace_size(ctypes.byref(dm), A, vocab, rank)
+        if need == 0:
+            raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=block.device)
+    L.check(L.lib().dspark_markov_draft(ctypes.byref(dm), A, vocab, rank, _ptr(block), _ptr(base_logits),
+                                        _ptr(anchor), _ptr(w1), _ptr(w2), _ptr(conf_w), _ptr(conf_b),
+                                        _ptr(tokens), _ptr(conf), _ptr(draft_logits), _ptr(ws),
+                                        ws.numel() * ws.element_size(), ts.cuda_stream))
+    return tokens, conf, draft_logits
 
 
 class PreparedCall:

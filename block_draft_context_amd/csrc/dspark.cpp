@@ -43,7 +43,7 @@ static dspark_status fail(dspark_status st, const char* fmt, ...) {
 // ---------------------------------------------------------------------------
 static const char* kNames[K_COUNT] = {
     "gemm_ctx_fuse",      "setup",      "gemm_ctx_kv", "attn_split_k",
-    "attn_combine_oproj", "block_gemm", "block_rows"};
+    "attn_combine_oproj", "block_gemm", "block_rows",  "markov"};
 
 const char* kernel_name(int kind) { return (kind >= 0 && kind < K_COUNT) ? kNames[kind] : ""; }
 
@@ -710,6 +710,88 @@ dspark_status dspark_block_propose(const dspark_dims* dims, int32_t A, int32_t c
   if (out_norm)
     DSPARK_HIP(launch_block_rows(Da, nullptr, A, dims->gamma, dims->d, out_norm, dims->eps, nullptr,
                                  block_out, s));
+  return DSPARK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Markov head, confidence head, greedy draft loop
+// ---------------------------------------------------------------------------
+struct MarkovPlan {
+  size_t E1 = 0, pv = 0, pi = 0, total = 0;
+};
+
+static dspark_status markov_plan(const dspark_dims* dims, int32_t A, int32_t vocab, int32_t rank,
+                                 MarkovPlan* mp) {
+  if (!dims) return fail(DSPARK_EINVAL, "dims is NULL");
+  if (dims->dtype != DSPARK_F32 && dims->dtype != DSPARK_BF16)
+    return fail(DSPARK_EUNSUPPORTED, "dtype %d not supported (0 = f32, 1 = bf16)", dims->dtype);
+  if (dims->d <= 0 || dims->d % 4 != 0) return fail(DSPARK_EINVAL, "d %d must be a positive multiple of 4", dims->d);
+  if (dims->gamma < 1 || dims->gamma > kMaxGamma)
+    return fail(DSPARK_EUNSUPPORTED, "gamma %d not in [1, %d]", dims->gamma, kMaxGamma);
+  if (A < 1 || (int64_t)A * dims->gamma > 1024)
+    return fail(A < 1 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "A = %d (A * gamma must be in [1, 1024])", A);
+  if (vocab < 8 || vocab % 8 != 0) return fail(DSPARK_EUNSUPPORTED, "vocab %d must be a multiple of 8", vocab);
+  if ((int64_t)dims->gamma * vocab >= ((int64_t)1 << 31))
+    return fail(DSPARK_EUNSUPPORTED, "gamma * vocab = %lld too large", (long long)dims->gamma * vocab);
+  if (rank < 64 || rank % 64 != 0 || rank > 16256)
+    return fail(DSPARK_EUNSUPPORTED, "rank %d must be a multiple of 64 in [64, 16256]", rank);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const int P = markov_partials(vocab);
+  mp->E1 = take((size_t)A * rank * 4);
+  mp->pv = take((size_t)A * P * 4);
+  mp->pi = take((size_t)A * P * 4);
+  mp->total = off;
+  return DSPARK_OK;
+}
+
+size_t dspark_markov_workspace_size(const dspark_dims* dims, int32_t A, int32_t vocab, int32_t rank) {
+  MarkovPlan mp;
+  if (markov_plan(dims, A, vocab, rank, &mp) != DSPARK_OK) return 0;
+  return mp.total;
+}
+
+dspark_status dspark_markov_draft(const dspark_dims* dims, int32_t A, int32_t vocab, int32_t rank,
+                                  const float* block, const float* base_logits, const int32_t* anchor,
+                                  const void* w1, const void* w2, const float* conf_w, const float* conf_b,
+                                  int32_t* tokens, float* conf, float* draft_logits, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  MarkovPlan mp;
+  dspark_status st = markov_plan(dims, A, vocab, rank, &mp);
+  if (st != DSPARK_OK) return st;
+  NEED_PTR(block);
+  NEED_PTR(base_logits);
+  NEED_PTR(anchor);
+  NEED_PTR(w1);
+  NEED_PTR(w2);
+  NEED_PTR(conf_w);
+  if (!conf_b) return fail(DSPARK_EINVAL, "conf_b is NULL");
+  NEED_PTR(tokens);
+  NEED_PTR(conf);
+  NEED_PTR(draft_logits);
+  NEED_PTR(ws);
+  if (ws_bytes < mp.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, mp.total);
+  MarkovArgs a;
+  a.A = A;
+  a.gamma = dims->gamma;
+  a.d = dims->d;
+  a.vocab = vocab;
+  a.rank = rank;
+  a.block = block;
+  a.base_logits = base_logits;
+  a.anchor = anchor;
+  a.w1 = w1;
+  a.w2 = w2;
+  a.conf_w = conf_w;
+  a.conf_b = conf_b;
+  a.tokens = tokens;
+  a.conf = conf;
+  a.logits = draft_logits;
+  a.E1 = at<float>(ws, mp.E1);
+  a.part_v = at<float>(ws, mp.pv);
+  a.part_i = at<int32_t>(ws, mp.pi);
+  DSPARK_HIP(launch_markov(dims->dtype, a, static_cast<hipStream_t>(stream)));
   return DSPARK_OK;
 }
 

@@ -20,6 +20,7 @@ enum KernelKind : int {
   K_COMBINE,          // (m, l) combine of the partials + block keys
   K_ROWGEMM,          // block-row projections (weight streaming, fused norm/epilogue)
   K_BLOCK_ROWS,       // D0 = block_in + block_pos and row norms
+  K_MARKOV,           // Markov draft loop: embedding gathers, argmax partials, token + confidence
   K_COUNT
 };
 
@@ -188,5 +189,25 @@ hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hip
 hipError_t launch_block_rows(const float* block_in, const float* block_pos, int A, int gamma,
                              int d, const float* g, float eps, float* D0, float* U0,
                              hipStream_t s);
+
+// ---- Markov head, confidence head, greedy draft loop ----------------------
+struct MarkovArgs {
+  int A = 0, gamma = 0, d = 0, vocab = 0, rank = 0;
+  const float* block = nullptr;        // [A][gamma][d]
+  const float* base_logits = nullptr;  // [A][gamma][vocab]
+  const int32_t* anchor = nullptr;     // [A]
+  const void* w1 = nullptr;            // [vocab][rank] storage type
+  const void* w2 = nullptr;            // [vocab][rank] storage type ([out, in])
+  const float* conf_w = nullptr;       // [d + rank]
+  const float* conf_b = nullptr;       // [1]
+  int32_t* tokens = nullptr;           // [A][gamma]
+  float* conf = nullptr;               // [A][gamma]
+  float* logits = nullptr;             // [A][gamma][vocab]: the draft logits
+  float* E1 = nullptr;                 // workspace [A][rank]
+  float* part_v = nullptr;             // workspace [A][markov_partials(vocab)]
+  int32_t* part_i = nullptr;
+};
+int markov_partials(int vocab);
+hipError_t launch_markov(int dtype, const MarkovArgs& a, hipStream_t s);
 
 }  // namespace dspark

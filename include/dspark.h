@@ -269,6 +269,37 @@ dspark_status dspark_block_propose(const dspark_dims* dims, int32_t A, int32_t c
                                    const float* out_norm, float* block_out, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* ---- Markov head, confidence head and the greedy draft loop --------------
+ * forwardInfer of module-dflash.ts after the backbone (#markov,
+ * #confidence), which the page "src/dspark-runtime.js" runs as markovEmbed
+ * -> markov -> addBias -> argmax per drafted position. For every sequence b,
+ * with prev = anchor[b], and for k = 0 .. gamma-1 in turn:
+ *   e1           = w1[prev]                            (Markov embedding, rank values)
+ *   logits[b, k] = base_logits[b, k] + e1 . w2^T       (w2 stored [vocab, rank])
+ *   tokens[b, k] = argmax_v logits[b, k, v]            (equal maxima: the lowest index)
+ *   conf[b, k]   = sigmoid([block[b, k], e1] . conf_w + conf_b)
+ *   prev         = tokens[b, k]
+ * The base logits are the target model's LM head applied to the draft block
+ * (#baseLogits); they are an input here. The logits are float32: the bias
+ * products multiply the stored w1 and w2 values and accumulate in float32.
+ *   block        [A, gamma, d] float32: the draft block (the output norm applied)
+ *   base_logits  [A, gamma, vocab] float32
+ *   anchor       [A] int32 device: the token each block continues (clamped to [0, vocab))
+ *   w1           [vocab, rank] dims->dtype: row v is token v's Markov embedding
+ *   w2           [vocab, rank] dims->dtype: row v holds the weights of logit v ([out, in])
+ *   conf_w       [d + rank] float32;  conf_b  [1] float32 (device)
+ *   tokens       out [A, gamma] int32;  conf  out [A, gamma] float32
+ *   draft_logits out [A, gamma, vocab] float32 (the logits of every position)
+ *   ws, ws_bytes dspark_markov_workspace_size(dims, A, vocab, rank) bytes
+ * Sizes: vocab a multiple of 8 (gamma * vocab < 2^31), rank a multiple of 64
+ * up to 16256, A * gamma <= 1024. Uses dims->d, gamma and dtype only. */
+size_t dspark_markov_workspace_size(const dspark_dims* dims, int32_t A, int32_t vocab, int32_t rank);
+dspark_status dspark_markov_draft(const dspark_dims* dims, int32_t A, int32_t vocab, int32_t rank,
+                                  const float* block, const float* base_logits, const int32_t* anchor,
+                                  const void* w1, const void* w2, const float* conf_w,
+                                  const float* conf_b, int32_t* tokens, float* conf,
+                                  float* draft_logits, void* ws, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* dspark_last_error(void);
 

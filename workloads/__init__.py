@@ -270,3 +270,34 @@ def make_inputs(w: Workload, *, gains: str = "unit", lengths=None,
     out["block_in"] = block_in
     out["block_pos"] = _normal(w.seed_id, _S_POS, (w.gamma, w.d), 0.02)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Markov head inputs (forwardInfer after the backbone)
+# ----------------------------------------------------------------------------
+_S_MK_BLOCK, _S_MK_U, _S_MK_ANCHOR, _S_MK_W1, _S_MK_W2, _S_MK_CW = 200, 201, 202, 203, 204, 205
+
+
+def markov_inputs(seed_id: int, *, A: int, gamma: int, d: int, vocab: int, rank: int,
+                  dtype: str = "bf16", u_std: float = 2.0, w1_std: float = 1.0,
+                  w2_std: float = 0.1, zero_w2: bool = False) -> dict:
+    """Seeded inputs of the greedy draft loop: the draft block [A, gamma, d]
+    (N(0,1), the scale of normalised rows), base logits [A, gamma, vocab]
+    ~ N(0, u_std^2), anchor tokens, w1 / w2 [vocab, rank] (w2 stored as
+    [vocab, rank], i.e. the transpose of module-dflash.ts's [rank, vocab]),
+    conf_w [d + rank] ~ N(0, 0.02^2), conf_b. w1 and w2 are rounded to the
+    storage precision. initFromDims starts w2 at zero (``zero_w2``); the
+    default scales make the Markov bias comparable to the base logits, so
+    the previous token matters."""
+    bf = dtype == "bf16"
+    out = {
+        "block": _normal(seed_id, _S_MK_BLOCK, (A, gamma, d), 1.0),
+        "base_logits": _normal(seed_id, _S_MK_U, (A, gamma, vocab), u_std),
+        "anchor": _rng(seed_id, _S_MK_ANCHOR).integers(0, vocab, size=A).astype(np.int32),
+        "w1": _normal(seed_id, _S_MK_W1, (vocab, rank), w1_std, round_bf16=bf),
+        "w2": (np.zeros((vocab, rank), dtype=np.float32) if zero_w2
+               else _normal(seed_id, _S_MK_W2, (vocab, rank), w2_std, round_bf16=bf)),
+        "conf_w": _normal(seed_id, _S_MK_CW, (d + rank,), 0.02),
+        "conf_b": np.array([0.1], dtype=np.float32),
+    }
+    return out
