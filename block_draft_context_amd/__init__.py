@@ -3,7 +3,8 @@
 The compute lives in libdspark.so (hand-written HIP for gfx950 behind the C
 ABI of include/dspark.h); this package is its Python binding.
 """
-from .api import (DraftCache, DsparkDims, DsparkError, PreparedForward, block_forward,  # noqa: F401
+from .api import (DraftCache, DsparkDims, DsparkError, PreparedForward, block_build,  # noqa: F401
+                  block_forward, block_forward_padded,
                   block_layer, block_layer_noalloc, cache_bytes, markov_draft, prepared_append,
                   prepared_propose,
                   ctx_fuse, kernel_names, plan_info, trace_begin, trace_end, version,

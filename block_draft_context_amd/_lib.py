@@ -18,7 +18,8 @@ EXPORTS = [
     "dspark_kernel_kinds", "dspark_kernel_name", "dspark_trace_begin",
     "dspark_trace_end", "dspark_plan_info", "dspark_block_layer_noalloc",
     "dspark_cache_bytes", "dspark_cache_reset", "dspark_ctx_append", "dspark_block_propose",
-    "dspark_markov_workspace_size", "dspark_markov_draft",
+    "dspark_markov_workspace_size", "dspark_markov_draft", "dspark_block_build",
+    "dspark_padded_workspace_size", "dspark_block_forward_padded",
 ]
 PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "attn_streaming",
                "workspace_bytes")
@@ -100,6 +101,14 @@ def lib() -> ctypes.CDLL:
     L.dspark_markov_workspace_size.restype = sz
     L.dspark_markov_draft.argtypes = [ctypes.POINTER(Dims), i32, i32, i32] + [vp] * 11 + [sz, vp]
     L.dspark_markov_draft.restype = i32
+    L.dspark_block_build.argtypes = [ctypes.POINTER(Dims), i32, vp, vp, vp, vp, vp]
+    L.dspark_block_build.restype = i32
+    L.dspark_padded_workspace_size.argtypes = [ctypes.POINTER(Dims), i32, i32]
+    L.dspark_padded_workspace_size.restype = sz
+    L.dspark_block_forward_padded.argtypes = [ctypes.POINTER(Dims), i32, i32, ctypes.POINTER(vp), i64,
+                                              vp, vp, vp, vp, vp, ctypes.POINTER(LayerWeights), vp, vp,
+                                              vp, vp, sz, vp]
+    L.dspark_block_forward_padded.restype = i32
     L.dspark_plan_info.argtypes = [i32, ctypes.POINTER(Dims), i32, pi32, ctypes.POINTER(ctypes.c_int64), i32]
     L.dspark_plan_info.restype = i32
     _lib = L

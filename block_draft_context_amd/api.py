@@ -22,7 +22,7 @@ __all__ = [
     "DsparkDims", "workspace_size", "ctx_fuse", "block_layer", "block_forward",
     "version", "kernel_names", "trace_begin", "trace_end", "DsparkError", "PreparedForward",
     "plan_info", "block_layer_noalloc", "cache_bytes", "DraftCache", "PreparedCall",
-    "prepared_propose", "prepared_append", "markov_draft",
+    "prepared_propose", "prepared_append", "markov_draft", "block_build", "block_forward_padded",
 ]
 
 DsparkError = L.DsparkError
@@ -313,6 +313,47 @@ class DraftCache:
                                              _ptr(out_norm), _ptr(block_out), _ptr(ws), nbytes,
                                              ts.cuda_stream))
         return block_out
+
+
+def block_build(dims: DsparkDims, anchor_emb, tok_proj, mask_emb, *, block_in=None,
+                stream=None) -> torch.Tensor:
+    """#buildBlock's token rows [A, gamma, d] (float32, before block_pos):
+    anchor_emb [A, H] float32, tok_proj [d, H] storage dtype, mask_emb
+    [gamma-1, d] float32."""
+    A = int(anchor_emb.shape[0])
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if block_in is None:
+            block_in = torch.empty((A, dims.gamma, dims.d), dtype=torch.float32, device=anchor_emb.device)
+    dm = dims.c()
+    L.check(L.lib().dspark_block_build(ctypes.byref(dm), A, _ptr(anchor_emb), _ptr(tok_proj),
+                                       _ptr(mask_emb), _ptr(block_in), ts.cuda_stream))
+    return block_in
+
+
+def block_forward_padded(dims: DsparkDims, taps, L_ctx: int, ctx_mask, w_c, ctx_norm, block_in,
+                         block_pos, layers, out_norm=None, *, h_ctx_out=None, block_out=None,
+                         ws=None, stream=None) -> torch.Tensor:
+    """The draft block of a padded batch: taps [A * L_ctx, H] per tap,
+    ctx_mask [A, L_ctx] uint8 (1 = real row, 0 = padding)."""
+    A = int(block_in.shape[0])
+    taps = _tap_list(taps, dims)
+    ts = _torch_stream(stream)
+    dm = dims.c()
+    with torch.cuda.stream(ts):
+        if block_out is None:
+            block_out = torch.empty_like(block_in)
+        need = L.lib().dspark_padded_workspace_size(ctypes.byref(dm), A, L_ctx)
+        if need == 0:
+            raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=block_in.device)
+    arr = (L.LayerWeights * len(layers))(*[_layer_struct(lw) for lw in layers])
+    L.check(L.lib().dspark_block_forward_padded(
+        ctypes.byref(dm), A, L_ctx, _tap_ptrs(taps), _tap_ld(taps), _ptr(w_c), _ptr(ctx_norm),
+        _ptr(ctx_mask), _ptr(block_in), _ptr(block_pos), arr, _ptr(out_norm), _ptr(h_ctx_out),
+        _ptr(block_out), _ptr(ws), ws.numel() * ws.element_size(), ts.cuda_stream))
+    return block_out
 
 
 def markov_draft(dims: DsparkDims, block, base_logits, anchor, w1, w2, conf_w, conf_b, *,

@@ -135,7 +135,8 @@ template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
-    int total_tiles, int64_t seq_stride, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int total_tiles, int64_t seq_stride, const uint8_t* __restrict__ key_mask, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
   constexpr int NKV = HD / E;            // K vectors per key row
@@ -208,10 +209,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   if (first <= blk1) {
     const int64_t last = first + ((blk1 - first) / bstep) * bstep;
     u32x4 kreg[NKV], vreg[NLD];
+    uint32_t kmask = 1;   // key-padding mask of this lane's key (padded batches only)
     auto load_k = [&](int64_t blk) __attribute__((always_inline)) {
       const S* kp = Kh + blk * 64 * HD + lane * E;
 #pragma unroll
       for (int i = 0; i < NKV; ++i) kreg[i] = ld16(kp + i * 64 * E);
+      if (key_mask) kmask = key_mask[min(blk * 64 + lane, T1 - 1)];
     };
     // V is read once per layer: non-temporal loads (measured 5% faster per
     // forward at T = 131072 and on a ragged 16-sequence batch; marking K as
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       const int64_t nxt = min(blk + bstep, last);
       // ---- scores: lane owns key blk*64 + lane
       const int64_t key = blk * 64 + lane;
-      const bool valid = key >= k0 && key < k1;
+      const bool valid = key >= k0 && key < k1 && kmask != 0;
       float s[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) s[j] = 0.f;
@@ -268,8 +271,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
         const float sv = valid ? s[j] : kNegInf;
         const float bm = wave_max(sv);
         const float mn = fmaxf(m_run[j], bm);
-        const float alpha = exp2f(m_run[j] - mn);   // 0 when m_run = -inf
-        const float p = exp2f(sv - mn);             // 0 for masked keys
+        // a block can be fully masked (padding rows): then mn = -inf, and the
+        // finite stand-in keeps alpha = 1 and p = 0 instead of NaN
+        const float mf = mn == kNegInf ? 0.f : mn;
+        const float alpha = exp2f(m_run[j] - mf);   // 0 when m_run = -inf
+        const float p = exp2f(sv - mf);             // 0 for masked keys
         l_run[j] = l_run[j] * alpha + p;
         o[j][0] *= alpha;
         o[j][1] *= alpha;
@@ -394,7 +400,8 @@ template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_hsplit_kernel(
     const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
-    int total_tiles, int64_t seq_stride, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int total_tiles, int64_t seq_stride, const uint8_t* __restrict__ key_mask, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   using L = KVLayout<S>;
   constexpr int E = L::E, R = L::R;
   constexpr int NKV = HD / E;            // K vectors per key row
@@ -485,15 +492,18 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
       __syncthreads();
       // ---- full scores and the online softmax (the same in every wave)
       const int64_t key = (blk0 + bb) * 64 + lane;
-      const bool valid = key >= k0 && key < k1;
+      const bool valid = key >= k0 && key < k1 && (!key_mask || key_mask[min(key, T1 - 1)] != 0);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float sc = (sp[0][j][lane] + sp[1][j][lane]) + (sp[2][j][lane] + sp[3][j][lane]);
         const float sv = valid ? sc : kNegInf;
         const float bm = wave_max(sv);
         const float mn = fmaxf(m_run[j], bm);
-        const float alpha = exp2f(m_run[j] - mn);   // 0 when m_run = -inf
-        const float p = exp2f(sv - mn);             // 0 for masked keys
+        // a block can be fully masked (padding rows): then mn = -inf, and the
+        // finite stand-in keeps alpha = 1 and p = 0 instead of NaN
+        const float mf = mn == kNegInf ? 0.f : mn;
+        const float alpha = exp2f(m_run[j] - mf);   // 0 when m_run = -inf
+        const float p = exp2f(sv - mf);             // 0 for masked keys
         l_run[j] = l_run[j] * alpha + p;
         o[j][0] *= alpha;
         o[j][1] *= alpha;
@@ -822,12 +832,12 @@ static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
   if (a.chunk == 64) {
     attn_hsplit_kernel<S, HD, G><<<grid, 256, 0, s>>>(
         a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-        a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.part_o, a.part_ml);
+        a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.kv.key_mask, a.part_o, a.part_ml);
     return;
   }
   attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(
       a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
-      a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.part_o, a.part_ml);
+      a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.kv.key_mask, a.part_o, a.part_ml);
 }
 
 template <typename S, int HD>

@@ -290,6 +290,7 @@ hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hip
   DSPARK_RG(RP_RMSNORM, RE_QKV)
   DSPARK_RG(RP_NONE, RE_RESID)
   DSPARK_RG(RP_RMSNORM, RE_SWIGLU)
+  DSPARK_RG(RP_NONE, RE_STORE)
 #undef DSPARK_RG
   trace_post(K_ROWGEMM, s);
   if (!ok) return hipErrorInvalidValue;
@@ -329,6 +330,41 @@ hipError_t launch_block_rows(const float* block_in, const float* block_pos, int 
                              const float* g, float eps, float* D0, float* U0, hipStream_t s) {
   trace_pre(K_BLOCK_ROWS, s);
   block_rows_kernel<<<A * gamma, 256, 0, s>>>(block_in, block_pos, gamma, d, g, eps, D0, U0);
+  trace_post(K_BLOCK_ROWS, s);
+  return hipGetLastError();
+}
+
+}  // namespace dspark
+
+namespace dspark {
+
+// Rows 1 .. gamma-1 of every sequence's block: the shared mask embeddings
+// (#buildBlock); row 0 (the anchor row) is written by the row GEMM.
+__global__ __launch_bounds__(256) void mask_rows_kernel(const float* __restrict__ mask_emb, int gamma, int d,
+                                                        float* __restrict__ block_in) {
+  const int b = blockIdx.y, j = blockIdx.x + 1;
+  const f32x4* src = reinterpret_cast<const f32x4*>(mask_emb + (int64_t)(j - 1) * d);
+  f32x4* dst = reinterpret_cast<f32x4*>(block_in + ((int64_t)b * gamma + j) * d);
+  for (int c = threadIdx.x; c < d / 4; c += 256) dst[c] = src[c];
+}
+
+hipError_t launch_block_build(int dtype, const float* anchor_emb, int A, int H, const void* tok_proj,
+                              const float* mask_emb, int gamma, int d, float* block_in, hipStream_t s) {
+  RowGemmArgs r{};
+  r.X = anchor_emb;
+  r.ldx = H;
+  r.M = A;
+  r.K = H;
+  r.N = d;
+  r.b.mat[0] = tok_proj;
+  r.b.n_per = d;
+  r.b.nmat = 1;
+  r.out = block_in;          // row 0 of sequence b: block_in[b * gamma * d]
+  r.ldo = gamma * d;
+  hipError_t e = launch_rowgemm(dtype, RP_NONE, RE_STORE, r, s);
+  if (e != hipSuccess || gamma == 1) return e;
+  trace_pre(K_BLOCK_ROWS, s);
+  mask_rows_kernel<<<dim3(gamma - 1, A), 256, 0, s>>>(mask_emb, gamma, d, block_in);
   trace_post(K_BLOCK_ROWS, s);
   return hipGetLastError();
 }

@@ -493,16 +493,16 @@ dspark_status dspark_block_layer_noalloc(const dspark_dims* dims, int32_t A, con
                           stream, p);
 }
 
-dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
-                                   const int32_t* cu_dev, const void* const* taps, int64_t ld_tap,
-                                   const void* w_c, const float* ctx_norm, const float* block_in,
-                                   const float* block_pos, const dspark_layer_weights* layers,
-                                   const float* out_norm, void* h_ctx_out, float* block_out,
-                                   void* ws, size_t ws_bytes, void* stream) {
-  Plan p;
-  dspark_status st = make_plan(DSPARK_OP_BLOCK_FORWARD, dims, A, cu_host, &p);
-  if (st != DSPARK_OK) return st;
-  NEED_PTR(cu_dev);
+// The forward's launch sequence; key_mask (nullable) marks the context rows
+// that are keys (a padded batch); `pre` runs first on the stream (nullable).
+static dspark_status forward_impl(const dspark_dims* dims, int32_t A, const int32_t* cu_dev,
+                                  const void* const* taps, int64_t ld_tap, const void* w_c,
+                                  const float* ctx_norm, const float* block_in, const float* block_pos,
+                                  const dspark_layer_weights* layers, const float* out_norm, void* h_ctx_out,
+                                  float* block_out, void* ws, size_t ws_bytes, void* stream, const Plan& p,
+                                  const uint8_t* key_mask, int32_t* fill_cu, int32_t fill_L) {
+  dspark_status st;
+  if (!fill_cu) NEED_PTR(cu_dev);
   st = check_taps(dims, taps, ld_tap, p.T);
   if (st != DSPARK_OK) return st;
   NEED_PTR(w_c);
@@ -521,6 +521,10 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   if (ws_bytes < p.total)
     return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fill_cu) {   // the offsets b * L of a padded batch, written in the workspace
+    DSPARK_HIP(launch_fill_offsets(fill_cu, A, fill_L, s));
+    cu_dev = fill_cu;
+  }
   void* h_ctx = h_ctx_out ? h_ctx_out : at<char>(ws, p.hctx);
   float* rinv = at<float>(ws, p.rinv);
   float* Da = at<float>(ws, p.D);
@@ -546,7 +550,8 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
     sa.rinv = rinv;
   }
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
-  const KVDesc kv = ws_kv(dims, p, ws);
+  KVDesc kv = ws_kv(dims, p, ws);
+  kv.key_mask = key_mask;
   st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, kv, ws, s);
   if (st != DSPARK_OK) return st;
   const int N = dims->n_layers;
@@ -559,6 +564,75 @@ dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int
   if (out_norm)   // out = RMSNorm(D^N; out_norm)
     DSPARK_HIP(launch_block_rows(Da, nullptr, A, dims->gamma, dims->d, out_norm, dims->eps, nullptr,
                                  block_out, s));
+  return DSPARK_OK;
+}
+
+dspark_status dspark_block_forward(const dspark_dims* dims, int32_t A, const int32_t* cu_host,
+                                   const int32_t* cu_dev, const void* const* taps, int64_t ld_tap,
+                                   const void* w_c, const float* ctx_norm, const float* block_in,
+                                   const float* block_pos, const dspark_layer_weights* layers,
+                                   const float* out_norm, void* h_ctx_out, float* block_out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_FORWARD, dims, A, cu_host, &p);
+  if (st != DSPARK_OK) return st;
+  return forward_impl(dims, A, cu_dev, taps, ld_tap, w_c, ctx_norm, block_in, block_pos, layers, out_norm,
+                      h_ctx_out, block_out, ws, ws_bytes, stream, p, nullptr, nullptr, 0);
+}
+
+// A padded batch: A sequences of L_ctx rows each (offsets b * L_ctx), with
+// the key-padding mask; the plan of the equal-length packed batch plus the
+// device copy of its offsets.
+static dspark_status padded_plan(const dspark_dims* dims, int32_t A, int32_t L_ctx, Plan* p, size_t* cu_off) {
+  if (A < 1) return fail(DSPARK_EINVAL, "A = %d < 1", A);
+  if (L_ctx < 0 || (int64_t)A * L_ctx > (1ll << 30))
+    return fail(L_ctx < 0 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "L_ctx = %d not supported", L_ctx);
+  std::vector<int32_t> cu(A + 1);
+  for (int b = 0; b <= A; ++b) cu[b] = b * L_ctx;
+  dspark_status st = make_plan(DSPARK_OP_BLOCK_FORWARD, dims, A, cu.data(), p);
+  if (st != DSPARK_OK) return st;
+  *cu_off = p->total;
+  p->total += align256((size_t)(A + 1) * 4);
+  return DSPARK_OK;
+}
+
+size_t dspark_padded_workspace_size(const dspark_dims* dims, int32_t A, int32_t L_ctx) {
+  Plan p;
+  size_t cu_off = 0;
+  if (padded_plan(dims, A, L_ctx, &p, &cu_off) != DSPARK_OK) return 0;
+  return p.total;
+}
+
+dspark_status dspark_block_forward_padded(const dspark_dims* dims, int32_t A, int32_t L_ctx,
+                                          const void* const* taps, int64_t ld_tap, const void* w_c,
+                                          const float* ctx_norm, const uint8_t* ctx_mask,
+                                          const float* block_in, const float* block_pos,
+                                          const dspark_layer_weights* layers, const float* out_norm,
+                                          void* h_ctx_out, float* block_out, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  Plan p;
+  size_t cu_off = 0;
+  dspark_status st = padded_plan(dims, A, L_ctx, &p, &cu_off);
+  if (st != DSPARK_OK) return st;
+  if (p.T > 0 && !ctx_mask) return fail(DSPARK_EINVAL, "ctx_mask is NULL");
+  if (!ws) return fail(DSPARK_EINVAL, "ws is NULL");
+  return forward_impl(dims, A, nullptr, taps, ld_tap, w_c, ctx_norm, block_in, block_pos, layers, out_norm,
+                      h_ctx_out, block_out, ws, ws_bytes, stream, p, ctx_mask, at<int32_t>(ws, cu_off), L_ctx);
+}
+
+dspark_status dspark_block_build(const dspark_dims* dims, int32_t A, const float* anchor_emb,
+                                 const void* tok_proj, const float* mask_emb, float* block_in, void* stream) {
+  dspark_status st = check_dims(dims, DSPARK_OP_BLOCK_LAYER);
+  if (st != DSPARK_OK) return st;
+  if (A < 1 || (int64_t)A * dims->gamma > 1024)
+    return fail(A < 1 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "A = %d (A * gamma must be in [1, 1024])", A);
+  if (dims->H > 16256) return fail(DSPARK_EUNSUPPORTED, "H %d above the supported 16256", dims->H);
+  NEED_PTR(anchor_emb);
+  NEED_PTR(tok_proj);
+  if (dims->gamma > 1) NEED_PTR(mask_emb);
+  NEED_PTR(block_in);
+  DSPARK_HIP(launch_block_build(dims->dtype, anchor_emb, A, dims->H, tok_proj, mask_emb, dims->gamma, dims->d,
+                                block_in, static_cast<hipStream_t>(stream)));
   return DSPARK_OK;
 }
 

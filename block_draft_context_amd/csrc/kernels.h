@@ -69,6 +69,7 @@ struct KVDesc {
   int32_t n_heads;
   int64_t seq_stride = 0;          // attention: 0 = packed by cu, else cache rows per sequence
   const int32_t* dst_row = nullptr;  // K/V product into a cache: slab row of each new row
+  const uint8_t* key_mask = nullptr; // attention: slab row t is a key only where key_mask[t] != 0
 };
 
 // ---- set-up pass ----------------------------------------------------------
@@ -116,6 +117,8 @@ struct SetupArgs {
   int32_t* dst_row = nullptr;
 };
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s);
+// cu[b] = b * L for b = 0 .. A
+hipError_t launch_fill_offsets(int32_t* cu, int A, int L, hipStream_t s);
 
 // ---- context side -------------------------------------------------------
 // K splits of the Eq 2 projection for these sizes (sizes the partial
@@ -189,6 +192,11 @@ hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hip
 hipError_t launch_block_rows(const float* block_in, const float* block_pos, int A, int gamma,
                              int d, const float* g, float eps, float* D0, float* U0,
                              hipStream_t s);
+
+// #buildBlock's token rows: block_in[b][0] = anchor_emb[b] . tok_proj^T
+// (tok_proj [d][H] storage type), block_in[b][j] = mask_emb[j-1] for j >= 1.
+hipError_t launch_block_build(int dtype, const float* anchor_emb, int A, int H, const void* tok_proj,
+                              const float* mask_emb, int gamma, int d, float* block_in, hipStream_t s);
 
 // ---- Markov head, confidence head, greedy draft loop ----------------------
 struct MarkovArgs {

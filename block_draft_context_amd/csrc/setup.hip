@@ -273,6 +273,19 @@ __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
     stats_row<S>(a, t, lane);
 }
 
+// cu[b] = b * L for b = 0 .. A (the offsets of a padded batch)
+__global__ __launch_bounds__(256) void fill_offsets_kernel(int32_t* __restrict__ cu, int A, int L) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b <= A) cu[b] = b * L;
+}
+
+hipError_t launch_fill_offsets(int32_t* cu, int A, int L, hipStream_t s) {
+  trace_pre(K_SETUP, s);
+  fill_offsets_kernel<<<(A + 1 + 255) / 256, 256, 0, s>>>(cu, A, L);
+  trace_post(K_SETUP, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s) {
   if (a.Bt && dtype != 1) return hipErrorInvalidValue;   // prep serves the bf16 MFMA path only
   const SetupGrid sg = setup_grid(a);

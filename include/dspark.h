@@ -203,6 +203,39 @@ typedef enum {
 int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host,
                          int64_t* out, int32_t n);
 
+/* ---- block construction and padded batches --------------------------------
+ * #buildBlock of module-dflash.ts: the block's token rows, before block_pos
+ * (dspark_block_forward adds it):
+ *   block_in[b, 0] = anchor_emb[b] . tok_proj^T   (the anchor token's embedding projected)
+ *   block_in[b, j] = mask_emb[j - 1]               for j = 1 .. gamma-1 (shared by all b)
+ *   anchor_emb  [A, H] float32 (the target's embedding of each anchor token)
+ *   tok_proj    [d, H] dims->dtype ([out, in])
+ *   mask_emb    [gamma-1, d] float32 (unused when gamma = 1; may be NULL then)
+ *   block_in    out [A, gamma, d] float32
+ * Uses dims->H, d, gamma and dtype; H up to 16256. */
+dspark_status dspark_block_build(const dspark_dims* dims, int32_t A, const float* anchor_emb,
+                                 const void* tok_proj, const float* mask_emb, float* block_in,
+                                 void* stream);
+
+/* #backbone on a padded batch with #maskBias's key-padding mask: A sequences
+ * of L_ctx context rows each (row t of sequence b is row b * L_ctx + t of
+ * every tap), where ctx_mask[b * L_ctx + t] != 0 marks a real row and 0 a
+ * padding row. Padding rows are projected like the others but are no keys:
+ * the -1e9 bias that #maskBias adds to their scores makes their softmax
+ * weight exactly 0 in float32, which the kernels realise by leaving them out.
+ * A sequence may be all padding (its block then attends to itself only).
+ * Otherwise as dspark_block_forward; h_ctx_out, when given, is [A * L_ctx, d].
+ *   ctx_mask   [A, L_ctx] uint8 device memory
+ *   ws_bytes   at least dspark_padded_workspace_size(dims, A, L_ctx) */
+size_t dspark_padded_workspace_size(const dspark_dims* dims, int32_t A, int32_t L_ctx);
+dspark_status dspark_block_forward_padded(const dspark_dims* dims, int32_t A, int32_t L_ctx,
+                                          const void* const* taps, int64_t ld_tap, const void* w_c,
+                                          const float* ctx_norm, const uint8_t* ctx_mask,
+                                          const float* block_in, const float* block_pos,
+                                          const dspark_layer_weights* layers, const float* out_norm,
+                                          void* h_ctx_out, float* block_out, void* ws,
+                                          size_t ws_bytes, void* stream);
+
 /* ---- incremental context ------------------------------------------------
  * The steady-state drafting loop of the page "src/dspark-runtime.js":
  * updateContext(position, count) runs Eq 2 on `count` new context rows and,

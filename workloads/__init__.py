@@ -301,3 +301,48 @@ def markov_inputs(seed_id: int, *, A: int, gamma: int, d: int, vocab: int, rank:
         "conf_b": np.array([0.1], dtype=np.float32),
     }
     return out
+
+
+# ----------------------------------------------------------------------------
+# #buildBlock inputs and padded batches
+# ----------------------------------------------------------------------------
+_S_BB_ANCHOR, _S_BB_TOKPROJ, _S_BB_MASK, _S_PAD_NOISE, _S_PAD_POS = 210, 211, 212, 213, 214
+
+
+def block_build_inputs(seed_id: int, *, A: int, H: int, d: int, gamma: int, dtype: str = "bf16") -> dict:
+    """anchor_emb [A, H] ~ N(0, 1) (an embedding row of the target), tok_proj
+    [H, d] ~ N(0, 0.02^2) rounded to the storage precision, mask_emb
+    [gamma-1, d] ~ N(0, 0.02^2) (initFromDims's distributions)."""
+    return {
+        "anchor_emb": _normal(seed_id, _S_BB_ANCHOR, (A, H), 1.0),
+        "tok_proj": _normal(seed_id, _S_BB_TOKPROJ, (H, d), 0.02, round_bf16=dtype == "bf16"),
+        "mask_emb": _normal(seed_id, _S_BB_MASK, (max(gamma - 1, 0), d), 0.02),
+    }
+
+
+def padded_layout(seed_id: int, taps, cu, L_ctx: int, placements, dtype: str = "bf16"):
+    """A padded batch holding packed context rows: sequence b's rows go to the
+    positions of placements[b] ("lead": the first L_b rows, "scatter":
+    seeded distinct positions, or an explicit index array) of its L_ctx slots;
+    the other slots are padding filled with N(0, 3^2) noise. Returns the taps
+    [A * L_ctx, H] and the mask [A, L_ctx] (uint8, 1 = real row)."""
+    A = len(cu) - 1
+    H = taps[0].shape[1]
+    rng = _rng(seed_id, _S_PAD_POS)
+    mask = np.zeros((A, L_ctx), dtype=np.uint8)
+    out = [_normal(seed_id, _S_PAD_NOISE + j, (A * L_ctx, H), 3.0, round_bf16=dtype == "bf16")
+           for j in range(len(taps))]
+    for b in range(A):
+        L = int(cu[b + 1] - cu[b])
+        pl = placements[b]
+        if isinstance(pl, str) and pl == "lead":
+            pos = np.arange(L)
+        elif isinstance(pl, str) and pl == "scatter":
+            pos = np.sort(rng.choice(L_ctx, size=L, replace=False))
+        else:
+            pos = np.asarray(pl)
+            assert len(pos) == L
+        mask[b, pos] = 1
+        for j, t in enumerate(taps):
+            out[j][b * L_ctx + pos] = t[cu[b]:cu[b + 1]]
+    return out, mask
