@@ -25,16 +25,22 @@ PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "att
                "workspace_bytes")
 
 
+QK_NORM, PLAIN_CTX_KV, GELU_FFN = 1, 2, 4   # dspark_variant bits
+
+
 class Dims(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("n_heads", ctypes.c_int32), ("gamma", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("ff", ctypes.c_int32),
-                ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down")]
+        "attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down",
+        "q_norm", "k_norm")]
 
 
 class DsparkError(RuntimeError):

@@ -28,7 +28,8 @@ __all__ = [
 DsparkError = L.DsparkError
 
 _TORCH_DTYPE = {L.F32: torch.float32, L.BF16: torch.bfloat16}
-LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down")
+LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down",
+              "q_norm", "k_norm")
 
 
 @dataclasses.dataclass
@@ -42,6 +43,11 @@ class DsparkDims:
     ff: int
     eps: float = 1e-6
     dtype: str = "bf16"      # "bf16" or "f32": storage of the long tensors
+    n_kv_heads: int = 0      # 0 = n_heads
+    qk_norm: bool = False    # variant switches (include/dspark.h, dspark_variant)
+    plain_ctx_kv: bool = False
+    gelu_ffn: bool = False
+    rope_theta: float = 0.0
 
     @property
     def code(self) -> int:
@@ -51,9 +57,15 @@ class DsparkDims:
     def torch_dtype(self) -> torch.dtype:
         return _TORCH_DTYPE[self.code]
 
+    @property
+    def variant(self) -> int:
+        return ((L.QK_NORM if self.qk_norm else 0) | (L.PLAIN_CTX_KV if self.plain_ctx_kv else 0)
+                | (L.GELU_FFN if self.gelu_ffn else 0))
+
     def c(self) -> L.Dims:
         return L.Dims(self.m, self.H, self.d, self.n_heads, self.gamma, self.n_layers, self.ff,
-                      float(self.eps), self.code)
+                      float(self.eps), self.code, int(self.n_kv_heads), self.variant,
+                      float(self.rope_theta))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -153,7 +165,7 @@ def _cu_dev(cu, cu_dev, device):
 
 
 def _layer_struct(lw: Dict[str, torch.Tensor]) -> L.LayerWeights:
-    return L.LayerWeights(*[_ptr(lw[k]) for k in LAYER_KEYS])
+    return L.LayerWeights(*[_ptr(lw.get(k)) for k in LAYER_KEYS])
 
 
 def ctx_fuse(dims: DsparkDims, cu, taps, w_c, ctx_norm, *, cu_dev=None, h_ctx=None, ws=None,

@@ -12,8 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdspark.so")
-SOURCES = ["gemm.hip", "attention.hip", "block.hip", "setup.hip", "markov.hip", "noalloc.hip",
-           "dspark.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "block.hip", "setup.hip", "markov.hip", "variant.hip",
+           "noalloc.hip", "dspark.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

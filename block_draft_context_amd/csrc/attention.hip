@@ -133,7 +133,7 @@ DSPARK_DEV bool tile_range(int tile, int A, int64_t T1, const int32_t* __restric
 // ---------------------------------------------------------------------------
 template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
-    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
+    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int n_kv, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
     int total_tiles, int64_t seq_stride, const uint8_t* __restrict__ key_mask, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
@@ -180,8 +180,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   __syncthreads();
 
-  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, h, n_heads, Tpad, HD);
-  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, h, n_heads, Tpad, HD);
+  // query head h reads the K/V of head h / (n_heads / n_kv) (grouped K/V heads)
+  const int kvh = h / (n_heads / n_kv);
+  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, kvh, n_kv, Tpad, HD);
+  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, kvh, n_kv, Tpad, HD);
 
   float m_run[G], l_run[G];
   float o[G][2];
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 // ---------------------------------------------------------------------------
 template <typename S, int HD, int G>
 __global__ __launch_bounds__(256) void attn_hsplit_kernel(
-    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int layer,
+    const float* __restrict__ Q, const S* __restrict__ kv_base, int64_t Tpad, int n_heads, int n_kv, int layer,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix, int A, int64_t T1, int chunk,
     int total_tiles, int64_t seq_stride, const uint8_t* __restrict__ key_mask, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
@@ -430,8 +432,10 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
   // when there is only one), then the queries are staged. A tile with no
   // keys (an empty sequence) loads nothing: its block index may lie past the
   // last block of the slab, or the K/V region may be empty altogether.
-  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, h, n_heads, Tpad, HD);
-  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, h, n_heads, Tpad, HD);
+  // query head h reads the K/V of head h / (n_heads / n_kv) (grouped K/V heads)
+  const int kvh = h / (n_heads / n_kv);
+  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, kvh, n_kv, Tpad, HD);
+  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, kvh, n_kv, Tpad, HD);
   u32x4 kreg[2][NKW], vreg[2][NLW];
   if (nblk > 0) {
 #pragma unroll
@@ -569,7 +573,8 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
 
 // ---------------------------------------------------------------------------
 // Combine + output projection: grid (d / NC column blocks, n_heads, A), 256
-// threads. Workgroup (nb, h, b) merges every context partial of sequence b
+// threads (query heads; with grouped K/V heads, head h's block keys are
+// those of K/V head h / (n_heads / n_kv)). Workgroup (nb, h, b) merges every context partial of sequence b
 // and head h with the gamma block keys (K_d, V_d in float32) into the head's
 // attention output o_h [gamma][hd], then adds o_h . W_o[cols, h*hd : (h+1)*hd]^T
 // for its NC output columns into E with float atomics, so the heads' shares
@@ -618,7 +623,7 @@ struct OProjShape {
 template <typename WT, int HD, int G>
 __global__ __launch_bounds__(256) void combine_oproj_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
-    int n_heads, const int32_t* __restrict__ prefix, int total_tiles,
+    int n_heads, int n_kv, const int32_t* __restrict__ prefix, int total_tiles,
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const WT* __restrict__ Wo,
     const float* __restrict__ resid, float* __restrict__ out) {
   using Sh = OProjShape<WT, HD>;
@@ -665,15 +670,18 @@ __global__ __launch_bounds__(256) void combine_oproj_kernel(
       }
     }
   }
+  // the block keys / values of this head's K/V head (rows of n_kv * HD)
+  const int kvh = h / (n_heads / n_kv), kvd = n_kv * HD;
   f32x4 qv[QE], kv[QE], vv[QE];
 #pragma unroll
   for (int u = 0; u < QE; ++u) {
     const int e = min(tid + 256 * u, G * C4 - 1);
     const int j = e / C4, c = e % C4;
     const int64_t off = (int64_t)(b * G + j) * d + h * HD + 4 * c;
+    const int64_t koff = (int64_t)(b * G + j) * kvd + kvh * HD + 4 * c;
     qv[u] = *reinterpret_cast<const f32x4*>(Q + off);
-    kv[u] = *reinterpret_cast<const f32x4*>(Kd + off);
-    vv[u] = *reinterpret_cast<const f32x4*>(Vd + off);
+    kv[u] = *reinterpret_cast<const f32x4*>(Kd + koff);
+    vv[u] = *reinterpret_cast<const f32x4*>(Vd + koff);
   }
 
   // context partials: online merge over this thread's tiles, TB at a time
@@ -799,7 +807,7 @@ __global__ __launch_bounds__(256) void combine_oproj_kernel(
 template <typename WT, int HD, int G>
 static hipError_t launch_oproj_t(const AttnArgs& a, hipStream_t s) {
   using Sh = OProjShape<WT, HD>;
-  const int d = HD * a.kv.n_heads;
+  const int d = HD * a.n_heads;
   if (d % Sh::NC != 0) return hipErrorInvalidValue;
   const size_t lds = (size_t)Sh::lds_floats(G) * 4;
   auto kern = combine_oproj_kernel<WT, HD, G>;
@@ -808,8 +816,8 @@ static hipError_t launch_oproj_t(const AttnArgs& a, hipStream_t s) {
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (set != hipSuccess) return set;
   }
-  dim3 grid(d / Sh::NC, a.kv.n_heads, a.A);
-  kern<<<grid, 256, lds, s>>>(a.Q, a.Kd, a.Vd, a.kv.n_heads, a.prefix, a.total_tiles, a.part_o,
+  dim3 grid(d / Sh::NC, a.n_heads, a.A);
+  kern<<<grid, 256, lds, s>>>(a.Q, a.Kd, a.Vd, a.n_heads, a.kv.n_heads, a.prefix, a.total_tiles, a.part_o,
                               a.part_ml, static_cast<const WT*>(a.wo), a.resid, a.out);
   return hipGetLastError();
 }
@@ -831,12 +839,12 @@ template <typename S, int HD, int G>
 static void launch_attn_t(dim3 grid, hipStream_t s, const AttnArgs& a) {
   if (a.chunk == 64) {
     attn_hsplit_kernel<S, HD, G><<<grid, 256, 0, s>>>(
-        a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
+        a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.n_heads, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
         a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.kv.key_mask, a.part_o, a.part_ml);
     return;
   }
   attn_partial_kernel<S, HD, G><<<grid, 256, 0, s>>>(
-      a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
+      a.Q, static_cast<const S*>(a.kv.base), a.kv.Tpad, a.n_heads, a.kv.n_heads, a.layer, a.cu, a.prefix, a.A,
       a.kv.T, a.chunk, a.total_tiles, a.kv.seq_stride, a.kv.key_mask, a.part_o, a.part_ml);
 }
 
@@ -855,7 +863,7 @@ static bool dispatch_gamma(int gamma, dim3 grid, hipStream_t s, const AttnArgs& 
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
   if (a.total_tiles < a.A) return hipErrorInvalidValue;   // every sequence has a tile
-  dim3 grid(a.total_tiles, a.kv.n_heads);
+  dim3 grid(a.total_tiles, a.n_heads);
   bool ok = false;
   trace_pre(K_ATTN, s);
   if (dtype == 1) {

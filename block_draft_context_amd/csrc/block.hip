@@ -252,14 +252,21 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
       g = __uint_as_float(r[0]);
       u = __uint_as_float(r[1]);
-      if (live && lane < 32) a.out[(int64_t)om * a.ldo + on] = g / (1.f + expf(-g)) * u;
+      if (live && lane < 32) {
+        float act;
+        if (a.act == 0) {
+          act = g / (1.f + expf(-g));   // SiLU (dspark-runtime.js)
+        } else {                        // tanh-GELU (module-dflash.ts, geluApprox)
+          const float c = 0.7978845608028654f;   // sqrt(2 / pi)
+          act = 0.5f * g * (1.f + tanhf(c * (g + 0.044715f * g * g * g)));
+        }
+        a.out[(int64_t)om * a.ldo + on] = act * u;
+      }
     } else if (live) {
       if constexpr (EPI == RE_QKV) {
-        const int seg = on / a.d, col = on % a.d;
-        const int64_t off = (int64_t)om * a.d + col;
-        if (seg == 0) a.q[off] = v * a.qscale;
-        else if (seg == 1) a.kd[off] = v;
-        else a.vd[off] = v;
+        if (on < a.d) a.q[(int64_t)om * a.d + on] = v * a.qscale;
+        else if (on < a.d + a.kvd) a.kd[(int64_t)om * a.kvd + (on - a.d)] = v;
+        else a.vd[(int64_t)om * a.kvd + (on - a.d - a.kvd)] = v;
       } else if constexpr (EPI == RE_RESID) {
         a.out[(int64_t)om * a.ldo + on] = resv + v;
       } else {

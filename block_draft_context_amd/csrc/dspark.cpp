@@ -82,6 +82,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   int64_t T = 0, Tpad = 0;
   int hd = 0, M = 0, chunk = 0, total_chunks = 0, kv_layers = 0;
+  int nkv = 0, kvd = 0;   // K/V heads and K/V columns (kvd = nkv * hd)
   CtxSplit ctx;   // K splits of the Eq 2 projection
   size_t esz = 4;
   // workspace offsets (bytes)
@@ -110,6 +111,15 @@ static dspark_status check_dims(const dspark_dims* dm, int op) {
   if (dm->ff % 128 != 0) return fail(DSPARK_EUNSUPPORTED, "ff %d must be a multiple of 128", dm->ff);
   if (dm->ff > 16256) return fail(DSPARK_EUNSUPPORTED, "ff %d above the supported 16256", dm->ff);
   if (!(dm->eps >= 0.f) || !std::isfinite(dm->eps)) return fail(DSPARK_EINVAL, "eps must be finite and >= 0");
+  const int nkv = dm->n_kv_heads == 0 ? dm->n_heads : dm->n_kv_heads;
+  if (nkv < 1 || dm->n_heads % nkv != 0)
+    return fail(DSPARK_EINVAL, "n_kv_heads %d must divide n_heads %d", dm->n_kv_heads, dm->n_heads);
+  if ((nkv * hd) % 128 != 0)
+    return fail(DSPARK_EUNSUPPORTED, "n_kv_heads * head_dim = %d must be a multiple of 128", nkv * hd);
+  if (dm->variant & ~(DSPARK_QK_NORM | DSPARK_PLAIN_CTX_KV | DSPARK_GELU_FFN))
+    return fail(DSPARK_EINVAL, "unknown variant bits 0x%x", dm->variant);
+  if (!(dm->rope_theta >= 0.f) || !std::isfinite(dm->rope_theta) || (dm->rope_theta > 0.f && dm->rope_theta <= 1.f))
+    return fail(DSPARK_EINVAL, "rope_theta must be 0 (no rotary positions) or finite and > 1");
   if ((op == DSPARK_OP_BLOCK_FORWARD || op == DSPARK_OP_CTX_APPEND || op == DSPARK_OP_BLOCK_PROPOSE) &&
       (dm->n_layers < 1 || dm->n_layers > 16))
     return fail(dm->n_layers < 1 ? DSPARK_EINVAL : DSPARK_EUNSUPPORTED, "n_layers %d not in [1, 16]",
@@ -140,6 +150,8 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   p->T = T;
   p->Tpad = ((T + 63) / 64) * 64;
   p->hd = dm->d / dm->n_heads;
+  p->nkv = dm->n_kv_heads == 0 ? dm->n_heads : dm->n_kv_heads;
+  p->kvd = p->nkv * p->hd;
   p->M = A * dm->gamma;
   // The context projections address H_ctx (the A operand of the K/V
   // product) and W_c with 32-bit byte offsets (the taps are checked with
@@ -168,11 +180,11 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   if (runs_eq2) p->ppart = take((size_t)p->ctx.splits * T * d * 4);
   if (runs_kv) {
-    if (bf) p->wkvt = take((size_t)2 * p->kv_layers * d * d * 2);
+    if (bf) p->wkvt = take((size_t)2 * p->kv_layers * p->kvd * d * 2);
     if (op != DSPARK_OP_BLOCK_LAYER) p->hctx = take((size_t)T * d * p->esz);
     p->rinv = take((size_t)T * 4);
     if (op == DSPARK_OP_CTX_APPEND) p->rowmap = take((size_t)T * 4);
-    else p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * d * p->esz);
+    else p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * p->kvd * p->esz);
   }
   if (runs_block) {
     p->prefix = take((size_t)(A + 1) * 4);
@@ -203,8 +215,13 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
     if ((p) && !aligned16(p)) return fail(DSPARK_EINVAL, "%s is not 16-byte aligned", #p); \
   } while (0)
 
-static dspark_status check_layer(const dspark_layer_weights* lw, int i) {
+static dspark_status check_layer(const dspark_layer_weights* lw, int i, const dspark_dims* dm) {
   if (!lw) return fail(DSPARK_EINVAL, "layer weights %d is NULL", i);
+  if (dm->variant & DSPARK_QK_NORM) {
+    if (!lw->q_norm || !lw->k_norm) return fail(DSPARK_EINVAL, "layer %d: q_norm / k_norm is NULL", i);
+    if (!aligned16(lw->q_norm) || !aligned16(lw->k_norm))
+      return fail(DSPARK_EINVAL, "layer %d: q_norm / k_norm is not 16-byte aligned", i);
+  }
   const void* ptrs[9] = {lw->attn_norm, lw->wq, lw->wk, lw->wv, lw->wo,
                          lw->ff_norm,   lw->w_gate, lw->w_up, lw->w_down};
   static const char* names[9] = {"attn_norm", "wq", "wk", "wv", "wo", "ff_norm", "w_gate", "w_up", "w_down"};
@@ -259,18 +276,45 @@ static dspark_status run_ctx_gemm(const dspark_dims* dm, const Plan& p, const vo
   return DSPARK_OK;
 }
 
-// The K/V GEMM's B operand: W_K, W_V of `nl` layers with the attn_norm gains.
-static BMats kv_mats(const dspark_layer_weights* layers, int nl, int d) {
+// The K/V GEMM's B operand: W_K, W_V ([kvd, d] each) of `nl` layers with the
+// attn_norm gains (none when the context rows enter W_K / W_V unnormalised).
+static BMats kv_mats(const dspark_dims* dm, const dspark_layer_weights* layers, int nl, int kvd) {
+  const bool plain = (dm->variant & DSPARK_PLAIN_CTX_KV) != 0;
   BMats b{};
   for (int i = 0; i < nl; ++i) {
     b.mat[2 * i] = layers[i].wk;
     b.mat[2 * i + 1] = layers[i].wv;
-    b.gain[2 * i] = layers[i].attn_norm;
-    b.gain[2 * i + 1] = layers[i].attn_norm;
+    b.gain[2 * i] = plain ? nullptr : layers[i].attn_norm;
+    b.gain[2 * i + 1] = plain ? nullptr : layers[i].attn_norm;
   }
-  b.n_per = d;
+  b.n_per = kvd;
   b.nmat = 2 * nl;
   return b;
+}
+
+// k_norm and rotary positions on the context keys the K/V product just
+// wrote (the variant's contextNormRope); nothing for the plain method.
+static dspark_status run_k_post(const dspark_dims* dm, const Plan& p, const dspark_layer_weights* layers,
+                                int nl, const KVDesc& kv, const int32_t* cu_dev, int A, hipStream_t s) {
+  const bool qkn = (dm->variant & DSPARK_QK_NORM) != 0;
+  if ((!qkn && dm->rope_theta <= 0.f) || p.T == 0) return DSPARK_OK;
+  KPostArgs a;
+  a.base = kv.base;
+  a.Tpad = kv.Tpad;
+  a.T = p.T;
+  a.n_kv = p.nkv;
+  a.hd = p.hd;
+  a.n_layers = nl;
+  for (int i = 0; i < nl; ++i) a.k_norm[i] = qkn ? layers[i].k_norm : nullptr;
+  a.eps = dm->eps;
+  a.rope = dm->rope_theta > 0.f;
+  a.log2_theta = dm->rope_theta > 0.f ? std::log2((double)dm->rope_theta) : 0.0;
+  a.cu = cu_dev;
+  a.A = A;
+  a.dst_row = kv.dst_row;
+  a.cap = kv.seq_stride;
+  DSPARK_HIP(launch_k_post(dm->dtype, a, s));
+  return DSPARK_OK;
 }
 
 // Context K/V of `nl` layers from H_ctx (rinv, and for bf16 the stacked
@@ -280,9 +324,9 @@ static dspark_status run_ctx_kv(const dspark_dims* dm, const Plan& p, const void
                                 hipStream_t s) {
   if (p.T == 0) return DSPARK_OK;
   const int d = dm->d;
-  const BMats b = kv_mats(layers, nl, d);
+  const BMats b = kv_mats(dm, layers, nl, p.kvd);
   void* wkvt = dm->dtype == DSPARK_BF16 ? at<char>(ws, p.wkvt) : nullptr;
-  DSPARK_HIP(launch_gemm_kv(dm->dtype, h_ctx, b, wkvt, rinv, kv, d, nl, s));
+  DSPARK_HIP(launch_gemm_kv(dm->dtype, h_ctx, b, wkvt, rinv, kv, d, p.kvd, nl, s));
   return DSPARK_OK;
 }
 
@@ -293,7 +337,7 @@ static KVDesc ws_kv(const dspark_dims* dm, const Plan& p, void* ws) {
   kv.Tpad = p.Tpad;
   kv.T = (int)p.T;
   kv.hd = p.hd;
-  kv.n_heads = dm->n_heads;
+  kv.n_heads = p.nkv;
   return kv;
 }
 
@@ -306,7 +350,7 @@ static KVDesc cache_kv(const dspark_dims* dm, const Plan& p, int A, int cap, voi
   kv.Tpad = (int64_t)A * cap;
   kv.T = (int)p.T;
   kv.hd = p.hd;
-  kv.n_heads = dm->n_heads;
+  kv.n_heads = p.nkv;
   kv.seq_stride = cap;
   kv.dst_row = dst_row;
   return kv;
@@ -328,7 +372,7 @@ static void setup_block_roles(const dspark_dims* dm, const Plan& p, int A, const
 static void setup_prep_role(const dspark_dims* dm, const Plan& p, const dspark_layer_weights* layers, int nl,
                             void* ws, SetupArgs* sa) {
   if (dm->dtype == DSPARK_BF16 && p.T > 0) {
-    sa->b = kv_mats(layers, nl, dm->d);
+    sa->b = kv_mats(dm, layers, nl, p.kvd);
     sa->Bt = at<char>(ws, p.wkvt);
   }
 }
@@ -345,20 +389,39 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   float* E = at<float>(ws, p.E) + (size_t)kv_layer * M * d;   // zeroed by the set-up pass
   float* GU = at<float>(ws, p.GU);
 
-  // Q (pre-scaled for the base-2 softmax), K_d, V_d from RMSNorm(D; attn_norm)
+  // Q (pre-scaled for the base-2 softmax), K_d, V_d from RMSNorm(D; attn_norm).
+  // The weights go in as kvd-row pieces: W_Q as d / kvd of them, then W_K, W_V.
+  const float qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
+  const bool qkn = (dm->variant & DSPARK_QK_NORM) != 0, rope = dm->rope_theta > 0.f;
+  const size_t esz = dt == DSPARK_BF16 ? 2 : 4;
+  const int kvd = p.kvd, npq = d / kvd;
   RowGemmArgs r{};
-  r.X = D; r.ldx = d; r.M = M; r.K = d; r.N = 3 * d;
+  r.X = D; r.ldx = d; r.M = M; r.K = d; r.N = d + 2 * kvd;
   r.g = lw.attn_norm; r.eps = dm->eps;
-  r.b.mat[0] = lw.wq; r.b.mat[1] = lw.wk; r.b.mat[2] = lw.wv;
-  r.b.n_per = d; r.b.nmat = 3;
-  r.q = Q; r.kd = Kd; r.vd = Vd; r.d = d;
-  r.qscale = (float)(1.0 / std::sqrt((double)p.hd) * 1.4426950408889634);
+  for (int i = 0; i < npq; ++i) r.b.mat[i] = static_cast<const char*>(lw.wq) + (size_t)i * kvd * d * esz;
+  r.b.mat[npq] = lw.wk; r.b.mat[npq + 1] = lw.wv;
+  r.b.n_per = kvd; r.b.nmat = npq + 2;
+  r.q = Q; r.kd = Kd; r.vd = Vd; r.d = d; r.kvd = kvd;
+  r.qscale = (qkn || rope) ? 1.f : qscale;   // with head norms / rotary positions the post pass scales
   DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_QKV, r, s));
+  if (qkn || rope) {   // the variant's noiseNormRope on the block rows
+    QkPostArgs qa;
+    qa.Q = Q; qa.Kd = Kd; qa.M = M; qa.gamma = G; qa.n_heads = dm->n_heads; qa.n_kv = p.nkv; qa.hd = p.hd;
+    qa.q_norm = qkn ? lw.q_norm : nullptr;
+    qa.k_norm = qkn ? lw.k_norm : nullptr;
+    qa.eps = dm->eps;
+    qa.rope = rope;
+    qa.log2_theta = rope ? std::log2((double)dm->rope_theta) : 0.0;
+    qa.cu = cu_dev;
+    qa.qscale = qscale;
+    DSPARK_HIP(launch_qk_post(qa, s));
+  }
   // attention over [context ++ block]: split-K partials, then the combine
   // with the output projection, E = D + Attn Wo^T
   AttnArgs aa{};
   aa.Q = Q; aa.Kd = Kd; aa.Vd = Vd;
   aa.kv = kv;
+  aa.n_heads = dm->n_heads;
   aa.layer = kv_layer;
   aa.cu = cu_dev;
   aa.prefix = at<int32_t>(ws, p.prefix);
@@ -375,6 +438,7 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   r.g = lw.ff_norm; r.eps = dm->eps;
   r.b.mat[0] = lw.w_gate; r.b.mat[1] = lw.w_up; r.b.n_per = ff; r.b.nmat = 2;
   r.out = GU; r.ldo = ff;
+  r.act = (dm->variant & DSPARK_GELU_FFN) ? 1 : 0;
   DSPARK_HIP(launch_rowgemm(dt, RP_RMSNORM, RE_SWIGLU, r, s));
   // D' = E + H Wdown^T
   r = RowGemmArgs{};
@@ -442,7 +506,7 @@ static dspark_status block_layer_impl(const dspark_dims* dims, int32_t A, const 
   if (p.T > 0) NEED_PTR(h_ctx);
   NEED_PTR(d_in);
   NEED_PTR(d_out);
-  st = check_layer(lw, 0);
+  st = check_layer(lw, 0, dims);
   if (st != DSPARK_OK) return st;
   NEED_PTR(ws);
   if (ws_bytes < p.total)
@@ -458,10 +522,13 @@ static dspark_status block_layer_impl(const dspark_dims* dims, int32_t A, const 
     sa.T = p.T;
     sa.h_in = h_ctx;
     sa.rinv = rinv;
+    sa.rinv_one = (dims->variant & DSPARK_PLAIN_CTX_KV) != 0;
   }
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   const KVDesc kv = ws_kv(dims, p, ws);
   st = run_ctx_kv(dims, p, h_ctx, rinv, lw, 1, kv, ws, s);
+  if (st != DSPARK_OK) return st;
+  st = run_k_post(dims, p, lw, 1, kv, cu_dev, A, s);
   if (st != DSPARK_OK) return st;
   return run_layer(dims, p, A, cu_dev, *lw, 0, kv, d_in, d_out, ws, s);
 }
@@ -511,7 +578,7 @@ static dspark_status forward_impl(const dspark_dims* dims, int32_t A, const int3
   NEED_PTR(block_pos);
   if (!layers) return fail(DSPARK_EINVAL, "layers is NULL");
   for (int i = 0; i < dims->n_layers; ++i) {
-    st = check_layer(&layers[i], i);
+    st = check_layer(&layers[i], i, dims);
     if (st != DSPARK_OK) return st;
   }
   OPT_PTR(out_norm);
@@ -548,11 +615,14 @@ static dspark_status forward_impl(const dspark_dims* dims, int32_t A, const int3
     sa.g = ctx_norm;
     sa.h = h_ctx;
     sa.rinv = rinv;
+    sa.rinv_one = (dims->variant & DSPARK_PLAIN_CTX_KV) != 0;
   }
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   KVDesc kv = ws_kv(dims, p, ws);
   kv.key_mask = key_mask;
   st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, kv, ws, s);
+  if (st != DSPARK_OK) return st;
+  st = run_k_post(dims, p, layers, dims->n_layers, kv, cu_dev, A, s);
   if (st != DSPARK_OK) return st;
   const int N = dims->n_layers;
   for (int i = 0; i < N; ++i) {
@@ -648,7 +718,8 @@ static dspark_status check_cache(const dspark_dims* dims, int32_t A, int32_t cap
     return fail(DSPARK_EUNSUPPORTED, "A * cap = %lld rows; at most 2^31 - 1 are supported",
                 (long long)A * cap);
   const size_t esz = dims->dtype == DSPARK_BF16 ? 2 : 4;
-  *bytes = (size_t)dims->n_layers * 2 * (size_t)A * cap * dims->d * esz;
+  const int nkv = dims->n_kv_heads == 0 ? dims->n_heads : dims->n_kv_heads;
+  *bytes = (size_t)dims->n_layers * 2 * (size_t)A * cap * nkv * (dims->d / dims->n_heads) * esz;
   return DSPARK_OK;
 }
 
@@ -698,7 +769,7 @@ dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
   NEED_PTR(ctx_norm);
   if (!layers) return fail(DSPARK_EINVAL, "layers is NULL");
   for (int i = 0; i < dims->n_layers; ++i) {
-    st = check_layer(&layers[i], i);
+    st = check_layer(&layers[i], i, dims);
     if (st != DSPARK_OK) return st;
   }
   NEED_PTR(cache);
@@ -721,6 +792,7 @@ dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
   sa.g = ctx_norm;
   sa.h = at<char>(ws, p.hctx);
   sa.rinv = at<float>(ws, p.rinv);
+  sa.rinv_one = (dims->variant & DSPARK_PLAIN_CTX_KV) != 0;
   sa.ncu = ncu_dev;
   sa.pos = pos_dev;
   sa.cap = cap;
@@ -728,7 +800,9 @@ dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
   sa.dst_row = at<int32_t>(ws, p.rowmap);
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   const KVDesc kv = cache_kv(dims, p, A, cap, cache, at<int32_t>(ws, p.rowmap));
-  return run_ctx_kv(dims, p, at<char>(ws, p.hctx), at<float>(ws, p.rinv), layers, dims->n_layers, kv, ws, s);
+  st = run_ctx_kv(dims, p, at<char>(ws, p.hctx), at<float>(ws, p.rinv), layers, dims->n_layers, kv, ws, s);
+  if (st != DSPARK_OK) return st;
+  return run_k_post(dims, p, layers, dims->n_layers, kv, ncu_dev, A, s);
 }
 
 dspark_status dspark_block_propose(const dspark_dims* dims, int32_t A, int32_t cap, const int32_t* cu_host,
@@ -752,7 +826,7 @@ dspark_status dspark_block_propose(const dspark_dims* dims, int32_t A, int32_t c
   NEED_PTR(block_pos);
   if (!layers) return fail(DSPARK_EINVAL, "layers is NULL");
   for (int i = 0; i < dims->n_layers; ++i) {
-    st = check_layer(&layers[i], i);
+    st = check_layer(&layers[i], i, dims);
     if (st != DSPARK_OK) return st;
   }
   OPT_PTR(out_norm);

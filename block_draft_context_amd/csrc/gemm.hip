@@ -43,7 +43,7 @@ struct EpiKV {                 // K/V of every layer, row scale, tiled layout
   S* base;
   const float* rinv;
   int64_t Tpad;
-  int T, d, hd, n_heads;
+  int T, d, hd, n_heads;       // d: columns of one K or V block (K/V heads * hd)
   const int32_t* dst_row;      // null: row r at r (zeros at T .. Tpad-1); else row r < T at dst_row[r]
   DSPARK_DEV void store(int /*z*/, int r, int n, float v, int /*M*/, int /*N*/) const {
     int64_t t;
@@ -318,7 +318,7 @@ struct EpiKVBig {              // all layers' K/V, row scale, attention layout
   S* base;
   const float* rinv;
   int64_t Tpad;
-  int T, d, hd, n_heads;
+  int T, d, hd, n_heads;       // d: columns of one K or V block (K/V heads * hd)
   int n_base;                  // column of the stacked K/V where this launch's columns start
   const int32_t* dst_row;      // null: row r at r (zeros at T .. Tpad-1); else row r < T at dst_row[r]
   static constexpr bool kStaged = true;
@@ -777,14 +777,16 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
 }
 
 hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const void* Bt,
-                          const float* rinv, const KVDesc& kv, int d, int n_layers,
+                          const float* rinv, const KVDesc& kv, int d, int kvd, int n_layers,
                           hipStream_t s) {
   ASegs a{};
   a.seg[0] = h_ctx;
   a.ld = d;
   a.seg_k = d;
   a.nseg = 1;
-  const int N = 2 * n_layers * d;
+  // the epilogues decode a column as (layer, K or V, head, value) with kvd
+  // columns per K or V block
+  const int N = 2 * n_layers * kvd;
   const int M = kv.T;
   // packed: rows T..Tpad-1 are written as zeros; cache: only the T new rows
   const int Mrows = kv.dst_row ? M : (int)kv.Tpad;
@@ -792,7 +794,7 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
   if (use_big_tiles(dtype, M, N)) {
     const bf16* B = static_cast<const bf16*>(Bt);
     const int nb = kv_big_columns(Mrows, N);
-    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, 0,
+    EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, kvd, kv.hd, kv.n_heads, 0,
                        kv.dst_row};
     const int tm = (Mrows + BG_M - 1) / BG_M;
     if (nb * BG_N == N) {   // 256x256 tiles only
@@ -818,7 +820,7 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
                                                                                epi);
     }
   } else if (dtype == 1) {
-    EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, kv.dst_row};
+    EpiKV<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, kvd, kv.hd, kv.n_heads, kv.dst_row};
     const bf16* B = static_cast<const bf16*>(Bt);
     if (pick_gemm_bm(M) == 128) {
       dim3 grid(((Mrows + 127) / 128) * (N / 128), 1, 1);
@@ -828,7 +830,7 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
       gemm_bf16_nt<64, 128, 2, 2, EpiKV<bf16>><<<grid, 256, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
     }
   } else {
-    EpiKV<float> epi{static_cast<float*>(kv.base), rinv, kv.Tpad, kv.T, d, kv.hd, kv.n_heads, kv.dst_row};
+    EpiKV<float> epi{static_cast<float*>(kv.base), rinv, kv.Tpad, kv.T, kvd, kv.hd, kv.n_heads, kv.dst_row};
     dim3 grid(((Mrows + 63) / 64) * (N / 64), 1, 1);
     gemm_f32<EpiKV<float>><<<grid, 256, 0, s>>>(a, b, M, Mrows, N, d, d, epi);
   }

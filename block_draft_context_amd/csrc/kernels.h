@@ -105,6 +105,7 @@ struct SetupArgs {
   void* h = nullptr;
   const void* h_in = nullptr;
   float* rinv = nullptr;
+  bool rinv_one = false;   // the context rows enter W_K / W_V unnormalised: rinv[t] = 1
   // cleared buffer
   float* zero = nullptr;
   int64_t zero_n = 0;
@@ -135,8 +136,9 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
 
 // K/V for all layers of `b` (2 matrices per layer: K then V) from H_ctx with
 // the row scale rinv, written in the attention layout of `kv`.
+// K = d input columns; kvd = K/V heads * hd output columns per K or V block.
 hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const void* Bt,
-                          const float* rinv, const KVDesc& kv, int d, int n_layers,
+                          const float* rinv, const KVDesc& kv, int d, int kvd, int n_layers,
                           hipStream_t s);
 
 // ---- attention ------------------------------------------------------------
@@ -147,9 +149,10 @@ int64_t attention_tiles(const int32_t* cu_host, int A, int chunk);
 
 struct AttnArgs {
   const float* Q;       // [A*gamma][d], pre-scaled by hd^-1/2 * log2(e)
-  const float* Kd;      // [A*gamma][d] block keys
-  const float* Vd;      // [A*gamma][d] block values
-  KVDesc kv;            // context K/V (attention layout)
+  const float* Kd;      // [A*gamma][kvd] block keys (kvd = kv.n_heads * hd)
+  const float* Vd;      // [A*gamma][kvd] block values
+  KVDesc kv;            // context K/V (attention layout; kv.n_heads = K/V heads)
+  int n_heads;          // query heads (a multiple of kv.n_heads)
   int layer;
   const int32_t* cu;    // device prefix offsets [A+1]
   const int32_t* prefix;  // device tile prefix [A+1]
@@ -179,11 +182,13 @@ struct RowGemmArgs {
   float* out = nullptr;       // RE_STORE / RE_RESID / RE_SWIGLU: out[m][n] (row stride ldo)
   int ldo = 0;
   const float* res = nullptr; // RE_RESID: out = res + X.W
-  float* q = nullptr;         // RE_QKV: columns [0,d) -> q (scaled), [d,2d) -> kd, [2d,3d) -> vd
+  float* q = nullptr;         // RE_QKV: columns [0,d) -> q (scaled), [d,d+kvd) -> kd, [d+kvd,d+2kvd) -> vd
   float* kd = nullptr;
   float* vd = nullptr;
   int d = 0;
+  int kvd = 0;                // K/V columns (grouped K/V heads: fewer than d)
   float qscale = 1.f;
+  int act = 0;                // RE_SWIGLU: 0 = SiLU(gate) * up, 1 = tanh-GELU(gate) * up
 };
 int rowgemm_rows_per_pass(int K);
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s);
@@ -197,6 +202,43 @@ hipError_t launch_block_rows(const float* block_in, const float* block_pos, int 
 // (tok_proj [d][H] storage type), block_in[b][j] = mask_emb[j-1] for j >= 1.
 hipError_t launch_block_build(int dtype, const float* anchor_emb, int A, int H, const void* tok_proj,
                               const float* mask_emb, int gamma, int d, float* block_in, hipStream_t s);
+
+// ---- layer variant: per-head norms and rotary positions -------------------
+constexpr int kMaxLayers = 16;
+// Block rows: Q [M][n_heads * hd], Kd [M][n_kv * hd]; q_norm / k_norm [hd]
+// (nullable: no norm); rope != 0 rotates at L_b + j (cu: prefix offsets of
+// the context lengths); Q is scaled by qscale last.
+struct QkPostArgs {
+  float* Q = nullptr;
+  float* Kd = nullptr;
+  int M = 0, gamma = 0, n_heads = 0, n_kv = 0, hd = 0;
+  const float* q_norm = nullptr;
+  const float* k_norm = nullptr;
+  float eps = 0.f;
+  int rope = 0;
+  double log2_theta = 0.0;
+  const int32_t* cu = nullptr;
+  float qscale = 1.f;
+};
+hipError_t launch_qk_post(const QkPostArgs& a, hipStream_t s);
+// Context keys in place (attention layout, every layer of the slab set):
+// the T rows the K/V product wrote, slab row dst_row[r] at position
+// dst_row[r] % cap (a cache), or row r of a packed context at r - cu[b].
+struct KPostArgs {
+  void* base = nullptr;
+  int64_t Tpad = 0;
+  int64_t T = 0;
+  int n_kv = 0, hd = 0, n_layers = 0;
+  const float* k_norm[kMaxLayers] = {};   // per layer, nullable
+  float eps = 0.f;
+  int rope = 0;
+  double log2_theta = 0.0;
+  const int32_t* cu = nullptr;
+  int A = 1;
+  const int32_t* dst_row = nullptr;
+  int64_t cap = 0;
+};
+hipError_t launch_k_post(int dtype, const KPostArgs& a, hipStream_t s);
 
 // ---- Markov head, confidence head, greedy draft loop ----------------------
 struct MarkovArgs {

@@ -170,7 +170,7 @@ __device__ __forceinline__ void norm_row(const SetupArgs& a, int64_t t, int lane
   }
   if (a.rinv) {
     ss2 = wave_sum(ss2);
-    if (lane == 0) a.rinv[t] = rsqrtf(ss2 / (float)d + a.eps);
+    if (lane == 0) a.rinv[t] = a.rinv_one ? 1.f : rsqrtf(ss2 / (float)d + a.eps);
   }
 }
 
@@ -189,7 +189,7 @@ __device__ __forceinline__ void stats_row(const SetupArgs& a, int64_t t, int lan
   for (int i = 0; i < 32; ++i)
     if (i < nv) ss += x[i] * x[i];
   ss = wave_sum(ss);
-  if (lane == 0) a.rinv[t] = rsqrtf(ss / (float)d + a.eps);
+  if (lane == 0) a.rinv[t] = a.rinv_one ? 1.f : rsqrtf(ss / (float)d + a.eps);
 }
 
 // Cache row map: new row r belongs to the sequence b with ncu[b] <= r <

@@ -93,31 +93,58 @@ typedef enum {
   DSPARK_OP_BLOCK_PROPOSE = 4   /* cu_host = offsets of the cached lengths */
 } dspark_op;
 
+/* The layer variant of the page "src/dspark-runtime.js" (its per-layer
+ * q_norm / k_norm weights, noiseNormRope / contextNormRope kernels, K/V
+ * heads fewer than query heads, and a context K/V projection with no
+ * per-layer norm), as switches on top of module-dflash.ts's #layer:
+ *   DSPARK_QK_NORM       RMSNorm over each head of the queries and keys (block
+ *                        and context) with the layer's q_norm / k_norm [hd] gains
+ *   DSPARK_PLAIN_CTX_KV  the context rows enter W_K / W_V as Eq 2 leaves them
+ *                        (no attn_norm on the context side)
+ *   DSPARK_GELU_FFN      the gated FFN's activation is tanh-GELU (module-dflash.ts
+ *                        geluApprox) instead of SiLU
+ * plus dims->rope_theta > 0 (rotary positions with base theta on queries and
+ * keys, pairs (c, c + hd/2), angle pos * theta^(-2c/hd); context row t of a
+ * sequence at position t, block row j at L_b + j) and dims->n_kv_heads (query
+ * head h reads K/V head h / (n_heads / n_kv_heads)). The positions and pairing
+ * are this library's reading: the page prints no formula. */
+typedef enum {
+  DSPARK_QK_NORM = 1,
+  DSPARK_PLAIN_CTX_KV = 2,
+  DSPARK_GELU_FFN = 4
+} dspark_variant;
+
 /* Problem sizes (DflashConfig and TargetDims of module-dflash.ts). */
 typedef struct {
   int32_t m;         /* number of tapped target layers */
   int32_t H;         /* target hidden width */
   int32_t d;         /* draft width dDraft */
-  int32_t n_heads;   /* attention heads; head_dim = d / n_heads */
+  int32_t n_heads;   /* attention (query) heads; head_dim = d / n_heads */
   int32_t gamma;     /* block size */
   int32_t n_layers;  /* draft layers (used by dspark_block_forward) */
   int32_t ff;        /* FFN width, ffMult * d */
   float eps;         /* RMSNorm epsilon (the target's rmsNormEps) */
   int32_t dtype;     /* dspark_dtype: storage type of the long tensors */
+  int32_t n_kv_heads;  /* K/V heads, dividing n_heads (0 = n_heads); n_kv_heads * hd a multiple of 128 */
+  int32_t variant;     /* dspark_variant bits (0 = #layer of module-dflash.ts) */
+  float rope_theta;    /* rotary base (0 = no rotary positions) */
 } dspark_dims;
 
 /* One draft layer's parameters (bb.{i}.* of module-dflash.ts), device
- * pointers. Matrices in dims->dtype, gains float32. */
+ * pointers. Matrices in dims->dtype, gains float32. kvd = n_kv_heads * hd
+ * (= d unless the K/V heads are grouped). */
 typedef struct {
   const float* attn_norm;   /* [d]    shared by block and context rows */
   const void* wq;           /* [d, d]   [out, in] */
-  const void* wk;           /* [d, d] */
-  const void* wv;           /* [d, d] */
+  const void* wk;           /* [kvd, d] */
+  const void* wv;           /* [kvd, d] */
   const void* wo;           /* [d, d] */
   const float* ff_norm;     /* [d] */
   const void* w_gate;       /* [ff, d] */
   const void* w_up;         /* [ff, d] */
   const void* w_down;       /* [d, ff] */
+  const float* q_norm;      /* [hd] with DSPARK_QK_NORM, else ignored (may be NULL) */
+  const float* k_norm;      /* [hd] with DSPARK_QK_NORM, else ignored (may be NULL) */
 } dspark_layer_weights;
 
 /* Bytes of workspace that `op` needs for these sizes (0 with a message in

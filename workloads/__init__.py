@@ -346,3 +346,34 @@ def padded_layout(seed_id: int, taps, cu, L_ctx: int, placements, dtype: str = "
         for j, t in enumerate(taps):
             out[j][b * L_ctx + pos] = t[cu[b]:cu[b + 1]]
     return out, mask
+
+
+# ----------------------------------------------------------------------------
+# The page-1 layer variant: grouped K/V heads and q/k-norm gains
+# ----------------------------------------------------------------------------
+_S_VAR = 300
+
+
+def variant_layers(w: Workload, layers: List[dict], n_kv_heads: int, *, gains: str = "random") -> List[dict]:
+    """Copies of the layers for the variant: W_K, W_V redrawn as [d, n_kv * hd]
+    when the K/V heads are grouped (N(0, 0.02^2), storage-rounded), and
+    per-head q_norm / k_norm gains [hd] (U(0.5, 1.5), or 1 with
+    gains="unit")."""
+    hd = w.head_dim
+    kvd = n_kv_heads * hd
+    bf = w.dtype == "bf16"
+    out = []
+    for i, lw in enumerate(layers):
+        v = dict(lw)
+        s = _S_VAR + 10 * i
+        if kvd != w.d:
+            v["wk"] = _normal(w.seed_id, s + 0, (w.d, kvd), 0.02, round_bf16=bf)
+            v["wv"] = _normal(w.seed_id, s + 1, (w.d, kvd), 0.02, round_bf16=bf)
+        if gains == "unit":
+            v["q_norm"] = np.ones(hd, dtype=np.float32)
+            v["k_norm"] = np.ones(hd, dtype=np.float32)
+        else:
+            v["q_norm"] = _rng(w.seed_id, s + 2).uniform(0.5, 1.5, size=hd).astype(np.float32)
+            v["k_norm"] = _rng(w.seed_id, s + 3).uniform(0.5, 1.5, size=hd).astype(np.float32)
+        out.append(v)
+    return out
