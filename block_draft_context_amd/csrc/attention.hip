@@ -211,12 +211,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   if (first <= blk1) {
     const int64_t last = first + ((blk1 - first) / bstep) * bstep;
     u32x4 kreg[NKV], vreg[NLD];
-    uint32_t kmask = 1;   // key-padding mask of this lane's key (padded batches only)
     auto load_k = [&](int64_t blk) __attribute__((always_inline)) {
       const S* kp = Kh + blk * 64 * HD + lane * E;
 #pragma unroll
       for (int i = 0; i < NKV; ++i) kreg[i] = ld16(kp + i * 64 * E);
-      if (key_mask) kmask = key_mask[min(blk * 64 + lane, T1 - 1)];
     };
     // V is read once per layer: non-temporal loads (measured 5% faster per
     // forward at T = 131072 and on a ragged 16-sequence batch; marking K as
@@ -233,7 +231,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       const int64_t nxt = min(blk + bstep, last);
       // ---- scores: lane owns key blk*64 + lane
       const int64_t key = blk * 64 + lane;
-      const bool valid = key >= k0 && key < k1 && kmask != 0;
+      // padded batches: the key's mask byte, read where it is used (held
+      // across the loop it pushed the kernel into register spills)
+      const bool valid = key >= k0 && key < k1 && (!key_mask || key_mask[min(key, T1 - 1)] != 0);
       float s[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) s[j] = 0.f;

@@ -139,7 +139,10 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
   // else, so they stream in while the input rows' latency passes
   load_batch(0);
 
-  for (int m0 = 0; m0 < M; m0 += mc) {
+  // One pass of mc rows per workgroup: pass blockIdx.y (the grid has one
+  // row of workgroups per pass), so many block rows run as parallel passes.
+  {
+    const int m0 = blockIdx.y * mc;
     const int mp = min(mc, M - m0);                             // live rows of this pass
     // this lane's output after the reduction: value index lane / (64 / V)
     const int vo = lane / (64 / V);
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int j0 = 0; j0 < cpl; j0 += RG_JB) {
-      if (j0 > 0 || m0 > 0) load_batch(j0);
+      if (j0 > 0) load_batch(j0);   // the first batch is in registers already
 #pragma unroll
       for (int b = 0; b < RG_JB; ++b) {
         if (j0 + b < cpl) {
@@ -279,7 +282,11 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s) {
   if (a.N % 8 != 0 || a.K % 64 != 0 || a.b.n_per % 8 != 0 || a.K > RG_XS) return hipErrorInvalidValue;
   const bool narrow = epi != RE_SWIGLU && a.N / 8 < 256;   // SwiGLU pairs need 2 columns per wave
-  dim3 grid(a.N / (narrow ? 4 : 8));
+  // one workgroup row per pass of rowgemm_mc rows; with N / COLS a multiple
+  // of 8 the workgroups of one column set land on one XCD (id % 8), so the
+  // passes re-read that set's weights from the XCD's L2
+  const int passes = (a.M + rowgemm_mc(a.M, a.K) - 1) / rowgemm_mc(a.M, a.K);
+  dim3 grid(a.N / (narrow ? 4 : 8), passes);
   const size_t lds = (size_t)rowgemm_mc(a.M, a.K) * a.K * sizeof(float);
   bool ok = false;
   trace_pre(K_ROWGEMM, s);
