@@ -15,7 +15,9 @@ same workload on the host cores.
 
 The line also carries, under "incremental", the steady-state drafting regime
 of the draft cache: one draft block over a cache of 8192 and of 131072
-context rows (dspark_block_propose) and an 8-row append (dspark_ctx_append).
+context rows (dspark_block_propose) and an 8-row append (dspark_ctx_append),
+and under "markov" the greedy draft loop after the backbone
+(dspark_markov_draft) for one and for 16 sequences.
 """
 from __future__ import annotations
 
@@ -216,6 +218,39 @@ def _time_calls(torch, call, stream, steps, warmup=3):
     return sorted(a.elapsed_time(b) for a, b in ev)
 
 
+def bench_markov(B, torch, steps, vocab=131072, rank=256, gamma=5, d=1024, batches=(1, 16)):
+    """The greedy draft loop after the backbone (dspark_markov_draft) for the
+    5-position block of the d = 1024 drafter with a Markov rank of 256 (the
+    module-dflash.ts defaults) over a 131072-entry vocabulary (the pages do
+    not print one), for one and for 16 sequences. HBM-bound: each position
+    streams w2 once for all sequences and moves the base and draft logits
+    (algorithmic bytes per draft: gamma * (vocab * rank * 2 + 3 * A * vocab * 4))."""
+    out = {"vocab": vocab, "rank": rank, "gamma": gamma, "d": d}
+    for A in batches:
+        x = W.markov_inputs(90 + A, A=A, gamma=gamma, d=d, vocab=vocab, rank=rank)
+        dev = "cuda:0"
+        f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=t)
+        g = dict(block=f(x["block"]), U=f(x["base_logits"]), anchor=f(x["anchor"], torch.int32),
+                 w1=f(x["w1"], torch.bfloat16), w2=f(x["w2"], torch.bfloat16), cw=f(x["conf_w"]),
+                 cb=f(x["conf_b"]))
+        dims = B.DsparkDims(m=1, H=64, d=d, n_heads=8, gamma=gamma, n_layers=1, ff=2 * d, dtype="bf16")
+        toks = torch.empty((A, gamma), dtype=torch.int32, device=dev)
+        conf = torch.empty((A, gamma), dtype=torch.float32, device=dev)
+        logits = torch.empty((A, gamma, vocab), dtype=torch.float32, device=dev)
+        call = lambda: B.markov_draft(dims, g["block"], g["U"], g["anchor"], g["w1"], g["w2"], g["cw"],
+                                      g["cb"], tokens=toks, conf=conf, draft_logits=logits)
+        t = _time_calls(torch, call, torch.cuda.current_stream(), steps)
+        ms = t[len(t) // 2]
+        amount = gamma * (vocab * rank * 2 + 3.0 * A * vocab * 4)
+        out[f"A{A}"] = {"draft_ms_median": round(ms, 4), "draft_ms_min": round(t[0], 4),
+                        "drafts_per_s": round(A * 1e3 / ms, 1),
+                        "hbm": {"bound": "hbm", "achieved": round(amount / ms / 1e6, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(amount / ms / 1e6 / PEAK_HBM_GBS, 4)}}
+        del g, logits
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_incremental(B, torch, steps, lengths=(8192, 131072), new_rows=8):
     """The steady-state drafting regime of the incremental context: one
     sequence of the 5-layer d = 1024 drafter (the long-context workload's
@@ -286,6 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-markov", action="store_true",
+                    help="skip the greedy draft loop measurement (dspark_markov_draft)")
     ap.add_argument("--no-incremental", action="store_true",
                     help="skip the draft-cache measurement (propose / append at L = 8192, 131072)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -408,6 +445,8 @@ def main():
         del fwd, u, x
         torch.cuda.empty_cache()
         res["incremental"] = bench_incremental(B, torch, max(args.steps, 20))
+    if not args.no_markov:
+        res["markov"] = bench_markov(B, torch, max(args.steps, 20))
     print(json.dumps(res), flush=True)
 
 
