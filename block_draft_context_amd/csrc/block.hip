@@ -279,7 +279,205 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row GEMM on the matrix cores, for many block rows with bf16 weights.
+// With more rows than one 8-row pass, the vector-ALU kernel above re-reads
+// the input rows for every 8 output columns; here a workgroup owns 16 output
+// columns (SwiGLU: 16 gate and the matching 16 up columns) for 32 rows and
+// multiplies on v_mfma_f32_16x16x32_bf16. The float32 rows enter as two bf16
+// terms, hi = bf16(x) and lo = bf16(x - hi), so each product is two MFMAs
+// and the input keeps about 16 bits of mantissa (relative error <= 2^-16);
+// the weights are bf16 as stored and the sums are float32. The four waves
+// split K and keep RF_PF chunks of 32 k in flight each; their partial sums
+// meet in LDS, where the epilogues of the vector-ALU kernel run unchanged.
+// 16x16x32 operand layout: lane l holds A[l % 16][8 (l / 16) .. + 8) and
+// B[8 (l / 16) .. + 8)[l % 16]; the result D[4 (l / 16) + r][l % 16], r < 4.
+// ---------------------------------------------------------------------------
+constexpr int RF_RB = 2;     // 16-row blocks per workgroup
+constexpr int RF_PF = 4;     // k chunks in flight per wave
+
+DSPARK_DEV uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, from_f32<bf16>(x)); }
+
+// x (8 floats) -> hi, lo bf16 vectors with x ~= hi + lo
+DSPARK_DEV void split_bf16(const f32x4& x0, const f32x4& x1, bf16x8& hi, bf16x8& lo) {
+  float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = from_f32<bf16>(xv[e]);
+    hi[e] = h;
+    lo[e] = from_f32<bf16>(xv[e] - static_cast<float>(h));
+  }
+}
+
+template <int PRO, int EPI>
+__global__ __launch_bounds__(256) void rowgemm_mfma_kernel(RowGemmArgs a) {
+  constexpr int NCB = EPI == RE_SWIGLU ? 2 : 1;    // 16-column blocks: gate and up for SwiGLU
+  __shared__ float red[4][RF_RB][NCB][256];
+  __shared__ float ssq[4][RF_RB * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, M = a.M;
+  const int nb = blockIdx.x;
+  const int m_base = blockIdx.y * RF_RB * 16;
+  const int c16 = lane & 15, kg = lane >> 4;
+  const bf16* wrow[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    if constexpr (EPI == RE_SWIGLU) {
+      wrow[cb] = static_cast<const bf16*>(a.b.mat[cb]) + (int64_t)(nb * 16 + c16) * K;
+    } else {
+      const int n = nb * 16 + c16;
+      wrow[cb] = static_cast<const bf16*>(a.b.mat[n / a.b.n_per]) + (int64_t)(n % a.b.n_per) * K;
+    }
+  }
+  const float* xrow[RF_RB];
+#pragma unroll
+  for (int rb = 0; rb < RF_RB; ++rb)
+    xrow[rb] = a.X + (int64_t)min(m_base + rb * 16 + c16, M - 1) * a.ldx;   // rows past M: a valid row, unused
+
+  const int kq = K / 4;                    // this wave's quarter of K (K % 128 == 0)
+  const int nch = kq / 32;
+  const int kw = wave * kq + 8 * kg;       // this lane's first k
+
+  f32x4 acc[RF_RB][NCB];
+  float ss[RF_RB];
+#pragma unroll
+  for (int rb = 0; rb < RF_RB; ++rb) {
+    ss[rb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 wb[RF_PF][NCB];
+  f32x4 xb[RF_PF][RF_RB][2];
+  auto load = [&](int c, int slot) __attribute__((always_inline)) {
+    const int k = kw + min(c, nch - 1) * 32;   // past the last chunk: repeat it (in bounds, unused)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) wb[slot][cb] = *reinterpret_cast<const bf16x8*>(wrow[cb] + k);
+#pragma unroll
+    for (int rb = 0; rb < RF_RB; ++rb) {
+      xb[slot][rb][0] = *reinterpret_cast<const f32x4*>(xrow[rb] + k);
+      xb[slot][rb][1] = *reinterpret_cast<const f32x4*>(xrow[rb] + k + 4);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < RF_PF; ++u) load(u, u);
+  for (int c0 = 0; c0 < nch; c0 += RF_PF) {
+#pragma unroll
+    for (int u = 0; u < RF_PF; ++u) {
+      const int c = c0 + u;
+      if (c < nch) {
+        const int k = kw + c * 32;
+        f32x4 g0 = f32x4{1.f, 1.f, 1.f, 1.f}, g1 = g0;
+        if constexpr (PRO == RP_RMSNORM) {
+          g0 = *reinterpret_cast<const f32x4*>(a.g + k);
+          g1 = *reinterpret_cast<const f32x4*>(a.g + k + 4);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RF_RB; ++rb) {
+          f32x4 x0 = xb[u][rb][0], x1 = xb[u][rb][1];
+          if constexpr (PRO == RP_RMSNORM) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss[rb] += x0[e] * x0[e] + x1[e] * x1[e];
+            x0 *= g0;
+            x1 *= g1;
+          }
+          bf16x8 hi, lo;
+          split_bf16(x0, x1, hi, lo);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wb[u][cb], acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wb[u][cb], acc[rb][cb], 0, 0, 0);
+          }
+        }
+      }
+      load(c + RF_PF, u);
+    }
+  }
+
+  // partial sums of the four waves (K quarters) into LDS
+#pragma unroll
+  for (int rb = 0; rb < RF_RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      *reinterpret_cast<f32x4*>(&red[wave][rb][cb][lane * 4]) = acc[rb][cb];
+  if constexpr (PRO == RP_RMSNORM) {
+#pragma unroll
+    for (int rb = 0; rb < RF_RB; ++rb) {
+      float t = ss[rb];
+      t += __shfl_xor(t, 16, kWave);
+      t += __shfl_xor(t, 32, kWave);
+      if (kg == 0) ssq[wave][rb * 16 + c16] = t;
+    }
+  }
+  __syncthreads();
+
+  // epilogue: element q = 4 * l + r of a 16x16 block is row 4 (l / 16) + r,
+  // column l % 16 of the block
+#pragma unroll
+  for (int rb = 0; rb < RF_RB; ++rb) {
+    const int q = tid;
+    const int l = q >> 2, r = q & 3;
+    const int row = 4 * (l >> 4) + r, col = l & 15;
+    const int om = m_base + rb * 16 + row;
+    float v[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      v[cb] = (red[0][rb][cb][q] + red[1][rb][cb][q]) + (red[2][rb][cb][q] + red[3][rb][cb][q]);
+    if constexpr (PRO == RP_RMSNORM) {
+      const int i = rb * 16 + row;
+      const float tot = (ssq[0][i] + ssq[1][i]) + (ssq[2][i] + ssq[3][i]);
+      const float rs = rsqrtf(tot / (float)K + a.eps);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) v[cb] *= rs;
+    }
+    if (om >= M) continue;
+    const int on = nb * 16 + col;
+    if constexpr (EPI == RE_SWIGLU) {
+      const float g = v[0], u = v[1];
+      float act;
+      if (a.act == 0) {
+        act = g / (1.f + expf(-g));
+      } else {
+        const float c = 0.7978845608028654f;
+        act = 0.5f * g * (1.f + tanhf(c * (g + 0.044715f * g * g * g)));
+      }
+      a.out[(int64_t)om * a.ldo + on] = act * u;
+    } else if constexpr (EPI == RE_QKV) {
+      if (on < a.d) a.q[(int64_t)om * a.d + on] = v[0] * a.qscale;
+      else if (on < a.d + a.kvd) a.kd[(int64_t)om * a.kvd + (on - a.d)] = v[0];
+      else a.vd[(int64_t)om * a.kvd + (on - a.d - a.kvd)] = v[0];
+    } else if constexpr (EPI == RE_RESID) {
+      a.out[(int64_t)om * a.ldo + on] = a.res[(int64_t)om * a.ldo + on] + v[0];
+    } else {
+      a.out[(int64_t)om * a.ldo + on] = v[0];
+    }
+  }
+}
+
+static bool use_rowgemm_mfma(int dtype, int epi, const RowGemmArgs& a) {
+  const int cols = epi == RE_SWIGLU ? a.b.n_per : a.N;
+  return dtype == 1 && a.M > rowgemm_mc(a.M, a.K) && a.K % 128 == 0 && cols % 16 == 0 && a.b.n_per % 16 == 0;
+}
+
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s) {
+  if (use_rowgemm_mfma(dtype, epi, a)) {
+    const int nblk = (epi == RE_SWIGLU ? a.b.n_per : a.N) / 16;
+    dim3 grid(nblk, (a.M + RF_RB * 16 - 1) / (RF_RB * 16));
+    bool ok = false;
+    trace_pre(K_ROWGEMM, s);
+#define DSPARK_RM(P, E)                                                       \
+    if (pro == P && epi == E) {                                               \
+      ok = true;                                                              \
+      rowgemm_mfma_kernel<P, E><<<grid, 256, 0, s>>>(a);                      \
+    }
+    DSPARK_RM(RP_RMSNORM, RE_QKV)
+    DSPARK_RM(RP_NONE, RE_RESID)
+    DSPARK_RM(RP_RMSNORM, RE_SWIGLU)
+    DSPARK_RM(RP_NONE, RE_STORE)
+#undef DSPARK_RM
+    trace_post(K_ROWGEMM, s);
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (a.N % 8 != 0 || a.K % 64 != 0 || a.b.n_per % 8 != 0 || a.K > RG_XS) return hipErrorInvalidValue;
   const bool narrow = epi != RE_SWIGLU && a.N / 8 < 256;   // SwiGLU pairs need 2 columns per wave
   // one workgroup row per pass of rowgemm_mc rows; with N / COLS a multiple
