@@ -572,68 +572,42 @@ __global__ __launch_bounds__(256) void attn_hsplit_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Combine + output projection: grid (d / NC column blocks, n_heads, A), 256
-// threads (query heads; with grouped K/V heads, head h's block keys are
-// those of K/V head h / (n_heads / n_kv)). Workgroup (nb, h, b) merges every context partial of sequence b
-// and head h with the gamma block keys (K_d, V_d in float32) into the head's
-// attention output o_h [gamma][hd], then adds o_h . W_o[cols, h*hd : (h+1)*hd]^T
-// for its NC output columns into E with float atomics, so the heads' shares
-// sum there: E = D + sum_h o_h W_o,h^T (the head-0 workgroups add D). E must
-// be zero on entry.
+// (m, l) combine: grid (1, n_heads, A), 256 threads. Workgroup (h, b) merges
+// every context partial of sequence b and query head h with the gamma block
+// keys (K_d, V_d in float32; with grouped K/V heads those of K/V head
+// h / (n_heads / n_kv)) into the head's attention output o_h [gamma][hd],
+// and writes it into Attn[b * gamma + j][h * hd ..] (heads concatenated).
+// The output projection E = D + Attn W_o^T is a row GEMM after it: the
+// heads' shares are summed in a fixed order, so the block rows are the same
+// from call to call.
 //
 // Merge: thread (tg, c4) runs an online log-sum-exp over tiles tg, tg + TG,
 // ... for four output columns of every query, with the loads of TB tiles in
-// flight together; the TG groups are merged in LDS. Projection: a 16-byte
-// weight load covers CPL columns, LPC lanes per column (VPL dims each); the
-// per-lane dot products are summed over each column's LPC lanes with DPP /
-// permlane moves. The weights, residual and block rows are requested before
-// the tile range is known, so the only dependent round trips are the tile
-// prefix (skipped for a single sequence) and the partials.
+// flight together; the TG groups are merged in LDS. The block rows are
+// requested before the tile range is known, so the only dependent round
+// trips are the tile prefix (skipped for a single sequence) and the partials.
 // ---------------------------------------------------------------------------
-template <int LPC>
-DSPARK_DEV float seg_sum(float v) {   // sum over aligned groups of LPC lanes
-  static_assert(LPC == 4 || LPC == 8 || LPC == 16 || LPC == 32, "segment");
-  v += dpp_f<kDppXor1>(v);
-  v += dpp_f<kDppXor2>(v);
-  if constexpr (LPC >= 8) v += dpp_f<kDppHalfMirror>(v);
-  if constexpr (LPC >= 16) v += dpp_f<kDppMirror>(v);
-  if constexpr (LPC >= 32) {
-    float x, y;
-    swap16(v, x, y);
-    v = x + y;
-  }
-  return v;
-}
-
-template <typename WT, int HD>
-struct OProjShape {
+template <int HD>
+struct CombineShape {
   static constexpr int C4 = HD / 4;               // float4 columns of a head
   static constexpr int TG = 256 / C4;             // tile groups of the merge
-  static constexpr int VPL = 16 / (int)sizeof(WT);  // weights per 16-byte load
-  static constexpr int LPC = HD / VPL;            // lanes per weight column
-  static constexpr int CPL = 64 / LPC;            // columns per wave load
-  static constexpr int kLoads = 2;                // wave loads per wave
-  static constexpr int NC = 4 * CPL * kLoads;     // columns per workgroup (divides d)
   // LDS floats: q, k, v rows, block scores, group (o, m, l)
   static constexpr int lds_floats(int g) {
     return 3 * g * HD + ((g * g + 3) & ~3) + TG * g * HD + 2 * TG * g;
   }
 };
 
-template <typename WT, int HD, int G>
-__global__ __launch_bounds__(256) void combine_oproj_kernel(
+template <int HD, int G>
+__global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kd, const float* __restrict__ Vd,
     int n_heads, int n_kv, const int32_t* __restrict__ prefix, int total_tiles,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, const WT* __restrict__ Wo,
-    const float* __restrict__ resid, float* __restrict__ out) {
-  using Sh = OProjShape<WT, HD>;
-  constexpr int C4 = Sh::C4, TG = Sh::TG, VPL = Sh::VPL, LPC = Sh::LPC, CPL = Sh::CPL;
-  constexpr int NL = Sh::kLoads;
-  constexpr int RPL = (G + LPC - 1) / LPC;   // output rows per lane and column
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, float* __restrict__ attn) {
+  using Sh = CombineShape<HD>;
+  constexpr int C4 = Sh::C4, TG = Sh::TG;
   constexpr int TB = G <= 5 ? 4 : (G <= 10 ? 2 : 1);   // tiles whose loads are issued together
   constexpr int QE = (G * C4 + 255) / 256;   // q / k / v float4 per thread
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  float* qs = lds;                        // [G][HD], later the merged o_h
+  float* qs = lds;                        // [G][HD]
   float* ks = qs + G * HD;                // [G][HD]
   float* vs = ks + G * HD;                // [G][HD]
   float* sb = vs + G * HD;                // [G][G] block-key scores
@@ -642,35 +616,11 @@ __global__ __launch_bounds__(256) void combine_oproj_kernel(
   float* lg = mg + TG * G;                // [TG][G]
 
   const int d = n_heads * HD;
-  const int b = blockIdx.z, h = blockIdx.y, col0 = blockIdx.x * Sh::NC;
+  const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cl = lane / LPC, ch = lane % LPC;
 
-  // Everything that does not depend on the tile range is requested first:
-  // this workgroup's W_o slice, the residual (head 0), the block rows.
-  u32x4 wv[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int col = col0 + (wave * NL + i) * CPL + cl;
-    wv[i] = ld16(Wo + (int64_t)col * d + h * HD + ch * VPL);
-  }
-  float rv[NL][RPL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i)
-#pragma unroll
-    for (int k = 0; k < RPL; ++k) rv[i][k] = 0.f;
-  if (h == 0) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int col = col0 + (wave * NL + i) * CPL + cl;
-#pragma unroll
-      for (int k = 0; k < RPL; ++k) {
-        const int j = min(ch + k * LPC, G - 1);
-        rv[i][k] = resid[(int64_t)(b * G + j) * d + col];
-      }
-    }
-  }
-  // the block keys / values of this head's K/V head (rows of n_kv * HD)
+  // the block rows first: this head's queries, the block keys / values of its
+  // K/V head (rows of n_kv * HD)
   const int kvh = h / (n_heads / n_kv), kvd = n_kv * HD;
   f32x4 qv[QE], kv[QE], vv[QE];
 #pragma unroll
@@ -779,54 +729,31 @@ __global__ __launch_bounds__(256) void combine_oproj_kernel(
       l += w;
       o += *reinterpret_cast<const f32x4*>(vs + jj * HD + 4 * c) * w;
     }
-    *reinterpret_cast<f32x4*>(qs + j * HD + 4 * c) = o * (1.f / l);
-  }
-  __syncthreads();
-  // E[b*G + j][col] += o_h[j] . W_o[col, h*hd : (h+1)*hd]  (+ D on head 0)
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int col = col0 + (wave * NL + i) * CPL + cl;
-    float w[VPL];
-    Vec16<WT>::unpack(wv[i], w);
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float* x = qs + j * HD + ch * VPL;
-      float sdot = 0.f;
-#pragma unroll
-      for (int e4 = 0; e4 < VPL / 4; ++e4) {
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(x + 4 * e4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sdot = fmaf(xv[e], w[4 * e4 + e], sdot);
-      }
-      sdot = seg_sum<LPC>(sdot);
-      if (ch == j % LPC) unsafeAtomicAdd(out + (int64_t)(b * G + j) * d + col, sdot + rv[i][j / LPC]);
-    }
+    *reinterpret_cast<f32x4*>(attn + (int64_t)(b * G + j) * d + h * HD + 4 * c) = o * (1.f / l);
   }
 }
 
-template <typename WT, int HD, int G>
-static hipError_t launch_oproj_t(const AttnArgs& a, hipStream_t s) {
-  using Sh = OProjShape<WT, HD>;
-  const int d = HD * a.n_heads;
-  if (d % Sh::NC != 0) return hipErrorInvalidValue;
+template <int HD, int G>
+static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t s) {
+  using Sh = CombineShape<HD>;
   const size_t lds = (size_t)Sh::lds_floats(G) * 4;
-  auto kern = combine_oproj_kernel<WT, HD, G>;
+  auto kern = combine_kernel<HD, G>;
   if (lds > 65536) {
     static hipError_t set = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (set != hipSuccess) return set;
   }
-  dim3 grid(d / Sh::NC, a.n_heads, a.A);
+  dim3 grid(1, a.n_heads, a.A);
   kern<<<grid, 256, lds, s>>>(a.Q, a.Kd, a.Vd, a.n_heads, a.kv.n_heads, a.prefix, a.total_tiles, a.part_o,
-                              a.part_ml, static_cast<const WT*>(a.wo), a.resid, a.out);
+                              a.part_ml, a.attn);
   return hipGetLastError();
 }
 
-template <typename WT, int HD>
-static hipError_t oproj_gamma(const AttnArgs& a, hipStream_t s) {
+template <int HD>
+static hipError_t combine_gamma(const AttnArgs& a, hipStream_t s) {
   switch (a.gamma) {
 #define DSPARK_G(g) \
-  case g: return launch_oproj_t<WT, HD, g>(a, s);
+  case g: return launch_combine_t<HD, g>(a, s);
     DSPARK_G(1) DSPARK_G(2) DSPARK_G(3) DSPARK_G(4) DSPARK_G(5) DSPARK_G(6) DSPARK_G(7)
     DSPARK_G(8) DSPARK_G(9) DSPARK_G(10) DSPARK_G(11) DSPARK_G(12) DSPARK_G(13) DSPARK_G(14)
     DSPARK_G(15) DSPARK_G(16)
@@ -880,15 +807,9 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   trace_pre(K_COMBINE, s);
-  if (dtype == 1) {
-    if (a.kv.hd == 128) e = oproj_gamma<bf16, 128>(a, s);
-    else if (a.kv.hd == 64) e = oproj_gamma<bf16, 64>(a, s);
-    else e = oproj_gamma<bf16, 32>(a, s);
-  } else {
-    if (a.kv.hd == 128) e = oproj_gamma<float, 128>(a, s);
-    else if (a.kv.hd == 64) e = oproj_gamma<float, 64>(a, s);
-    else e = oproj_gamma<float, 32>(a, s);
-  }
+  if (a.kv.hd == 128) e = combine_gamma<128>(a, s);
+  else if (a.kv.hd == 64) e = combine_gamma<64>(a, s);
+  else e = combine_gamma<32>(a, s);
   trace_post(K_COMBINE, s);
   return e;
 }

@@ -79,6 +79,7 @@ void trace_post(int kind, hipStream_t s) {
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+
 struct Plan {
   int64_t T = 0, Tpad = 0;
   int hd = 0, M = 0, chunk = 0, total_chunks = 0, kv_layers = 0;
@@ -87,7 +88,7 @@ struct Plan {
   size_t esz = 4;
   // workspace offsets (bytes)
   size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0, rowmap = 0;
-  size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, E = 0, GU = 0;
+  size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, E = 0, GU = 0, O = 0;
   size_t total = 0;
 };
 
@@ -196,7 +197,8 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
     p->Q = take(row);
     p->Kd = take(row);
     p->Vd = take(row);
-    p->E = take(row * p->kv_layers);   // one accumulator per layer, cleared by the set-up pass
+    p->E = take(row);   // D + Attn Wo^T of the current layer
+    p->O = take(row);   // Attn: the heads' attention outputs
     p->GU = take((size_t)M * 2 * ff * 4);
   }
   p->total = off == 0 ? 256 : off;
@@ -364,8 +366,7 @@ static void setup_block_roles(const dspark_dims* dm, const Plan& p, int A, const
   sa->A = A;
   sa->chunk = p.chunk;
   sa->prefix = at<int32_t>(ws, p.prefix);
-  sa->zero = at<float>(ws, p.E);
-  sa->zero_n = (int64_t)p.kv_layers * p.M * dm->d;
+
 }
 
 // The K/V product's stacked, gain-folded weights (bf16 only).
@@ -386,7 +387,7 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   float* Q = at<float>(ws, p.Q);
   float* Kd = at<float>(ws, p.Kd);
   float* Vd = at<float>(ws, p.Vd);
-  float* E = at<float>(ws, p.E) + (size_t)kv_layer * M * d;   // zeroed by the set-up pass
+  float* E = at<float>(ws, p.E);
   float* GU = at<float>(ws, p.GU);
 
   // Q (pre-scaled for the base-2 softmax), K_d, V_d from RMSNorm(D; attn_norm).
@@ -428,10 +429,16 @@ static dspark_status run_layer(const dspark_dims* dm, const Plan& p, int A, cons
   aa.A = A; aa.gamma = G; aa.chunk = p.chunk; aa.total_tiles = p.total_chunks;
   aa.part_o = at<float>(ws, p.po);
   aa.part_ml = at<float>(ws, p.pml);
-  aa.wo = lw.wo;
-  aa.resid = D;
-  aa.out = E;
+  // the combine writes Attn; E = D + Attn Wo^T is a row GEMM (the heads'
+  // shares summed in a fixed order: the block rows repeat bitwise)
+  float* O = at<float>(ws, p.O);
+  aa.attn = O;
   DSPARK_HIP(launch_attention(dt, aa, s));
+  r = RowGemmArgs{};
+  r.X = O; r.ldx = d; r.M = M; r.K = d; r.N = d;
+  r.b.mat[0] = lw.wo; r.b.n_per = d; r.b.nmat = 1;
+  r.res = D; r.out = E; r.ldo = d;
+  DSPARK_HIP(launch_rowgemm(dt, RP_NONE, RE_RESID, r, s));
   // H = SiLU(Z Wgate^T) * (Z Wup^T), Z = RMSNorm(E; ff_norm)
   r = RowGemmArgs{};
   r.X = E; r.ldx = d; r.M = M; r.K = d; r.N = 2 * ff;

@@ -159,11 +159,9 @@ struct AttnArgs {
   int A, gamma, chunk, total_tiles;
   float* part_o;        // [tiles][n_heads][gamma][hd]
   float* part_ml;       // [tiles][n_heads][gamma][2]
-  const void* wo;       // W_o [d][d] ([out, in], storage type)
-  const float* resid;   // D [A*gamma][d]
-  float* out;           // E [A*gamma][d]: zero on entry, D + Attn W_o^T on exit
+  float* attn;          // out: Attn [A*gamma][d], the heads' outputs concatenated
 };
-// partial kernel, then the combine + output projection kernel
+// partial kernel, then the (m, l) combine into Attn
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 // ---- block side -----------------------------------------------------------

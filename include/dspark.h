@@ -49,10 +49,10 @@
  *   workspaces. The library allocates no device memory on these paths.
  * - stream is a hipStream_t (NULL = the default stream). Calls enqueue work
  *   and return without synchronising the device.
- * - Repeatability: H_ctx (and the context K/V) are bitwise the same from call
- *   to call. The block rows are not: the attention output projection adds
- *   the heads' shares of each row with float atomics, in arrival order, so
- *   repeated calls agree up to float reassociation (about 1e-7 relative).
+ * - Repeatability: every output is bitwise the same from call to call for
+ *   the same inputs and sizes (no float atomics; every sum has a fixed
+ *   order). Different sizes may take different kernels or splits and so
+ *   round differently.
  * - Errors: on any non-OK status nothing has been enqueued and no output has
  *   been written; dspark_last_error() returns a message for the calling
  *   thread. A failed kernel launch returns DSPARK_EHIP (work enqueued before
