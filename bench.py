@@ -224,7 +224,8 @@ def bench_markov(B, torch, steps, vocab=131072, rank=256, gamma=5, d=1024, batch
     module-dflash.ts defaults) over a 131072-entry vocabulary (the pages do
     not print one), for one and for 16 sequences. HBM-bound: each position
     streams w2 once for all sequences and moves the base and draft logits
-    (algorithmic bytes per draft: gamma * (vocab * rank * 2 + 3 * A * vocab * 4))."""
+    (algorithmic bytes per draft: gamma * (vocab * rank * 2 + 2 * A * vocab *
+    4), that is w2, the base logits read and the draft logits written)."""
     out = {"vocab": vocab, "rank": rank, "gamma": gamma, "d": d}
     for A in batches:
         x = W.markov_inputs(90 + A, A=A, gamma=gamma, d=d, vocab=vocab, rank=rank)
@@ -241,7 +242,7 @@ def bench_markov(B, torch, steps, vocab=131072, rank=256, gamma=5, d=1024, batch
                                       g["cb"], tokens=toks, conf=conf, draft_logits=logits)
         t = _time_calls(torch, call, torch.cuda.current_stream(), steps)
         ms = t[len(t) // 2]
-        amount = gamma * (vocab * rank * 2 + 3.0 * A * vocab * 4)
+        amount = gamma * (vocab * rank * 2 + 2.0 * A * vocab * 4)
         out[f"A{A}"] = {"draft_ms_median": round(ms, 4), "draft_ms_min": round(t[0], 4),
                         "drafts_per_s": round(A * 1e3 / ms, 1),
                         "hbm": {"bound": "hbm", "achieved": round(amount / ms / 1e6, 1), "peak": PEAK_HBM_GBS,

@@ -87,7 +87,9 @@ struct Plan {
   CtxSplit ctx;   // K splits of the Eq 2 projection
   size_t esz = 4;
   // workspace offsets (bytes)
-  size_t wkvt = 0, ppart = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0, rowmap = 0;
+  // ppart: the Eq 2 split-K partials, or with ctx.fused its Y rows; ysum: the
+  // fused epilogue's row sums
+  size_t wkvt = 0, ppart = 0, ysum = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0, rowmap = 0;
   size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, E = 0, GU = 0, O = 0;
   size_t total = 0;
 };
@@ -179,10 +181,17 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
 
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  if (runs_eq2) p->ppart = take((size_t)p->ctx.splits * T * d * 4);
+  const bool fused = runs_eq2 && p->ctx.fused;
+  if (fused) {
+    p->ppart = take((size_t)T * d * 2);
+    p->ysum = take((size_t)T * (d / kCtxSumCols) * 2 * 4);
+  } else if (runs_eq2) {
+    p->ppart = take((size_t)p->ctx.splits * T * d * 4);
+  }
   if (runs_kv) {
     if (bf) p->wkvt = take((size_t)2 * p->kv_layers * p->kvd * d * 2);
-    if (op != DSPARK_OP_BLOCK_LAYER) p->hctx = take((size_t)T * d * p->esz);
+    // the K/V product reads H_ctx, or with the fused Eq 2 path the Y rows
+    if (op != DSPARK_OP_BLOCK_LAYER && !fused) p->hctx = take((size_t)T * d * p->esz);
     p->rinv = take((size_t)T * 4);
     if (op == DSPARK_OP_CTX_APPEND) p->rowmap = take((size_t)T * 4);
     else p->kv = take((size_t)p->kv_layers * 2 * p->Tpad * p->kvd * p->esz);
@@ -256,10 +265,12 @@ static T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<cha
 // ---------------------------------------------------------------------------
 // launch sequences
 // ---------------------------------------------------------------------------
-// Eq 2 projection: split-K fp32 partials of X . W_c^T into the workspace (the
-// RMSNorm row pass runs in the set-up launch).
+// Eq 2 projection: split-K fp32 partials of X . W_c^T into the workspace, or
+// in one split Y = P * ctx_norm and its row sums (the RMSNorm row pass, or
+// the row scales, run in the set-up launch).
 static dspark_status run_ctx_gemm(const dspark_dims* dm, const Plan& p, const void* const* taps,
-                                  int64_t ld_tap, const void* w_c, void* ws, hipStream_t s) {
+                                  int64_t ld_tap, const void* w_c, const float* ctx_norm, void* ws,
+                                  hipStream_t s) {
   if (p.T == 0) return DSPARK_OK;
   const int d = dm->d, mH = dm->m * dm->H;
   ASegs a{};
@@ -273,8 +284,15 @@ static dspark_status run_ctx_gemm(const dspark_dims* dm, const Plan& p, const vo
   b.n_per = d;
   b.nmat = 1;
   // W_c [d, m*H] is already the K-contiguous B operand
-  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, w_c, at<float>(ws, p.ppart), (int)p.T, d, mH,
-                             p.ctx, s));
+  CtxOut o;
+  if (p.ctx.fused) {
+    o.y = at<char>(ws, p.ppart);
+    o.sums = at<float>(ws, p.ysum);
+    o.g = ctx_norm;
+  } else {
+    o.part = at<float>(ws, p.ppart);
+  }
+  DSPARK_HIP(launch_gemm_ctx(dm->dtype, a, b, w_c, o, (int)p.T, d, mH, p.ctx, s));
   return DSPARK_OK;
 }
 
@@ -462,6 +480,31 @@ using namespace dspark;
 
 extern "C" {
 
+// The set-up pass's Eq 2 row work. Split-K: sum the splits, H_ctx =
+// RMSNorm(.; ctx_norm) into `h`, and rinv from the stored rows. Fused: rinv
+// from the epilogue's row sums, and H_ctx into `h` only if `h` is given.
+static void setup_eq2_role(const dspark_dims* dm, const Plan& p, const float* ctx_norm, void* h, float* rinv,
+                           void* ws, SetupArgs* sa) {
+  sa->T = p.T;
+  sa->rinv = rinv;
+  sa->rinv_one = (dm->variant & DSPARK_PLAIN_CTX_KV) != 0;
+  sa->h = h;
+  if (p.ctx.fused) {
+    sa->rsum = at<float>(ws, p.ysum);
+    sa->nts = dm->d / kCtxSumCols;
+    sa->y = at<char>(ws, p.ppart);
+  } else {
+    sa->part = at<float>(ws, p.ppart);
+    sa->splits = p.ctx.splits;
+    sa->g = ctx_norm;
+  }
+}
+
+// The K/V product's A operand after Eq 2: H_ctx, or the fused path's Y rows.
+static const void* kv_rows(const Plan& p, const void* h_ctx, void* ws) {
+  return p.ctx.fused ? static_cast<const void*>(at<char>(ws, p.ppart)) : h_ctx;
+}
+
 size_t dspark_workspace_size(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host) {
   if (op < DSPARK_OP_CTX_FUSE || op > DSPARK_OP_BLOCK_PROPOSE) {
     fail(DSPARK_EINVAL, "unknown op %d", op);
@@ -490,16 +533,12 @@ dspark_status dspark_ctx_fuse(const dspark_dims* dims, int32_t A, const int32_t*
     return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.T == 0) return DSPARK_OK;
-  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ws, s);
+  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ctx_norm, ws, s);
   if (st != DSPARK_OK) return st;
   SetupArgs sa{};
   sa.d = dims->d;
   sa.eps = dims->eps;
-  sa.T = p.T;
-  sa.part = at<float>(ws, p.ppart);
-  sa.splits = p.ctx.splits;
-  sa.g = ctx_norm;
-  sa.h = h_ctx;
+  setup_eq2_role(dims, p, ctx_norm, h_ctx, nullptr, ws, &sa);
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   return DSPARK_OK;
 }
@@ -599,11 +638,13 @@ static dspark_status forward_impl(const dspark_dims* dims, int32_t A, const int3
     DSPARK_HIP(launch_fill_offsets(fill_cu, A, fill_L, s));
     cu_dev = fill_cu;
   }
-  void* h_ctx = h_ctx_out ? h_ctx_out : at<char>(ws, p.hctx);
+  // H_ctx: the caller's buffer, else (split-K Eq 2) the workspace's; the
+  // fused Eq 2 path writes it only for the caller
+  void* h_ctx = h_ctx_out ? h_ctx_out : (p.ctx.fused ? nullptr : at<char>(ws, p.hctx));
   float* rinv = at<float>(ws, p.rinv);
   float* Da = at<float>(ws, p.D);
   float* Db = at<float>(ws, p.D2);
-  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ws, s);
+  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ctx_norm, ws, s);
   if (st != DSPARK_OK) return st;
   // Eq 2's row norm, K/V weight prep, tile plan and D0 = block_in + block_pos
   SetupArgs sa{};
@@ -615,19 +656,11 @@ static dspark_status forward_impl(const dspark_dims* dims, int32_t A, const int3
   sa.block_pos = block_pos;
   sa.gamma = dims->gamma;
   sa.D0 = Da;
-  if (p.T > 0) {
-    sa.T = p.T;
-    sa.part = at<float>(ws, p.ppart);
-    sa.splits = p.ctx.splits;
-    sa.g = ctx_norm;
-    sa.h = h_ctx;
-    sa.rinv = rinv;
-    sa.rinv_one = (dims->variant & DSPARK_PLAIN_CTX_KV) != 0;
-  }
+  if (p.T > 0) setup_eq2_role(dims, p, ctx_norm, h_ctx, rinv, ws, &sa);
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   KVDesc kv = ws_kv(dims, p, ws);
   kv.key_mask = key_mask;
-  st = run_ctx_kv(dims, p, h_ctx, rinv, layers, dims->n_layers, kv, ws, s);
+  st = run_ctx_kv(dims, p, kv_rows(p, h_ctx, ws), rinv, layers, dims->n_layers, kv, ws, s);
   if (st != DSPARK_OK) return st;
   st = run_k_post(dims, p, layers, dims->n_layers, kv, cu_dev, A, s);
   if (st != DSPARK_OK) return st;
@@ -785,7 +818,7 @@ dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
     return fail(DSPARK_EWORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, p.total);
   if (p.T == 0) return DSPARK_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ws, s);
+  st = run_ctx_gemm(dims, p, taps, ld_tap, w_c, ctx_norm, ws, s);
   if (st != DSPARK_OK) return st;
   // Eq 2's row norm of the new rows, the stacked K/V weights, the row map
   SetupArgs sa{};
@@ -793,13 +826,8 @@ dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
   sa.eps = dims->eps;
   sa.A = A;
   setup_prep_role(dims, p, layers, dims->n_layers, ws, &sa);
-  sa.T = p.T;
-  sa.part = at<float>(ws, p.ppart);
-  sa.splits = p.ctx.splits;
-  sa.g = ctx_norm;
-  sa.h = at<char>(ws, p.hctx);
-  sa.rinv = at<float>(ws, p.rinv);
-  sa.rinv_one = (dims->variant & DSPARK_PLAIN_CTX_KV) != 0;
+  void* h_new = p.ctx.fused ? nullptr : at<char>(ws, p.hctx);
+  setup_eq2_role(dims, p, ctx_norm, h_new, at<float>(ws, p.rinv), ws, &sa);
   sa.ncu = ncu_dev;
   sa.pos = pos_dev;
   sa.cap = cap;
@@ -807,7 +835,7 @@ dspark_status dspark_ctx_append(const dspark_dims* dims, int32_t A, int32_t cap,
   sa.dst_row = at<int32_t>(ws, p.rowmap);
   DSPARK_HIP(launch_setup(dims->dtype, sa, s));
   const KVDesc kv = cache_kv(dims, p, A, cap, cache, at<int32_t>(ws, p.rowmap));
-  st = run_ctx_kv(dims, p, at<char>(ws, p.hctx), at<float>(ws, p.rinv), layers, dims->n_layers, kv, ws, s);
+  st = run_ctx_kv(dims, p, kv_rows(p, h_new, ws), at<float>(ws, p.rinv), layers, dims->n_layers, kv, ws, s);
   if (st != DSPARK_OK) return st;
   return run_k_post(dims, p, layers, dims->n_layers, kv, ncu_dev, A, s);
 }
@@ -892,7 +920,7 @@ static dspark_status markov_plan(const dspark_dims* dims, int32_t A, int32_t voc
     return fail(DSPARK_EUNSUPPORTED, "rank %d must be a multiple of 64 in [64, 16256]", rank);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const int P = markov_partials(vocab);
+  const int P = markov_grid(dims->dtype, vocab, rank).P;
   mp->E1 = take((size_t)A * rank * 4);
   mp->pv = take((size_t)A * P * 4);
   mp->pi = take((size_t)A * P * 4);
@@ -962,8 +990,9 @@ int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const i
   }
   Plan p;
   if (make_plan(op, dims, A, cu_host, &p) != DSPARK_OK) return 0;
+  const bool eq2 = op == DSPARK_OP_CTX_FUSE || op == DSPARK_OP_BLOCK_FORWARD || op == DSPARK_OP_CTX_APPEND;
   const int64_t v[DSPARK_PLAN_COUNT] = {p.ctx.splits, p.ctx.k_per_split, p.chunk, p.total_chunks,
-                                        p.chunk != 64 ? 1 : 0, (int64_t)p.total};
+                                        p.chunk != 64 ? 1 : 0, (int64_t)p.total, eq2 && p.ctx.fused ? 1 : 0};
   const int k = std::min<int32_t>(n, DSPARK_PLAN_COUNT);
   for (int i = 0; i < k; ++i) out[i] = v[i];
   return k;

@@ -306,11 +306,27 @@ DSPARK_DEV void lds_load16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)l, 16, 0, 0);
 }
 
+// Epilogues of the big-tile kernel (kKind): 0 float32 split-K partials,
+// 1 the context K/V in the attention layout, 2 Eq 2 with its row norm
+// deferred.
 struct EpiPartialBig {         // out[z][r][n] = acc for r < M
   float* out;
   int64_t split_stride;
-  static constexpr bool kStaged = false;
+  static constexpr int kKind = 0;
   static constexpr bool kSwap = false;
+};
+
+// Eq 2 in one K split: Y = P * g (P = X W_c^T, g = ctx_norm) rounded to
+// bf16, and per row and 256-column tile the sums of P^2 and of Y^2 (Y as
+// stored). The row's RMS factor is then a per-row scalar: H_ctx = Y / rms(P),
+// so the K/V product can take Y as its A operand and fold both norms into
+// its row scale.
+struct EpiNormBig {
+  bf16* y;                     // [M][N]
+  float* sums;                 // [M][N / 256][2]
+  const float* g;              // [N]
+  static constexpr int kKind = 2;
+  static constexpr bool kSwap = true;     // a lane holds one row
 };
 
 template <typename S>
@@ -321,7 +337,7 @@ struct EpiKVBig {              // all layers' K/V, row scale, attention layout
   int T, d, hd, n_heads;       // d: columns of one K or V block (K/V heads * hd)
   int n_base;                  // column of the stacked K/V where this launch's columns start
   const int32_t* dst_row;      // null: row r at r (zeros at T .. Tpad-1); else row r < T at dst_row[r]
-  static constexpr bool kStaged = true;
+  static constexpr int kKind = 1;
   static constexpr bool kSwap = true;     // accumulate C^T: a lane holds one row
 };
 
@@ -501,7 +517,7 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   // A cache target also stages each row's slab row (the row map) the same way.
   float* rsc_lds = reinterpret_cast<float*>(smem + BG_LDS);
   int32_t* dst_lds = reinterpret_cast<int32_t*>(smem + BG_LDS + TM * 4);
-  if constexpr (Epi::kSwap) {
+  if constexpr (Epi::kKind == 1) {
     if (nsteps > 0 && wave < TM / 64) {
       const int row = min(m0 + wave * 64 + lane, epi.T - 1);
       __builtin_amdgcn_global_load_lds(epi.rinv + row, (lds_ptr_t)(rsc_lds + wave * 64), 4, 0, 0);
@@ -555,7 +571,65 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
     wait_vmcnt<0>();
   }
 
-  if constexpr (!Epi::kSwap) {
+  if constexpr (Epi::kKind == 2) {
+    // Transposed accumulators, as in the K/V epilogue below: (i, j, r) of
+    // this lane is tile row wm*WSM + i*32 + lane%32 and tile column
+    // wn*WSN + j*32 + 8*(r/4) + 4*(lane/32) + r%4. Y leaves as 16-byte
+    // vectors of 8 columns of one row (lanes l and l^32 trade halves); the
+    // row sums meet in LDS past the stage ring (lanes l and l^32 first, then
+    // the NWN waves of a row block), and one thread per tile row writes them.
+    float* red = reinterpret_cast<float*>(smem + BG_LDS);   // [NWN][TM][2]
+    const int nw = n0 + wn * WSN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lr = wm * WSM + i * 32 + r32;
+      const int64_t row = (int64_t)m0 + lr;
+      float sp = 0.f, sy = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cb = nw + j * 32;
+        uint32_t P[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(epi.g + cb + 8 * q + 4 * hi);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const float p0 = acc[i][j][4 * q + 2 * x], p1 = acc[i][j][4 * q + 2 * x + 1];
+            const float y0 = static_cast<float>(from_f32<bf16>(p0 * gv[2 * x]));
+            const float y1 = static_cast<float>(from_f32<bf16>(p1 * gv[2 * x + 1]));
+            sp += p0 * p0 + p1 * p1;
+            sy += y0 * y0 + y1 * y1;
+            P[q][x] = pack_bf16x2(y0, y1);   // exact: y0, y1 are bf16 values
+          }
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
+          const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          if (row < M) st16(epi.y + row * N + cb + 8 * (qq + 2 * hi), v);
+        }
+      }
+      sp += __shfl_xor(sp, 32, kWave);
+      sy += __shfl_xor(sy, 32, kWave);
+      if (hi == 0) {
+        red[2 * (wn * TM + lr)] = sp;
+        red[2 * (wn * TM + lr) + 1] = sy;
+      }
+    }
+    wait_lgkm0();
+    stage_barrier();
+    if (tid < TM && m0 + tid < M) {
+      float sp = 0.f, sy = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NWN; ++w) {
+        sp += red[2 * (w * TM + tid)];
+        sy += red[2 * (w * TM + tid) + 1];
+      }
+      *reinterpret_cast<f32x2*>(epi.sums + 2 * ((int64_t)(m0 + tid) * (N / TM) + tn)) = f32x2{sp, sy};
+    }
+  } else if constexpr (Epi::kKind == 0) {
     // accumulator (i, j, r) of this lane: tile row wm*WSM + i*32 + 8*(r/4) +
     // 4*(lane/32) + r%4, tile column wn*WSN + j*32 + lane%32
 #pragma unroll
@@ -656,15 +730,18 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   }
 }
 
-// the stage ring, then (K/V epilogue) the tile's row scales; one LDS object,
-// so the compiler's tracking of direct LDS loads sees a single target
-template <class Epi, int WT>
-constexpr int big_lds_bytes() { return BG_LDS + (Epi::kSwap ? 2 * 64 * WT * 4 : 0); }
+// the stage ring, then the epilogue's own part: the tile's row scales and
+// row map (K/V) or its row sums of each column wave (Eq 2 norm); one LDS
+// object, so the compiler's tracking of direct LDS loads sees a single target
+template <class Epi, int WT, int NW>
+constexpr int big_lds_bytes() {
+  return BG_LDS + (Epi::kKind == 1 ? 2 * 64 * WT * 4 : Epi::kKind == 2 ? (NW / 2) * 64 * WT * 2 * 4 : 0);
+}
 
 template <class Epi, int HD, int BK, int WT, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
                                                            int MR, int N, int K, int k_per_split, Epi epi) {
-  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, WT>()];
+  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, WT, NW>()];
   const int ntiles = ((MR + 64 * WT - 1) / (64 * WT)) * (N / (64 * WT));
   gemm_big_body<Epi, HD, BK, WT, NW>(smem, blockIdx.x + (int)gridDim.x * (int)blockIdx.y,
                                      ntiles * (int)gridDim.y, a, Bt, M, MR, N, K, k_per_split, epi);
@@ -678,7 +755,7 @@ template <class Epi, int HD, int BK, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_kv_tail_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
                                                                int MR, int N, int K, int nb, int nbig,
                                                                Epi epi) {
-  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, 4>()];
+  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, 4, NW>()];
   const int bid = blockIdx.x;
   if (bid < nbig) {
     gemm_big_body<Epi, HD, BK, 4, NW>(smem, bid, nbig, a, Bt, M, MR, nb, K, K, epi);
@@ -744,15 +821,23 @@ CtxSplit ctx_gemm_split(int dtype, int64_t M, int N, int K) {
   CtxSplit r;
   r.k_per_split = (int)kps;
   r.splits = (int)((K + kps - 1) / kps);
+  r.fused = use_big_tiles(dtype, M, N) && r.splits == 1;
   return r;
 }
 
-hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, float* out,
+hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, const CtxOut& o,
                            int M, int N, int K, const CtxSplit& sp, hipStream_t s) {
   const int splits = sp.splits, kps = sp.k_per_split;
   if ((int64_t)splits * kps < K || (int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
+  if (sp.fused != (use_big_tiles(dtype, M, N) && splits == 1)) return hipErrorInvalidValue;
+  float* out = o.part;
   trace_pre(K_GEMM_CTX, s);
-  if (use_big_tiles(dtype, M, N)) {
+  if (sp.fused) {
+    EpiNormBig epi{static_cast<bf16*>(o.y), o.sums, o.g};
+    dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), 1, 1);
+    gemm_big_kernel<EpiNormBig, 128, kFuseBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(
+        a, static_cast<const bf16*>(Bt), M, M, N, K, kps, epi);
+  } else if (use_big_tiles(dtype, M, N)) {
     EpiPartialBig epi{out, (int64_t)M * N};
     dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);
     gemm_big_kernel<EpiPartialBig, 128, kFuseBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, static_cast<const bf16*>(Bt),

@@ -106,6 +106,12 @@ struct SetupArgs {
   const void* h_in = nullptr;
   float* rinv = nullptr;
   bool rinv_one = false;   // the context rows enter W_K / W_V unnormalised: rinv[t] = 1
+  // or, after the fused Eq 2 epilogue: its row sums [T][nts][2] (sum P^2,
+  // sum Y^2) and Y = bf16(P * ctx_norm); rinv[t] is then the K/V product's
+  // row scale for Y rows, and h (if given) receives H_ctx = Y / rms(P)
+  const float* rsum = nullptr;
+  int nts = 0;
+  const void* y = nullptr;
   // cleared buffer
   float* zero = nullptr;
   int64_t zero_n = 0;
@@ -128,11 +134,23 @@ hipError_t launch_fill_offsets(int32_t* cu, int A, int L, hipStream_t s);
 struct CtxSplit {
   int splits = 1;
   int k_per_split = 0;
+  // one split on the big-tile kernel: its epilogue writes Y = P * ctx_norm
+  // (bf16) and per-row sums instead of float32 partials
+  bool fused = false;
 };
 CtxSplit ctx_gemm_split(int dtype, int64_t M, int N, int K);
-// out[z][r][n] = sum_{k in split z} A(r,k) B(k,n); float32 partials.
-hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt,
-                           float* out, int M, int N, int K, const CtxSplit& sp, hipStream_t s);
+// Where the Eq 2 product goes. Split-K: part[z][r][n] = sum_{k in split z}
+// A(r,k) B(k,n) in float32. Fused: y[r][n] = bf16(P[r][n] * g[n]) and
+// sums[r][n / 256] = (sum P^2, sum y^2) over that 256-column tile.
+struct CtxOut {
+  float* part = nullptr;
+  void* y = nullptr;
+  float* sums = nullptr;
+  const float* g = nullptr;
+};
+hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, const CtxOut& o,
+                           int M, int N, int K, const CtxSplit& sp, hipStream_t s);
+constexpr int kCtxSumCols = 256;   // columns per row-sum pair of the fused Eq 2 epilogue
 
 // K/V for all layers of `b` (2 matrices per layer: K then V) from H_ctx with
 // the row scale rinv, written in the attention layout of `kv`.
@@ -252,10 +270,17 @@ struct MarkovArgs {
   float* conf = nullptr;               // [A][gamma]
   float* logits = nullptr;             // [A][gamma][vocab]: the draft logits
   float* E1 = nullptr;                 // workspace [A][rank]
-  float* part_v = nullptr;             // workspace [A][markov_partials(vocab)]
+  float* part_v = nullptr;             // workspace [A][markov_grid(...).P]
   int32_t* part_i = nullptr;
 };
-int markov_partials(int vocab);
+// Vocabulary chunks of one position: P chunks of `chunk` rows, each reduced
+// to one (max, index) partial per sequence; mfma: the matrix-core logits
+// kernel runs (bf16 weights, rank a multiple of 64 up to 512).
+struct MarkovGrid {
+  int P = 0, chunk = 0;
+  bool mfma = false;
+};
+MarkovGrid markov_grid(int dtype, int vocab, int rank);
 hipError_t launch_markov(int dtype, const MarkovArgs& a, hipStream_t s);
 
 }  // namespace dspark

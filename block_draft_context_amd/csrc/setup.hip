@@ -8,7 +8,9 @@
 //          the layer's attn_norm gain folded into the columns
 //   norm   H_ctx = RMSNorm(sum of the projection's K splits; ctx_norm) and the
 //          inverse RMS of each stored row, or, when H_ctx is given, only the
-//          inverse RMS ("DFlash draft layer", `#buildContext` and `#layer`)
+//          inverse RMS ("DFlash draft layer", `#buildContext` and `#layer`);
+//          after the fused one-split projection, the row scales from its
+//          row sums (and H_ctx only when asked for)
 //   zero   clears the per-layer accumulators that the attention output
 //          projection adds its heads' shares into
 // Each is a range of workgroups of one grid (256 threads, one wave per row),
@@ -192,6 +194,53 @@ __device__ __forceinline__ void stats_row(const SetupArgs& a, int64_t t, int lan
   if (lane == 0) a.rinv[t] = a.rinv_one ? 1.f : rsqrtf(ss / (float)d + a.eps);
 }
 
+// After the fused Eq 2 epilogue (bf16): the row's sums of P^2 and of the
+// stored Y^2 over its nts column tiles give
+//   ms = mean P^2 + eps,      H_ctx = Y / sqrt(ms)
+//   mean H^2 = (mean Y^2) / ms, so the layer norm of an H_ctx row scales Y by
+//   1 / (sqrt(ms) * sqrt(mean H^2 + eps)) = 1 / sqrt(mean Y^2 + eps * ms)
+// which is the K/V product's row scale for Y rows (1 / sqrt(ms) when the
+// context rows enter W_K / W_V unnormalised).
+struct RowScales {
+  float inv_rms, kv;
+};
+__device__ __forceinline__ RowScales fused_scales(const SetupArgs& a, int64_t t) {
+  const f32x2* sm = reinterpret_cast<const f32x2*>(a.rsum) + t * a.nts;
+  float sp = 0.f, sy = 0.f;
+  for (int i = 0; i < a.nts; ++i) {
+    const f32x2 v = sm[i];
+    sp += v[0];
+    sy += v[1];
+  }
+  const float ms = sp / (float)a.d + a.eps;
+  RowScales r;
+  r.inv_rms = rsqrtf(ms);
+  r.kv = a.rinv_one ? r.inv_rms : rsqrtf(sy / (float)a.d + a.eps * ms);
+  return r;
+}
+
+// One thread per row: the row scale only.
+__device__ __forceinline__ void fused_rinv(const SetupArgs& a, int64_t t) {
+  a.rinv[t] = fused_scales(a, t).kv;
+}
+
+// One wave per row: the row scale and H_ctx = Y / rms(P), bf16, a 16-byte
+// vector of 8 columns per lane and step.
+__device__ __forceinline__ void fused_h_row(const SetupArgs& a, int64_t t, int lane) {
+  const RowScales r = fused_scales(a, t);
+  if (a.rinv && lane == 0) a.rinv[t] = r.kv;
+  const bf16* y = static_cast<const bf16*>(a.y) + t * a.d;
+  bf16* h = static_cast<bf16*>(a.h) + t * a.d;
+  for (int c = lane; c < a.d / 8; c += 64) {
+    float f[8];
+    Vec16<bf16>::unpack(ld16(y + 8 * c), f);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(f[e] * r.inv_rms);
+    *reinterpret_cast<bf16x8*>(h + 8 * c) = o;
+  }
+}
+
 // Cache row map: new row r belongs to the sequence b with ncu[b] <= r <
 // ncu[b+1] (the last b with ncu[b] <= r, which skips empty sequences) and
 // lands at slab row b * cap + pos[b] + (r - ncu[b]). One thread per row.
@@ -219,7 +268,8 @@ static SetupGrid setup_grid(const SetupArgs& a) {
   g.zero = a.zero ? (int)((a.zero_n + kZeroPerBlock - 1) / kZeroPerBlock) : 0;
   g.d0 = a.D0 ? (a.A * a.gamma + 3) / 4 : 0;
   g.prep = a.Bt ? (a.b.n_per * a.b.nmat + 3) / 4 : 0;
-  g.norm = (a.part || a.h_in) ? (int)((a.T + 3) / 4) : 0;
+  if (a.rsum) g.norm = a.h ? (int)((a.T + 3) / 4) : (int)((a.T + 255) / 256);
+  else g.norm = (a.part || a.h_in) ? (int)((a.T + 3) / 4) : 0;
   return g;
 }
 
@@ -265,9 +315,16 @@ __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
     return;
   }
   blk -= sg.prep;
+  if (a.rsum && !a.h) {
+    const int64_t t = (int64_t)blk * 256 + threadIdx.x;
+    if (t < a.T && a.rinv) fused_rinv(a, t);
+    return;
+  }
   const int64_t t = (int64_t)blk * 4 + w;
   if (t >= a.T) return;
-  if (a.part)
+  if (a.rsum) {
+    if constexpr (sizeof(S) == 2) fused_h_row(a, t, lane);
+  } else if (a.part)
     norm_row<S, CPL>(a, t, lane);
   else
     stats_row<S>(a, t, lane);
@@ -288,6 +345,7 @@ hipError_t launch_fill_offsets(int32_t* cu, int A, int L, hipStream_t s) {
 
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s) {
   if (a.Bt && dtype != 1) return hipErrorInvalidValue;   // prep serves the bf16 MFMA path only
+  if (a.rsum && (dtype != 1 || (a.h && !a.y))) return hipErrorInvalidValue;   // the fused Eq 2 path is bf16
   const SetupGrid sg = setup_grid(a);
   if (sg.total() == 0) return hipSuccess;
   trace_pre(K_SETUP, s);

@@ -193,9 +193,10 @@ def test_python_binding_raises_with_message(L):
 
 
 def _plan(L, op, dm, cu):
-    out = (ctypes.c_int64 * 6)()
-    n = L.lib().dspark_plan_info(op, ctypes.byref(dm), len(cu) - 1, _cu(cu), out, 6)
-    assert n == 6, L.lib().dspark_last_error().decode()
+    k = len(L.PLAN_FIELDS)
+    out = (ctypes.c_int64 * k)()
+    n = L.lib().dspark_plan_info(op, ctypes.byref(dm), len(cu) - 1, _cu(cu), out, k)
+    assert n == k, L.lib().dspark_last_error().decode()
     return dict(zip(L.PLAN_FIELDS, list(out)))
 
 
@@ -221,6 +222,27 @@ def test_ctx_splits_cover_every_column(L):
                         assert s * kps >= K and (s - 1) * kps < K, (dtype, m, H, d, T, p)
                         checked += 1
     assert checked > 1000
+
+
+def test_plan_fuses_the_eq2_norm_in_one_split(L):
+    """Eq 2 takes the fused epilogue (bf16 Y rows and row sums, the row norm
+    folded into the K/V row scale) exactly when it runs as one K split on
+    the big-tile kernel: bf16, d a multiple of 256, at least 512 rows and
+    enough 256x256 tiles to fill the chip; ops without Eq 2 never do."""
+    for dtype in (L.F32, L.BF16):
+        for d in (128, 768, 1024, 2048):
+            for T in (64, 2048, 8192, 16128, 16129, 131072):
+                dm = _dims(L, m=4, H=2560, d=d, n_heads=d // 128, dtype=dtype)
+                p = _plan(L, L.OP_BLOCK_FORWARD, dm, [0, T])
+                big = dtype == L.BF16 and d % 256 == 0 and T >= 512
+                assert p["ctx_fused_norm"] == int(big and p["ctx_splits"] == 1), (dtype, d, T, p)
+                assert _plan(L, L.OP_BLOCK_LAYER, dm, [0, T])["ctx_fused_norm"] == 0
+    dm = _dims(L, m=4, H=2560, d=1024, n_heads=8, dtype=L.BF16)
+    assert _plan(L, L.OP_BLOCK_FORWARD, dm, [0, 16128])["ctx_fused_norm"] == 0    # 252 tiles: split
+    p = _plan(L, L.OP_BLOCK_FORWARD, dm, [0, 16129])
+    assert p["ctx_fused_norm"] == 1 and p["ctx_splits"] == 1                     # 256 tiles
+    assert _plan(L, L.OP_CTX_FUSE, dm, [0, 131072])["ctx_fused_norm"] == 1
+    assert _plan(L, L.OP_CTX_APPEND, dm, [0, 131072])["ctx_fused_norm"] == 1
 
 
 def test_plan_reports_the_attention_path(L):

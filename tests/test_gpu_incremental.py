@@ -155,8 +155,20 @@ def test_streaming_attention_over_the_cache():
     _check_cache(w, cache, ocache)
 
 
+def test_fused_eq2_append():
+    """An append large enough for Eq 2 in one split with the row norm folded
+    into the K/V row scale (the fused epilogue writes Y = P * ctx_norm and
+    row sums; no H_ctx is stored), then a small split-K append."""
+    w, x = _workload(75, [20000, 13000], d=512, n_heads=4, gamma=5, n_layers=1)
+    dims = dims_of(B, w)
+    assert B.plan_info(B.OP_CTX_APPEND, dims, [0, 20000, 32600])["ctx_fused_norm"] == 1
+    assert B.plan_info(B.OP_CTX_APPEND, dims, [0, 0, 400])["ctx_fused_norm"] == 0
+    cache, ocache, u, _ = _run(w, x, 20032, [[20000, 12600], [0, 400]], check_every=True)
+    _check_cache(w, cache, ocache)
+
+
 for _name in ("test_appends_then_propose_match_oracle", "test_incremental_equals_full_forward",
-              "test_streaming_attention_over_the_cache"):
+              "test_streaming_attention_over_the_cache", "test_fused_eq2_append"):
     for _m in gpu:
         globals()[_name] = _m(globals()[_name])
 

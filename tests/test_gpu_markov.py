@@ -68,11 +68,7 @@ def _teacher_forced(x, toks):
     return logits, conf, bound
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_markov_draft_matches_oracle(dtype):
-    A, G, d, V, r = 5, 6, 256, 5000, 128
-    x = W.markov_inputs(81 if dtype == "bf16" else 82, A=A, gamma=G, d=d, vocab=V, rank=r, dtype=dtype)
-    toks, conf, logits = _run(x, d, G, dtype)
+def _check(x, d, G, dtype, toks, conf, logits):
     ol, oc, bound = _teacher_forced(x, toks)
     top2 = np.sort(ol, axis=-1)[..., -2:]
     margin = top2[..., 1] - top2[..., 0]
@@ -90,6 +86,27 @@ def test_markov_draft_matches_oracle(dtype):
     el = float(np.max(np.abs(logits - ol)) / np.max(np.abs(ol)))
     print(f"  confidence max abs err {np.max(np.abs(conf - oc)):.2e}, draft logits rel err {el:.2e}")
     assert el < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_markov_draft_matches_oracle(dtype):
+    A, G, d, V, r = 5, 6, 256, 5000, 128
+    x = W.markov_inputs(81 if dtype == "bf16" else 82, A=A, gamma=G, d=d, vocab=V, rank=r, dtype=dtype)
+    _check(x, d, G, dtype, *_run(x, d, G, dtype))
+
+
+# (A, gamma, vocab, rank): more than 16 sequences (two sequence groups of the
+# matrix-core logits kernel), every rank class it instantiates up to 512
+# with ragged last vocabulary chunks, and ranks above 512 (the row-GEMM path)
+SHAPES = [(20, 5, 5000, 256), (3, 4, 4104, 512), (17, 3, 3000, 192), (1, 5, 2056, 64),
+          (2, 2, 1000, 576), (33, 2, 808, 320)]
+
+
+@pytest.mark.parametrize("A,G,V,r", SHAPES, ids=[f"A{a}-g{g}-V{v}-r{r}" for a, g, v, r in SHAPES])
+def test_markov_draft_shapes(A, G, V, r):
+    d = 128
+    x = W.markov_inputs(85 + r, A=A, gamma=G, d=d, vocab=V, rank=r)
+    _check(x, d, G, "bf16", *_run(x, d, G, "bf16"))
 
 
 def test_markov_ties_and_closed_forms():

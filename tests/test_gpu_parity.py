@@ -103,11 +103,25 @@ STREAMING_CASES = {
                                     gamma=7, n_layers=2, ff=256, dtype="bf16",
                                     lengths=[12000, 6000]),
 }
+# bf16 Eq 2 in several K splits on the big-tile kernel (float32 partials
+# summed by the set-up pass's row norm), over two layers
+CASES["bf16-split-eq2"] = dict(name="b13", seed_id=25, A=2, m=4, H=256, d=256, n_heads=4, gamma=6,
+                               n_layers=2, ff=512, dtype="bf16", lengths=[1500, 700])
 # Eq 2 with a K split count that does not divide m*H (float32, m = 3,
 # H = 2304: 6912 columns over 40 splits of 176)
 CASES["f32-uneven-splits"] = dict(name="f3", seed_id=38, A=1, m=3, H=2304, d=768, n_heads=6,
                                   gamma=5, n_layers=1, ff=256, dtype="f32", lengths=[64])
-ALL_CASES = {**CASES, **STREAMING_CASES}
+# Cases whose Eq 2 runs as one K split on the big-tile kernel, whose epilogue
+# writes Y = P * ctx_norm (bf16) and row sums; the row norm becomes the K/V
+# product's row scale and H_ctx is written only when asked for. One and two
+# 256-column tiles per row, ragged last row tiles.
+FUSED_CASES = {
+    "fused-bf16-d256": dict(name="u1", seed_id=41, A=2, m=2, H=128, d=256, n_heads=2, gamma=5,
+                            n_layers=2, ff=512, dtype="bf16", lengths=[40000, 26000]),
+    "fused-bf16-d512-hd64": dict(name="u2", seed_id=42, A=3, m=3, H=64, d=512, n_heads=8, gamma=4,
+                                 n_layers=1, ff=1024, dtype="bf16", lengths=[20000, 0, 12600]),
+}
+ALL_CASES = {**CASES, **STREAMING_CASES, **FUSED_CASES}
 
 
 def _make(case, gains="unit"):
@@ -130,6 +144,10 @@ def test_block_forward_matches_oracle(case):
     plan = B.plan_info(B.OP_BLOCK_FORWARD, dims_of(B, w), x["cu"])
     if case in STREAMING_CASES:
         assert plan["attn_streaming"] == 1 and plan["attn_chunk"] > 64, plan
+    if case in FUSED_CASES:
+        assert plan["ctx_fused_norm"] == 1, plan
+    if case == "bf16-split-eq2":
+        assert plan["ctx_fused_norm"] == 0 and plan["ctx_splits"] > 1, plan
     print(f"{case}: lengths={x['lengths'].tolist()} plan={plan}", flush=True)
     out, h, _ = _forward(w, x, h_ctx_out=True)
     tr = {}
@@ -145,7 +163,7 @@ def test_block_forward_matches_oracle(case):
         assert eh < TOL[w.dtype]
 
 
-@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-hd64-gamma8"])
+@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-hd64-gamma8", "fused-bf16-d256"])
 def test_random_gains(case):
     """Norm gains ~ U(0.5, 1.5): unit gains would hide a kernel that skips them."""
     w, x = _make(case, gains="random")
@@ -156,7 +174,7 @@ def test_random_gains(case):
     assert rel_err(h.float().cpu().numpy(), tr["C"]) < TOL[w.dtype]
 
 
-@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-hd32-gamma1"])
+@pytest.mark.parametrize("case", ["tiny-f32", "bf16-ragged-hd128", "bf16-hd32-gamma1", "fused-bf16-d512-hd64"])
 def test_ctx_fuse_matches_oracle(case):
     w, x = _make(case, gains="random")
     u = Uploaded(w, x)
@@ -208,9 +226,15 @@ def test_block_layer_in_place():
     assert torch.equal(d2, ref)
 
 
-def test_layer_chain_equals_forward():
-    """ctx_fuse + block_layer per layer + output norm reproduces block_forward."""
-    w, x = _make("bf16-hd64-gamma8", gains="random")
+@pytest.mark.parametrize("case,tol", [("bf16-split-eq2", 1e-5), ("bf16-hd64-gamma8", 5e-3)])
+def test_layer_chain_equals_forward(case, tol):
+    """ctx_fuse + block_layer per layer + output norm reproduces block_forward.
+    With Eq 2 in K splits the layers read the same stored H_ctx as the
+    forward's K/V product (1e-5). On the fused one-split path the forward's
+    K/V product takes Y = P * ctx_norm with both norms in its row scale,
+    while the layers read H_ctx = Y / rms(P) rounded to bf16 once more, so
+    the two agree to that rounding."""
+    w, x = _make(case, gains="random")
     out, h, u = _forward(w, x, h_ctx_out=True)
     dims = dims_of(B, w)
     h2 = B.ctx_fuse(dims, u.cu, u.taps, u.w_c, u.ctx_norm, cu_dev=u.cu_dev)
@@ -221,10 +245,27 @@ def test_layer_chain_equals_forward():
         D = B.block_layer(dims, u.cu, h2, D, lw, cu_dev=u.cu_dev)
     torch.cuda.synchronize()
     ref = O.rmsnorm(D.cpu().numpy().astype(np.float64), x["out_norm"], w.eps)
-    assert rel_err(out.cpu().numpy(), ref) < 1e-5
+    e = rel_err(out.cpu().numpy(), ref)
+    print(f"{case}: layer chain vs forward rel diff {e:.3e}")
+    assert e < tol
 
 
-@pytest.mark.parametrize("case", ["bf16-ragged-hd128", "bf16-16seq", "stream-bf16-hd64"])
+def test_fused_eq2_output_independent_of_h_ctx_out():
+    """On the fused Eq 2 path H_ctx is only written for the caller: the
+    block rows are bitwise the same with and without h_ctx_out, and match
+    the oracle with random gains."""
+    w, x = _make("fused-bf16-d512-hd64", gains="random")
+    a, h, u = _forward(w, x, h_ctx_out=True)
+    b, _, _ = _forward(w, x, u)
+    assert torch.equal(a, b)
+    tr = {}
+    ref = oracle_forward(O, w, x, trace=tr)
+    e, eh = rel_err(b.cpu().numpy(), ref), rel_err(h.float().cpu().numpy(), tr["C"])
+    print(f"  block_out rel err {e:.3e}, H_ctx rel err {eh:.3e}")
+    assert e < TOL["bf16"] and eh < TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", ["bf16-ragged-hd128", "bf16-16seq", "stream-bf16-hd64", "fused-bf16-d256"])
 def test_repeatable(case):
     """Repeat runs give bitwise the same H_ctx and block rows (no float
     atomics anywhere: the heads' shares are summed in a fixed order)."""
@@ -248,12 +289,13 @@ def test_varlen_equals_separate_runs():
         xb["block_in"] = x["block_in"][b:b + 1]
         wb = W.Workload(**{**w.__dict__, "A": 1})
         ob, _, _ = _forward(wb, xb)
-        # a single-sequence run may take a different GEMM tiling than the
-        # packed one (its K/V round to bf16 differently); a packing error
-        # would be O(1)
+        # a single-sequence run may take a different Eq 2 path than the
+        # packed one (split-K with a stored H_ctx, or one split with the row
+        # norm in the K/V row scale), so its K/V round to bf16 differently; a
+        # packing error would be O(1)
         e = rel_err(ob[0].cpu().numpy(), out[b].cpu().numpy())
         print(f"  sequence {b}: packed vs alone rel err {e:.2e}")
-        assert e < 1e-3, b
+        assert e < 5e-3, b
 
 
 def test_block_permutation_equivariance():

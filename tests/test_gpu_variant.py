@@ -32,6 +32,11 @@ CASES = {
     "bf16-streaming-gqa": (dict(name="v6", seed_id=106, A=1, m=1, H=64, d=512, n_heads=8, gamma=5,
                                 n_layers=1, ff=512, dtype="bf16"), [20000], 2,
                            dict(qk_norm=True, rope_theta=10000.0)),
+    # Eq 2 in one split with the fused row norm: the unnormalised context K/V
+    # take 1 / rms(P) as their row scale
+    "bf16-fused-plain": (dict(name="v7", seed_id=107, A=2, m=2, H=128, d=512, n_heads=4, gamma=5,
+                              n_layers=1, ff=1024, dtype="bf16"), [20000, 12600], 2,
+                         dict(qk_norm=True, plain_ctx_kv=True, rope_theta=10000.0)),
 }
 
 
@@ -61,6 +66,8 @@ def test_variant_forward_matches_oracle(case):
     print(f"{case}: lengths {x['lengths'].tolist()} n_kv {n_kv} {sw} plan {plan}", flush=True)
     if "streaming" in case:
         assert plan["attn_streaming"] == 1
+    if "fused" in case:
+        assert plan["ctx_fused_norm"] == 1, plan
     out = B.block_forward(dims, u.cu, u.taps, u.w_c, u.ctx_norm, u.block_in, u.block_pos, u.layers,
                           u.out_norm, cu_dev=u.cu_dev)
     torch.cuda.synchronize()
