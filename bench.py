@@ -93,7 +93,7 @@ def measured_traffic(kernel, workload):
 
 
 # rocprofv3 kernel names -> kernel kinds of the roofline (substring match)
-PMC_KINDS = (("EpiKV", "gemm_ctx_kv"), ("EpiPartial", "gemm_ctx_fuse"),
+PMC_KINDS = (("EpiKV", "gemm_ctx_kv"), ("EpiPartial", "gemm_ctx_fuse"), ("EpiNormBig", "gemm_ctx_fuse"),
              ("attn_partial_kernel", "attn_split_k"), ("attn_hsplit_kernel", "attn_split_k"))
 CALIBRATION_KERNEL = "AUnaryFunctor"   # torch.mul(src, 1.0, out=dst) of --copy-calibration
 
