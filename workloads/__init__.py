@@ -11,9 +11,13 @@ exact same values.
 Shapes, distributions and defaults follow the DFlash drafter on the page
 "mlx-bun 0.0.7 -> 0.0.9, package/src/spec/dspark/module-dflash.ts"
 (``DEFAULT_DFLASH_CONFIG`` and ``initFromDims``): weights are [in, out] and
-applied as ``x @ W``; matrices ~ N(0, 0.02); norm gains start at 1; the
-block rows are the anchor row ``anchor_emb @ tok_proj`` followed by the
-``gamma - 1`` mask-embedding rows (``#buildBlock``).
+applied as ``x @ W``; matrices ~ N(0, 0.02); norm gains start at 1. The
+block rows follow ``#buildBlock``'s shape: row 0 stands for the anchor row
+``anchor_emb @ tok_proj`` and is drawn directly from that product's
+distribution, N(0, H * 0.02^2), rather than computed (this module holds no
+arithmetic of the method; the product itself is ``dspark_block_build``,
+whose inputs ``block_build_inputs`` draws); rows 1 .. gamma-1 are the shared
+mask-embedding rows.
 """
 from __future__ import annotations
 
