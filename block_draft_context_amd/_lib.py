@@ -22,7 +22,7 @@ EXPORTS = [
     "dspark_padded_workspace_size", "dspark_block_forward_padded",
 ]
 PLAN_FIELDS = ("ctx_splits", "ctx_k_per_split", "attn_chunk", "attn_tiles", "attn_streaming",
-               "workspace_bytes", "ctx_fused_norm")
+               "workspace_bytes", "ctx_fused_norm", "ctx_tail_rows")
 
 
 QK_NORM, PLAIN_CTX_KV, GELU_FFN = 1, 2, 4   # dspark_variant bits

@@ -89,7 +89,8 @@ struct Plan {
   // workspace offsets (bytes)
   // ppart: the Eq 2 split-K partials, or with ctx.fused its Y rows; ysum: the
   // fused epilogue's row sums
-  size_t wkvt = 0, ppart = 0, ysum = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0, rowmap = 0;
+  size_t wkvt = 0, ppart = 0, ysum = 0, ptail = 0, hctx = 0, rinv = 0, kv = 0, prefix = 0, po = 0, pml = 0,
+         rowmap = 0;
   size_t D = 0, D2 = 0, Q = 0, Kd = 0, Vd = 0, E = 0, GU = 0, O = 0;
   size_t total = 0;
 };
@@ -185,6 +186,7 @@ static dspark_status make_plan(int op, const dspark_dims* dm, int32_t A, const i
   if (fused) {
     p->ppart = take((size_t)T * d * 2);
     p->ysum = take((size_t)T * (d / kCtxSumCols) * 2 * 4);
+    if (p->ctx.tail_row < T) p->ptail = take((size_t)p->ctx.tail_splits * (T - p->ctx.tail_row) * d * 4);
   } else if (runs_eq2) {
     p->ppart = take((size_t)p->ctx.splits * T * d * 4);
   }
@@ -289,6 +291,7 @@ static dspark_status run_ctx_gemm(const dspark_dims* dm, const Plan& p, const vo
     o.y = at<char>(ws, p.ppart);
     o.sums = at<float>(ws, p.ysum);
     o.g = ctx_norm;
+    if (p.ctx.tail_row < p.T) o.tail_part = at<float>(ws, p.ptail);
   } else {
     o.part = at<float>(ws, p.ppart);
   }
@@ -493,6 +496,12 @@ static void setup_eq2_role(const dspark_dims* dm, const Plan& p, const float* ct
     sa->rsum = at<float>(ws, p.ysum);
     sa->nts = dm->d / kCtxSumCols;
     sa->y = at<char>(ws, p.ppart);
+    if (p.ctx.tail_row < p.T) {
+      sa->tail_part = at<float>(ws, p.ptail);
+      sa->tail_splits = p.ctx.tail_splits;
+      sa->tail_from = p.ctx.tail_row;
+      sa->g = ctx_norm;
+    }
   } else {
     sa->part = at<float>(ws, p.ppart);
     sa->splits = p.ctx.splits;
@@ -992,7 +1001,8 @@ int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const i
   if (make_plan(op, dims, A, cu_host, &p) != DSPARK_OK) return 0;
   const bool eq2 = op == DSPARK_OP_CTX_FUSE || op == DSPARK_OP_BLOCK_FORWARD || op == DSPARK_OP_CTX_APPEND;
   const int64_t v[DSPARK_PLAN_COUNT] = {p.ctx.splits, p.ctx.k_per_split, p.chunk, p.total_chunks,
-                                        p.chunk != 64 ? 1 : 0, (int64_t)p.total, eq2 && p.ctx.fused ? 1 : 0};
+                                        p.chunk != 64 ? 1 : 0, (int64_t)p.total, eq2 && p.ctx.fused ? 1 : 0,
+                                        eq2 && p.ctx.fused ? p.T - p.ctx.tail_row : 0};
   const int k = std::min<int32_t>(n, DSPARK_PLAN_COUNT);
   for (int i = 0; i < k; ++i) out[i] = v[i];
   return k;

@@ -822,6 +822,24 @@ CtxSplit ctx_gemm_split(int dtype, int64_t M, int N, int K) {
   r.k_per_split = (int)kps;
   r.splits = (int)((K + kps - 1) / kps);
   r.fused = use_big_tiles(dtype, M, N) && r.splits == 1;
+  r.tail_row = M;
+  if (r.fused) {
+    // Tiles beyond the last whole round of kCUs: if they would fill at most
+    // half a round, their row tiles run as K splits of a few times as many
+    // workgroups (each tile of Eq 2 lasts K / 64 k-steps, so an almost empty
+    // last round costs a whole tile's time).
+    const int64_t tn = N / BG_N, tm = (M + BG_M - 1) / BG_M;
+    const int64_t rest = (tm * tn) % kCUs;   // a multiple of tn, since tn divides kCUs
+    if (rest > 0 && 2 * rest <= kCUs) {
+      int64_t ts = std::min<int64_t>(kCUs / rest, K / (4 * kFuseBK));
+      if (ts >= 2) {
+        const int64_t tkps = ((K + ts * kFuseBK - 1) / (ts * kFuseBK)) * kFuseBK;
+        r.tail_splits = (int)((K + tkps - 1) / tkps);
+        r.tail_kps = (int)tkps;
+        r.tail_row = (tm - rest / tn) * BG_M;
+      }
+    }
+  }
   return r;
 }
 
@@ -833,10 +851,20 @@ hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void
   float* out = o.part;
   trace_pre(K_GEMM_CTX, s);
   if (sp.fused) {
+    const int M1 = (int)sp.tail_row;
+    if (M1 < M && (!o.tail_part || sp.tail_splits < 2 || M1 % BG_M != 0)) return hipErrorInvalidValue;
     EpiNormBig epi{static_cast<bf16*>(o.y), o.sums, o.g};
-    dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), 1, 1);
+    dim3 grid(((M1 + BG_M - 1) / BG_M) * (N / BG_N), 1, 1);
     gemm_big_kernel<EpiNormBig, 128, kFuseBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(
-        a, static_cast<const bf16*>(Bt), M, M, N, K, kps, epi);
+        a, static_cast<const bf16*>(Bt), M1, M1, N, K, kps, epi);
+    if (M1 < M) {   // the tail rows as K splits, float32 partials
+      ASegs at = a;
+      for (int j = 0; j < a.nseg; ++j) at.seg[j] = static_cast<const bf16*>(a.seg[j]) + (int64_t)M1 * a.ld;
+      EpiPartialBig pe{o.tail_part, (int64_t)(M - M1) * N};
+      dim3 tg(((M - M1 + BG_M - 1) / BG_M) * (N / BG_N), sp.tail_splits, 1);
+      gemm_big_kernel<EpiPartialBig, 128, kFuseBK, 4, kBigWaves><<<tg, 64 * kBigWaves, 0, s>>>(
+          at, static_cast<const bf16*>(Bt), M - M1, M - M1, N, K, sp.tail_kps, pe);
+    }
   } else if (use_big_tiles(dtype, M, N)) {
     EpiPartialBig epi{out, (int64_t)M * N};
     dim3 grid(((M + BG_M - 1) / BG_M) * (N / BG_N), splits, 1);

@@ -112,6 +112,12 @@ struct SetupArgs {
   const float* rsum = nullptr;
   int nts = 0;
   const void* y = nullptr;
+  // rows [tail_from, T) of the fused path come as tail_splits float32 K
+  // partials [tail_splits][T - tail_from][d]: summed here into Y and the row
+  // scales (tail_part null: no tail)
+  const float* tail_part = nullptr;
+  int tail_splits = 0;
+  int64_t tail_from = 0;
   // cleared buffer
   float* zero = nullptr;
   int64_t zero_n = 0;
@@ -137,6 +143,12 @@ struct CtxSplit {
   // one split on the big-tile kernel: its epilogue writes Y = P * ctx_norm
   // (bf16) and per-row sums instead of float32 partials
   bool fused = false;
+  // fused, when its 256x256 tiles would leave the last round of the CUs at
+  // most half filled: rows [tail_row, M) run instead as tail_splits K splits
+  // of tail_kps columns (float32 partials), which the set-up pass sums and
+  // finishes like the fused epilogue; tail_row = M when there is no tail
+  int64_t tail_row = 0;
+  int tail_splits = 0, tail_kps = 0;
 };
 CtxSplit ctx_gemm_split(int dtype, int64_t M, int N, int K);
 // Where the Eq 2 product goes. Split-K: part[z][r][n] = sum_{k in split z}
@@ -147,6 +159,7 @@ struct CtxOut {
   void* y = nullptr;
   float* sums = nullptr;
   const float* g = nullptr;
+  float* tail_part = nullptr;   // [tail_splits][M - tail_row][N] with a fused tail
 };
 hipError_t launch_gemm_ctx(int dtype, const ASegs& a, const BMats& b, const void* Bt, const CtxOut& o,
                            int M, int N, int K, const CtxSplit& sp, hipStream_t s);

@@ -241,6 +241,71 @@ __device__ __forceinline__ void fused_h_row(const SetupArgs& a, int64_t t, int l
   }
 }
 
+// A tail row of the fused path (t >= tail_from): P = the sum of its K
+// splits, then what the fused epilogue and fused_h_row do for the other
+// rows: Y = bf16(P * g) stored for the K/V product, the row scale, and H_ctx
+// when asked for. Lane l owns the 8-column chunks l + 64 i, i < CPL.
+template <int CPL>
+__device__ __forceinline__ void fused_tail_row(const SetupArgs& a, int64_t t, int lane) {
+  const int d = a.d, nch = d / 8;
+  const int64_t Tt = a.T - a.tail_from, r = t - a.tail_from;
+  f32x4 acc[CPL][2];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < a.tail_splits; ++z) {
+    const f32x4* row = reinterpret_cast<const f32x4*>(a.tail_part + ((int64_t)z * Tt + r) * d);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = min(lane + 64 * i, nch - 1);
+      acc[i][0] += row[2 * c];
+      acc[i][1] += row[2 * c + 1];
+    }
+  }
+  const f32x4* g4 = reinterpret_cast<const f32x4*>(a.g);
+  bf16* y = static_cast<bf16*>(const_cast<void*>(a.y)) + t * d;
+  float sp = 0.f, sy = 0.f;
+  float yv[CPL][8];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      bf16x8 o;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f32x4 gv = g4[2 * c + h2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = acc[i][h2][e];
+          const bf16 q = from_f32<bf16>(p * gv[e]);
+          yv[i][4 * h2 + e] = static_cast<float>(q);
+          o[4 * h2 + e] = q;
+          sp += p * p;
+          sy += yv[i][4 * h2 + e] * yv[i][4 * h2 + e];
+        }
+      }
+      *reinterpret_cast<bf16x8*>(y + 8 * c) = o;
+    }
+  }
+  sp = wave_sum(sp);
+  sy = wave_sum(sy);
+  const float ms = sp / (float)d + a.eps;
+  const float inv_rms = rsqrtf(ms);
+  if (a.rinv && lane == 0) a.rinv[t] = a.rinv_one ? inv_rms : rsqrtf(sy / (float)d + a.eps * ms);
+  if (a.h) {
+    bf16* h = static_cast<bf16*>(a.h) + t * d;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(yv[i][e] * inv_rms);
+        *reinterpret_cast<bf16x8*>(h + 8 * c) = o;
+      }
+    }
+  }
+}
+
 // Cache row map: new row r belongs to the sequence b with ncu[b] <= r <
 // ncu[b+1] (the last b with ncu[b] <= r, which skips empty sequences) and
 // lands at slab row b * cap + pos[b] + (r - ncu[b]). One thread per row.
@@ -256,8 +321,8 @@ __device__ __forceinline__ void map_rows(const SetupArgs& a, int64_t r) {
 // Workgroup ranges, in dispatch order: [plan][map][zero][D0][prep][norm].
 // The small roles come first so that none of them lands in the grid's tail.
 struct SetupGrid {
-  int plan, map, zero, d0, prep, norm;
-  int total() const { return plan + map + zero + d0 + prep + norm; }
+  int plan, map, zero, d0, prep, norm, tail;
+  int total() const { return plan + map + zero + d0 + prep + norm + tail; }
 };
 constexpr int kZeroPerBlock = 256 * 4 * 4;   // floats cleared per workgroup
 
@@ -268,8 +333,10 @@ static SetupGrid setup_grid(const SetupArgs& a) {
   g.zero = a.zero ? (int)((a.zero_n + kZeroPerBlock - 1) / kZeroPerBlock) : 0;
   g.d0 = a.D0 ? (a.A * a.gamma + 3) / 4 : 0;
   g.prep = a.Bt ? (a.b.n_per * a.b.nmat + 3) / 4 : 0;
-  if (a.rsum) g.norm = a.h ? (int)((a.T + 3) / 4) : (int)((a.T + 255) / 256);
+  const int64_t rows = a.tail_part ? a.tail_from : a.T;   // rows of the norm role
+  if (a.rsum) g.norm = a.h ? (int)((rows + 3) / 4) : (int)((rows + 255) / 256);
   else g.norm = (a.part || a.h_in) ? (int)((a.T + 3) / 4) : 0;
+  g.tail = a.tail_part ? (int)((a.T - a.tail_from + 3) / 4) : 0;
   return g;
 }
 
@@ -315,13 +382,21 @@ __global__ __launch_bounds__(256) void setup_kernel(SetupArgs a, SetupGrid sg) {
     return;
   }
   blk -= sg.prep;
+  if (blk >= sg.norm) {   // tail rows of the fused path
+    if constexpr (sizeof(S) == 2) {
+      const int64_t t = a.tail_from + (int64_t)(blk - sg.norm) * 4 + w;
+      if (t < a.T) fused_tail_row<CPL>(a, t, lane);
+    }
+    return;
+  }
+  const int64_t rows = a.tail_part ? a.tail_from : a.T;
   if (a.rsum && !a.h) {
     const int64_t t = (int64_t)blk * 256 + threadIdx.x;
-    if (t < a.T && a.rinv) fused_rinv(a, t);
+    if (t < rows && a.rinv) fused_rinv(a, t);
     return;
   }
   const int64_t t = (int64_t)blk * 4 + w;
-  if (t >= a.T) return;
+  if (t >= rows) return;
   if (a.rsum) {
     if constexpr (sizeof(S) == 2) fused_h_row(a, t, lane);
   } else if (a.part)
@@ -345,7 +420,9 @@ hipError_t launch_fill_offsets(int32_t* cu, int A, int L, hipStream_t s) {
 
 hipError_t launch_setup(int dtype, const SetupArgs& a, hipStream_t s) {
   if (a.Bt && dtype != 1) return hipErrorInvalidValue;   // prep serves the bf16 MFMA path only
-  if (a.rsum && (dtype != 1 || (a.h && !a.y))) return hipErrorInvalidValue;   // the fused Eq 2 path is bf16
+  if (a.rsum && (dtype != 1 || !a.y)) return hipErrorInvalidValue;   // the fused Eq 2 path is bf16
+  if (a.tail_part && (!a.rsum || a.tail_splits < 1 || a.tail_from < 0 || a.tail_from > a.T || !a.g))
+    return hipErrorInvalidValue;
   const SetupGrid sg = setup_grid(a);
   if (sg.total() == 0) return hipSuccess;
   trace_pre(K_SETUP, s);

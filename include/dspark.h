@@ -228,6 +228,8 @@ typedef enum {
   DSPARK_PLAN_CTX_FUSED_NORM,     /* 1: Eq 2 in one split whose epilogue writes
                                      H_ctx * rms(P) (bf16) and row sums, with the
                                      row norm folded into the K/V row scale */
+  DSPARK_PLAN_CTX_TAIL_ROWS,      /* with it: context rows of a partly filled last
+                                     round of tiles run as K splits instead */
   DSPARK_PLAN_COUNT
 } dspark_plan_field;
 int32_t dspark_plan_info(int32_t op, const dspark_dims* dims, int32_t A, const int32_t* cu_host,

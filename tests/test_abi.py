@@ -245,6 +245,24 @@ def test_plan_fuses_the_eq2_norm_in_one_split(L):
     assert _plan(L, L.OP_CTX_APPEND, dm, [0, 131072])["ctx_fused_norm"] == 1
 
 
+def test_plan_splits_the_last_partial_round_of_eq2(L):
+    """Fused Eq 2 tiles beyond whole rounds of 256 CUs: when they would fill at
+    most half a round, their row tiles run as K splits (at most 256 / tiles,
+    and no split narrower than 4 k-tiles); whole rounds and fuller last
+    rounds keep one split."""
+    dm = _dims(L, m=4, H=2560, d=1024, n_heads=8, dtype=L.BF16)
+    for T in (16129, 20000, 131072, 131073, 184592, 200000, 245000):
+        p = _plan(L, L.OP_BLOCK_FORWARD, dm, [0, T])
+        tiles = -(-T // 256) * 4
+        rest = tiles % 256
+        want = (T - (tiles - rest) // 4 * 256) if 0 < rest <= 128 else 0
+        assert p["ctx_fused_norm"] == 1 and p["ctx_tail_rows"] == want, (T, p)
+    assert _plan(L, L.OP_BLOCK_FORWARD, dm, [0, 184592])["ctx_tail_rows"] == 4368
+    # K = m*H too small for two splits of 4 k-tiles: no tail
+    small = _dims(L, m=1, H=256, d=256, n_heads=2, dtype=L.BF16)
+    assert _plan(L, L.OP_BLOCK_FORWARD, small, [0, 66000])["ctx_tail_rows"] == 0
+
+
 def test_plan_reports_the_attention_path(L):
     """Long contexts take the streaming split-K kernel (more than 1024 64-key
     blocks over the heads), short ones the head-split kernel."""
