@@ -730,12 +730,409 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
   }
 }
 
+// The same body, persistent (one K split, an even number of k-steps): the
+// workgroup goes on to items logical + stride, logical + 2 stride, ..., and
+// the last k-steps of one tile load the first stages of the next, so the
+// next tile's operands arrive while this tile's epilogue runs. A separate
+// function: folding the tile loop into the body above changed the register
+// allocation of the single-tile kernels (the K/V tail kernel spilled, the
+// fuse GEMM ran 3% slower).
+template <class Epi, int HD, int BK, int WT, int NW>
+DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASegs a,
+                                         const bf16* __restrict__ Bt, int M, int MR, int N, int K,
+                                         int k_per_split, Epi epi, int stride) {
+  constexpr bool PERSIST = true;
+  using C = BigCfg<BK, WT, NW>;
+  constexpr int TM = C::TM, WSM = C::WSM, WSN = C::WSN, FM = C::FM, FN = C::FN;
+  static_assert(C::NST == 2, "the persistent loop hands over two stages");
+  const int tiles_m = (MR + TM - 1) / TM;
+  const int tiles_n = N / TM;
+  const int ntiles = tiles_m * tiles_n;
+  // Work items (split z, tile) are dealt to the 8 XCDs (workgroup i runs on
+  // XCD i % 8) in contiguous runs, z-major, so an XCD owns whole K slices;
+  // inside a slice, tiles go in groups of up to 4 m-tiles swept n by n, so
+  // the XCD's L2 holds a few A panels while it walks the B panels (groups of
+  // 4 measured 0.5-1% faster per forward than 8, and 16 5% slower). A
+  // persistent workgroup's items logical + i * stride (stride a multiple of
+  // 8) stay on its XCD, and the XCD's workgroups walk its run together.
+  auto decode = [&](int item, int& z_, int& m0_, int& tn_) __attribute__((always_inline)) {
+    if (total % 8 == 0) item = (item % 8) * (total / 8) + item / 8;
+    z_ = item / ntiles;
+    const int t = item % ntiles;
+    const int G = min(tiles_m, 4);
+    const int gsize = G * tiles_n;
+    const int grp = t / gsize, first_m = grp * G;
+    const int gm = min(tiles_m - first_m, G);
+    m0_ = (first_m + (t % gsize) % gm) * TM;
+    tn_ = (t % gsize) / gm;
+  };
+  int z, m0, tn;
+  decode(logical, z, m0, tn);
+  int n0 = tn * TM;
+  const int kbeg = z * k_per_split;   // z = 0 for every item
+  const int kend = min(K, kbeg + k_per_split);
+  const int nsteps = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
+  const int wm = wave / C::NWN, wn = wave % C::NWN;
+  const int r32 = lane & 31, hi = lane >> 5;
+
+  // lane i holds the address of A segment i; the loop reads it with a lane
+  // select instead of a scalar memory load, whose wait would also drain the
+  // LDS reads in flight
+  uint64_t my_seg = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSegs; ++i)
+    if (lane == i && i < a.nseg) my_seg = reinterpret_cast<uint64_t>(a.seg[i]);
+  const uint32_t seg_lo = (uint32_t)my_seg, seg_hi = (uint32_t)(my_seg >> 32);
+
+  // ---- direct global -> LDS loads of one stage (LPO for A, LPO for B per
+  // thread). A wave's load instruction fills RPI LDS rows: lane l takes row
+  // l / CPR and slot l % CPR. Each lane's byte offsets from the stage's scalar
+  // base addresses are fixed for the whole tile, so a load is one
+  // instruction on a scalar base and a 32-bit lane offset (the host
+  // guarantees the offsets fit), and the LDS destinations are scalar values.
+  const int rl = lane / C::CPR, slot = lane % C::CPR;
+  uint32_t aoff[C::LPO], boff[C::LPO];
+  auto set_offsets = [&](int m0_, int n0_) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::LPO; ++i) {
+      const int row = (i * NW + wave) * C::RPI + rl;
+      const int ch = slot ^ C::swz_f(row);
+      aoff[i] = (uint32_t)min(m0_ + row, M - 1) * (uint32_t)(a.ld * 2) + (uint32_t)(ch * 16);
+      boff[i] = (uint32_t)(n0_ + row) * (uint32_t)(K * 2) + (uint32_t)(ch * 16);
+    }
+  };
+  set_offsets(m0, n0);
+  auto issue = [&](int step, int stage) __attribute__((always_inline)) {
+    const int k0 = kbeg + step * BK;
+    const int sgi = k0 / a.seg_k;
+    const int kin = k0 - sgi * a.seg_k;
+    const uint64_t ap = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)seg_hi, sgi) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)seg_lo, sgi);
+    const char* __restrict__ abase = reinterpret_cast<const char*>(ap) + (int64_t)kin * 2;
+    const char* __restrict__ bbase = reinterpret_cast<const char*>(Bt) + (int64_t)k0 * 2;
+    char* base = smem + stage * C::STAGE + wave * C::RPI * C::ROWB;
+#pragma unroll
+    for (int i = 0; i < C::LPO; ++i)
+      lds_load16(abase + aoff[i], base + i * NW * C::RPI * C::ROWB);
+#pragma unroll
+    for (int i = 0; i < C::LPO; ++i)
+      lds_load16(bbase + boff[i], base + TM * C::ROWB + i * NW * C::RPI * C::ROWB);
+  };
+  auto read_ops = [&](int stage, int ks, bf16x8 (&av)[FM], bf16x8 (&bv)[FN]) __attribute__((always_inline)) {
+    const char* As = smem + stage * C::STAGE;
+    const char* Bs = As + TM * C::ROWB;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      av[i] = *reinterpret_cast<const bf16x8*>(As + C::swz(wm * WSM + i * 32 + r32, 2 * ks + hi));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bv[j] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * WSN + j * 32 + r32, 2 * ks + hi));
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mfma16 = [&](const bf16x8 (&av)[FM], const bf16x8 (&bv)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = Epi::kSwap
+                        ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Row scales of the K/V epilogue: one direct LDS load per lane of the
+  // first TM / 64 waves (the tile's TM rows), issued ahead of the stage
+  // loads, so they hold no registers through the main loop and are waited
+  // for with the first stage.
+  // A cache target also stages each row's slab row (the row map) the same way.
+  // Two buffers, by tile parity: a persistent workgroup loads the next
+  // tile's while this tile's epilogue reads its own.
+  int par = 0;
+  float* rsc_lds = reinterpret_cast<float*>(smem + BG_LDS);
+  int32_t* dst_lds = reinterpret_cast<int32_t*>(smem + BG_LDS + TM * 4);
+  auto load_rows = [&](int m0_, int par_) __attribute__((always_inline)) {
+    if constexpr (Epi::kKind == 1) {
+      if (nsteps > 0 && wave < TM / 64) {
+        float* rs = reinterpret_cast<float*>(smem + BG_LDS + par_ * 2 * TM * 4);
+        int32_t* ds = reinterpret_cast<int32_t*>(smem + BG_LDS + par_ * 2 * TM * 4 + TM * 4);
+        const int row = min(m0_ + wave * 64 + lane, epi.T - 1);
+        __builtin_amdgcn_global_load_lds(epi.rinv + row, (lds_ptr_t)(rs + wave * 64), 4, 0, 0);
+        if (epi.dst_row)
+          __builtin_amdgcn_global_load_lds(epi.dst_row + row, (lds_ptr_t)(ds + wave * 64), 4, 0, 0);
+      }
+    }
+  };
+  load_rows(m0, 0);
+
+  // Ring of NST stages of LPS direct loads per thread. Steps 0 .. NST-1 are
+  // loaded up front (after the row-scale load, which the first wait covers).
+  // In step s, once every wave has read its last operands of stage s % NST
+  // and stage (s+1) % NST has landed (the barrier), the loads of step s+NST
+  // go into stage s % NST. Near the end those loads repeat the last step
+  // into the freed stage (in bounds, never read), which keeps every wait
+  // count fixed; a persistent workgroup with a next tile loads that tile's
+  // first step there instead (its offsets replace this tile's, which no
+  // later load needs).
+  bool has_next = false;
+  int nm0 = 0, nn0 = 0, ntn = 0;
+  bf16x8 av0[FM], bv0[FN], av1[FM], bv1[FN];
+  auto run_step = [&](int step, auto last) __attribute__((always_inline)) {
+    const int st = step % C::NST;
+#pragma unroll
+    for (int ks = 1; ks < C::SUB; ++ks) {
+      if (ks & 1) {
+        read_ops(st, ks, av1, bv1);
+        mfma16(av0, bv0);
+      } else {
+        read_ops(st, ks, av0, bv0);
+        mfma16(av1, bv1);
+      }
+      DSPARK_BIG_SCHED_A(C::NR, C::NM);
+    }
+    // SUB is even: the last substep's operands are in av1 / bv1
+    if constexpr (!decltype(last)::value) {
+      wait_vmcnt<C::LPS * (C::NST - 2)>();
+      wait_lgkm0();
+      stage_barrier();
+      read_ops((step + 1) % C::NST, 0, av0, bv0);
+      if (step + C::NST < nsteps) {
+        issue(step + C::NST, st);
+      } else if (PERSIST && has_next) {
+        if (step + C::NST == nsteps) set_offsets(nm0, nn0);
+        issue(step + C::NST - nsteps, st);
+      } else {
+        issue(nsteps - 1, st);
+      }
+      mfma16(av1, bv1);
+      DSPARK_BIG_SCHED_ISSUE(C::NR, C::NM, C::LPS);
+    } else {
+      mfma16(av1, bv1);
+    }
+  };
+  if (nsteps > 0) {
+#pragma unroll
+    for (int st = 0; st < C::NST; ++st) issue(min(st, nsteps - 1), st);
+    wait_vmcnt<C::LPS * (C::NST - 1)>();
+    stage_barrier();
+    read_ops(0, 0, av0, bv0);
+  }
+  for (;;) {
+  if constexpr (PERSIST) {
+    has_next = logical + stride < total && nsteps >= 2;
+    if (has_next) {
+      int nz;
+      decode(logical + stride, nz, nm0, ntn);
+      nn0 = ntn * TM;
+    }
+  }
+  if (nsteps > 0) {
+    for (int step = 0; step < nsteps - 1; ++step) run_step(step, std::false_type{});
+    run_step(nsteps - 1, std::true_type{});
+    if (PERSIST && has_next) {
+      // every wave is done with the last stage: the next tile's second step
+      // goes there, and its row scales into the other buffer
+      wait_lgkm0();
+      stage_barrier();
+      issue(1, 1);
+      load_rows(nm0, par ^ 1);
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
+
+  if constexpr (Epi::kKind == 2) {
+    // Transposed accumulators, as in the K/V epilogue below: (i, j, r) of
+    // this lane is tile row wm*WSM + i*32 + lane%32 and tile column
+    // wn*WSN + j*32 + 8*(r/4) + 4*(lane/32) + r%4. Y leaves as 16-byte
+    // vectors of 8 columns of one row (lanes l and l^32 trade halves); the
+    // row sums meet in LDS past the stage ring (lanes l and l^32 first, then
+    // the NWN waves of a row block), and one thread per tile row writes them.
+    float* red = reinterpret_cast<float*>(smem + BG_LDS);   // [NWN][TM][2]
+    const int nw = n0 + wn * WSN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lr = wm * WSM + i * 32 + r32;
+      const int64_t row = (int64_t)m0 + lr;
+      float sp = 0.f, sy = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cb = nw + j * 32;
+        uint32_t P[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(epi.g + cb + 8 * q + 4 * hi);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const float p0 = acc[i][j][4 * q + 2 * x], p1 = acc[i][j][4 * q + 2 * x + 1];
+            const float y0 = static_cast<float>(from_f32<bf16>(p0 * gv[2 * x]));
+            const float y1 = static_cast<float>(from_f32<bf16>(p1 * gv[2 * x + 1]));
+            sp += p0 * p0 + p1 * p1;
+            sy += y0 * y0 + y1 * y1;
+            P[q][x] = pack_bf16x2(y0, y1);   // exact: y0, y1 are bf16 values
+          }
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
+          const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          if (row < M) st16(epi.y + row * N + cb + 8 * (qq + 2 * hi), v);
+        }
+      }
+      sp += __shfl_xor(sp, 32, kWave);
+      sy += __shfl_xor(sy, 32, kWave);
+      if (hi == 0) {
+        red[2 * (wn * TM + lr)] = sp;
+        red[2 * (wn * TM + lr) + 1] = sy;
+      }
+    }
+    wait_lgkm0();
+    stage_barrier();
+    if (tid < TM && m0 + tid < M) {
+      float sp = 0.f, sy = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NWN; ++w) {
+        sp += red[2 * (w * TM + tid)];
+        sy += red[2 * (w * TM + tid) + 1];
+      }
+      *reinterpret_cast<f32x2*>(epi.sums + 2 * ((int64_t)(m0 + tid) * (N / TM) + tn)) = f32x2{sp, sy};
+    }
+  } else if constexpr (Epi::kKind == 0) {
+    // accumulator (i, j, r) of this lane: tile row wm*WSM + i*32 + 8*(r/4) +
+    // 4*(lane/32) + r%4, tile column wn*WSN + j*32 + lane%32
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WSM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * WSN + j * 32 + (lane & 31);
+          if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
+        }
+  } else {
+    // The K/V vectors are stored non-temporally: the attention that reads
+    // them later streams about 12% faster (T = 131072 and a ragged batch;
+    // the forward 1-3% faster at T >= 8192, neutral at T = 2048).
+    // Transposed accumulators: (i, j, r) of this lane is tile row (token)
+    // wm*WSM + i*32 + lane%32 and tile column wn*WSN + j*32 + 8*(r/4) +
+    // 4*(lane/32) + r%4. After the row scale and rounding, each 32x32 block
+    // becomes 16-byte vectors of the attention layout with lane exchanges
+    // only: K (one token x 8 columns) pairs lane l with l^32, V (4 tokens x 2
+    // columns) transposes dwords among the 4 lanes of consecutive tokens.
+    // With a row map (a cache target) row r < T goes to slab row dst_row[r]
+    // and no padding rows are written; a V vector whose four rows land on
+    // four consecutive slab rows starting at a multiple of 4 is stored
+    // whole, any other as four dwords.
+    using S = std::remove_pointer_t<decltype(epi.base)>;
+    using L = KVLayout<S>;
+    static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
+    const int nw = epi.n_base + n0 + wn * WSN;   // the wave's WSN columns lie in one K or V block
+    const int layer = nw / (2 * epi.d);
+    const int kv = (nw / epi.d) & 1;
+    const int k4 = lane & 3;
+    const bool mapped = epi.dst_row != nullptr;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t tb = (int64_t)m0 + wm * WSM + i * 32;
+      const int lr = wm * WSM + i * 32;   // the block's first row within the tile
+      // padding rows (T <= row < Tpad) are written as zeros
+      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[lr + r32] : 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int w = (nw + j * 32) % epi.d;
+        const int head = w / HD, c0 = w % HD;
+        S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
+        // P[q][x]: columns 8q + 4*(lane/32) + 2x, +1 of token tb + lane%32
+        uint32_t P[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rs, acc[i][j][4 * q + 2 * x + 1] * rs);
+        if (kv == 0) {
+          const int64_t t = mapped ? (int64_t)dst_lds[lr + r32] : tb + r32;
+          const bool live = mapped ? tb + r32 < epi.T : t < epi.Tpad;
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
+            const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
+            const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+            const int g = qq + 2 * hi;
+            if (live)
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)));
+          }
+        } else {
+          const int64_t t0 = tb + (r32 & ~3);
+          const int q0 = lr + (r32 & ~3);   // the quad's first row within the tile
+#pragma unroll
+          for (int set = 0; set < 2; ++set) {
+            // a[c] = column pair 4*(2*set + c/2) + 2*(lane/32) + c%2 of this
+            // lane's token; after the transpose lane k of the quad holds pair
+            // c = k for tokens t0 .. t0+3
+            uint32_t a[4] = {P[2 * set][0], P[2 * set][1], P[2 * set + 1][0], P[2 * set + 1][1]};
+            transpose4_quad(a, k4);
+            const int p = 4 * (2 * set + (k4 >> 1)) + 2 * hi + (k4 & 1);
+            const u32x4 v = {a[0], a[1], a[2], a[3]};
+            if (!mapped) {
+              if (t0 < epi.Tpad)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)));
+            } else {
+              const int64_t d0 = dst_lds[q0];
+              const bool whole = t0 + 3 < epi.T && (d0 & 3) == 0 && dst_lds[q0 + 3] == d0 + 3;
+              if (whole) {
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(d0, c0 + 2 * p, HD)));
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (t0 + e < epi.T)
+                    __builtin_nontemporal_store(
+                        a[e], reinterpret_cast<uint32_t*>(hb + L::v_off(dst_lds[q0 + e], c0 + 2 * p, HD)));
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  if (!(PERSIST && has_next)) break;
+  // the next tile: its first two stages and row scales were requested
+  // before the epilogue above
+  logical += stride;
+  m0 = nm0;
+  n0 = nn0;
+  tn = ntn;
+  par ^= 1;
+  rsc_lds = reinterpret_cast<float*>(smem + BG_LDS + par * 2 * TM * 4);
+  dst_lds = reinterpret_cast<int32_t*>(smem + BG_LDS + par * 2 * TM * 4 + TM * 4);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  wait_vmcnt<0>();
+  stage_barrier();
+  read_ops(0, 0, av0, bv0);
+  }
+}
+
 // the stage ring, then the epilogue's own part: the tile's row scales and
 // row map (K/V) or its row sums of each column wave (Eq 2 norm); one LDS
 // object, so the compiler's tracking of direct LDS loads sees a single target
 template <class Epi, int WT, int NW>
 constexpr int big_lds_bytes() {
-  return BG_LDS + (Epi::kKind == 1 ? 2 * 64 * WT * 4 : Epi::kKind == 2 ? (NW / 2) * 64 * WT * 2 * 4 : 0);
+  return BG_LDS + (Epi::kKind == 1 ? 4 * 64 * WT * 4 : Epi::kKind == 2 ? (NW / 2) * 64 * WT * 2 * 4 : 0);
 }
 
 template <class Epi, int HD, int BK, int WT, int NW>
@@ -745,6 +1142,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_big_kernel(ASegs a, const bf16* 
   const int ntiles = ((MR + 64 * WT - 1) / (64 * WT)) * (N / (64 * WT));
   gemm_big_body<Epi, HD, BK, WT, NW>(smem, blockIdx.x + (int)gridDim.x * (int)blockIdx.y,
                                      ntiles * (int)gridDim.y, a, Bt, M, MR, N, K, k_per_split, epi);
+}
+
+// The K/V product in whole rounds of 256x256 tiles, persistent: one
+// workgroup per CU walks tiles blockIdx.x, + gridDim.x, ..., loading each next
+// tile's first two stages and row scales before the current tile's epilogue
+// (a K/V tile lasts only d / 64 k-steps, so the pipeline fill of every tile
+// is a visible share of its time).
+template <class Epi, int HD, int BK, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_kv_persistent_kernel(ASegs a, const bf16* __restrict__ Bt, int M,
+                                                                     int MR, int N, int K, Epi epi) {
+  __shared__ __attribute__((aligned(16))) char smem[big_lds_bytes<Epi, 4, NW>()];
+  const int ntiles = ((MR + 255) / 256) * (N / 256);
+  gemm_big_body_persistent<Epi, HD, BK, 4, NW>(smem, blockIdx.x, ntiles, a, Bt, M, MR, N, K, K, epi,
+                                                (int)gridDim.x);
 }
 
 // The K/V product with its partly filled last round of 256x256 tiles done as
@@ -910,14 +1321,14 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
     EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, kvd, kv.hd, kv.n_heads, 0,
                        kv.dst_row};
     const int tm = (Mrows + BG_M - 1) / BG_M;
-    if (nb * BG_N == N) {   // 256x256 tiles only
-      dim3 grid(tm * (N / BG_N), 1, 1);
+    if (nb * BG_N == N) {   // 256x256 tiles only, one persistent workgroup per CU
+      dim3 grid((unsigned)std::min<int64_t>((int64_t)tm * (N / BG_N), kCUs), 1, 1);
       if (kv.hd == 128)
-        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+        gemm_kv_persistent_kernel<EpiKVBig<bf16>, 128, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, epi);
       else if (kv.hd == 64)
-        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+        gemm_kv_persistent_kernel<EpiKVBig<bf16>, 64, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, epi);
       else
-        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+        gemm_kv_persistent_kernel<EpiKVBig<bf16>, 32, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, epi);
     } else {                // columns [0, nb * 256) in 256x256 tiles, the rest in 128x128 tiles
       const int Nb = nb * BG_N, nbig = tm * nb;
       const int nsmall = ((Mrows + 127) / 128) * ((N - Nb) / 128);
