@@ -282,10 +282,10 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
 // ---------------------------------------------------------------------------
 // Row GEMM on the matrix cores, for many block rows with bf16 weights.
 // With more rows than one 8-row pass, the vector-ALU kernel above re-reads
-// the input rows for every 8 output columns; here a workgroup owns 16 output
-// columns (SwiGLU: 16 gate and the matching 16 up columns) for 32 rows and
-// multiplies on v_mfma_f32_16x16x32_bf16. The float32 rows enter as two bf16
-// terms, hi = bf16(x) and lo = bf16(x - hi), so each product is two MFMAs
+// the input rows for every 8 output columns; here a workgroup owns CB blocks
+// of 16 output columns (SwiGLU: CB gate blocks and the matching up blocks)
+// for RB blocks of 16 rows and multiplies on v_mfma_f32_16x16x32_bf16. The
+// float32 rows enter as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi), so each product is two MFMAs
 // and the input keeps about 16 bits of mantissa (relative error <= 2^-16);
 // the weights are bf16 as stored and the sums are float32. The four waves
 // split K and keep RF_PF chunks of 32 k in flight each; their partial sums
@@ -293,8 +293,6 @@ __global__ __launch_bounds__(RG_THREADS) void rowgemm_kernel(RowGemmArgs a) {
 // 16x16x32 operand layout: lane l holds A[l % 16][8 (l / 16) .. + 8) and
 // B[8 (l / 16) .. + 8)[l % 16]; the result D[4 (l / 16) + r][l % 16], r < 4.
 // ---------------------------------------------------------------------------
-constexpr int RF_RB = 2;     // 16-row blocks per workgroup
-constexpr int RF_PF = 4;     // k chunks in flight per wave
 
 DSPARK_DEV uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, from_f32<bf16>(x)); }
 
@@ -309,9 +307,13 @@ DSPARK_DEV void split_bf16(const f32x4& x0, const f32x4& x1, bf16x8& hi, bf16x8&
   }
 }
 
-template <int PRO, int EPI>
+// RB 16-row blocks and CB 16-column blocks per workgroup (for SwiGLU, CB
+// gate blocks and the matching CB up blocks); RF_PF k chunks in flight.
+template <int PRO, int EPI, int RB, int CB>
 __global__ __launch_bounds__(256) void rowgemm_mfma_kernel(RowGemmArgs a) {
-  constexpr int NCB = EPI == RE_SWIGLU ? 2 : 1;    // 16-column blocks: gate and up for SwiGLU
+  constexpr int RF_RB = RB;
+  constexpr int RF_PF = RB * CB > 4 ? 2 : 4;
+  constexpr int NCB = EPI == RE_SWIGLU ? 2 * CB : CB;   // 16-column blocks: gate ones first for SwiGLU
   __shared__ float red[4][RF_RB][NCB][256];
   __shared__ float ssq[4][RF_RB * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -323,9 +325,10 @@ __global__ __launch_bounds__(256) void rowgemm_mfma_kernel(RowGemmArgs a) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     if constexpr (EPI == RE_SWIGLU) {
-      wrow[cb] = static_cast<const bf16*>(a.b.mat[cb]) + (int64_t)(nb * 16 + c16) * K;
+      const int half = cb / CB, n = (nb * CB + cb % CB) * 16 + c16;
+      wrow[cb] = static_cast<const bf16*>(a.b.mat[half]) + (int64_t)n * K;
     } else {
-      const int n = nb * 16 + c16;
+      const int n = (nb * CB + cb) * 16 + c16;
       wrow[cb] = static_cast<const bf16*>(a.b.mat[n / a.b.n_per]) + (int64_t)(n % a.b.n_per) * K;
     }
   }
@@ -413,24 +416,29 @@ __global__ __launch_bounds__(256) void rowgemm_mfma_kernel(RowGemmArgs a) {
   // epilogue: element q = 4 * l + r of a 16x16 block is row 4 (l / 16) + r,
   // column l % 16 of the block
 #pragma unroll
-  for (int rb = 0; rb < RF_RB; ++rb) {
+  for (int rb = 0; rb < RF_RB; ++rb)
+#pragma unroll
+  for (int cc = 0; cc < CB; ++cc) {
     const int q = tid;
     const int l = q >> 2, r = q & 3;
     const int row = 4 * (l >> 4) + r, col = l & 15;
     const int om = m_base + rb * 16 + row;
-    float v[NCB];
+    constexpr int NV = EPI == RE_SWIGLU ? 2 : 1;
+    float v[NV];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      v[cb] = (red[0][rb][cb][q] + red[1][rb][cb][q]) + (red[2][rb][cb][q] + red[3][rb][cb][q]);
+    for (int h = 0; h < NV; ++h) {
+      const int cb = cc + h * CB;
+      v[h] = (red[0][rb][cb][q] + red[1][rb][cb][q]) + (red[2][rb][cb][q] + red[3][rb][cb][q]);
+    }
     if constexpr (PRO == RP_RMSNORM) {
       const int i = rb * 16 + row;
       const float tot = (ssq[0][i] + ssq[1][i]) + (ssq[2][i] + ssq[3][i]);
       const float rs = rsqrtf(tot / (float)K + a.eps);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) v[cb] *= rs;
+      for (int h = 0; h < NV; ++h) v[h] *= rs;
     }
     if (om >= M) continue;
-    const int on = nb * 16 + col;
+    const int on = (nb * CB + cc) * 16 + col;
     if constexpr (EPI == RE_SWIGLU) {
       const float g = v[0], u = v[1];
       float act;
@@ -458,16 +466,37 @@ static bool use_rowgemm_mfma(int dtype, int epi, const RowGemmArgs& a) {
   return dtype == 1 && a.M > rowgemm_mc(a.M, a.K) && a.K % 128 == 0 && cols % 16 == 0 && a.b.n_per % 16 == 0;
 }
 
+// Workgroup shape of the matrix-core row GEMM: RB 16-row blocks by CB
+// 16-column blocks (column pairs for SwiGLU). At 80 block rows (16
+// sequences) alternating runs of a layer's four row GEMMs measured (RB, CB)
+// = (1, 2) 14% faster than (2, 1) and (2, 2) 5% faster, with (5, 1), (3, 2),
+// (1, 1) and (2, 4) no faster or slower: more workgroups with fewer rows
+// each beat fewer re-reads of the block rows. Beyond 128 rows the weights'
+// re-reads per 16-row block weigh more, so two row blocks.
+struct MfmaShape {
+  int rb, cb;
+};
+static MfmaShape rowgemm_mfma_shape(int epi, const RowGemmArgs& a) {
+  const int cols = epi == RE_SWIGLU ? a.b.n_per : a.N;
+  MfmaShape sh{a.M <= 128 ? 1 : 2, 2};
+  if (cols % (16 * sh.cb) != 0 || a.b.n_per % (16 * sh.cb) != 0) sh.cb = 1;
+  return sh;
+}
+
 hipError_t launch_rowgemm(int dtype, int pro, int epi, const RowGemmArgs& a, hipStream_t s) {
   if (use_rowgemm_mfma(dtype, epi, a)) {
-    const int nblk = (epi == RE_SWIGLU ? a.b.n_per : a.N) / 16;
-    dim3 grid(nblk, (a.M + RF_RB * 16 - 1) / (RF_RB * 16));
+    const MfmaShape sh = rowgemm_mfma_shape(epi, a);
+    const int nblk = (epi == RE_SWIGLU ? a.b.n_per : a.N) / (16 * sh.cb);
+    dim3 grid(nblk, (a.M + sh.rb * 16 - 1) / (sh.rb * 16));
     bool ok = false;
     trace_pre(K_ROWGEMM, s);
-#define DSPARK_RM(P, E)                                                       \
-    if (pro == P && epi == E) {                                               \
-      ok = true;                                                              \
-      rowgemm_mfma_kernel<P, E><<<grid, 256, 0, s>>>(a);                      \
+#define DSPARK_RM(P, E)                                                                   \
+    if (pro == P && epi == E) {                                                           \
+      ok = true;                                                                          \
+      if (sh.rb == 1 && sh.cb == 1) rowgemm_mfma_kernel<P, E, 1, 1><<<grid, 256, 0, s>>>(a); \
+      else if (sh.rb == 1) rowgemm_mfma_kernel<P, E, 1, 2><<<grid, 256, 0, s>>>(a);        \
+      else if (sh.cb == 1) rowgemm_mfma_kernel<P, E, 2, 1><<<grid, 256, 0, s>>>(a);        \
+      else rowgemm_mfma_kernel<P, E, 2, 2><<<grid, 256, 0, s>>>(a);                        \
     }
     DSPARK_RM(RP_RMSNORM, RE_QKV)
     DSPARK_RM(RP_NONE, RE_RESID)
