@@ -216,6 +216,33 @@ def test_block_layer_matches_oracle_and_keeps_context(case):
     assert e < TOL[w.dtype]
 
 
+@pytest.mark.parametrize("case", ["stream-bf16-hd128-gamma1", "stream-bf16-hd64", "bf16-ragged-hd128"])
+def test_attention_error_isolated(case):
+    """The attention's own error: with W_o = I and W_down = 0 a layer returns
+    D + Attn, so (out - D) is the attention output after the Q/K/V
+    projections, the bf16 K/V storage and, on the streaming path, the bf16
+    products of Q with K and of the softmax weights with V. It is compared
+    elementwise-normwise with the oracle's float64 attention over the same
+    stored context."""
+    w, x = _make(case, gains="random")
+    lw = dict(x["layers"][0])
+    lw["wo"] = np.eye(w.d, dtype=np.float32)
+    lw["w_down"] = np.zeros_like(lw["w_down"])
+    x = dict(x)
+    x["layers"] = [lw] + x["layers"][1:]
+    u = Uploaded(w, x)
+    C = _storage(w, O.ctx_fuse(x["taps"], x["w_c"], x["ctx_norm"], w.eps))
+    D = O.block_init(x["block_in"], x["block_pos"]).astype(np.float32)
+    h = torch.from_numpy(C).to(device="cuda:0", dtype=u.dt)
+    out = B.block_layer(dims_of(B, w), u.cu, h, torch.from_numpy(D).to("cuda:0"), u.layers[0], cu_dev=u.cu_dev)
+    torch.cuda.synchronize()
+    attn = out.cpu().numpy().astype(np.float64) - D
+    ref = O.block_layer(C, x["cu"], D, lw, w.n_heads, w.eps) - D.astype(np.float64)
+    e, ee = rel_err(attn, ref), elem_rel_err(attn, ref)
+    print(f"{case}: attention rel err {e:.3e} (elementwise {ee:.3e})")
+    assert e < 1e-2
+
+
 def test_block_layer_in_place():
     """d_out may alias d_in: the same block rows, bit for bit."""
     w, x = _make("bf16-ragged-hd128")
