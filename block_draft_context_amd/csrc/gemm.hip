@@ -1020,19 +1020,13 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
           if (row < M) epi.out[z * epi.split_stride + (int64_t)row * N + col] = acc[i][j][r];
         }
   } else {
-    // The K/V vectors are stored non-temporally: the attention that reads
-    // them later streams about 12% faster (T = 131072 and a ragged batch;
-    // the forward 1-3% faster at T >= 8192, neutral at T = 2048).
-    // Transposed accumulators: (i, j, r) of this lane is tile row (token)
-    // wm*WSM + i*32 + lane%32 and tile column wn*WSN + j*32 + 8*(r/4) +
-    // 4*(lane/32) + r%4. After the row scale and rounding, each 32x32 block
-    // becomes 16-byte vectors of the attention layout with lane exchanges
-    // only: K (one token x 8 columns) pairs lane l with l^32, V (4 tokens x 2
-    // columns) transposes dwords among the 4 lanes of consecutive tokens.
-    // With a row map (a cache target) row r < T goes to slab row dst_row[r]
-    // and no padding rows are written; a V vector whose four rows land on
-    // four consecutive slab rows starting at a multiple of 4 is stored
-    // whole, any other as four dwords.
+    // The K/V epilogue of the single-tile body (see there), with the
+    // addresses of the packed (unmapped) target split into a per-lane 32-bit
+    // byte offset inside a head slab, fixed per row block, and a wave-uniform
+    // head base: a store then costs no 64-bit address arithmetic. A head slab
+    // of the packed workspace holds Tpad * HD elements, under 4 GiB because
+    // H_ctx (T * d >= Tpad * HD elements, checked on the host) is. A cache
+    // target (row map) keeps the general form.
     using S = std::remove_pointer_t<decltype(epi.base)>;
     using L = KVLayout<S>;
     static_assert(sizeof(S) == 2 && L::R == 4, "bf16 K/V layout");
@@ -1041,63 +1035,118 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
     const int kv = (nw / epi.d) & 1;
     const int k4 = lane & 3;
     const bool mapped = epi.dst_row != nullptr;
+    if (!mapped) {
+      const int w0 = nw - (2 * layer + kv) * epi.d;   // the wave's first column in its K or V block
+      constexpr int KG = 128 / HD;
+      // lane parts of the K and V offsets (elements), independent of the row block
+      const uint32_t k_lane = (uint32_t)hi * 1024u;
+      const uint32_t v_lane = 32u * (uint32_t)(k4 >> 1) + 16u * (uint32_t)hi + 8u * (uint32_t)(k4 & 1);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t tb = (int64_t)m0 + wm * WSM + i * 32;
-      const int lr = wm * WSM + i * 32;   // the block's first row within the tile
-      // padding rows (T <= row < Tpad) are written as zeros
-      const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[lr + r32] : 0.f;
+      for (int i = 0; i < FM; ++i) {
+        const int tb = m0 + wm * WSM + i * 32;
+        const int lr = wm * WSM + i * 32;
+        const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[lr + r32] : 0.f;
+        const int t = tb + r32;                 // K: this lane's token
+        const int t0 = tb + (r32 & ~3);         // V: the token quad of this lane
+        const int kk = t0 & 63;
+        const uint32_t kofs = (uint32_t)(t >> 6) * (HD * 64u) + (uint32_t)(t & 63) * 8u + k_lane;
+        const uint32_t vofs = (uint32_t)(t0 >> 6) * (HD * 64u) +
+                              (uint32_t)((kk / (KG * 4)) * 64 + ((kk / 4) % KG) * (HD / 2)) * 8u + v_lane;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int w = (nw + j * 32) % epi.d;
-        const int head = w / HD, c0 = w % HD;
-        S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
-        // P[q][x]: columns 8q + 4*(lane/32) + 2x, +1 of token tb + lane%32
-        uint32_t P[4][2];
+        for (int j = 0; j < FN; ++j) {
+          const int w = w0 + j * 32;
+          const int head = w / HD, c0 = w % HD;
+          S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
+          uint32_t P[4][2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int x = 0; x < 2; ++x)
-            P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rs, acc[i][j][4 * q + 2 * x + 1] * rs);
-        if (kv == 0) {
-          const int64_t t = mapped ? (int64_t)dst_lds[lr + r32] : tb + r32;
-          const bool live = mapped ? tb + r32 < epi.T : t < epi.Tpad;
+            for (int x = 0; x < 2; ++x)
+              P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rs, acc[i][j][4 * q + 2 * x + 1] * rs);
+          if (kv == 0) {
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
-            // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
-            const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
-            const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-            const int g = qq + 2 * hi;
-            if (live)
-              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)));
-          }
-        } else {
-          const int64_t t0 = tb + (r32 & ~3);
-          const int q0 = lr + (r32 & ~3);   // the quad's first row within the tile
+            for (int qq = 0; qq < 2; ++qq) {
+              const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
+              const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+              S* base = hb + (c0 / 8 + qq) * 512;   // wave-uniform
+              if (t < epi.Tpad)
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + (size_t)(kofs * 2u)));
+            }
+          } else {
 #pragma unroll
-          for (int set = 0; set < 2; ++set) {
-            // a[c] = column pair 4*(2*set + c/2) + 2*(lane/32) + c%2 of this
-            // lane's token; after the transpose lane k of the quad holds pair
-            // c = k for tokens t0 .. t0+3
-            uint32_t a[4] = {P[2 * set][0], P[2 * set][1], P[2 * set + 1][0], P[2 * set + 1][1]};
-            transpose4_quad(a, k4);
-            const int p = 4 * (2 * set + (k4 >> 1)) + 2 * hi + (k4 & 1);
-            const u32x4 v = {a[0], a[1], a[2], a[3]};
-            if (!mapped) {
+            for (int set = 0; set < 2; ++set) {
+              uint32_t a[4] = {P[2 * set][0], P[2 * set][1], P[2 * set + 1][0], P[2 * set + 1][1]};
+              transpose4_quad(a, k4);
+              const u32x4 v = {a[0], a[1], a[2], a[3]};
+              S* base = hb + c0 * 4 + 64 * set;       // wave-uniform
               if (t0 < epi.Tpad)
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)));
-            } else {
-              const int64_t d0 = dst_lds[q0];
-              const bool whole = t0 + 3 < epi.T && (d0 & 3) == 0 && dst_lds[q0 + 3] == d0 + 3;
-              if (whole) {
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(d0, c0 + 2 * p, HD)));
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + (size_t)(vofs * 2u)));
+            }
+          }
+        }
+      }
+    } else {
+  #pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t tb = (int64_t)m0 + wm * WSM + i * 32;
+        const int lr = wm * WSM + i * 32;   // the block's first row within the tile
+        // padding rows (T <= row < Tpad) are written as zeros
+        const float rs = (nsteps > 0 && tb + r32 < epi.T) ? rsc_lds[lr + r32] : 0.f;
+  #pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int w = (nw + j * 32) % epi.d;
+          const int head = w / HD, c0 = w % HD;
+          S* hb = epi.base + L::head_base(layer, kv, head, epi.n_heads, epi.Tpad, HD);
+          // P[q][x]: columns 8q + 4*(lane/32) + 2x, +1 of token tb + lane%32
+          uint32_t P[4][2];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+  #pragma unroll
+            for (int x = 0; x < 2; ++x)
+              P[q][x] = pack_bf16x2(acc[i][j][4 * q + 2 * x] * rs, acc[i][j][4 * q + 2 * x + 1] * rs);
+          if (kv == 0) {
+            const int64_t t = mapped ? (int64_t)dst_lds[lr + r32] : tb + r32;
+            const bool live = mapped ? tb + r32 < epi.T : t < epi.Tpad;
+  #pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              // lanes < 32 finish column group qq of 8, lanes >= 32 group qq + 2
+              const auto s0 = __builtin_amdgcn_permlane32_swap(P[qq][0], P[qq + 2][0], false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(P[qq][1], P[qq + 2][1], false, false);
+              const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+              const int g = qq + 2 * hi;
+              if (live)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::k_off(t, c0 + 8 * g, HD)));
+            }
+          } else {
+            const int64_t t0 = tb + (r32 & ~3);
+            const int q0 = lr + (r32 & ~3);   // the quad's first row within the tile
+  #pragma unroll
+            for (int set = 0; set < 2; ++set) {
+              // a[c] = column pair 4*(2*set + c/2) + 2*(lane/32) + c%2 of this
+              // lane's token; after the transpose lane k of the quad holds pair
+              // c = k for tokens t0 .. t0+3
+              uint32_t a[4] = {P[2 * set][0], P[2 * set][1], P[2 * set + 1][0], P[2 * set + 1][1]};
+              transpose4_quad(a, k4);
+              const int p = 4 * (2 * set + (k4 >> 1)) + 2 * hi + (k4 & 1);
+              const u32x4 v = {a[0], a[1], a[2], a[3]};
+              if (!mapped) {
+                if (t0 < epi.Tpad)
+                  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(t0, c0 + 2 * p, HD)));
               } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  if (t0 + e < epi.T)
-                    __builtin_nontemporal_store(
-                        a[e], reinterpret_cast<uint32_t*>(hb + L::v_off(dst_lds[q0 + e], c0 + 2 * p, HD)));
+                const int64_t d0 = dst_lds[q0];
+                const bool whole = t0 + 3 < epi.T && (d0 & 3) == 0 && dst_lds[q0 + 3] == d0 + 3;
+                if (whole) {
+                  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(hb + L::v_off(d0, c0 + 2 * p, HD)));
+                } else {
+  #pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    if (t0 + e < epi.T)
+                      __builtin_nontemporal_store(
+                          a[e], reinterpret_cast<uint32_t*>(hb + L::v_off(dst_lds[q0 + e], c0 + 2 * p, HD)));
+                }
               }
             }
           }
@@ -1321,7 +1370,18 @@ hipError_t launch_gemm_kv(int dtype, const void* h_ctx, const BMats& b, const vo
     EpiKVBig<bf16> epi{static_cast<bf16*>(kv.base), rinv, kv.Tpad, kv.T, kvd, kv.hd, kv.n_heads, 0,
                        kv.dst_row};
     const int tm = (Mrows + BG_M - 1) / BG_M;
-    if (nb * BG_N == N) {   // 256x256 tiles only, one persistent workgroup per CU
+    // 256x256 tiles only, one persistent workgroup per CU; its packed-target
+    // stores take 32-bit byte offsets inside a head slab of Tpad * hd elements
+    const bool slab32 = kv.dst_row || (uint64_t)kv.Tpad * kv.hd * 2 < ((uint64_t)1 << 32);
+    if (nb * BG_N == N && !slab32) {
+      dim3 grid(tm * (N / BG_N), 1, 1);
+      if (kv.hd == 128)
+        gemm_big_kernel<EpiKVBig<bf16>, 128, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+      else if (kv.hd == 64)
+        gemm_big_kernel<EpiKVBig<bf16>, 64, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+      else
+        gemm_big_kernel<EpiKVBig<bf16>, 32, kKvBK, 4, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, d, epi);
+    } else if (nb * BG_N == N) {
       dim3 grid((unsigned)std::min<int64_t>((int64_t)tm * (N / BG_N), kCUs), 1, 1);
       if (kv.hd == 128)
         gemm_kv_persistent_kernel<EpiKVBig<bf16>, 128, kKvBK, kBigWaves><<<grid, 64 * kBigWaves, 0, s>>>(a, B, M, Mrows, N, d, epi);
