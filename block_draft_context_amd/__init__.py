@@ -5,7 +5,8 @@ ABI of include/dspark.h); this package is its Python binding.
 """
 from .api import (DraftCache, DsparkDims, DsparkError, PreparedForward, block_build,  # noqa: F401
                   block_forward, block_forward_padded,
-                  block_layer, block_layer_noalloc, cache_bytes, markov_draft, prepared_append,
+                  block_layer, block_layer_noalloc, cache_bytes, markov_draft, markov_workspace_size,
+                  padded_workspace_size, prepared_append,
                   prepared_propose,
                   ctx_fuse, kernel_names, plan_info, trace_begin, trace_end, version,
                   workspace_size)

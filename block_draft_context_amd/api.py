@@ -343,6 +343,24 @@ def block_build(dims: DsparkDims, anchor_emb, tok_proj, mask_emb, *, block_in=No
     return block_in
 
 
+def padded_workspace_size(dims: DsparkDims, A: int, L_ctx: int) -> int:
+    """Workspace bytes of block_forward_padded (dspark_padded_workspace_size)."""
+    dm = dims.c()
+    n = L.lib().dspark_padded_workspace_size(ctypes.byref(dm), A, L_ctx)
+    if n == 0:
+        raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+    return int(n)
+
+
+def markov_workspace_size(dims: DsparkDims, A: int, vocab: int, rank: int) -> int:
+    """Workspace bytes of markov_draft (dspark_markov_workspace_size)."""
+    dm = dims.c()
+    n = L.lib().dspark_markov_workspace_size(ctypes.byref(dm), A, vocab, rank)
+    if n == 0:
+        raise DsparkError(L.EINVAL, L.lib().dspark_last_error().decode(errors="replace"))
+    return int(n)
+
+
 def block_forward_padded(dims: DsparkDims, taps, L_ctx: int, ctx_mask, w_c, ctx_norm, block_in,
                          block_pos, layers, out_norm=None, *, h_ctx_out=None, block_out=None,
                          ws=None, stream=None) -> torch.Tensor:
