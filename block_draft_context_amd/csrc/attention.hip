@@ -165,6 +165,46 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   // the sequence's keys; this tile owns every nt-th of its 64-key blocks
   const int64_t k0 = tr.s0, k1 = tr.s1;
 
+  // query head h reads the K/V of head h / (n_heads / n_kv) (grouped K/V heads)
+  const int kvh = h / (n_heads / n_kv);
+  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, kvh, n_kv, Tpad, HD);
+  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, kvh, n_kv, Tpad, HD);
+
+  // The sequence's 64-key blocks blk0 .. blk1 are dealt to its nt tiles in
+  // turn, and a tile's to its four waves in turn: wave w of tile c takes
+  // blocks blk0 + c + (w + 4i) nt. The workgroups of one head thus read one
+  // window of consecutive blocks at a time instead of nt separate streams,
+  // which keeps the HBM accesses local. A block's K (NKV vectors) and V (NLD
+  // vectors) live in registers; the next block's K is requested as soon as
+  // the scores are done and its V as soon as P.V is done, so each load's
+  // latency hides behind the other half's arithmetic. On the wave's last
+  // block the "next" loads repeat that block (in bounds, unused), which keeps
+  // every wait count static. The first block's loads are issued before the
+  // queries are staged, so the two latencies overlap (a wave of a short
+  // context has only one block).
+  const int64_t blk0 = k0 >> 6, blk1 = k1 > k0 ? (k1 - 1) >> 6 : blk0 - 1;
+  const int64_t bstep = 4 * (int64_t)tr.nt;
+  const int64_t first = blk0 + tr.c + (int64_t)wave * tr.nt;
+  const bool any = first <= blk1;
+  u32x4 kreg[NKV], vreg[NLD];
+  auto load_k = [&](int64_t blk) __attribute__((always_inline)) {
+    const S* kp = Kh + blk * 64 * HD + lane * E;
+#pragma unroll
+    for (int i = 0; i < NKV; ++i) kreg[i] = ld16(kp + i * 64 * E);
+  };
+  // V is read once per layer: non-temporal loads (measured 5% faster per
+  // forward at T = 131072 and on a ragged 16-sequence batch; marking K as
+  // well was faster on the first and slower on the second)
+  auto load_v = [&](int64_t blk) __attribute__((always_inline)) {
+    const S* vp = Vh + blk * 64 * HD + lane * E;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 64 * E));
+  };
+  if (any) {
+    load_k(first);
+    load_v(first);
+  }
   const int d = HD * n_heads;
   if constexpr (kDot2) {
     for (int i = tid; i < G * HD / 2; i += 256) {
@@ -180,11 +220,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   __syncthreads();
 
-  // query head h reads the K/V of head h / (n_heads / n_kv) (grouped K/V heads)
-  const int kvh = h / (n_heads / n_kv);
-  const S* __restrict__ Kh = kv_base + L::head_base(layer, 0, kvh, n_kv, Tpad, HD);
-  const S* __restrict__ Vh = kv_base + L::head_base(layer, 1, kvh, n_kv, Tpad, HD);
-
   float m_run[G], l_run[G];
   float o[G][2];
 #pragma unroll
@@ -195,38 +230,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
   const int kg = lane / (HD / 2), cp = lane % (HD / 2);
 
-  // The sequence's 64-key blocks blk0 .. blk1 are dealt to its nt tiles in
-  // turn, and a tile's to its four waves in turn: wave w of tile c takes
-  // blocks blk0 + c + (w + 4i) nt. The workgroups of one head thus read one
-  // window of consecutive blocks at a time instead of nt separate streams,
-  // which keeps the HBM accesses local. A block's K (NKV vectors) and V (NLD
-  // vectors) live in registers; the next block's K is requested as soon as
-  // the scores are done and its V as soon as P.V is done, so each load's
-  // latency hides behind the other half's arithmetic. On the wave's last
-  // block the "next" loads repeat that block (in bounds, unused), which keeps
-  // every wait count static.
-  const int64_t blk0 = k0 >> 6, blk1 = k1 > k0 ? (k1 - 1) >> 6 : blk0 - 1;
-  const int64_t bstep = 4 * (int64_t)tr.nt;
-  const int64_t first = blk0 + tr.c + (int64_t)wave * tr.nt;
-  if (first <= blk1) {
+  if (any) {
     const int64_t last = first + ((blk1 - first) / bstep) * bstep;
-    u32x4 kreg[NKV], vreg[NLD];
-    auto load_k = [&](int64_t blk) __attribute__((always_inline)) {
-      const S* kp = Kh + blk * 64 * HD + lane * E;
-#pragma unroll
-      for (int i = 0; i < NKV; ++i) kreg[i] = ld16(kp + i * 64 * E);
-    };
-    // V is read once per layer: non-temporal loads (measured 5% faster per
-    // forward at T = 131072 and on a ragged 16-sequence batch; marking K as
-    // well was faster on the first and slower on the second)
-    auto load_v = [&](int64_t blk) __attribute__((always_inline)) {
-      const S* vp = Vh + blk * 64 * HD + lane * E;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * 64 * E));
-    };
-    load_k(first);
-    load_v(first);
     for (int64_t blk = first; blk <= last; blk += bstep) {
       const int64_t nxt = min(blk + bstep, last);
       // ---- scores: lane owns key blk*64 + lane
