@@ -929,10 +929,16 @@ static dspark_status markov_plan(const dspark_dims* dims, int32_t A, int32_t voc
     return fail(DSPARK_EUNSUPPORTED, "rank %d must be a multiple of 64 in [64, 16256]", rank);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const int P = markov_grid(dims->dtype, vocab, rank).P;
-  mp->E1 = take((size_t)A * rank * 4);
-  mp->pv = take((size_t)A * P * 4);
-  mp->pi = take((size_t)A * P * 4);
+  const MarkovGrid mg = markov_grid(dims->dtype, vocab, rank, A);
+  const int P = mg.P;
+  if (mg.mfma) {
+    // two positions' (value, index) partials; the kernels read w1 rows directly
+    mp->pv = take((size_t)2 * A * P * 8);
+  } else {
+    mp->E1 = take((size_t)A * rank * 4);
+    mp->pv = take((size_t)A * P * 4);
+    mp->pi = take((size_t)A * P * 4);
+  }
   mp->total = off;
   return DSPARK_OK;
 }

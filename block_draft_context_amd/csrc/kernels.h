@@ -282,8 +282,9 @@ struct MarkovArgs {
   int32_t* tokens = nullptr;           // [A][gamma]
   float* conf = nullptr;               // [A][gamma]
   float* logits = nullptr;             // [A][gamma][vocab]: the draft logits
-  float* E1 = nullptr;                 // workspace [A][rank]
-  float* part_v = nullptr;             // workspace [A][markov_grid(...).P]
+  float* E1 = nullptr;                 // workspace [A][rank] (the row-GEMM path only)
+  float* part_v = nullptr;             // workspace [A][markov_grid(...).P]; the matrix-core
+                                       // path: [2][A][P] (value, index) pairs
   int32_t* part_i = nullptr;
 };
 // Vocabulary chunks of one position: P chunks of `chunk` rows, each reduced
@@ -293,7 +294,7 @@ struct MarkovGrid {
   int P = 0, chunk = 0;
   bool mfma = false;
 };
-MarkovGrid markov_grid(int dtype, int vocab, int rank);
+MarkovGrid markov_grid(int dtype, int vocab, int rank, int A);
 hipError_t launch_markov(int dtype, const MarkovArgs& a, hipStream_t s);
 
 }  // namespace dspark

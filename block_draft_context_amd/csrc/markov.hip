@@ -10,15 +10,18 @@
 //   token_k  = argmax logits_k                (the lowest index among equal maxima)
 //   conf_k   = sigmoid([block[b, k], e1] . conf_w + conf_b)
 // and prev = token_k. The positions depend on each other through the token,
-// so the loop runs position by position, all sequences together. A position
-// is two launches:
-//   the logits, which stream all of w2 once: with bf16 weights and a rank up
-//   to 512, markov_logits_kernel multiplies on the matrix cores and also
-//   reduces its vocabulary chunk to (max, index) partials; otherwise the
-//   weight-streaming row GEMM of block.hip (the base logits as its residual)
-//   followed by markov_argmax_kernel;
-//   markov_final_kernel, which picks the token from the partials, computes
-//   the confidence and gathers the next position's embedding rows.
+// so the loop runs position by position, all sequences together.
+// With bf16 weights and a rank up to 512 a position is one launch,
+// markov_step_kernel: every workgroup first reduces the previous position's
+// (max, index) partials of its sequences to their tokens (the anchors at
+// position 0); all but one then gather those tokens' rows of w1 and stream
+// w2 once on the matrix cores, writing the draft logits and their own
+// vocabulary chunk's partials, while the last writes the tokens and the
+// position's confidences. markov_last_kernel turns the last position's
+// partials into its tokens. Otherwise (float32, larger ranks) a position is the weight-
+// streaming row GEMM of block.hip (the base logits as its residual),
+// markov_argmax_kernel and markov_final_kernel (token, confidence, next
+// embedding rows), after markov_embed_kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -127,79 +130,183 @@ __global__ __launch_bounds__(256) void markov_final_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Logits and argmax partials of one position on v_mfma_f32_16x16x32_bf16.
-// The A operand is 16 vocabulary rows of w2 (lane l: row l % 16, ranks
-// 8 (l / 16) + 32 s .. + 8), the B operand the embeddings of 16 sequences
-// (lane l: sequence l % 16, the same ranks). The embeddings are rows of the
-// bf16 w1 held in float32, so their bf16 form is exact; the products are
-// exact and the sums float32. The result D[4 (l / 16) + r][l % 16] is the
-// logit of vocabulary row 4 (l / 16) + r for sequence l % 16: a lane holds
-// four consecutive logits of one sequence, stored as one 16-byte vector.
-// Grid (P, ceil(A / 16)): workgroup p owns vocabulary rows
-// [p * chunk, min(vocab, (p + 1) * chunk)) for 16 sequences, so w2 is read
-// once per 16 sequences. Its four waves take 16-row groups in batches of G,
-// with all of a batch's weight loads in flight before the first product.
+// One drafted position k on v_mfma_f32_16x16x32_bf16, grid (P + 1,
+// ceil(A / 16)); column y serves sequences 16 y .. 16 y + 15.
+// Workgroups p < P stream the vocabulary rows [p * chunk, min(vocab, (p + 1)
+// * chunk)) of w2 for those 16 sequences, so w2 is read once per 16
+// sequences. The A operand is 16 rows of w2 (lane l: row l % 16, ranks
+// 8 (l / 16) + 32 s .. + 8), the B operand the Markov embeddings of the 16
+// sequences (lane l: sequence l % 16, the same ranks), read straight from the
+// bf16 w1 rows of their previous tokens; the products are exact and the sums
+// float32. D[4 (l / 16) + r][l % 16] is the logit of row 4 (l / 16) + r for
+// sequence l % 16: a lane holds four consecutive logits of one sequence,
+// stored as one 16-byte vector. The four waves take 16-row groups in batches
+// of G; a wave's first batch of weight loads is issued before the previous
+// tokens are known, so its latency overlaps theirs. Each workgroup writes
+// the (max, index) of its chunk per sequence.
+// Workgroup p = P writes the tokens of position k-1 and the confidences of
+// position k of the column's sequences and streams nothing.
 // ---------------------------------------------------------------------------
 struct MarkovStep {
+  const bf16* w1 = nullptr;       // [vocab][rank]
   const bf16* w2 = nullptr;       // [vocab][rank]
-  const float* E1 = nullptr;      // [A][rank]
+  const int32_t* anchor = nullptr;   // position 0: the previous tokens
+  const int2* prev = nullptr;     // position k > 0: position k-1's partials [A][P] (value bits, index)
+  int2* part = nullptr;           // this position's partials [A][P]
   const float* base = nullptr;    // base_logits + k * vocab, row stride ld
   float* logits = nullptr;        // draft logits + k * vocab, row stride ld
-  float* pv = nullptr;            // [A][P]
-  int32_t* pi = nullptr;
+  const float* block = nullptr;   // [A][gamma][d]
+  const float* conf_w = nullptr;  // [d + rank]
+  const float* conf_b = nullptr;  // [1]
+  int32_t* tokens = nullptr;      // [A][gamma]
+  float* conf = nullptr;          // [A][gamma]
   int64_t ld = 0;
-  int A = 0, vocab = 0, rank = 0, chunk = 0;
+  int A = 0, vocab = 0, rank = 0, chunk = 0, P = 0, k = 0, gamma = 0, d = 0;
 };
 
 template <int KS> constexpr int markov_groups() { return KS <= 4 ? 4 : KS <= 8 ? 2 : 1; }
 
+DSPARK_DEV int clamp_token(int t, int vocab) { return min(max(t, 0), vocab - 1); }
+
+// tok[j] = the previous token of sequence y0 + j (j < 16): its anchor at
+// position 0, else the argmax over position k-1's P partials; token 0 past
+// A. A column with n sequences gives each 256 / 2^ceil(log2 n) threads.
+DSPARK_DEV void markov_prev_tokens(const MarkovStep& a, int y0, int* tok, int2* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(16, a.A - y0);
+  if (a.k == 0) {
+    if (tid < 16) tok[tid] = tid < n ? clamp_token(a.anchor[y0 + tid], a.vocab) : 0;
+    __syncthreads();
+    return;
+  }
+  const int lg = n <= 1 ? 0 : n <= 2 ? 1 : n <= 4 ? 2 : n <= 8 ? 3 : 4;
+  const int tps = 256 >> lg, j = tid >> (8 - lg), q = tid & (tps - 1);
+  float best = -__builtin_inff();
+  int bi = a.vocab;
+  if (j < n) {
+    // 16 loads in flight per round; indices past P repeat the last pair,
+    // which cannot change the result
+    const int2* pp = a.prev + (int64_t)(y0 + j) * a.P;
+    for (int i0 = q; i0 < a.P; i0 += 16 * tps) {
+      int2 e[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) e[u] = pp[min(i0 + u * tps, a.P - 1)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) arg_better(best, bi, __int_as_float(e[u].x), e[u].y);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    if (off < tps) {   // uniform
+      const float v2 = __shfl_xor(best, off, kWave);
+      const int i2 = __shfl_xor(bi, off, kWave);
+      arg_better(best, bi, v2, i2);
+    }
+  }
+  if (tps <= 64) {
+    if (q == 0 && j < n) tok[j] = clamp_token(bi, a.vocab);
+  } else {
+    // a sequence spans tps / 64 waves
+    if (lane == 0) red[wave] = make_int2(__float_as_int(best), bi);
+    __syncthreads();
+    if (tid < n) {
+      const int wpj = tps >> 6;
+      best = __int_as_float(red[tid * wpj].x);
+      bi = red[tid * wpj].y;
+      for (int w = 1; w < wpj; ++w) arg_better(best, bi, __int_as_float(red[tid * wpj + w].x), red[tid * wpj + w].y);
+      tok[tid] = clamp_token(bi, a.vocab);
+    }
+  }
+  if (tid >= n && tid < 16) tok[tid] = 0;
+  __syncthreads();
+}
+
+// Workgroup P of a column: the tokens of position k-1 and the confidences
+// sigmoid([block[b, k], w1[prev]] . conf_w + conf_b) of position k; wave w
+// takes sequences w, w + 4, w + 8, w + 12.
+DSPARK_DEV void markov_duty(const MarkovStep& a, int y0, int* tok, int2* red) {
+  markov_prev_tokens(a, y0, tok, red);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(16, a.A - y0);
+  if (a.k > 0 && tid < n) a.tokens[(int64_t)(y0 + tid) * a.gamma + a.k - 1] = tok[tid];
+  for (int j = wave; j < n; j += 4) {
+    const int b = y0 + j;
+    const float* brow = a.block + ((int64_t)b * a.gamma + a.k) * a.d;
+    const bf16* erow = a.w1 + (int64_t)tok[j] * a.rank;
+    float z = 0.f;
+#pragma unroll 4
+    for (int i = 4 * lane; i < a.d; i += 256) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(brow + i);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(a.conf_w + i);
+      z = fmaf(x[0], c[0], z);
+      z = fmaf(x[1], c[1], z);
+      z = fmaf(x[2], c[2], z);
+      z = fmaf(x[3], c[3], z);
+    }
+#pragma unroll 4
+    for (int i = lane; i < a.rank; i += 64) z = fmaf(static_cast<float>(erow[i]), a.conf_w[a.d + i], z);
+    z = wave_sum(z);
+    if (lane == 0) a.conf[(int64_t)b * a.gamma + a.k] = 1.f / (1.f + expf(-(z + a.conf_b[0])));
+  }
+}
+
 template <int KS>
-__global__ __launch_bounds__(256) void markov_logits_kernel(MarkovStep a) {
+__global__ __launch_bounds__(256) void markov_step_kernel(MarkovStep a) {
   constexpr int G = markov_groups<KS>();
   __shared__ float sv[4][16];
   __shared__ int si[4][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int tok[16];
+  __shared__ int2 red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kg = lane >> 4;
-  const int p = blockIdx.x, P = gridDim.x;
-  const int b = blockIdx.y * 16 + c16;
+  const int p = blockIdx.x;
+  const int y0 = blockIdx.y * 16;
+  if (p == a.P) {   // uniform
+    markov_duty(a, y0, tok, red);
+    return;
+  }
+  const int b = y0 + c16;
   const bool bok = b < a.A;
   const int v_begin = p * a.chunk, v_end = min(a.vocab, v_begin + a.chunk);
   const int ng = (v_end - v_begin + 15) >> 4;    // 16-row groups of this chunk
-
-  bf16x8 eb[KS];
-  {
-    const float* er = a.E1 + (int64_t)min(b, a.A - 1) * a.rank + 8 * kg;   // sequences past A: unused
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(er + 32 * s);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(er + 32 * s + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        eb[s][e] = from_f32<bf16>(x0[e]);
-        eb[s][e + 4] = from_f32<bf16>(x1[e]);
-      }
-    }
-  }
   const float* brow = a.base + (int64_t)min(b, a.A - 1) * a.ld;
   float* lrow = a.logits + (int64_t)min(b, a.A - 1) * a.ld;
 
-  float best = -__builtin_inff();
-  int bi = a.vocab;
-  for (int g0 = wave * G; g0 < ng; g0 += 4 * G) {
-    bf16x8 wv[G][KS];
-    f32x4 bl[G];
+  // Loads past the chunk (or of sequences past A) read valid addresses and
+  // their results are never stored: the weight row is clamped to the last
+  // one and the logit offset to the chunk's last four (v_end % 4 == 0).
+  bf16x8 wv[G][KS];
+  f32x4 bl[G];
+  auto load_w = [&](int g0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int row = min(v_begin + (g0 + g) * 16 + c16, a.vocab - 1);   // past the chunk: a valid row, unused
+      const int row = min(v_begin + (g0 + g) * 16 + c16, a.vocab - 1);
       const bf16* wr = a.w2 + (int64_t)row * a.rank + 8 * kg;
 #pragma unroll
       for (int s = 0; s < KS; ++s) wv[g][s] = *reinterpret_cast<const bf16x8*>(wr + 32 * s);
     }
+  };
+  auto load_base = [&](int g0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int vo = v_begin + (g0 + g) * 16 + 4 * kg;   // v_end % 4 == 0: all four or none in range
-      bl[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (bok && g0 + g < ng && vo < v_end) bl[g] = *reinterpret_cast<const f32x4*>(brow + vo);
+    for (int g = 0; g < G; ++g)
+      bl[g] = *reinterpret_cast<const f32x4*>(brow + min(v_begin + (g0 + g) * 16 + 4 * kg, v_end - 4));
+  };
+  load_w(wave * G);
+  markov_prev_tokens(a, y0, tok, red);
+  bf16x8 eb[KS];
+  {
+    const bf16* er = a.w1 + (int64_t)tok[c16] * a.rank + 8 * kg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) eb[s] = *reinterpret_cast<const bf16x8*>(er + 32 * s);
+  }
+  load_base(wave * G);
+
+  float best = -__builtin_inff();
+  int bi = a.vocab;
+  for (int g0 = wave * G; g0 < ng; g0 += 4 * G) {
+    if (g0 != wave * G) {
+      load_w(g0);
+      load_base(g0);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -229,25 +336,51 @@ __global__ __launch_bounds__(256) void markov_logits_kernel(MarkovStep a) {
   __syncthreads();
   if (wave == 0 && kg == 0) {
     for (int w = 1; w < 4; ++w) arg_better(best, bi, sv[w][c16], si[w][c16]);
-    if (bok) {
-      a.pv[(int64_t)b * P + p] = best;
-      a.pi[(int64_t)b * P + p] = bi;
-    }
+    if (bok) a.part[(int64_t)b * a.P + p] = make_int2(__float_as_int(best), bi);
+  }
+}
+
+// The last position's tokens from its partials; one workgroup per sequence.
+__global__ __launch_bounds__(256) void markov_last_kernel(const int2* __restrict__ part, int P, int k, int gamma,
+                                                          int vocab, int32_t* __restrict__ tokens) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float best = -__builtin_inff();
+  int bi = vocab;
+#pragma unroll 8
+  for (int q = tid; q < P; q += 256) {
+    const int2 e = part[(int64_t)b * P + q];
+    arg_better(best, bi, __int_as_float(e.x), e.y);
+  }
+  wave_argmax(best, bi);
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) arg_better(best, bi, sv[w], si[w]);
+    tokens[(int64_t)b * gamma + k] = clamp_token(bi, vocab);
   }
 }
 
 static bool markov_mfma(int dtype, int rank) { return dtype == 1 && rank % 64 == 0 && rank <= 512; }
 
-static int markov_rows_per_wg(int dtype, int rank) {
+// Vocabulary rows per workgroup. The matrix-core step kernel's workgroups
+// each read the previous position's partials of up to 16 sequences, so with
+// more sequences they take longer chunks (fewer partials).
+static int markov_rows_per_wg(int dtype, int rank, int A) {
   if (!markov_mfma(dtype, rank)) return 2048;
   const int ks = rank / 32;
   const int G = ks <= 4 ? 4 : ks <= 8 ? 2 : 1;
-  return 64 * G;
+  const int seqs = std::min(A, 16);
+  return 64 * G * (seqs <= 2 ? 1 : seqs <= 8 ? 2 : 4);
 }
 
-MarkovGrid markov_grid(int dtype, int vocab, int rank) {
+MarkovGrid markov_grid(int dtype, int vocab, int rank, int A) {
   // one chunk per workgroup; at most 2048 chunks (the partials per sequence)
-  const int64_t unit = markov_rows_per_wg(dtype, rank);
+  const int64_t unit = markov_rows_per_wg(dtype, rank, A);
   const int64_t need = (vocab + 2047) / 2048;
   const int64_t chunk = std::max(unit, (need + unit - 1) / unit * unit);
   MarkovGrid g;
@@ -258,8 +391,55 @@ MarkovGrid markov_grid(int dtype, int vocab, int rank) {
 }
 
 hipError_t launch_markov(int dtype, const MarkovArgs& a, hipStream_t s) {
-  const MarkovGrid mg = markov_grid(dtype, a.vocab, a.rank);
+  const MarkovGrid mg = markov_grid(dtype, a.vocab, a.rank, a.A);
   const int P = mg.P;
+  const int64_t ld = (int64_t)a.gamma * a.vocab;
+  const int64_t pstride = (int64_t)a.A * P;   // one position's partials; two buffers, by parity
+  hipError_t e = hipSuccess;
+  if (mg.mfma) {
+    int2* part = reinterpret_cast<int2*>(a.part_v);   // [2][A][P] pairs, alternating by position
+    for (int k = 0; k < a.gamma; ++k) {
+      MarkovStep st;
+      st.w1 = static_cast<const bf16*>(a.w1);
+      st.w2 = static_cast<const bf16*>(a.w2);
+      st.anchor = a.anchor;
+      st.prev = part + (int64_t)((k + 1) & 1) * pstride;
+      st.part = part + (int64_t)(k & 1) * pstride;
+      st.base = a.base_logits + (int64_t)k * a.vocab;
+      st.logits = a.logits + (int64_t)k * a.vocab;
+      st.block = a.block;
+      st.conf_w = a.conf_w;
+      st.conf_b = a.conf_b;
+      st.tokens = a.tokens;
+      st.conf = a.conf;
+      st.ld = ld;
+      st.A = a.A;
+      st.vocab = a.vocab;
+      st.rank = a.rank;
+      st.chunk = mg.chunk;
+      st.P = P;
+      st.k = k;
+      st.gamma = a.gamma;
+      st.d = a.d;
+      const dim3 grid(P + 1, (a.A + 15) / 16);
+      trace_pre(K_MARKOV, s);
+      switch (a.rank / 32) {
+#define DSPARK_MK(KS) \
+        case KS: markov_step_kernel<KS><<<grid, 256, 0, s>>>(st); break;
+        DSPARK_MK(2) DSPARK_MK(4) DSPARK_MK(6) DSPARK_MK(8) DSPARK_MK(10) DSPARK_MK(12) DSPARK_MK(14) DSPARK_MK(16)
+#undef DSPARK_MK
+        default: return hipErrorInvalidValue;
+      }
+      trace_post(K_MARKOV, s);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int kl = a.gamma - 1;
+    trace_pre(K_MARKOV, s);
+    markov_last_kernel<<<a.A, 256, 0, s>>>(part + (int64_t)(kl & 1) * pstride, P, kl, a.gamma, a.vocab, a.tokens);
+    trace_post(K_MARKOV, s);
+    return hipGetLastError();
+  }
   trace_pre(K_MARKOV, s);
   if (dtype == 1)
     markov_embed_kernel<bf16><<<a.A, 256, 0, s>>>(static_cast<const bf16*>(a.w1), a.vocab, a.rank, a.anchor, a.E1);
@@ -267,61 +447,35 @@ hipError_t launch_markov(int dtype, const MarkovArgs& a, hipStream_t s) {
     markov_embed_kernel<float><<<a.A, 256, 0, s>>>(static_cast<const float*>(a.w1), a.vocab, a.rank, a.anchor,
                                                    a.E1);
   trace_post(K_MARKOV, s);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ld = (int64_t)a.gamma * a.vocab;
   for (int k = 0; k < a.gamma; ++k) {
-    if (mg.mfma) {
-      // logits_k = base_logits[:, k] + E1 . w2^T into draft_logits[:, k], and the partials
-      MarkovStep st;
-      st.w2 = static_cast<const bf16*>(a.w2);
-      st.E1 = a.E1;
-      st.base = a.base_logits + (int64_t)k * a.vocab;
-      st.logits = a.logits + (int64_t)k * a.vocab;
-      st.pv = a.part_v;
-      st.pi = a.part_i;
-      st.ld = ld;
-      st.A = a.A;
-      st.vocab = a.vocab;
-      st.rank = a.rank;
-      st.chunk = mg.chunk;
-      const dim3 grid(P, (a.A + 15) / 16);
-      trace_pre(K_MARKOV, s);
-      switch (a.rank / 32) {
-#define DSPARK_MK(KS) \
-        case KS: markov_logits_kernel<KS><<<grid, 256, 0, s>>>(st); break;
-        DSPARK_MK(2) DSPARK_MK(4) DSPARK_MK(6) DSPARK_MK(8) DSPARK_MK(10) DSPARK_MK(12) DSPARK_MK(14) DSPARK_MK(16)
-#undef DSPARK_MK
-        default: return hipErrorInvalidValue;
-      }
-    } else {
-      // logits_k = base_logits[:, k] + E1 . w2^T, into draft_logits[:, k]
-      RowGemmArgs r{};
-      r.X = a.E1;
-      r.ldx = a.rank;
-      r.M = a.A;
-      r.K = a.rank;
-      r.N = a.vocab;
-      r.b.mat[0] = a.w2;
-      r.b.n_per = a.vocab;
-      r.b.nmat = 1;
-      r.res = a.base_logits + (int64_t)k * a.vocab;
-      r.out = a.logits + (int64_t)k * a.vocab;
-      r.ldo = (int)ld;   // gamma * vocab < 2^31 (checked on the host)
-      e = launch_rowgemm(dtype, RP_NONE, RE_RESID, r, s);
-      if (e != hipSuccess) return e;
-      trace_pre(K_MARKOV, s);
-      markov_argmax_kernel<<<dim3(P, a.A), 256, 0, s>>>(a.logits + (int64_t)k * a.vocab, ld, a.vocab, mg.chunk,
-                                                       a.part_v, a.part_i);
-    }
+    // logits_k = base_logits[:, k] + E1 . w2^T, into draft_logits[:, k]
+    RowGemmArgs r{};
+    r.X = a.E1;
+    r.ldx = a.rank;
+    r.M = a.A;
+    r.K = a.rank;
+    r.N = a.vocab;
+    r.b.mat[0] = a.w2;
+    r.b.n_per = a.vocab;
+    r.b.nmat = 1;
+    r.res = a.base_logits + (int64_t)k * a.vocab;
+    r.out = a.logits + (int64_t)k * a.vocab;
+    r.ldo = (int)ld;   // gamma * vocab < 2^31 (checked on the host)
+    e = launch_rowgemm(dtype, RP_NONE, RE_RESID, r, s);
+    if (e != hipSuccess) return e;
+    trace_pre(K_MARKOV, s);
+    markov_argmax_kernel<<<dim3(P, a.A), 256, 0, s>>>(a.logits + (int64_t)k * a.vocab, ld, a.vocab, mg.chunk,
+                                                     a.part_v, a.part_i);
     if (dtype == 1)
       markov_final_kernel<bf16><<<a.A, 256, 0, s>>>(a.part_v, a.part_i, P, k, a.gamma, a.d, a.vocab, a.rank,
-                                                   a.block, a.conf_w, a.conf_b,
-                                                   static_cast<const bf16*>(a.w1), a.E1, a.tokens, a.conf);
+                                                    a.block, a.conf_w, a.conf_b,
+                                                    static_cast<const bf16*>(a.w1), a.E1, a.tokens, a.conf);
     else
       markov_final_kernel<float><<<a.A, 256, 0, s>>>(a.part_v, a.part_i, P, k, a.gamma, a.d, a.vocab, a.rank,
-                                                    a.block, a.conf_w, a.conf_b,
-                                                    static_cast<const float*>(a.w1), a.E1, a.tokens, a.conf);
+                                                     a.block, a.conf_w, a.conf_b,
+                                                     static_cast<const float*>(a.w1), a.E1, a.tokens, a.conf);
     trace_post(K_MARKOV, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
