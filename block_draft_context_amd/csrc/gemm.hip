@@ -831,21 +831,27 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
       bv[j] = *reinterpret_cast<const bf16x8*>(Bs + C::swz(wn * WSN + j * 32 + r32, 2 * ks + hi));
   };
 
+  // A tile's first MFMAs take a zero accumulator instead of the previous
+  // tile's values, so no instructions clear the accumulators between tiles.
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto mfma16 = [&](const bf16x8 (&av)[FM], const bf16x8 (&bv)[FN]) __attribute__((always_inline)) {
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = Epi::kSwap
-                        ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0)
-                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  auto mfma16 = [&](const bf16x8 (&av)[FM], const bf16x8 (&bv)[FN], auto fresh) __attribute__((always_inline)) {
+    constexpr f32x16 zero = {};
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const f32x16 c = decltype(fresh)::value ? zero : acc[i][j];
+        acc[i][j] = Epi::kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], c, 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], c, 0, 0, 0);
+      }
   };
 
   // Row scales of the K/V epilogue: one direct LDS load per lane of the
@@ -884,16 +890,19 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
   bool has_next = false;
   int nm0 = 0, nn0 = 0, ntn = 0;
   bf16x8 av0[FM], bv0[FN], av1[FM], bv1[FN];
-  auto run_step = [&](int step, auto last) __attribute__((always_inline)) {
+  auto run_step = [&](int step, auto last, auto first) __attribute__((always_inline)) {
     const int st = step % C::NST;
 #pragma unroll
     for (int ks = 1; ks < C::SUB; ++ks) {
       if (ks & 1) {
         read_ops(st, ks, av1, bv1);
-        mfma16(av0, bv0);
+        if (ks == 1 && decltype(first)::value)
+          mfma16(av0, bv0, std::true_type{});
+        else
+          mfma16(av0, bv0, std::false_type{});
       } else {
         read_ops(st, ks, av0, bv0);
-        mfma16(av1, bv1);
+        mfma16(av1, bv1, std::false_type{});
       }
       DSPARK_BIG_SCHED_A(C::NR, C::NM);
     }
@@ -911,10 +920,10 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
       } else {
         issue(nsteps - 1, st);
       }
-      mfma16(av1, bv1);
+      mfma16(av1, bv1, std::false_type{});
       DSPARK_BIG_SCHED_ISSUE(C::NR, C::NM, C::LPS);
     } else {
-      mfma16(av1, bv1);
+      mfma16(av1, bv1, std::false_type{});
     }
   };
   if (nsteps > 0) {
@@ -933,9 +942,16 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
       nn0 = ntn * TM;
     }
   }
+  if (nsteps > 1) {
+    run_step(0, std::false_type{}, std::true_type{});
+    for (int step = 1; step < nsteps - 1; ++step) run_step(step, std::false_type{}, std::false_type{});
+    run_step(nsteps - 1, std::true_type{}, std::false_type{});
+  } else if (nsteps == 1) {
+    run_step(0, std::true_type{}, std::true_type{});
+  } else {
+    zero_acc();
+  }
   if (nsteps > 0) {
-    for (int step = 0; step < nsteps - 1; ++step) run_step(step, std::false_type{});
-    run_step(nsteps - 1, std::true_type{});
     if (PERSIST && has_next) {
       // every wave is done with the last stage: the next tile's second step
       // goes there, and its row scales into the other buffer
@@ -1164,12 +1180,6 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
   par ^= 1;
   rsc_lds = reinterpret_cast<float*>(smem + BG_LDS + par * 2 * TM * 4);
   dst_lds = reinterpret_cast<int32_t*>(smem + BG_LDS + par * 2 * TM * 4 + TM * 4);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   wait_vmcnt<0>();
   stage_barrier();
   read_ops(0, 0, av0, bv0);
