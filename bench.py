@@ -218,6 +218,33 @@ def _time_calls(torch, call, stream, steps, warmup=3):
     return sorted(a.elapsed_time(b) for a, b in ev)
 
 
+def bench_library_gemms(torch, w, steps):
+    """Calibration, not the product: torch.matmul (hipBLASLt) on the two
+    context products of the workload (the Eq 2 projection T x (m*H) -> d and
+    the K/V of all layers T x d -> 2*N*d) on seeded bf16 operands, with plain
+    bf16 output and none of the norms, row scales or attention layout, timed
+    with HIP events on torch's stream. It marks what a tuned general GEMM
+    reaches on the same shapes and part."""
+    T = int(W.context_lengths(w).sum())
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(7)
+    out = {"workload": w.name, "T": T}
+    for name, (M, K, N) in (("gemm_ctx_fuse", (T, w.m * w.H, w.d)),
+                            ("gemm_ctx_kv", (T, w.d, 2 * w.n_layers * w.d))):
+        a = torch.randn(M, K, dtype=torch.bfloat16, device="cuda:0", generator=gen)
+        b = torch.randn(N, K, dtype=torch.bfloat16, device="cuda:0", generator=gen)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+        bt = b.t()
+        t = _time_calls(torch, lambda: torch.matmul(a, bt, out=y), torch.cuda.current_stream(), steps)
+        ms = t[len(t) // 2]
+        tflops = 2.0 * M * K * N / ms / 1e9
+        out[name] = {"m_k_n": [M, K, N], "ms_median": round(ms, 4), "ms_min": round(t[0], 4),
+                     "tflops": round(tflops, 1), "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+        del a, b, y, bt
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_markov(B, torch, steps, vocab=131072, rank=256, gamma=5, d=1024, batches=(1, 16)):
     """The greedy draft loop after the backbone (dspark_markov_draft) for the
     5-position block of the d = 1024 drafter with a Markov rank of 256 (the
@@ -331,6 +358,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain elementwise copy of BYTES bytes (3 launches), the "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="no forward: time torch.matmul (hipBLASLt) on the workload's two context "
+                         "products with plain bf16 output, a calibration of what a tuned library "
+                         "GEMM reaches on the same shapes, and print it as one JSON line")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no run: turn the counter_collection.csv files of two rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE) of this script into profiles/hbm_traffic.json")
@@ -345,6 +376,10 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.library_gemms:
+        print(json.dumps({"library_gemms": bench_library_gemms(torch, W.get_workload(args.workload),
+                                                               max(args.steps, 5))}))
+        return
     import block_draft_context_amd as B
     from gpu_helpers import Uploaded, dims_of
 
