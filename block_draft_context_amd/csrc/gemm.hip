@@ -358,19 +358,25 @@ DSPARK_DEV void wait_vmcnt() {
 DSPARK_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 // Each k-step is one scheduling region per k-substep (NM MFMAs). The MFMAs
-// of a substep run with the NR operand reads of the next one interleaved; in
-// the last region, after the stage barrier, with the reads of the next
-// step's first substep and the NL direct loads of the stage NST steps ahead.
-#define DSPARK_BIG_SCHED_A(NR, NM)                                                         \
+// of a substep run with the NR operand reads of the next one interleaved,
+// each read behind an MFMA, so that the wait for a substep's operands never
+// covers a read issued just before it; in the last region, after the stage
+// barrier, with the reads of the next step's first substep and the NL direct
+// loads of the stage NST steps ahead. FRONT puts all the reads behind the
+// first half of the MFMAs (two per MFMA where there are more reads than
+// half the MFMAs), which leaves more MFMAs to cover the last read; measured
+// 6% faster for the K/V product and 1.5% slower for the Eq 2 product than
+// one read per MFMA.
+#define DSPARK_BIG_SCHED_A(NR, NM, FRONT)                                                  \
   do {                                                                                     \
-    constexpr int kPairs = (NR) < (NM) ? (NR) : (NM);                                     \
-    _Pragma("unroll") for (int q = 0; q < kPairs; ++q) {                                   \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+    constexpr int kHalf = (FRONT) ? ((NM) / 2 > 0 ? (NM) / 2 : 1) : (NM);                  \
+    constexpr int kPer = ((NR) + kHalf - 1) / kHalf;                                       \
+    constexpr int kGroups = ((NR) + kPer - 1) / kPer;                                      \
+    _Pragma("unroll") for (int q = 0; q < kGroups; ++q) {                                  \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);                                \
     }                                                                                      \
-    _Pragma("unroll") for (int q = kPairs; q < (NR); ++q)                                  \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
-    _Pragma("unroll") for (int q = kPairs; q < (NM); ++q)                                  \
+    _Pragma("unroll") for (int q = kGroups; q < (NM); ++q)                                 \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
   } while (0)
 // The first quarter of the MFMAs (at least one) with the operand reads, the
@@ -545,7 +551,7 @@ DSPARK_DEV void gemm_big_body(char* smem, int logical, int total, ASegs a, const
         read_ops(st, ks, av0, bv0);
         mfma16(av1, bv1);
       }
-      DSPARK_BIG_SCHED_A(C::NR, C::NM);
+      DSPARK_BIG_SCHED_A(C::NR, C::NM, Epi::kKind == 1);
     }
     // SUB is even: the last substep's operands are in av1 / bv1
     if constexpr (!decltype(last)::value) {
@@ -904,7 +910,7 @@ DSPARK_DEV void gemm_big_body_persistent(char* smem, int logical, int total, ASe
         read_ops(st, ks, av0, bv0);
         mfma16(av1, bv1, std::false_type{});
       }
-      DSPARK_BIG_SCHED_A(C::NR, C::NM);
+      DSPARK_BIG_SCHED_A(C::NR, C::NM, Epi::kKind == 1);
     }
     // SUB is even: the last substep's operands are in av1 / bv1
     if constexpr (!decltype(last)::value) {
