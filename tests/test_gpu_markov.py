@@ -98,9 +98,11 @@ def test_markov_draft_matches_oracle(dtype):
 # (A, gamma, vocab, rank): more than 16 sequences (two sequence groups of the
 # matrix-core step kernel), every rank class it instantiates up to 512
 # with ragged last vocabulary chunks, ranks above 512 (the row-GEMM path),
-# and the measured size (1 and 16 sequences, vocabulary 131072, rank 256)
+# the measured size (1 and 16 sequences, vocabulary 131072, rank 256) and a
+# one-position block
 SHAPES = [(20, 5, 5000, 256), (3, 4, 4104, 512), (17, 3, 3000, 192), (1, 5, 2056, 64),
-          (2, 2, 1000, 576), (33, 2, 808, 320), (16, 5, 131072, 256), (1, 5, 131072, 256)]
+          (2, 2, 1000, 576), (33, 2, 808, 320), (16, 5, 131072, 256), (1, 5, 131072, 256),
+          (4, 1, 1000, 128)]
 
 
 @pytest.mark.parametrize("A,G,V,r", SHAPES, ids=[f"A{a}-g{g}-V{v}-r{r}" for a, g, v, r in SHAPES])
