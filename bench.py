@@ -147,6 +147,16 @@ def write_traffic(fetch_csv, write_csv, workload, copy_bytes):
     print(json.dumps(rec[workload], indent=1))
 
 
+def run_environment(B, torch):
+    """What the line was measured on: device, software versions, host."""
+    props = torch.cuda.get_device_properties(0)
+    model, _ = host_cpu()
+    return {"device": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+            "torch": torch.__version__, "library": B.version(), "host_cpu": model,
+            "host_threads": len(os.sched_getaffinity(0))}
+
+
 def host_cpu():
     """The host CPU model and the threads the oracle's BLAS uses."""
     model = "unknown"
@@ -483,6 +493,7 @@ def main():
         res["incremental"] = bench_incremental(B, torch, max(args.steps, 20))
     if not args.no_markov:
         res["markov"] = bench_markov(B, torch, max(args.steps, 20))
+    res["env"] = run_environment(B, torch)
     print(json.dumps(res), flush=True)
 
 
