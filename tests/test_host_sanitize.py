@@ -4,7 +4,7 @@ UndefinedBehaviorSanitizer, and exercised on the CPU by
 tests/sanitize/abi_driver.c over a grid of problem sizes, invalid
 arguments and workspaces one byte short of the reported size. The
 sanitizers instrument the host pass only (the device code is compiled as
-usual and never runs), and the driver makes no call that reaches the GPU."""
+usual and never runs), and the test program makes no call that reaches the GPU."""
 import os
 import shutil
 import subprocess
@@ -44,7 +44,7 @@ def test_abi_host_code_under_asan_and_ubsan(tmp_path):
                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     assert r.returncode == 0, r.stdout.decode(errors="replace")[-3000:]
     exe = str(tmp_path / "abi_driver")
-    # the driver carries the sanitizer runtimes the library's host code calls into
+    # the test program carries the sanitizer runtimes the library's host code calls into
     r = subprocess.run([CLANG, "-O1", "-g", "-std=c11", "-fsanitize=address,undefined",
                         "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
                         "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "sanitize", "abi_driver.c"),
